@@ -1,0 +1,184 @@
+"""Benchmark of the L3 layer forward on one MI355X.
+
+One step = plan (sort by id, segments, work items) + forward (segment
+softmax-aggregate, W_up projection, LayerNorm, W_mix projection) of one
+batch, all resident in HBM before timing starts. Default workload: the
+large-prefill configuration (65536 tokens, vocab 131072, 2^22-row budget,
+d = 2048, d_e = 512, bf16 inputs, float32 accumulation and output).
+
+Prints one JSON line. `roofline` is the gather/aggregate kernel (seg_fwd):
+algorithmic bytes per launch (each distinct id's K_t and V_t rows once, x
+read, a written, ids and segment records) over its mean launch time taken
+from HIP events recorded around it on its own stream during the timed
+steps. `cpu_baseline` is the fp64 oracle on a bounded sample of the same
+batch on the host CPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "L3 layer fwd tokens/sec + achieved HBM GB/s of K/V gather vs peak, bf16"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def algorithmic_bytes(w, plan) -> dict:
+    """Bytes the gather/aggregate step must move, per launch."""
+    e = 2 if w.spec.dtype == "bf16" else 4
+    d, d_e, B = w.spec.d, w.spec.d_e, w.batch
+    n = np.asarray(plan["seg_n"], np.int64)
+    table = int(n.sum()) * (d + d_e) * e
+    x_read = B * d * e
+    a_write = B * d_e * e
+    misc = B * 4 + plan["S"] * 16
+    return dict(total=table + x_read + a_write + misc, table=table,
+                x=x_read, a=a_write, misc=misc)
+
+
+def gemm_flops(w) -> dict:
+    B, d, d_e = w.batch, w.spec.d, w.spec.d_e
+    return dict(up_proj=2.0 * B * d * d_e, mix_proj=2.0 * B * d * 2 * d)
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The oracle (as it stands) on a bounded sample of the batch."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import l3_oracle
+    from static_token_routed_id_amd import workloads as wl
+    dd = wl.decoded(w)
+    args = [dd[k] for k in ("x", "ids", "K", "V", "offsets", "W_up", "gamma",
+                            "beta", "W_mix")]
+    rng = np.random.default_rng(1234)
+    order = rng.permutation(w.batch)
+    with threadpool_limits(limits=1):
+        n = 16
+        t0 = time.perf_counter()
+        l3_oracle.forward(*args, tokens=order[:n])
+        dt = time.perf_counter() - t0
+        n = int(min(w.batch, max(16, budget_s / max(dt / 16, 1e-6))))
+        t0 = time.perf_counter()
+        l3_oracle.forward(*args, tokens=order[:n])
+        dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} tokens drawn at random (seed 1234) from the "
+                      f"{w.batch}-token batch, full layer forward in float64, "
+                      f"one thread, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="large_prefill_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the oracle baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not "
+              "supported (this build runs on a single MI355X)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from static_token_routed_id_amd import _lib as L
+    from static_token_routed_id_amd import workloads as wl
+    from static_token_routed_id_amd.layer import L3Layer, to_device
+
+    t_gen = time.time()
+    w = wl.make(args.workload)
+    print(f"# generated {args.workload} in {time.time() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    dtype = L.L3_BF16 if w.spec.dtype == "bf16" else L.L3_F32
+    desc = L.make_desc(w.spec.vocab, w.rows, w.spec.d, w.spec.d_e,
+                       w.spec.k_max, dtype, L.L3_F32)
+    dev = {k: to_device(getattr(w, k)) for k in
+           ("x", "K", "V", "W_up", "gamma", "beta", "W_mix")}
+    ids = torch.from_numpy(w.ids).cuda()
+    offsets = torch.from_numpy(w.offsets).cuda()
+    params = [dev[k] for k in ("x", "K", "V", "W_up", "gamma", "beta",
+                               "W_mix")]
+    layer = L3Layer(desc, w.batch)
+    y = torch.empty((w.batch, w.spec.d), dtype=torch.float32, device="cuda")
+    layer.make_plan(ids, offsets)
+    assert L.l3_plan_check(layer.plan) == L.L3_OK
+    plan_np = L.l3_plan_export(layer.plan)
+
+    def step():
+        layer.make_plan(ids, offsets)
+        layer.forward(*params, y=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    L.l3_timing_read(layer.plan)          # drop warm-up events
+    L.l3_timing_enable(layer.plan, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.l3_timing_enable(layer.plan, False)
+    stages = L.l3_timing_read(layer.plan)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = w.batch * args.steps / (t1 - t0)
+
+    ab = algorithmic_bytes(w, plan_np)
+    seg_ms, seg_n = stages["seg_fwd"]
+    seg_avg_ms = seg_ms / max(seg_n, 1)
+    achieved = ab["total"] / (seg_avg_ms * 1e-3) / 1e9
+    fl = gemm_flops(w)
+    stage_avg = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in stages.items()
+                 if v[1]}
+    mfma = {}
+    for k in ("up_proj", "mix_proj"):
+        if k in stage_avg and stage_avg[k] > 0:
+            tf = fl[k] / (stage_avg[k] * 1e-3) / 1e12
+            mfma[k] = {"tflops": round(tf, 1),
+                       "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFS, 4)}
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.spec.dtype,
+        "data": "synthetic (seeded Zipf ids and allocation, Gaussian tables "
+                "and weights)",
+        "config": {"workload": w.spec.name, "tokens": w.batch,
+                   "vocab": w.spec.vocab, "table_rows": w.rows,
+                   "d": w.spec.d, "d_e": w.spec.d_e, "k_max": w.spec.k_max,
+                   "distinct_ids": int(plan_np["S"])},
+        "roofline": {"kernel": "seg_fwd", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "algorithmic_bytes_per_launch": ab["total"],
+                     "avg_launch_ms": round(seg_avg_ms, 4)},
+        "stage_ms": {k: round(v, 4) for k, v in stage_avg.items()},
+        "mfma": mfma,
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

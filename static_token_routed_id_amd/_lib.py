@@ -1,0 +1,239 @@
+"""ctypes binding of libl3 (include/l3.h), with the C entry points' names.
+
+Argument marshalling only: tensors become device pointers, the stream is the
+current torch stream, and a non-zero status raises L3Error. Every step of the
+computation runs in the HIP library. If libl3.so is missing this module
+raises at import: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import (POINTER, Structure, byref, c_char_p, c_double, c_float,
+                    c_int, c_int32, c_int64, c_size_t, c_void_p)
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libl3.so")
+
+L3_OK = 0
+L3_ERR_NULL = -1
+L3_ERR_SHAPE = -2
+L3_ERR_DTYPE = -3
+L3_ERR_WORKSPACE = -4
+L3_ERR_HIP = -5
+L3_ERR_TOKEN_RANGE = -6
+L3_ERR_COUNT = -7
+L3_ERR_STATE = -8
+L3_F32 = 0
+L3_BF16 = 1
+L3_MAX_ROWS_PER_ID = 512
+
+
+class L3Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {l3_status_str(status)} ({status})")
+
+
+class l3_desc(Structure):
+    _fields_ = [("vocab", c_int64), ("rows", c_int64), ("d", c_int32),
+                ("d_k", c_int32), ("d_e", c_int32), ("k_max", c_int32),
+                ("dtype", c_int32), ("y_dtype", c_int32), ("ln_eps", c_float)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run "
+            "`python -m static_token_routed_id_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = c_void_p
+    sig = {
+        "l3_status_str": (c_char_p, [c_int]),
+        "l3_stage_name": (c_char_p, [c_int]),
+        "l3_workspace_size": (c_int, [POINTER(l3_desc), c_int64,
+                                      POINTER(c_size_t), POINTER(c_size_t),
+                                      POINTER(c_size_t)]),
+        "l3_plan": (c_int, [POINTER(l3_desc), P, c_int64, P, P, c_size_t, P,
+                            POINTER(c_void_p)]),
+        "l3_replan": (c_int, [P, P, c_int64, P, P]),
+        "l3_forward": (c_int, [P, P, P, P, P, P, P, P, P, P, c_size_t, P,
+                               c_size_t, P]),
+        "l3_backward": (c_int, [P, P, P, P, P, P, P, P, P, P, c_size_t, P, P,
+                                P, P, P, P, P, P, c_size_t, P]),
+        "l3_plan_check": (c_int, [P, P]),
+        "l3_plan_export": (c_int, [P, P, P, P, P, P, P, P]),
+        "l3_plan_release": (None, [P]),
+        "l3_plan_tokens": (c_int64, [P]),
+        "l3_timing_enable": (c_int, [P, c_int]),
+        "l3_timing_read": (c_int, [P, POINTER(c_double), POINTER(c_int64),
+                                   c_int, POINTER(c_int)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("l3_workspace_size", "l3_plan", "l3_replan", "l3_forward",
+            "l3_backward", "l3_plan_check", "l3_plan_export",
+            "l3_plan_release", "l3_plan_tokens", "l3_status_str",
+            "l3_timing_enable", "l3_timing_read", "l3_stage_name")
+
+
+def lib():
+    return _lib
+
+
+def l3_status_str(status: int) -> str:
+    return _lib.l3_status_str(int(status)).decode()
+
+
+def l3_stage_name(stage: int):
+    s = _lib.l3_stage_name(int(stage))
+    return s.decode() if s else None
+
+
+def _check(status: int, where: str) -> None:
+    if status != L3_OK:
+        raise L3Error(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t):
+    if t is None or isinstance(t, int):
+        return 0
+    return t.numel() * t.element_size()
+
+
+def make_desc(vocab, rows, d, d_e, k_max=512, dtype=L3_BF16, y_dtype=L3_F32,
+              ln_eps=1e-5, d_k=None) -> l3_desc:
+    return l3_desc(int(vocab), int(rows), int(d), int(d if d_k is None else d_k),
+                   int(d_e), int(k_max), int(dtype), int(y_dtype),
+                   float(ln_eps))
+
+
+def l3_workspace_size(desc: l3_desc, max_tokens: int):
+    p, s, c = c_size_t(), c_size_t(), c_size_t()
+    _check(_lib.l3_workspace_size(byref(desc), int(max_tokens), byref(p),
+                                  byref(s), byref(c)), "l3_workspace_size")
+    return p.value, s.value, c.value
+
+
+class Plan:
+    """Owns an l3_plan_t handle (released on garbage collection)."""
+
+    def __init__(self, handle: int, desc: l3_desc, plan_ws):
+        self.handle = handle
+        self.desc = desc
+        self.plan_ws = plan_ws  # keep the workspace alive
+
+    @property
+    def tokens(self) -> int:
+        return int(_lib.l3_plan_tokens(self.handle))
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            _lib.l3_plan_release(h)
+            self.handle = None
+
+
+def l3_plan(desc: l3_desc, ids, offsets, plan_ws, stream=None,
+            check_status=True) -> Plan:
+    out = c_void_p()
+    B = 0 if ids is None else ids.numel()
+    st = _lib.l3_plan(byref(desc), _ptr(ids), B, _ptr(offsets), _ptr(plan_ws),
+                      _nbytes(plan_ws), _stream(stream), byref(out))
+    if out.value is None:
+        _check(st, "l3_plan")
+    plan = Plan(out.value, desc, plan_ws)
+    if check_status:
+        _check(st, "l3_plan")
+    return plan
+
+
+def l3_replan(plan: Plan, ids, offsets, stream=None) -> None:
+    B = 0 if ids is None else ids.numel()
+    _check(_lib.l3_replan(plan.handle, _ptr(ids), B, _ptr(offsets),
+                          _stream(stream)), "l3_replan")
+
+
+def l3_forward(plan: Plan, x, K, V, W_up, gamma, beta, W_mix, y, save,
+               scratch, stream=None) -> None:
+    _check(_lib.l3_forward(plan.handle, _ptr(x), _ptr(K), _ptr(V), _ptr(W_up),
+                           _ptr(gamma), _ptr(beta), _ptr(W_mix), _ptr(y),
+                           _ptr(save), _nbytes(save), _ptr(scratch),
+                           _nbytes(scratch), _stream(stream)), "l3_forward")
+
+
+def l3_backward(plan: Plan, dy, x, K, V, W_up, gamma, beta, W_mix, save, dx,
+                dK, dV, dW_up, dgamma, dbeta, dW_mix, scratch,
+                stream=None) -> None:
+    _check(_lib.l3_backward(plan.handle, _ptr(dy), _ptr(x), _ptr(K), _ptr(V),
+                            _ptr(W_up), _ptr(gamma), _ptr(beta), _ptr(W_mix),
+                            _ptr(save), _nbytes(save), _ptr(dx), _ptr(dK),
+                            _ptr(dV), _ptr(dW_up), _ptr(dgamma), _ptr(dbeta),
+                            _ptr(dW_mix), _ptr(scratch), _nbytes(scratch),
+                            _stream(stream)), "l3_backward")
+
+
+def l3_plan_check(plan: Plan, stream=None) -> int:
+    """Returns the plan's device-side status (0, or L3_ERR_TOKEN_RANGE /
+    L3_ERR_COUNT); raises only on a HIP failure."""
+    st = _lib.l3_plan_check(plan.handle, _stream(stream))
+    if st == L3_ERR_HIP or st == L3_ERR_NULL:
+        raise L3Error(st, "l3_plan_check")
+    return st
+
+
+def l3_plan_export(plan: Plan, stream=None) -> dict:
+    B = plan.tokens
+    perm = np.zeros(max(B, 1), np.int32)
+    S = np.zeros(1, np.int32)
+    seg_id = np.zeros(max(B, 1), np.int32)
+    seg_tok_start = np.zeros(B + 1, np.int32)
+    seg_row_off = np.zeros(max(B, 1), np.int64)
+    seg_n = np.zeros(max(B, 1), np.int32)
+    P = lambda a: a.ctypes.data_as(c_void_p)
+    _check(_lib.l3_plan_export(plan.handle, P(perm), P(S), P(seg_id),
+                               P(seg_tok_start), P(seg_row_off), P(seg_n),
+                               _stream(stream)), "l3_plan_export")
+    n = int(S[0])
+    return dict(perm=perm[:B].copy(), S=n, seg_id=seg_id[:n].copy(),
+                seg_tok_start=seg_tok_start[:n + 1].copy(),
+                seg_row_off=seg_row_off[:n].copy(), seg_n=seg_n[:n].copy())
+
+
+def l3_timing_enable(plan: Plan, enable: bool = True) -> None:
+    _check(_lib.l3_timing_enable(plan.handle, 1 if enable else 0),
+           "l3_timing_enable")
+
+
+def l3_timing_read(plan: Plan) -> dict:
+    n = c_int()
+    ms = (c_double * 32)()
+    cnt = (c_int64 * 32)()
+    _check(_lib.l3_timing_read(plan.handle, ms, cnt, 32, byref(n)),
+           "l3_timing_read")
+    return {l3_stage_name(i): (ms[i], int(cnt[i])) for i in range(n.value)}

@@ -1,0 +1,776 @@
+// C-ABI layer of libl3: argument checks, workspace carving and the launch
+// sequence of the plan, forward and backward passes on the caller's stream.
+// Nothing here allocates device memory or synchronises the stream on the
+// plan / forward / backward path. No C++ exception leaves an extern "C"
+// function.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "l3.h"
+#include "l3_internal.h"
+
+using namespace l3;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Bump allocator over a caller workspace (base == nullptr only measures).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = align_up(off);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+  size_t bytes() const { return align_up(off); }
+};
+
+enum Stage {
+  ST_PLAN,
+  ST_SEG,
+  ST_COMBINE,
+  ST_UP,
+  ST_LN,
+  ST_MIX,
+  ST_BWD_MIX,
+  ST_BWD_LN,
+  ST_BWD_UP,
+  ST_BWD_SEG,
+  ST_COUNT
+};
+const char* const kStageNames[ST_COUNT] = {
+    "plan",    "seg_fwd",   "seg_combine",   "up_proj", "layernorm",
+    "mix_proj", "bwd_mix",  "bwd_layernorm", "bwd_up",  "bwd_seg"};
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("L3_DEBUG_SYNC");
+    return e && e[0] && e[0] != '0';
+  }();
+  return on;
+}
+
+inline size_t elem_bytes(int dtype) { return dtype == L3_BF16 ? 2 : 4; }
+
+l3_status check_desc(const l3_desc* d) {
+  if (!d) return L3_ERR_NULL;
+  if (d->dtype != L3_F32 && d->dtype != L3_BF16) return L3_ERR_DTYPE;
+  if (d->y_dtype != L3_F32 && d->y_dtype != L3_BF16) return L3_ERR_DTYPE;
+  if (d->vocab < 1 || d->rows < 1) return L3_ERR_SHAPE;
+  if (d->d < 64 || d->d % 64 != 0 || d->d > 4096) return L3_ERR_SHAPE;
+  if (d->d_k != d->d) return L3_ERR_SHAPE;
+  if (d->d_e < 64 || d->d_e % 64 != 0 || d->d_e > 4096) return L3_ERR_SHAPE;
+  if (d->k_max < 1 || d->k_max > L3_MAX_ROWS_PER_ID) return L3_ERR_SHAPE;
+  if (!(d->ln_eps >= 0.0f) || !std::isfinite(d->ln_eps)) return L3_ERR_SHAPE;
+  if (d->vocab > (int64_t(1) << 31) - 2) return L3_ERR_SHAPE;
+  return L3_OK;
+}
+
+// Rows of one forward work item: small batches split an id's rows so that
+// enough wavefronts stream them; large batches keep every id in one chunk.
+int chunk_rows_for(int64_t B, int k_max) {
+  int ch = B <= 256 ? 32 : (B <= 2048 ? 128 : 512);
+  int kp = 16;
+  while (kp < k_max) kp <<= 1;
+  return ch < kp ? ch : kp;
+}
+int nch_for(int64_t B, int k_max) {
+  const int ch = chunk_rows_for(B, k_max);
+  return (k_max + ch - 1) / ch;
+}
+
+PlanDev carve_plan(Carver& c, int64_t B) {
+  const size_t nb = static_cast<size_t>(B);
+  const size_t nblk = (nb + kSortTile - 1) / kSortTile;
+  PlanDev p;
+  p.header = c.take<int32_t>(16);
+  p.perm = c.take<int32_t>(nb);
+  p.sorted_ids = c.take<int32_t>(nb);
+  p.seg_id = c.take<int32_t>(nb);
+  p.seg_tok_start = c.take<int32_t>(nb + 1);
+  p.seg_row_off = c.take<int64_t>(nb);
+  p.seg_n = c.take<int32_t>(nb);
+  p.seg_item_start = c.take<int32_t>(nb + 1);
+  p.keys_alt = c.take<int32_t>(nb);
+  p.vals_alt = c.take<int32_t>(nb);
+  p.hist = c.take<int32_t>(256 * nblk);
+  p.blk = c.take<int32_t>(nblk + 1);
+  return p;
+}
+
+struct SaveBufs {
+  float* a32;   // [B x d_e]
+  float* uhat;  // [B x d]
+  float* h32;   // [B x d]
+  float* rstd;  // [B]
+};
+SaveBufs carve_save(Carver& c, const l3_desc& d, int64_t B) {
+  SaveBufs s;
+  s.a32 = c.take<float>(B * d.d_e);
+  s.uhat = c.take<float>(B * d.d);
+  s.h32 = c.take<float>(B * d.d);
+  s.rstd = c.take<float>(B);
+  return s;
+}
+
+struct FwdBufs {
+  void* a_act;  // [B x d_e] dtype
+  float* U;     // [B x d]
+  void* h_act;  // [B x d] dtype
+  float* part;
+  float* part_ml;
+};
+FwdBufs carve_fwd(Carver& c, const l3_desc& d, int64_t B) {
+  FwdBufs f;
+  const size_t es = elem_bytes(d.dtype);
+  f.a_act = c.take<char>(B * d.d_e * es);
+  f.U = c.take<float>(B * d.d);
+  f.h_act = c.take<char>(B * d.d * es);
+  const int nch = nch_for(B, d.k_max);
+  if (nch > 1) {
+    f.part = c.take<float>(B * nch * d.d_e);
+    f.part_ml = c.take<float>(B * nch * 2);
+  } else {
+    f.part = nullptr;
+    f.part_ml = nullptr;
+  }
+  return f;
+}
+
+struct BwdBufs {
+  float* dH;
+  float* dU;
+  float* dA;
+};
+BwdBufs carve_bwd(Carver& c, const l3_desc& d, int64_t B) {
+  BwdBufs b;
+  b.dH = c.take<float>(B * d.d);
+  b.dU = c.take<float>(B * d.d);
+  b.dA = c.take<float>(B * d.d_e);
+  return b;
+}
+
+size_t plan_bytes(int64_t B) {
+  Carver c(nullptr);
+  carve_plan(c, B);
+  return c.bytes();
+}
+size_t save_bytes_for(const l3_desc& d, int64_t B) {
+  Carver c(nullptr);
+  carve_save(c, d, B);
+  return c.bytes();
+}
+size_t fwd_bytes_for(const l3_desc& d, int64_t B) {
+  Carver c(nullptr);
+  carve_fwd(c, d, B);
+  return c.bytes();
+}
+size_t bwd_bytes_for(const l3_desc& d, int64_t B) {
+  Carver c(nullptr);
+  carve_bwd(c, d, B);
+  return c.bytes();
+}
+size_t scratch_bytes_for(const l3_desc& d, int64_t B) {
+  size_t f = fwd_bytes_for(d, B), b = bwd_bytes_for(d, B);
+  return f > b ? f : b;
+}
+
+}  // namespace
+
+struct l3_plan_s {
+  l3_desc desc;
+  int64_t B = 0;
+  int64_t capacity = 0;  // largest B the workspace holds
+  int chunk_rows = 32;
+  int nch_max = 1;
+  PlanDev dev;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  bool timing = false;
+  struct Ev {
+    hipEvent_t a, b;
+    int stage;
+  };
+  std::vector<Ev> events;
+  const void* saved = nullptr;  // save workspace of the last training forward
+};
+
+namespace {
+
+// Records a pair of events around one stage when timing is on.
+struct StageTimer {
+  l3_plan_s* p;
+  int stage;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  bool on;
+  StageTimer(l3_plan_s* plan, int st, hipStream_t stream)
+      : p(plan), stage(st), s(stream), on(plan->timing) {
+    if (on) {
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+        on = false;
+        return;
+      }
+      hipEventRecord(a, s);
+    }
+  }
+  ~StageTimer() {
+    if (on) {
+      hipEventRecord(b, s);
+      p->events.push_back({a, b, stage});
+    }
+  }
+};
+
+l3_status finish(l3_plan_s* p, hipError_t e, hipStream_t s) {
+  if (e != hipSuccess) return L3_ERR_HIP;
+  if (debug_sync()) {
+    if (hipStreamSynchronize(s) != hipSuccess) return L3_ERR_HIP;
+    if (p && p->B > 0) {
+      int32_t h = 0;
+      if (hipMemcpy(&h, p->dev.header, sizeof(h), hipMemcpyDeviceToHost) !=
+          hipSuccess)
+        return L3_ERR_HIP;
+      if (h & kBadId) return L3_ERR_TOKEN_RANGE;
+      if (h & kBadCount) return L3_ERR_COUNT;
+    }
+  }
+  return L3_OK;
+}
+
+l3_status do_plan(l3_plan_s* p, const int32_t* ids, int64_t B,
+                  const int64_t* offsets, hipStream_t s) {
+  if (B < 0) return L3_ERR_SHAPE;
+  if (B > p->capacity) return L3_ERR_WORKSPACE;
+  if (B > 0 && (!ids || !offsets)) return L3_ERR_NULL;
+  p->B = B;
+  p->saved = nullptr;
+  p->chunk_rows = chunk_rows_for(B, p->desc.k_max);
+  p->nch_max = nch_for(B, p->desc.k_max);
+  Carver c(p->ws);
+  p->dev = carve_plan(c, B);
+  if (B == 0) return L3_OK;
+  PlanParams pp;
+  pp.ids = ids;
+  pp.offsets = offsets;
+  pp.vocab = p->desc.vocab;
+  pp.rows = p->desc.rows;
+  pp.B = static_cast<int>(B);
+  pp.k_max = p->desc.k_max;
+  pp.chunk_rows = p->chunk_rows;
+  hipError_t e;
+  {
+    StageTimer t(p, ST_PLAN, s);
+    e = plan_launch(p->dev, pp, s);
+  }
+  return finish(p, e, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* l3_status_str(l3_status st) {
+  switch (st) {
+    case L3_OK: return "ok";
+    case L3_ERR_NULL: return "a required pointer is NULL";
+    case L3_ERR_SHAPE: return "unsupported or inconsistent sizes";
+    case L3_ERR_DTYPE: return "unknown element type";
+    case L3_ERR_WORKSPACE: return "workspace too small";
+    case L3_ERR_HIP: return "HIP runtime error";
+    case L3_ERR_TOKEN_RANGE: return "token id outside [0, vocab)";
+    case L3_ERR_COUNT: return "an id owns 0 or more than k_max rows, or rows outside the table";
+    case L3_ERR_STATE: return "call out of order";
+    default: return "unknown status";
+  }
+}
+
+const char* l3_stage_name(int stage) {
+  return (stage >= 0 && stage < ST_COUNT) ? kStageNames[stage] : nullptr;
+}
+
+l3_status l3_workspace_size(const l3_desc* desc, int64_t max_tokens,
+                            size_t* plan_ws, size_t* save_ws,
+                            size_t* scratch_ws) {
+  l3_status st = check_desc(desc);
+  if (st != L3_OK) return st;
+  if (max_tokens < 0 || max_tokens >= (int64_t(1) << 31)) return L3_ERR_SHAPE;
+  if (plan_ws) *plan_ws = plan_bytes(max_tokens);
+  if (save_ws) *save_ws = save_bytes_for(*desc, max_tokens);
+  if (scratch_ws) {
+    // the forward's split-row partials depend on the batch size actually
+    // planned; take the largest need over every batch up to max_tokens
+    size_t m = scratch_bytes_for(*desc, max_tokens);
+    const int64_t probes[2] = {256, 2048};
+    for (int64_t b : probes) {
+      if (b < max_tokens) {
+        size_t v = scratch_bytes_for(*desc, b);
+        if (v > m) m = v;
+      }
+    }
+    *scratch_ws = m;
+  }
+  return L3_OK;
+}
+
+l3_status l3_plan(const l3_desc* desc, const int32_t* ids, int64_t B,
+                  const int64_t* offsets, void* plan_ws, size_t plan_ws_bytes,
+                  void* stream, l3_plan_t* out) {
+  try {
+    if (!out) return L3_ERR_NULL;
+    *out = nullptr;
+    l3_status st = check_desc(desc);
+    if (st != L3_OK) return st;
+    if (B < 0 || B >= (int64_t(1) << 31)) return L3_ERR_SHAPE;
+    if (!plan_ws) return L3_ERR_NULL;
+    if (plan_ws_bytes < plan_bytes(B)) return L3_ERR_WORKSPACE;
+    // capacity: the largest batch whose plan fits this workspace
+    int64_t lo = B, hi = (int64_t(1) << 31) - 1;
+    while (lo < hi) {
+      int64_t mid = lo + (hi - lo + 1) / 2;
+      if (plan_bytes(mid) <= plan_ws_bytes)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    l3_plan_s* p = new (std::nothrow) l3_plan_s();
+    if (!p) return L3_ERR_HIP;
+    p->desc = *desc;
+    p->ws = plan_ws;
+    p->ws_bytes = plan_ws_bytes;
+    p->capacity = lo;
+    st = do_plan(p, ids, B, offsets, static_cast<hipStream_t>(stream));
+    if (st != L3_OK && st != L3_ERR_TOKEN_RANGE && st != L3_ERR_COUNT) {
+      delete p;
+      return st;
+    }
+    *out = p;
+    return st;
+  } catch (...) {
+    return L3_ERR_HIP;
+  }
+}
+
+l3_status l3_replan(l3_plan_t plan, const int32_t* ids, int64_t B,
+                    const int64_t* offsets, void* stream) {
+  try {
+    if (!plan) return L3_ERR_NULL;
+    return do_plan(plan, ids, B, offsets, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return L3_ERR_HIP;
+  }
+}
+
+void l3_plan_release(l3_plan_t plan) {
+  if (!plan) return;
+  for (auto& e : plan->events) {
+    hipEventDestroy(e.a);
+    hipEventDestroy(e.b);
+  }
+  delete plan;
+}
+
+int64_t l3_plan_tokens(l3_plan_t plan) { return plan ? plan->B : -1; }
+
+l3_status l3_plan_check(l3_plan_t plan, void* stream) {
+  if (!plan) return L3_ERR_NULL;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+    return L3_ERR_HIP;
+  if (plan->B == 0) return L3_OK;
+  int32_t h = 0;
+  if (hipMemcpy(&h, plan->dev.header, sizeof(h), hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return L3_ERR_HIP;
+  if (h & kBadId) return L3_ERR_TOKEN_RANGE;
+  if (h & kBadCount) return L3_ERR_COUNT;
+  return L3_OK;
+}
+
+l3_status l3_plan_export(l3_plan_t plan, int32_t* perm, int32_t* S,
+                         int32_t* seg_id, int32_t* seg_tok_start,
+                         int64_t* seg_row_off, int32_t* seg_n, void* stream) {
+  if (!plan) return L3_ERR_NULL;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+    return L3_ERR_HIP;
+  const int64_t B = plan->B;
+  int32_t hdr[4] = {0, 0, 0, 0};
+  if (B > 0 && hipMemcpy(hdr, plan->dev.header, sizeof(hdr),
+                         hipMemcpyDeviceToHost) != hipSuccess)
+    return L3_ERR_HIP;
+  const int64_t nS = hdr[1];
+  if (S) *S = static_cast<int32_t>(nS);
+  auto cp = [](void* dst, const void* src, size_t bytes) {
+    return bytes == 0 || !dst ||
+           hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost) == hipSuccess;
+  };
+  bool ok = true;
+  if (B > 0) {
+    ok = ok && cp(perm, plan->dev.perm, B * sizeof(int32_t));
+    ok = ok && cp(seg_id, plan->dev.seg_id, nS * sizeof(int32_t));
+    ok = ok && cp(seg_tok_start, plan->dev.seg_tok_start,
+                  (nS + 1) * sizeof(int32_t));
+    ok = ok && cp(seg_row_off, plan->dev.seg_row_off, nS * sizeof(int64_t));
+    ok = ok && cp(seg_n, plan->dev.seg_n, nS * sizeof(int32_t));
+  } else if (seg_tok_start) {
+    seg_tok_start[0] = 0;
+  }
+  return ok ? L3_OK : L3_ERR_HIP;
+}
+
+l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
+                     const void* V, const void* W_up, const void* gamma,
+                     const void* beta, const void* W_mix, void* y, void* save,
+                     size_t save_bytes, void* scratch, size_t scratch_bytes,
+                     void* stream) {
+  try {
+    if (!plan) return L3_ERR_NULL;
+    plan->saved = nullptr;
+    const int64_t B = plan->B;
+    if (B == 0) return L3_OK;
+    if (!x || !K || !V || !W_up || !gamma || !beta || !W_mix || !y ||
+        !scratch)
+      return L3_ERR_NULL;
+    const l3_desc& d = plan->desc;
+    if (scratch_bytes < fwd_bytes_for(d, B)) return L3_ERR_WORKSPACE;
+    if (save && save_bytes < save_bytes_for(d, B)) return L3_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Carver cs(scratch);
+    FwdBufs f = carve_fwd(cs, d, B);
+    SaveBufs sv{nullptr, nullptr, nullptr, nullptr};
+    if (save) {
+      Carver cv(save);
+      sv = carve_save(cv, d, B);
+    }
+    const PlanDev& pd = plan->dev;
+    hipError_t e = hipSuccess;
+
+    SegFwdArgs sa;
+    sa.header = pd.header;
+    sa.perm = pd.perm;
+    sa.seg_tok_start = pd.seg_tok_start;
+    sa.seg_row_off = pd.seg_row_off;
+    sa.seg_n = pd.seg_n;
+    sa.seg_item_start = pd.seg_item_start;
+    sa.x = x;
+    sa.K = K;
+    sa.V = V;
+    sa.d = d.d;
+    sa.d_e = d.d_e;
+    sa.chunk_rows = plan->chunk_rows;
+    sa.nch_max = plan->nch_max;
+    sa.a_out = f.a_act;
+    sa.a_save = sv.a32;
+    sa.part = f.part;
+    sa.part_ml = f.part_ml;
+    const int64_t distinct = B < d.vocab ? B : d.vocab;
+    const int64_t items_ub = ((B + kTokTile - 1) / kTokTile + distinct) *
+                             static_cast<int64_t>(plan->nch_max);
+    {
+      StageTimer t(plan, ST_SEG, s);
+      e = seg_fwd_launch(sa, d.dtype, static_cast<int>(B),
+                         static_cast<int>(items_ub < (1 << 30) ? items_ub
+                                                               : (1 << 30)),
+                         s);
+    }
+    if (e != hipSuccess) return L3_ERR_HIP;
+    if (plan->nch_max > 1) {
+      CombineArgs ca;
+      ca.header = pd.header;
+      ca.perm = pd.perm;
+      ca.seg_tok_start = pd.seg_tok_start;
+      ca.seg_n = pd.seg_n;
+      ca.B = static_cast<int>(B);
+      ca.d_e = d.d_e;
+      ca.chunk_rows = plan->chunk_rows;
+      ca.nch_max = plan->nch_max;
+      ca.part = f.part;
+      ca.part_ml = f.part_ml;
+      ca.a_out = f.a_act;
+      ca.a_save = sv.a32;
+      StageTimer t(plan, ST_COMBINE, s);
+      e = seg_combine_launch(ca, d.dtype, s);
+      if (e != hipSuccess) return L3_ERR_HIP;
+    }
+    // u = a W_up^T  (float32 out)
+    GemmArgs up{};
+    up.A1 = f.a_act;
+    up.A2 = f.a_act;
+    up.a1_m = up.a2_m = d.d_e;
+    up.a1_k = up.a2_k = 1;
+    up.K1 = d.d_e;
+    up.Bm = W_up;
+    up.b_k = 1;
+    up.b_n = d.d_e;
+    up.C = f.U;
+    up.c_m = d.d;
+    up.M = static_cast<int>(B);
+    up.N = d.d;
+    up.K = d.d_e;
+    up.header = pd.header;
+    {
+      StageTimer t(plan, ST_UP, s);
+      if (d.dtype == L3_BF16 && gemm_nt_mfma_ok(up))
+        e = gemm_nt_mfma_launch(up, kF32, s);
+      else
+        e = gemm_launch(up, d.dtype, d.dtype, kF32, s);
+    }
+    if (e != hipSuccess) return L3_ERR_HIP;
+    LnArgs ln;
+    ln.header = pd.header;
+    ln.U = f.U;
+    ln.gamma = gamma;
+    ln.beta = beta;
+    ln.B = static_cast<int>(B);
+    ln.d = d.d;
+    ln.eps = d.ln_eps;
+    ln.h = f.h_act;
+    ln.h_save = sv.h32;
+    ln.uhat_save = sv.uhat;
+    ln.rstd_save = sv.rstd;
+    {
+      StageTimer t(plan, ST_LN, s);
+      e = ln_launch(ln, d.dtype, s);
+    }
+    if (e != hipSuccess) return L3_ERR_HIP;
+    // y = [h ; x] W_mix^T, the A operand switching from h to x at k = d
+    GemmArgs mx{};
+    mx.A1 = f.h_act;
+    mx.A2 = x;
+    mx.a1_m = mx.a2_m = d.d;
+    mx.a1_k = mx.a2_k = 1;
+    mx.K1 = d.d;
+    mx.Bm = W_mix;
+    mx.b_k = 1;
+    mx.b_n = 2 * static_cast<int64_t>(d.d);
+    mx.C = y;
+    mx.c_m = d.d;
+    mx.M = static_cast<int>(B);
+    mx.N = d.d;
+    mx.K = 2 * d.d;
+    mx.header = pd.header;
+    {
+      StageTimer t(plan, ST_MIX, s);
+      if (d.dtype == L3_BF16 && gemm_nt_mfma_ok(mx))
+        e = gemm_nt_mfma_launch(mx, d.y_dtype, s);
+      else
+        e = gemm_launch(mx, d.dtype, d.dtype, d.y_dtype, s);
+    }
+    l3_status st = finish(plan, e, s);
+    if (st == L3_OK && save) plan->saved = save;
+    return st;
+  } catch (...) {
+    return L3_ERR_HIP;
+  }
+}
+
+l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
+                      const void* K, const void* V, const void* W_up,
+                      const void* gamma, const void* beta, const void* W_mix,
+                      const void* save, size_t save_bytes, float* dx,
+                      float* dK, float* dV, float* dW_up, float* dgamma,
+                      float* dbeta, float* dW_mix, void* scratch,
+                      size_t scratch_bytes, void* stream) {
+  try {
+    if (!plan) return L3_ERR_NULL;
+    const l3_desc& d = plan->desc;
+    const int64_t B = plan->B;
+    if (!dK || !dV || !dW_up || !dgamma || !dbeta || !dW_mix) return L3_ERR_NULL;
+    if (B > 0 && (!dy || !x || !K || !V || !W_up || !gamma || !beta ||
+                  !W_mix || !save || !dx || !scratch))
+      return L3_ERR_NULL;
+    (void)beta;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    const int64_t es = static_cast<int64_t>(elem_bytes(d.dtype));
+    if (B == 0) {
+      // no tokens: every gradient is zero
+      e = fill_zero_launch(dK, d.rows * d.d, s);
+      if (e == hipSuccess) e = fill_zero_launch(dV, d.rows * d.d_e, s);
+      if (e == hipSuccess) e = fill_zero_launch(dW_up, int64_t(d.d) * d.d_e, s);
+      if (e == hipSuccess) e = fill_zero_launch(dgamma, d.d, s);
+      if (e == hipSuccess) e = fill_zero_launch(dbeta, d.d, s);
+      if (e == hipSuccess) e = fill_zero_launch(dW_mix, int64_t(d.d) * 2 * d.d, s);
+      return finish(plan, e, s);
+    }
+    if (plan->saved != save) return L3_ERR_STATE;
+    if (save_bytes < save_bytes_for(d, B)) return L3_ERR_WORKSPACE;
+    if (scratch_bytes < bwd_bytes_for(d, B)) return L3_ERR_WORKSPACE;
+    Carver cv(const_cast<void*>(save));
+    SaveBufs sv = carve_save(cv, d, B);
+    Carver cs(scratch);
+    BwdBufs bb = carve_bwd(cs, d, B);
+    const PlanDev& pd = plan->dev;
+    const int Bi = static_cast<int>(B);
+    const int64_t D = d.d, DE = d.d_e;
+    {
+      StageTimer t(plan, ST_BWD_MIX, s);
+      // dH = dY W_a  (W_a = W_mix[:, :d]; B(k=j, n) = W_mix[j, n])
+      GemmArgs g{};
+      g.A1 = g.A2 = dy;
+      g.a1_m = g.a2_m = D;
+      g.a1_k = g.a2_k = 1;
+      g.K1 = d.d;
+      g.Bm = W_mix;
+      g.b_k = 2 * D;
+      g.b_n = 1;
+      g.C = bb.dH;
+      g.c_m = D;
+      g.M = Bi;
+      g.N = d.d;
+      g.K = d.d;
+      g.header = pd.header;
+      e = gemm_launch(g, d.dtype, d.dtype, kF32, s);
+      // dx = dY W_b  (W_b = W_mix[:, d:])
+      if (e == hipSuccess) {
+        g.Bm = static_cast<const char*>(W_mix) + D * es;
+        g.C = dx;
+        e = gemm_launch(g, d.dtype, d.dtype, kF32, s);
+      }
+      // dW_mix[:, :d] = dY^T H, dW_mix[:, d:] = dY^T X  (sums over tokens)
+      if (e == hipSuccess) {
+        GemmArgs w{};
+        w.A1 = w.A2 = dy;
+        w.a1_m = w.a2_m = 1;
+        w.a1_k = w.a2_k = D;
+        w.K1 = Bi;
+        w.Bm = sv.h32;
+        w.b_k = D;
+        w.b_n = 1;
+        w.C = dW_mix;
+        w.c_m = 2 * D;
+        w.M = d.d;
+        w.N = d.d;
+        w.K = Bi;
+        w.header = pd.header;
+        e = gemm_launch(w, d.dtype, kF32, kF32, s);
+        if (e == hipSuccess) {
+          w.Bm = x;
+          w.C = dW_mix + D;
+          e = gemm_launch(w, d.dtype, d.dtype, kF32, s);
+        }
+      }
+    }
+    if (e != hipSuccess) return L3_ERR_HIP;
+    BwdArgs ba;
+    ba.header = pd.header;
+    ba.perm = pd.perm;
+    ba.seg_tok_start = pd.seg_tok_start;
+    ba.seg_row_off = pd.seg_row_off;
+    ba.seg_n = pd.seg_n;
+    ba.B = Bi;
+    ba.d = d.d;
+    ba.d_e = d.d_e;
+    ba.x = x;
+    ba.K = K;
+    ba.V = V;
+    ba.gamma = gamma;
+    ba.uhat = sv.uhat;
+    ba.rstd = sv.rstd;
+    ba.dH = bb.dH;
+    ba.dU = bb.dU;
+    ba.dA = bb.dA;
+    ba.dx = dx;
+    ba.dK = dK;
+    ba.dV = dV;
+    ba.dgamma = dgamma;
+    ba.dbeta = dbeta;
+    ba.rows = d.rows;
+    {
+      StageTimer t(plan, ST_BWD_LN, s);
+      e = ln_bwd_launch(ba, d.dtype, s);
+    }
+    if (e != hipSuccess) return L3_ERR_HIP;
+    {
+      StageTimer t(plan, ST_BWD_UP, s);
+      // dW_up = dU^T A (sum over tokens)
+      GemmArgs w{};
+      w.A1 = w.A2 = bb.dU;
+      w.a1_m = w.a2_m = 1;
+      w.a1_k = w.a2_k = D;
+      w.K1 = Bi;
+      w.Bm = sv.a32;
+      w.b_k = DE;
+      w.b_n = 1;
+      w.C = dW_up;
+      w.c_m = DE;
+      w.M = d.d;
+      w.N = d.d_e;
+      w.K = Bi;
+      w.header = pd.header;
+      e = gemm_launch(w, kF32, kF32, kF32, s);
+      // dA = dU W_up
+      if (e == hipSuccess) {
+        GemmArgs g{};
+        g.A1 = g.A2 = bb.dU;
+        g.a1_m = g.a2_m = D;
+        g.a1_k = g.a2_k = 1;
+        g.K1 = d.d;
+        g.Bm = W_up;
+        g.b_k = DE;
+        g.b_n = 1;
+        g.C = bb.dA;
+        g.c_m = DE;
+        g.M = Bi;
+        g.N = d.d_e;
+        g.K = d.d;
+        g.header = pd.header;
+        e = gemm_launch(g, kF32, d.dtype, kF32, s);
+      }
+    }
+    if (e != hipSuccess) return L3_ERR_HIP;
+    {
+      StageTimer t(plan, ST_BWD_SEG, s);
+      e = fill_zero_launch(dK, d.rows * D, s);
+      if (e == hipSuccess) e = fill_zero_launch(dV, d.rows * DE, s);
+      if (e == hipSuccess) e = seg_bwd_launch(ba, d.dtype, Bi, s);
+    }
+    return finish(plan, e, s);
+  } catch (...) {
+    return L3_ERR_HIP;
+  }
+}
+
+l3_status l3_timing_enable(l3_plan_t plan, int enable) {
+  if (!plan) return L3_ERR_NULL;
+  plan->timing = enable != 0;
+  return L3_OK;
+}
+
+l3_status l3_timing_read(l3_plan_t plan, double* ms, int64_t* count,
+                         int max_stages, int* n_stages) {
+  if (!plan) return L3_ERR_NULL;
+  if (n_stages) *n_stages = ST_COUNT;
+  std::vector<double> acc(ST_COUNT, 0.0);
+  std::vector<int64_t> cnt(ST_COUNT, 0);
+  l3_status st = L3_OK;
+  for (auto& e : plan->events) {
+    float v = 0.f;
+    if (hipEventSynchronize(e.b) != hipSuccess ||
+        hipEventElapsedTime(&v, e.a, e.b) != hipSuccess)
+      st = L3_ERR_HIP;
+    acc[e.stage] += v;
+    cnt[e.stage] += 1;
+    hipEventDestroy(e.a);
+    hipEventDestroy(e.b);
+  }
+  plan->events.clear();
+  for (int i = 0; i < max_stages && i < ST_COUNT; ++i) {
+    if (ms) ms[i] = acc[i];
+    if (count) count[i] = cnt[i];
+  }
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// Device helpers for gfx950 (CDNA4, 64-wide wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace l3 {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float floatx4;
+
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Element access for the two storage types.
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld<float>(const float* p, int64_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf2f(p[i]);
+}
+
+template <typename T>
+__device__ __forceinline__ void st(T* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void st<float>(float* p, int64_t i, float v) {
+  p[i] = v;
+}
+template <>
+__device__ __forceinline__ void st<uint16_t>(uint16_t* p, int64_t i,
+                                             float v) {
+  p[i] = f2bf(v);
+}
+
+// 16x16x32 bf16 MFMA: lane l supplies row (l & 15) of A and column (l & 15)
+// of B, eight consecutive k values from group (l >> 4); the 16x16 float
+// result lands as rows 4*(l >> 4) + i, column l & 15 in element i.
+__device__ __forceinline__ floatx4 mfma_bf16(const uint4& a, const uint4& b,
+                                             floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0,
+      0, 0);
+}
+// 16x16x4 float32 MFMA, same output layout; lane l supplies one k value
+// (group l >> 4) of row / column l & 15.
+__device__ __forceinline__ floatx4 mfma_f32(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+// Reductions over the 16 lanes that share (lane >> 4).
+__device__ __forceinline__ float group16_sum(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Inclusive prefix sum over a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT a multiple of 64).
+// `tmp` must hold NT/64 + 1 ints. Returns the thread's exclusive prefix and
+// writes the block total to *total. Contains __syncthreads().
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = wave_incl_scan(v, lane);
+  if (lane == 63) tmp[w] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < NT / 64; ++i) {
+      int t = tmp[i];
+      tmp[i] = run;
+      run += t;
+    }
+    tmp[NT / 64] = run;
+  }
+  __syncthreads();
+  int res = tmp[w] + inc - v;
+  *total = tmp[NT / 64];
+  __syncthreads();
+  return res;
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) {
+  return (a + b - 1) / b;
+}
+
+}  // namespace l3

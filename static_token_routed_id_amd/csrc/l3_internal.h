@@ -1,0 +1,156 @@
+// Internal declarations shared by the C-ABI layer (api.cpp) and the HIP
+// kernels. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "l3.h"
+
+namespace l3 {
+
+// Tokens handled by one work item of the segment forward kernel (the M size
+// of one 16x16 MFMA block).
+constexpr int kTokTile = 16;
+// Largest batch sorted by the single-workgroup plan kernel.
+constexpr int kSmallPlanMax = 8192;
+// Elements per block of the multi-kernel radix sort.
+constexpr int kSortTile = 1024;
+
+// Bits of the device-side validation word of a plan.
+constexpr int kBadId = 1;
+constexpr int kBadCount = 2;
+
+// Device arrays of one plan, carved out of the caller's plan workspace.
+struct PlanDev {
+  int32_t* header;          // [0] status bits, [1] S, [2] work items
+  int32_t* perm;            // [B] token index at sorted position
+  int32_t* sorted_ids;      // [B]
+  int32_t* seg_id;          // [B]
+  int32_t* seg_tok_start;   // [B+1]
+  int64_t* seg_row_off;     // [B]
+  int32_t* seg_n;           // [B]
+  int32_t* seg_item_start;  // [B+1]
+  int32_t* keys_alt;        // [B] radix ping-pong
+  int32_t* vals_alt;        // [B]
+  int32_t* hist;            // [256 * ceil(B / kSortTile)]
+  int32_t* blk;             // [ceil(B / kSortTile) + 1]
+};
+
+struct PlanParams {
+  const int32_t* ids;
+  const int64_t* offsets;
+  int64_t vocab, rows;
+  int B;
+  int k_max;
+  int chunk_rows;  // rows of one forward work item (multiple of 16)
+};
+
+// Arguments of the segment forward kernel (softmax-attention of each token
+// over its id's rows).
+struct SegFwdArgs {
+  const int32_t* header;
+  const int32_t* perm;
+  const int32_t* seg_tok_start;
+  const int64_t* seg_row_off;
+  const int32_t* seg_n;
+  const int32_t* seg_item_start;
+  const void* x;
+  const void* K;
+  const void* V;
+  int d, d_e;
+  int chunk_rows;   // rows per work item
+  int nch_max;      // ceil(k_max / chunk_rows)
+  void* a_out;      // [B x d_e] activation dtype, original token order
+  float* a_save;    // [B x d_e] float32 or NULL
+  float* part;      // [B x nch_max x d_e] partial sums (split rows only)
+  float* part_ml;   // [B x nch_max x 2] partial (max, sum)
+};
+
+struct CombineArgs {
+  const int32_t* header;
+  const int32_t* perm;
+  const int32_t* seg_tok_start;
+  const int32_t* seg_n;
+  int B, d_e, chunk_rows, nch_max;
+  const float* part;
+  const float* part_ml;
+  void* a_out;
+  float* a_save;
+};
+
+// Generic strided GEMM: C[m, n] = sum_k A(m, k) * B(k, n) with
+//   A(m, k) = k < K1 ? A1[m*a1_m + k*a1_k] : A2[m*a2_m + (k-K1)*a2_k]
+//   B(k, n) = Bm[k*b_k + n*b_n]
+// float32 accumulation, fixed summation order.
+struct GemmArgs {
+  const void* A1;
+  const void* A2;
+  int64_t a1_m, a1_k, a2_m, a2_k;
+  int K1;
+  const void* Bm;
+  int64_t b_k, b_n;
+  void* C;
+  int64_t c_m;
+  int M, N, K;
+  const int32_t* header;  // plan status word (kernel does nothing if set)
+};
+
+// LayerNorm of float32 rows (one wave per row).
+struct LnArgs {
+  const int32_t* header;
+  const float* U;
+  const void* gamma;
+  const void* beta;
+  int B, d;
+  float eps;
+  void* h;        // [B x d] activation dtype
+  float* h_save;  // [B x d] or NULL
+  float* uhat_save;
+  float* rstd_save;
+};
+
+enum ElemType { kF32 = L3_F32, kBF16 = L3_BF16 };
+
+// ---- launchers (return the first HIP error) -------------------------------
+hipError_t plan_launch(const PlanDev& pd, const PlanParams& pp,
+                       hipStream_t s);
+hipError_t seg_fwd_launch(const SegFwdArgs& a, int dtype, int B, int items_ub,
+                          hipStream_t s);
+hipError_t seg_combine_launch(const CombineArgs& a, int dtype, hipStream_t s);
+hipError_t gemm_launch(const GemmArgs& g, int a_type, int b_type, int c_type,
+                       hipStream_t s);
+hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s);
+bool gemm_nt_mfma_ok(const GemmArgs& g);
+hipError_t ln_launch(const LnArgs& a, int dtype, hipStream_t s);
+
+struct BwdArgs {
+  const int32_t* header;
+  const int32_t* perm;
+  const int32_t* seg_tok_start;
+  const int64_t* seg_row_off;
+  const int32_t* seg_n;
+  int B, d, d_e;
+  const void* x;
+  const void* K;
+  const void* V;
+  const void* gamma;
+  const float* uhat;   // saved
+  const float* rstd;   // saved
+  const float* dH;     // [B x d]
+  float* dU;           // [B x d]
+  const float* dA;     // [B x d_e]
+  float* dx;           // [B x d], holds dX_b on entry
+  float* dK;
+  float* dV;
+  float* dgamma;
+  float* dbeta;
+  int64_t rows;
+};
+hipError_t fill_zero_launch(float* p, int64_t n, hipStream_t s);
+hipError_t ln_bwd_launch(const BwdArgs& a, int dtype, hipStream_t s);
+hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int S_ub,
+                          hipStream_t s);
+
+}  // namespace l3

@@ -1,0 +1,369 @@
+// Plan: sort the batch by token id and cut it into one segment per id.
+//
+// gist.science explainer of "L^3: Large Lookup Layers", Technical Summary,
+// Systems-Friendly Design, Batch Sorting: sorting the tokens of a batch by id
+// makes the layer's attention mask block-diagonal, i.e. every token of one id
+// attends over the same rows K_t, V_t. Core Architecture, Static Routing: the
+// rows of id t are known from t alone (here: offsets[t] .. offsets[t+1]-1),
+// and Information-Theoretic Embedding Allocation, Constraints: each id owns
+// between 1 and k rows, which the plan checks for every id that occurs.
+//
+// The sort key is (id, position), unique, so every correct sort gives the
+// same permutation. Two implementations:
+//   * batches up to 8192 tokens: one 1024-thread workgroup, bitonic sort of
+//     64-bit keys in LDS, then segment cut and work-item count in the same
+//     launch (one launch: decode-sized batches are latency bound);
+//   * larger batches: LSD radix sort of the 32-bit ids with the position as
+//     payload (stable, 8-bit digits, histogram / scan / ranked scatter per
+//     digit), then segment cut kernels.
+// After the segments, the plan counts the forward pass's work items: segment
+// g with m_g tokens and n_g rows yields ceil(m_g / 16) * ceil(n_g / chunk)
+// items, and seg_item_start is their exclusive prefix sum.
+
+#include "l3_device.h"
+#include "l3_internal.h"
+
+namespace l3 {
+
+// Record a bad id / bad row count, read one id's rows. Returns false if the
+// id is unusable.
+__device__ __forceinline__ bool id_rows(const PlanParams& p, int t,
+                                        int64_t* r0, int* n,
+                                        int32_t* header) {
+  if (t < 0 || t >= p.vocab) {
+    atomicOr(&header[0], kBadId);
+    *r0 = 0;
+    *n = 1;
+    return false;
+  }
+  int64_t a = p.offsets[t], b = p.offsets[t + 1];
+  int64_t cnt = b - a;
+  if (cnt < 1 || cnt > p.k_max || a < 0 || b > p.rows) {
+    atomicOr(&header[0], kBadCount);
+    *r0 = 0;
+    *n = 1;
+    return false;
+  }
+  *r0 = a;
+  *n = static_cast<int>(cnt);
+  return true;
+}
+
+__device__ __forceinline__ int items_of(int m, int n, int chunk) {
+  return ceil_div(m, kTokTile) * ceil_div(n, chunk);
+}
+
+// ---------------------------------------------------------------- small ---
+__global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
+                                                          PlanParams p) {
+  __shared__ unsigned long long keys[kSmallPlanMax];
+  __shared__ int tmp[1024 / 64 + 1];
+  __shared__ int s_total;
+  const int tid = threadIdx.x;
+  const int B = p.B;
+  int B2 = 1;
+  while (B2 < B) B2 <<= 1;
+  if (tid == 0) {
+    pd.header[0] = 0;
+  }
+  __syncthreads();
+
+  for (int i = tid; i < B2; i += 1024) {
+    unsigned long long k = ~0ull;
+    if (i < B) {
+      int t = p.ids[i];
+      if (t < 0 || t >= p.vocab) atomicOr(&pd.header[0], kBadId);
+      k = (static_cast<unsigned long long>(static_cast<uint32_t>(t)) << 32) |
+          static_cast<uint32_t>(i);
+    }
+    keys[i] = k;
+  }
+  __syncthreads();
+  // bitonic sort, ascending
+  for (int size = 2; size <= B2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (B2 >> 1); i += 1024) {
+        int lo = 2 * i - (i & (stride - 1));
+        int hi = lo + stride;
+        bool up = (lo & size) == 0;
+        unsigned long long a = keys[lo], b = keys[hi];
+        if ((a > b) == up) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // perm, sorted ids; segment flags scanned in contiguous chunks per thread
+  const int per = ceil_div(B, 1024);
+  const int j0 = min(B, tid * per), j1 = min(B, j0 + per);
+  int cnt = 0;
+  for (int j = j0; j < j1; ++j) {
+    unsigned long long k = keys[j];
+    int t = static_cast<int>(k >> 32);
+    pd.perm[j] = static_cast<int>(k & 0xffffffffu);
+    pd.sorted_ids[j] = t;
+    cnt += (j == 0 || t != static_cast<int>(keys[j - 1] >> 32)) ? 1 : 0;
+  }
+  int total;
+  int s = block_excl_scan<1024>(cnt, tmp, &total);
+  const int S = total;
+  for (int j = j0; j < j1; ++j) {
+    int t = static_cast<int>(keys[j] >> 32);
+    if (j == 0 || t != static_cast<int>(keys[j - 1] >> 32)) {
+      int64_t r0;
+      int n;
+      id_rows(p, t, &r0, &n, pd.header);
+      pd.seg_id[s] = t;
+      pd.seg_tok_start[s] = j;
+      pd.seg_row_off[s] = r0;
+      pd.seg_n[s] = n;
+      ++s;
+    }
+  }
+  if (tid == 0) {
+    pd.seg_tok_start[S] = B;
+    pd.header[1] = S;
+  }
+  __syncthreads();
+  // work items per segment, exclusive scan
+  const int sper = ceil_div(S, 1024);
+  const int s0 = min(S, tid * sper), s1 = min(S, s0 + sper);
+  int icnt = 0;
+  for (int g = s0; g < s1; ++g)
+    icnt += items_of(pd.seg_tok_start[g + 1] - pd.seg_tok_start[g],
+                     pd.seg_n[g], p.chunk_rows);
+  int ibase = block_excl_scan<1024>(icnt, tmp, &total);
+  for (int g = s0; g < s1; ++g) {
+    pd.seg_item_start[g] = ibase;
+    ibase += items_of(pd.seg_tok_start[g + 1] - pd.seg_tok_start[g],
+                      pd.seg_n[g], p.chunk_rows);
+  }
+  if (tid == 0) {
+    pd.seg_item_start[S] = total;
+    pd.header[2] = total;
+  }
+  (void)s_total;
+}
+
+// ---------------------------------------------------------------- large ---
+__global__ void header_init_kernel(int32_t* header) {
+  if (threadIdx.x < 4) header[threadIdx.x] = 0;
+}
+
+// Digit histogram of one 1024-key tile; pass 0 also checks the id range.
+__global__ __launch_bounds__(256) void radix_hist_kernel(
+    const int32_t* kin, int B, int shift, int32_t* hist, int nblk,
+    int64_t vocab, int32_t* header, int validate) {
+  __shared__ int h[256];
+  const int tid = threadIdx.x;
+  h[tid] = 0;
+  __syncthreads();
+  for (int r = 0; r < kSortTile / 256; ++r) {
+    int i = blockIdx.x * kSortTile + r * 256 + tid;
+    if (i < B) {
+      int k = kin[i];
+      if (validate && (k < 0 || k >= vocab)) atomicOr(&header[0], kBadId);
+      atomicAdd(&h[(static_cast<uint32_t>(k) >> shift) & 255u], 1);
+    }
+  }
+  __syncthreads();
+  hist[tid * nblk + blockIdx.x] = h[tid];
+}
+
+// In-place exclusive scan of n ints by one 1024-thread workgroup; the total
+// goes to *total_out when given.
+__global__ __launch_bounds__(1024) void scan_single_kernel(int32_t* a, int n,
+                                                           int32_t* total_out) {
+  __shared__ int tmp[1024 / 64 + 1];
+  const int tid = threadIdx.x;
+  const int per = ceil_div(n, 1024);
+  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  int sum = 0;
+  for (int i = i0; i < i1; ++i) sum += a[i];
+  int total;
+  int run = block_excl_scan<1024>(sum, tmp, &total);
+  for (int i = i0; i < i1; ++i) {
+    int v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  if (tid == 0 && total_out) *total_out = total;
+}
+
+// Stable scatter of one 1024-key tile by one digit. Keys of a tile are taken
+// in order, 256 at a time; within a wave the rank among equal digits comes
+// from a ballot match on the 8 digit bits, across waves from LDS counts.
+__global__ __launch_bounds__(256) void radix_scatter_kernel(
+    const int32_t* kin, const int32_t* vin, int32_t* kout, int32_t* vout,
+    int B, int shift, const int32_t* hist, int nblk) {
+  __shared__ int base[256];
+  __shared__ int wcnt[4][256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  base[tid] = hist[tid * nblk + blockIdx.x];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
+  __syncthreads();
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int r = 0; r < kSortTile / 256; ++r) {
+    const int i = blockIdx.x * kSortTile + r * 256 + tid;
+    const bool valid = i < B;
+    const int key = valid ? kin[i] : 0;
+    const int val = valid ? (vin ? vin[i] : i) : 0;
+    const uint32_t dig = (static_cast<uint32_t>(key) >> shift) & 255u;
+    unsigned long long match = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (dig >> b) & 1u;
+      const unsigned long long bal = __ballot(bit);
+      match &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(match & below);
+    if (valid && rank == 0) wcnt[w][dig] = __popcll(match);
+    __syncthreads();
+    if (valid) {
+      int pre = 0;
+      for (int q = 0; q < w; ++q) pre += wcnt[q][dig];
+      const int pos = base[dig] + pre + rank;
+      kout[pos] = key;
+      vout[pos] = val;
+    }
+    __syncthreads();
+    base[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
+    __syncthreads();
+  }
+}
+
+// Segment boundaries per 1024-token tile.
+__global__ __launch_bounds__(256) void seg_count_kernel(const int32_t* sid,
+                                                        int B, int32_t* blk) {
+  __shared__ int tmp[256 / 64 + 1];
+  const int tid = threadIdx.x;
+  int c = 0;
+  for (int r = 0; r < kSortTile / 256; ++r) {
+    int j = blockIdx.x * kSortTile + r * 256 + tid;
+    if (j < B && (j == 0 || sid[j] != sid[j - 1])) ++c;
+  }
+  int total;
+  block_excl_scan<256>(c, tmp, &total);
+  if (tid == 0) blk[blockIdx.x] = total;
+}
+
+// Write the segment arrays; blk holds the exclusive scan of the tile counts
+// and blk[nblk] the total S.
+__global__ __launch_bounds__(256) void seg_write_kernel(PlanDev pd,
+                                                        PlanParams p,
+                                                        int nblk) {
+  __shared__ int tmp[256 / 64 + 1];
+  const int tid = threadIdx.x;
+  const int B = p.B;
+  // each thread takes 4 consecutive positions of the tile, in order
+  const int j0 = blockIdx.x * kSortTile + tid * 4;
+  int c = 0;
+  for (int q = 0; q < 4; ++q) {
+    int j = j0 + q;
+    if (j < B && (j == 0 || pd.sorted_ids[j] != pd.sorted_ids[j - 1])) ++c;
+  }
+  int total;
+  int s = pd.blk[blockIdx.x] + block_excl_scan<256>(c, tmp, &total);
+  for (int q = 0; q < 4; ++q) {
+    int j = j0 + q;
+    if (j < B && (j == 0 || pd.sorted_ids[j] != pd.sorted_ids[j - 1])) {
+      int t = pd.sorted_ids[j];
+      int64_t r0;
+      int n;
+      id_rows(p, t, &r0, &n, pd.header);
+      pd.seg_id[s] = t;
+      pd.seg_tok_start[s] = j;
+      pd.seg_row_off[s] = r0;
+      pd.seg_n[s] = n;
+      ++s;
+    }
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    const int S = pd.blk[nblk];
+    pd.seg_tok_start[S] = B;
+    pd.header[1] = S;
+  }
+}
+
+// Work items per segment (into seg_item_start, scanned afterwards).
+__global__ __launch_bounds__(256) void seg_items_kernel(PlanDev pd,
+                                                        PlanParams p) {
+  const int S = pd.header[1];
+  for (int g = blockIdx.x * 256 + threadIdx.x; g < S;
+       g += gridDim.x * 256) {
+    pd.seg_item_start[g] = items_of(
+        pd.seg_tok_start[g + 1] - pd.seg_tok_start[g], pd.seg_n[g],
+        p.chunk_rows);
+  }
+}
+
+// Scan seg_item_start[0..S) in place; the count S is read on the device.
+__global__ __launch_bounds__(1024) void seg_items_scan_kernel(PlanDev pd) {
+  __shared__ int tmp[1024 / 64 + 1];
+  const int n = pd.header[1];
+  int32_t* a = pd.seg_item_start;
+  const int tid = threadIdx.x;
+  const int per = ceil_div(n, 1024);
+  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  int sum = 0;
+  for (int i = i0; i < i1; ++i) sum += a[i];
+  int total;
+  int run = block_excl_scan<1024>(sum, tmp, &total);
+  for (int i = i0; i < i1; ++i) {
+    int v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  if (tid == 0) {
+    a[n] = total;
+    pd.header[2] = total;
+  }
+}
+
+static int digit_passes(int64_t vocab) {
+  int bits = 1;
+  while (bits < 32 && (int64_t(1) << bits) < vocab) ++bits;
+  return (bits + 7) / 8;
+}
+
+hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
+                       hipStream_t s) {
+  const int B = p.B;
+  if (B <= kSmallPlanMax) {
+    plan_small_kernel<<<1, 1024, 0, s>>>(pd, p);
+    return hipGetLastError();
+  }
+  const int nblk = ceil_div(B, kSortTile);
+  header_init_kernel<<<1, 64, 0, s>>>(pd.header);
+  const int passes = digit_passes(p.vocab);
+  // ping-pong so that the last pass lands in (sorted_ids, perm)
+  int32_t* ka[2] = {pd.sorted_ids, pd.keys_alt};
+  int32_t* va[2] = {pd.perm, pd.vals_alt};
+  int out = (passes % 2 == 1) ? 0 : 1;
+  const int32_t* kin = p.ids;
+  const int32_t* vin = nullptr;
+  for (int ps = 0; ps < passes; ++ps) {
+    const int shift = 8 * ps;
+    radix_hist_kernel<<<nblk, 256, 0, s>>>(kin, B, shift, pd.hist, nblk,
+                                           p.vocab, pd.header, ps == 0);
+    scan_single_kernel<<<1, 1024, 0, s>>>(pd.hist, 256 * nblk, nullptr);
+    radix_scatter_kernel<<<nblk, 256, 0, s>>>(kin, vin, ka[out], va[out], B,
+                                              shift, pd.hist, nblk);
+    kin = ka[out];
+    vin = va[out];
+    out ^= 1;
+  }
+  seg_count_kernel<<<nblk, 256, 0, s>>>(pd.sorted_ids, B, pd.blk);
+  scan_single_kernel<<<1, 1024, 0, s>>>(pd.blk, nblk, pd.blk + nblk);
+  seg_write_kernel<<<nblk, 256, 0, s>>>(pd, p, nblk);
+  seg_items_kernel<<<ceil_div(B, 256), 256, 0, s>>>(pd, p);
+  seg_items_scan_kernel<<<1, 1024, 0, s>>>(pd);
+  return hipGetLastError();
+}
+
+}  // namespace l3

@@ -1,0 +1,445 @@
+// Segment forward: a_i = V_t^T Softmax(K_t x_i) for every token, with the
+// batch grouped by id so that each id's rows are read once per 16 tokens.
+//
+// gist.science explainer of "L^3: Large Lookup Layers", Technical Summary,
+// Core Architecture: after the static lookup of K_t and V_t, the hidden
+// state attends over them (Context-Dependent Aggregation), giving
+// V_t^T Softmax(K_t x) inside the Mathematical Formulation. Systems-Friendly
+// Design, Batch Sorting: grouping tokens by id makes the mask
+// block-diagonal, so one block of tokens shares one read of K_t, V_t.
+//
+// Work item = (segment, tile of <= 16 of its tokens, chunk of its rows). One
+// wavefront owns one item at a time; the four wavefronts of a workgroup are
+// independent (no workgroup barrier), and wavefronts loop over the items
+// round-robin.
+//   1. scores S = X K_chunk^T with 16x16 MFMA blocks (bf16 16x16x32 or f32
+//      16x16x4), both operands streamed straight from global memory into
+//      registers: lane l reads 16 (bf16) or 4 (f32) consecutive elements of
+//      row l & 15, so each 64-element slice of a row is one full 128-byte
+//      line, and the two (or four) MFMAs of a slice use the same lane->k
+//      assignment for A and B (the contraction does not care which k a slot
+//      holds as long as both operands agree);
+//   2. exact softmax over the chunk (row max and row sum across the 16 lanes
+//      holding a row), unnormalised weights to this wave's LDS (fp16 for
+//      bf16 inputs, f32 for f32 inputs), laid out [row j][token];
+//   3. aggregation acc[t][e] += p[t][j] * V[j][e] on the vector ALU: lane l
+//      owns columns e = l*EPL .. l*EPL+EPL-1, so every V row is one
+//      coalesced load, and the token loop is bounded by the real tile size;
+//   4. single chunk: a = acc / rowsum, written in original token order;
+//      several chunks: (max, sum, acc) partials, merged by seg_combine in a
+//      fixed chunk order (exact, deterministic).
+
+#include "l3_device.h"
+#include "l3_internal.h"
+
+namespace l3 {
+
+constexpr int kNBMax = 32;  // 16-row blocks per item: 512 rows
+
+template <bool BF16>
+struct Types;
+template <>
+struct Types<true> {
+  typedef uint16_t T;
+  typedef _Float16 P;
+};
+template <>
+struct Types<false> {
+  typedef float T;
+  typedef float P;
+};
+
+// ---- scores --------------------------------------------------------------
+template <int NB>
+__device__ __forceinline__ void scores_bf16(const uint16_t* __restrict__ xr,
+                                            const uint16_t* __restrict__ kt,
+                                            int d, int nc, int r, int g,
+                                            floatx4 (&acc)[kNBMax]) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  int koff[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    koff[nb] = min(nb * 16 + r, nc - 1) * d + g * 16;
+  const uint16_t* xp = xr + g * 16;
+  for (int kc = 0; kc < d; kc += 64) {
+    const uint4 x0 = *reinterpret_cast<const uint4*>(xp + kc);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(xp + kc + 8);
+    constexpr int G = NB < 8 ? NB : 8;  // blocks whose loads are in flight
+#pragma unroll
+    for (int nb0 = 0; nb0 < NB; nb0 += G) {
+      uint4 k0[G], k1[G];
+#pragma unroll
+      for (int q = 0; q < G; ++q) {
+        k0[q] = *reinterpret_cast<const uint4*>(kt + koff[nb0 + q] + kc);
+        k1[q] = *reinterpret_cast<const uint4*>(kt + koff[nb0 + q] + kc + 8);
+      }
+#pragma unroll
+      for (int q = 0; q < G; ++q) {
+        acc[nb0 + q] = mfma_bf16(x0, k0[q], acc[nb0 + q]);
+        acc[nb0 + q] = mfma_bf16(x1, k1[q], acc[nb0 + q]);
+      }
+    }
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void scores_f32(const float* __restrict__ xr,
+                                           const float* __restrict__ kt,
+                                           int d, int nc, int r, int g,
+                                           floatx4 (&acc)[kNBMax]) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  int koff[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    koff[nb] = min(nb * 16 + r, nc - 1) * d + g * 4;
+  const float* xp = xr + g * 4;
+  for (int kc = 0; kc < d; kc += 16) {
+    const float4 xv = *reinterpret_cast<const float4*>(xp + kc);
+    float4 kv[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      kv[nb] = *reinterpret_cast<const float4*>(kt + koff[nb] + kc);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      acc[nb] = mfma_f32(xv.x, kv[nb].x, acc[nb]);
+      acc[nb] = mfma_f32(xv.y, kv[nb].y, acc[nb]);
+      acc[nb] = mfma_f32(xv.z, kv[nb].z, acc[nb]);
+      acc[nb] = mfma_f32(xv.w, kv[nb].w, acc[nb]);
+    }
+  }
+}
+
+// ---- softmax --------------------------------------------------------------
+// Row 4g+i of the tile is token 4g+i; column nb*16 + r is row j of the chunk.
+template <int NB, typename PT>
+__device__ __forceinline__ void softmax_rows(floatx4 (&acc)[kNBMax], int nc,
+                                             int r, int g, PT* P, float* ml) {
+  float mx[4], sm[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mx[i] = -INFINITY;
+    sm[i] = 0.f;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if (nb * 16 + r < nc) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], acc[nb][i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mx[i] = group16_max(mx[i]);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int col = nb * 16 + r;
+    if (col < nc) {
+      PT* dst = P + col * kTokTile + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __expf(acc[nb][i] - mx[i]);
+        sm[i] += p;
+        dst[i] = static_cast<PT>(p);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sm[i] = group16_sum(sm[i]);
+  if (r == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ml[(4 * g + i) * 2] = mx[i];
+      ml[(4 * g + i) * 2 + 1] = sm[i];
+    }
+  }
+}
+
+// ---- aggregation ------------------------------------------------------------
+template <int EPL>
+__device__ __forceinline__ void load_row(const uint16_t* p, float (&v)[EPL]) {
+  if constexpr (EPL == 8) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+  } else if constexpr (EPL == 4) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(u.x << 16);
+    v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16);
+    v[3] = __uint_as_float(u.y & 0xffff0000u);
+  } else if constexpr (EPL == 2) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+    v[0] = __uint_as_float(u << 16);
+    v[1] = __uint_as_float(u & 0xffff0000u);
+  } else {
+    v[0] = bf2f(*p);
+  }
+}
+template <int EPL>
+__device__ __forceinline__ void load_row(const float* p, float (&v)[EPL]) {
+  if constexpr (EPL % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < EPL / 4; ++q) {
+      const float4 f = reinterpret_cast<const float4*>(p)[q];
+      v[4 * q] = f.x;
+      v[4 * q + 1] = f.y;
+      v[4 * q + 2] = f.z;
+      v[4 * q + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[e] = p[e];
+  }
+}
+
+template <int MTOK, int EPL, typename T, typename PT>
+__device__ __forceinline__ void aggregate(const T* __restrict__ vt, int d_e,
+                                          int nc, const PT* P,
+                                          float (&acc)[16][EPL]) {
+#pragma unroll
+  for (int t = 0; t < MTOK; ++t)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
+#pragma unroll 4
+  for (int j = 0; j < nc; ++j) {
+    float v[EPL];
+    load_row<EPL>(vt + static_cast<int64_t>(j) * d_e, v);
+    const PT* pj = P + j * kTokTile;
+#pragma unroll
+    for (int t = 0; t < MTOK; ++t) {
+      const float p = static_cast<float>(pj[t]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[t][e] = fmaf(p, v[e], acc[t][e]);
+    }
+  }
+}
+
+template <int EPL, typename T>
+__device__ __forceinline__ void store_row(T* dst, const float (&v)[EPL]);
+template <int EPL>
+__device__ __forceinline__ void store_row(uint16_t* dst,
+                                          const float (&v)[EPL]) {
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dst[e] = f2bf(v[e]);
+}
+template <int EPL>
+__device__ __forceinline__ void store_row(float* dst, const float (&v)[EPL]) {
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dst[e] = v[e];
+}
+
+template <int MTOK, int EPL, bool BF16>
+__device__ __forceinline__ void aggregate_and_store(
+    const SegFwdArgs& a, const typename Types<BF16>::T* vt, int nc,
+    const typename Types<BF16>::P* P, const float* ml, int tok0, int mcount,
+    int nch, int chunk, int lane) {
+  typedef typename Types<BF16>::T T;
+  const int passes = a.d_e / (64 * EPL);
+  for (int ps = 0; ps < passes; ++ps) {
+    const int e0 = ps * 64 * EPL + lane * EPL;
+    float acc[16][EPL];
+    aggregate<MTOK, EPL>(vt + e0, a.d_e, nc, P, acc);
+#pragma unroll
+    for (int t = 0; t < MTOK; ++t) {
+      if (t < mcount) {
+        const int pos = tok0 + t;
+        if (nch == 1) {
+          const float inv = 1.0f / ml[2 * t + 1];
+          float o[EPL];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[e] = acc[t][e] * inv;
+          const int64_t orig = a.perm[pos];
+          store_row<EPL>(static_cast<T*>(a.a_out) + orig * a.d_e + e0, o);
+          if (a.a_save) store_row<EPL>(a.a_save + orig * a.d_e + e0, o);
+        } else {
+          const int64_t slot =
+              static_cast<int64_t>(pos) * a.nch_max + chunk;
+          store_row<EPL>(a.part + slot * a.d_e + e0, acc[t]);
+          if (ps == 0 && lane == 0) {
+            a.part_ml[slot * 2] = ml[2 * t];
+            a.part_ml[slot * 2 + 1] = ml[2 * t + 1];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int NB, bool BF16>
+__device__ __forceinline__ void scores_softmax(
+    const typename Types<BF16>::T* xr, const typename Types<BF16>::T* kt,
+    int d, int nc, int r, int g, typename Types<BF16>::P* P, float* ml) {
+  floatx4 acc[kNBMax];
+  if constexpr (BF16)
+    scores_bf16<NB>(xr, kt, d, nc, r, g, acc);
+  else
+    scores_f32<NB>(xr, kt, d, nc, r, g, acc);
+  softmax_rows<NB>(acc, nc, r, g, P, ml);
+}
+
+template <bool BF16, int EPL>
+__global__ __launch_bounds__(256) void seg_fwd_kernel(SegFwdArgs a) {
+  typedef typename Types<BF16>::T T;
+  typedef typename Types<BF16>::P PT;
+  __shared__ PT s_p[4][kNBMax * 16 * kTokTile];
+  __shared__ float s_ml[4][2 * kTokTile];
+  if (a.header[0] != 0) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int S = a.header[1];
+  const int n_items = a.header[2];
+  PT* P = s_p[w];
+  float* ml = s_ml[w];
+  const T* X = static_cast<const T*>(a.x);
+  const T* K = static_cast<const T*>(a.K);
+  const T* V = static_cast<const T*>(a.V);
+  for (int item = blockIdx.x * 4 + w; item < n_items;
+       item += gridDim.x * 4) {
+    // segment owning this item: last s with seg_item_start[s] <= item
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.seg_item_start[mid] <= item)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int s = lo;
+    const int t_begin = a.seg_tok_start[s];
+    const int m = a.seg_tok_start[s + 1] - t_begin;
+    const int n = a.seg_n[s];
+    const int nch = ceil_div(n, a.chunk_rows);
+    const int local = item - a.seg_item_start[s];
+    const int tile = local / nch, chunk = local - tile * nch;
+    const int tok0 = t_begin + tile * kTokTile;
+    const int mcount = min(kTokTile, m - tile * kTokTile);
+    const int j0 = chunk * a.chunk_rows;
+    const int nc = min(a.chunk_rows, n - j0);
+    const int64_t rowbase = a.seg_row_off[s] + j0;
+
+    const int64_t xrow = a.perm[tok0 + min(r, mcount - 1)];
+    const T* xr = X + xrow * a.d;
+    const T* kt = K + rowbase * a.d;
+    const int nbc = ceil_div(nc, 16);
+    __builtin_amdgcn_wave_barrier();
+    if (nbc <= 1)
+      scores_softmax<1, BF16>(xr, kt, a.d, nc, r, g, P, ml);
+    else if (nbc <= 2)
+      scores_softmax<2, BF16>(xr, kt, a.d, nc, r, g, P, ml);
+    else if (nbc <= 4)
+      scores_softmax<4, BF16>(xr, kt, a.d, nc, r, g, P, ml);
+    else if (nbc <= 8)
+      scores_softmax<8, BF16>(xr, kt, a.d, nc, r, g, P, ml);
+    else if (nbc <= 16)
+      scores_softmax<16, BF16>(xr, kt, a.d, nc, r, g, P, ml);
+    else
+      scores_softmax<32, BF16>(xr, kt, a.d, nc, r, g, P, ml);
+    __builtin_amdgcn_wave_barrier();
+
+    const T* vt = V + rowbase * a.d_e;
+    if (mcount <= 1)
+      aggregate_and_store<1, EPL, BF16>(a, vt, nc, P, ml, tok0, mcount, nch,
+                                        chunk, lane);
+    else if (mcount <= 2)
+      aggregate_and_store<2, EPL, BF16>(a, vt, nc, P, ml, tok0, mcount, nch,
+                                        chunk, lane);
+    else if (mcount <= 4)
+      aggregate_and_store<4, EPL, BF16>(a, vt, nc, P, ml, tok0, mcount, nch,
+                                        chunk, lane);
+    else if (mcount <= 8)
+      aggregate_and_store<8, EPL, BF16>(a, vt, nc, P, ml, tok0, mcount, nch,
+                                        chunk, lane);
+    else
+      aggregate_and_store<16, EPL, BF16>(a, vt, nc, P, ml, tok0, mcount, nch,
+                                         chunk, lane);
+  }
+}
+
+// Merge the row-chunk partials of every token whose id needed more than one
+// chunk: M = max_c m_c, L = sum_c l_c e^(m_c - M),
+// a = sum_c acc_c e^(m_c - M) / L, chunks taken in order.
+template <bool BF16>
+__global__ __launch_bounds__(256) void seg_combine_kernel(CombineArgs a) {
+  typedef typename Types<BF16>::T T;
+  if (a.header[0] != 0) return;
+  const int lane = threadIdx.x & 63;
+  const int pos = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pos >= a.B) return;
+  const int S = a.header[1];
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.seg_tok_start[mid] <= pos)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int nch = ceil_div(a.seg_n[lo], a.chunk_rows);
+  if (nch <= 1) return;
+  const int64_t slot0 = static_cast<int64_t>(pos) * a.nch_max;
+  float M = -INFINITY;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, a.part_ml[(slot0 + c) * 2]);
+  float L = 0.f;
+  for (int c = 0; c < nch; ++c)
+    L += a.part_ml[(slot0 + c) * 2 + 1] * __expf(a.part_ml[(slot0 + c) * 2] - M);
+  const float invL = 1.0f / L;
+  const int64_t orig = a.perm[pos];
+  for (int e = lane; e < a.d_e; e += 64) {
+    float acc = 0.f;
+    for (int c = 0; c < nch; ++c)
+      acc += a.part[(slot0 + c) * a.d_e + e] *
+             __expf(a.part_ml[(slot0 + c) * 2] - M);
+    const float v = acc * invL;
+    st<T>(static_cast<T*>(a.a_out), orig * a.d_e + e, v);
+    if (a.a_save) a.a_save[orig * a.d_e + e] = v;
+  }
+}
+
+template <bool BF16>
+static hipError_t seg_fwd_dispatch(const SegFwdArgs& a, int grid,
+                                   hipStream_t s) {
+  const int q = a.d_e / 64;  // d_e is a multiple of 64
+  const int epl = q % 8 == 0 ? 8 : q % 4 == 0 ? 4 : q % 2 == 0 ? 2 : 1;
+  switch (epl) {
+    case 8:
+      seg_fwd_kernel<BF16, 8><<<grid, 256, 0, s>>>(a);
+      break;
+    case 4:
+      seg_fwd_kernel<BF16, 4><<<grid, 256, 0, s>>>(a);
+      break;
+    case 2:
+      seg_fwd_kernel<BF16, 2><<<grid, 256, 0, s>>>(a);
+      break;
+    default:
+      seg_fwd_kernel<BF16, 1><<<grid, 256, 0, s>>>(a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t seg_fwd_launch(const SegFwdArgs& a, int dtype, int B, int items_ub,
+                          hipStream_t s) {
+  (void)B;
+  int grid = ceil_div(items_ub, 4);
+  if (grid > 2048) grid = 2048;
+  if (grid < 1) grid = 1;
+  return dtype == kBF16 ? seg_fwd_dispatch<true>(a, grid, s)
+                        : seg_fwd_dispatch<false>(a, grid, s);
+}
+
+hipError_t seg_combine_launch(const CombineArgs& a, int dtype,
+                              hipStream_t s) {
+  const int grid = ceil_div(a.B, 4);
+  if (dtype == kBF16)
+    seg_combine_kernel<true><<<grid, 256, 0, s>>>(a);
+  else
+    seg_combine_kernel<false><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace l3

@@ -13,7 +13,8 @@ Layers", Technical Summary):
     frequency-proportional count stands in for the paper's corpus-driven
     allocation, and Zipf-distributed ids stand in for natural-text tokens.
 
-Recipe (all draws in float64, then rounded once to the storage dtype):
+Recipe (draws in float64 -- tables in float32 -- then rounded once to the
+storage dtype):
   * f_t = (t+1)^-s / sum_u (u+1)^-s over t in [0, V)  (id = frequency rank)
   * n_t = clamp(floor(budget * f_t), 1, cap); offsets = exclusive prefix sum
   * ids ~ Categorical(f) through the inverse CDF of uniform draws
@@ -181,10 +182,41 @@ def batch_ids(spec: Spec, cfg: int, batch: Optional[int] = None) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- tables ---
-def _normal_block(cfg, stream, block, rows, cols, sigma, dtype):
+_SUB_ROWS_ELEMS = 1 << 20  # elements drawn per sub-chunk (4 MB of float32)
+
+
+def _fill_block(out_block: np.ndarray, cfg: int, stream: int, block: int,
+                sigma: float) -> None:
+    """Fill one table block with N(0, sigma) draws (float32 generator).
+
+    Tables are drawn in float32 (they end as bf16 or float32 anyway), in
+    sub-chunks of whole rows through reused buffers, and rounded straight
+    into the output; fresh multi-GB temporaries are never allocated.
+    """
     g = _rng(cfg, stream, block)
-    v = g.standard_normal((rows, cols)) * sigma
-    return store(v, dtype)
+    rows, cols = out_block.shape
+    step = max(1, _SUB_ROWS_ELEMS // cols)
+    buf = np.empty((step, cols), np.float32)
+    tmp = np.empty((step, cols), np.uint32) if out_block.dtype == np.uint16 \
+        else None
+    sig = np.float32(sigma)
+    for r0 in range(0, rows, step):
+        n = min(step, rows - r0)
+        b = buf[:n]
+        g.standard_normal(out=b, dtype=np.float32)
+        np.multiply(b, sig, out=b)
+        if tmp is None:
+            out_block[r0:r0 + n] = b
+        else:
+            u = b.view(np.uint32)
+            t = tmp[:n]
+            # round to nearest even: u + 0x7FFF + ((u >> 16) & 1), then >> 16
+            np.right_shift(u, np.uint32(16), out=t)
+            np.bitwise_and(t, np.uint32(1), out=t)
+            np.add(t, np.uint32(0x7FFF), out=t)
+            np.add(t, u, out=t)
+            np.right_shift(t, np.uint32(16), out=t)
+            np.copyto(out_block[r0:r0 + n], t, casting="unsafe")
 
 
 def draw_table(cfg: int, stream: int, rows: int, cols: int, sigma: float,
@@ -196,7 +228,7 @@ def draw_table(cfg: int, stream: int, rows: int, cols: int, sigma: float,
     def fill(b):
         r0 = b * TABLE_BLOCK
         r1 = min(rows, r0 + TABLE_BLOCK)
-        out[r0:r1] = _normal_block(cfg, stream, b, r1 - r0, cols, sigma, dtype)
+        _fill_block(out[r0:r1], cfg, stream, b, sigma)
 
     if threads is None:
         threads = min(16, os.cpu_count() or 1)
