@@ -503,10 +503,11 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       e = seg_combine_launch(ca, d.dtype, s);
       if (e != hipSuccess) return L3_ERR_HIP;
     }
-    // u = a W_up^T  (float32 out)
+    // u = a W_up^T  (float32 out). When training, the float32 aggregate is
+    // the operand, so the saved LayerNorm state carries no bf16 rounding of a.
     GemmArgs up{};
-    up.A1 = f.a_act;
-    up.A2 = f.a_act;
+    up.A1 = save ? static_cast<const void*>(sv.a32) : f.a_act;
+    up.A2 = up.A1;
     up.a1_m = up.a2_m = d.d_e;
     up.a1_k = up.a2_k = 1;
     up.K1 = d.d_e;
@@ -521,10 +522,10 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     up.header = pd.header;
     {
       StageTimer t(plan, ST_UP, s);
-      if (d.dtype == L3_BF16 && gemm_nt_mfma_ok(up))
+      if (!save && d.dtype == L3_BF16 && gemm_nt_mfma_ok(up))
         e = gemm_nt_mfma_launch(up, kF32, s);
       else
-        e = gemm_launch(up, d.dtype, d.dtype, kF32, s);
+        e = gemm_launch(up, save ? kF32 : d.dtype, d.dtype, kF32, s);
     }
     if (e != hipSuccess) return L3_ERR_HIP;
     LnArgs ln;
