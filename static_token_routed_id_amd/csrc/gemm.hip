@@ -194,6 +194,225 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmArgs g) {
   }
 }
 
+// ------------------------------------------------- bf16 MFMA, 256 x 256 ---
+// One workgroup (4 waves, one per SIMD) owns a 256 x 256 tile of C; wave
+// (wm, wn) owns rows wm*128.. and columns wn*128.. as 4 x 4 blocks of
+// 32x32x16 MFMA results (256 float accumulators per lane, in AGPRs). The K
+// loop walks 64-wide slices: both operand slices (256 rows x 128 bytes)
+// sit in LDS, double buffered (2 x 2 x 36 KB, rows padded to 72 elements so
+// the 8 lanes served per LDS cycle hit distinct banks), and the slice two
+// steps ahead is loaded from global memory into registers while the current
+// one is multiplied, so one barrier per slice suffices. The prefetch is
+// unconditional (clamped to the last slice) so the staging registers are
+// never demoted to scratch memory.
+//
+// Tile order is XCD-aware: workgroup b runs on XCD b % 8, so tiles are
+// renumbered to give each XCD a contiguous range of the logical order, which
+// walks groups of 4 row-tiles x all column-tiles; the workgroups resident
+// on one XCD at a time share A and B panels in that XCD's L2.
+constexpr int kTM = 256, kTN = 256, kTK = 64, kTL = kTK + 8;
+constexpr int kXcd = 8, kGroupM = 4;
+
+template <typename TC, bool STATS>
+__global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
+  __shared__ uint16_t lds[2][2][kTM * kTL];
+  if (g.header && g.header[0] != 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int mt = ceil_div(g.M, kTM), nt = g.N / kTN;
+  const int T = mt * nt;
+  int tile = blockIdx.x;
+  if (T % kXcd == 0 && mt % kGroupM == 0)
+    tile = (blockIdx.x % kXcd) * (T / kXcd) + blockIdx.x / kXcd;
+  int m_tile, n_tile;
+  if (mt % kGroupM == 0) {
+    const int grp = tile / (kGroupM * nt), in = tile % (kGroupM * nt);
+    m_tile = grp * kGroupM + in % kGroupM;
+    n_tile = in / kGroupM;
+  } else {
+    m_tile = tile / nt;
+    n_tile = tile % nt;
+  }
+  const int m0 = m_tile * kTM, n0 = n_tile * kTN;
+  const uint16_t* A1 = static_cast<const uint16_t*>(g.A1);
+  const uint16_t* A2 = static_cast<const uint16_t*>(g.A2);
+  const uint16_t* Bm = static_cast<const uint16_t*>(g.Bm);
+
+  // global -> register mapping: 8 lanes per 128-byte row slice, 32 rows per
+  // pass, 8 passes per operand
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
+  int64_t aoff1[8], aoff2[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int64_t row = min(m0 + lr + 32 * q, g.M - 1);
+    aoff1[q] = row * g.a1_m + lc;
+    aoff2[q] = row * g.a2_m + lc;
+  }
+  const uint16_t* bbase = Bm + static_cast<int64_t>(n0 + lr) * g.b_n + lc;
+  const int64_t bstep = 32 * g.b_n;
+  u32x4 ra[8], rb[8];
+#define L3_LOAD_SLICE(k0)                                                     \
+  {                                                                           \
+    const int kk0 = (k0);                                                     \
+    const bool first = kk0 < g.K1;                                            \
+    const uint16_t* ab = first ? A1 + kk0 : A2 + (kk0 - g.K1);                \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                           \
+      ra[q] = *reinterpret_cast<const u32x4*>(ab + (first ? aoff1[q]          \
+                                                          : aoff2[q]));       \
+      rb[q] = *reinterpret_cast<const u32x4*>(bbase + q * bstep + kk0);       \
+    }                                                                         \
+  }
+#define L3_STORE_SLICE(buf)                                                   \
+  {                                                                           \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                           \
+      *reinterpret_cast<u32x4*>(&lds[buf][0][(lr + 32 * q) * kTL + lc]) =     \
+          ra[q];                                                              \
+      *reinterpret_cast<u32x4*>(&lds[buf][1][(lr + 32 * q) * kTL + lc]) =     \
+          rb[q];                                                              \
+    }                                                                         \
+  }
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+
+  const int nk = g.K / kTK;
+  const int r = lane & 31, kh = (lane >> 5) * 8;
+  L3_LOAD_SLICE(0)
+  L3_STORE_SLICE(0)
+  L3_LOAD_SLICE(min(1, nk - 1) * kTK)
+  __syncthreads();
+  for (int it = 0; it < nk; ++it) {
+    const uint16_t* As = lds[it & 1][0] + (wm * 128 + r) * kTL + kh;
+    const uint16_t* Bs = lds[it & 1][1] + (wn * 128 + r) * kTL + kh;
+#pragma unroll
+    for (int kk = 0; kk < kTK; kk += 16) {
+      u32x4 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(As + i * 32 * kTL + kk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bf[j] = *reinterpret_cast<const u32x4*>(Bs + j * 32 * kTL + kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = mfma32_bf16(af[i], bf[j], acc[i][j]);
+    }
+    // the slice after next lands in the buffer just read; its global loads
+    // overlap the next slice's multiplies (clamped: the tail reloads the
+    // last slice into a buffer nobody reads again)
+    L3_STORE_SLICE((it + 1) & 1)
+    L3_LOAD_SLICE(min(it + 2, nk - 1) * kTK)
+    __syncthreads();
+  }
+#undef L3_LOAD_SLICE
+#undef L3_STORE_SLICE
+
+  TC* C = static_cast<TC*>(g.C);
+  const int h4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int gm = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + h4 + (e & 3);
+      if (STATS) {
+        // 128 columns of row gm live in this wave: 4 per lane across the 32
+        // lanes of this half; mean and squared deviations of the float32
+        // values (two passes over registers)
+        float sm = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sm += acc[i][j][e];
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
+        const float mean = sm * (1.0f / 128.0f);
+        float m2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float c = acc[i][j][e] - mean;
+          m2 += c * c;
+        }
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) m2 += __shfl_xor(m2, o);
+        if (r == 0 && gm < g.M) {
+          const int chunk = (n0 + wn * 128) >> 7;
+          *reinterpret_cast<float2*>(
+              g.row_stats +
+              (static_cast<int64_t>(gm) * (g.N >> 7) + chunk) * 2) =
+              make_float2(mean, m2);
+        }
+      }
+      if (gm >= g.M) continue;
+      TC* crow = C + static_cast<int64_t>(gm) * g.c_m + n0 + wn * 128 + r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st<TC>(crow, j * 32, acc[i][j][e]);
+    }
+  }
+}
+
+bool gemm_nt_256_ok(const GemmArgs& g) {
+  return g.M >= 1024 && g.N % kTN == 0 && g.K % kTK == 0 &&
+         g.K1 % kTK == 0 && g.a1_k == 1 && g.a2_k == 1 && g.b_k == 1 &&
+         g.a1_m % 8 == 0 && g.a2_m % 8 == 0 && g.b_n % 8 == 0;
+}
+
+// ------------------------------------------------ LayerNorm from partials ---
+// One wave per row: combine the row's per-128-column (mean, M2) partials with
+// Chan's formula (equal chunk sizes), then h = gamma * (u - mean) * rstd +
+// beta on 8 bf16 elements per lane and step.
+__global__ __launch_bounds__(256) void ln_apply_kernel(LnApplyArgs a) {
+  if (a.header[0] != 0) return;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.B) return;
+  const int nch = a.d >> 7;
+  const float* st = a.stats + static_cast<int64_t>(row) * nch * 2;
+  float cm = 0.f, cq = 0.f;
+  if (lane < nch) {
+    const float2 v = *reinterpret_cast<const float2*>(st + 2 * lane);
+    cm = v.x;
+    cq = v.y;
+  }
+  const float mean = wave_sum(cm) / nch;
+  const float dev = lane < nch ? (cm - mean) : 0.f;
+  const float m2 = wave_sum(cq + 128.0f * dev * dev);
+  const float rstd = 1.0f / sqrtf(m2 / a.d + a.eps);
+  const int64_t base = static_cast<int64_t>(row) * a.d;
+  for (int e0 = lane * 8; e0 < a.d; e0 += 512) {
+    const uint4 u = *reinterpret_cast<const uint4*>(a.U + base + e0);
+    const uint4 gv = *reinterpret_cast<const uint4*>(a.gamma + e0);
+    const uint4 bv = *reinterpret_cast<const uint4*>(a.beta + e0);
+    const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+    uint32_t ow[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float u0 = __uint_as_float(uw[q] << 16);
+      const float u1 = __uint_as_float(uw[q] & 0xffff0000u);
+      const float g0 = __uint_as_float(gw[q] << 16);
+      const float g1 = __uint_as_float(gw[q] & 0xffff0000u);
+      const float b0 = __uint_as_float(bw[q] << 16);
+      const float b1 = __uint_as_float(bw[q] & 0xffff0000u);
+      const float h0 = g0 * ((u0 - mean) * rstd) + b0;
+      const float h1 = g1 * ((u1 - mean) * rstd) + b1;
+      ow[q] = static_cast<uint32_t>(f2bf(h0)) |
+              (static_cast<uint32_t>(f2bf(h1)) << 16);
+    }
+    *reinterpret_cast<uint4*>(a.h + base + e0) =
+        make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  }
+}
+
+hipError_t ln_apply_launch(const LnApplyArgs& a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  ln_apply_kernel<<<ceil_div(a.B, 4), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 bool gemm_nt_mfma_ok(const GemmArgs& g) {
   return g.M > 0 && g.N % kBN == 0 && g.K % kBK == 0 && g.K1 % kBK == 0 &&
          g.a1_k == 1 && g.a2_k == 1 && g.b_k == 1 && g.a1_m % 8 == 0 &&
@@ -202,6 +421,19 @@ bool gemm_nt_mfma_ok(const GemmArgs& g) {
 
 hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
+  if (gemm_nt_256_ok(g)) {
+    const int grid = ceil_div(g.M, kTM) * (g.N / kTN);
+    if (g.row_stats) {
+      if (c_type != kBF16) return hipErrorInvalidValue;
+      gemm_nt_256_kernel<uint16_t, true><<<grid, 256, 0, s>>>(g);
+    } else if (c_type == kBF16) {
+      gemm_nt_256_kernel<uint16_t, false><<<grid, 256, 0, s>>>(g);
+    } else {
+      gemm_nt_256_kernel<float, false><<<grid, 256, 0, s>>>(g);
+    }
+    return hipGetLastError();
+  }
+  if (g.row_stats) return hipErrorInvalidValue;
   dim3 grid(g.N / kBN, ceil_div(g.M, kBM));
   if (c_type == kBF16)
     gemm_nt_mfma_kernel<uint16_t><<<grid, 256, 0, s>>>(g);

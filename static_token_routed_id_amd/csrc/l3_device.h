@@ -8,6 +8,11 @@ namespace l3 {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float floatx4;
+typedef __attribute__((ext_vector_type(16))) float floatx16;
+// Native 16-byte vector: unlike the struct-based uint4, arrays of it stay in
+// registers (the struct type made the compiler keep staging arrays in
+// scratch memory).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -50,6 +55,15 @@ __device__ __forceinline__ void st<uint16_t>(uint16_t* p, int64_t i,
 __device__ __forceinline__ floatx4 mfma_bf16(const uint4& a, const uint4& b,
                                              floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0,
+      0, 0);
+}
+// 32x32x16 bf16 MFMA: lane l supplies row (l & 31) of A and column (l & 31)
+// of B, eight consecutive k values from half (l >> 5); element e of the
+// 32x32 float result is row 8*(e/4) + 4*(l >> 5) + (e % 4), column l & 31.
+__device__ __forceinline__ floatx16 mfma32_bf16(const u32x4& a,
+                                                const u32x4& b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
       __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0,
       0, 0);
 }

@@ -95,6 +95,9 @@ struct GemmArgs {
   int64_t c_m;
   int M, N, K;
   const int32_t* header;  // plan status word (kernel does nothing if set)
+  // Optional epilogue output: per row and per 128-column chunk of C, the
+  // chunk mean and sum of squared deviations (float2), [M x N/128].
+  float* row_stats;
 };
 
 // LayerNorm of float32 rows (one wave per row).
@@ -111,6 +114,19 @@ struct LnArgs {
   float* rstd_save;
 };
 
+// LayerNorm applied to bf16 rows whose per-128-column (mean, M2) partials
+// were written by the producing GEMM.
+struct LnApplyArgs {
+  const int32_t* header;
+  const uint16_t* U;       // [B x d] bf16
+  const float* stats;      // [B x d/128 x 2]
+  const uint16_t* gamma;
+  const uint16_t* beta;
+  int B, d;
+  float eps;
+  uint16_t* h;             // [B x d] bf16
+};
+
 enum ElemType { kF32 = L3_F32, kBF16 = L3_BF16 };
 
 // ---- launchers (return the first HIP error) -------------------------------
@@ -123,6 +139,9 @@ hipError_t gemm_launch(const GemmArgs& g, int a_type, int b_type, int c_type,
                        hipStream_t s);
 hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s);
 bool gemm_nt_mfma_ok(const GemmArgs& g);
+// The 256 x 256 tile kernel (needed for the row-statistics epilogue).
+bool gemm_nt_256_ok(const GemmArgs& g);
+hipError_t ln_apply_launch(const LnApplyArgs& a, hipStream_t s);
 hipError_t ln_launch(const LnArgs& a, int dtype, hipStream_t s);
 
 struct BwdArgs {

@@ -50,9 +50,12 @@ def test_tiny_fp32(ln_perturb):
     _check(w, res, gu.oracle_forward(w))
 
 
-def test_prefill_bf16():
-    w = gu.workload("prefill_bf16")
-    res = gu.run(w, training=True)
+@pytest.mark.parametrize("training", [False, True])
+def test_prefill_bf16(training):
+    """Inference (bf16 u + LayerNorm partials from the W_up epilogue) and
+    training (float32 u, saved state) paths."""
+    w = gu.workload("prefill_bf16", True)
+    res = gu.run(w, training=training)
     _check(w, res, gu.oracle_forward(w))
 
 
