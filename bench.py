@@ -6,11 +6,12 @@ batch, all resident in HBM before timing starts. Default workload: the
 large-prefill configuration (65536 tokens, vocab 131072, 2^22-row budget,
 d = 2048, d_e = 512, bf16 inputs, float32 accumulation and output).
 
-Prints one JSON line. `roofline` is the gather/aggregate kernel (seg_fwd):
-algorithmic bytes per launch (each distinct id's K_t and V_t rows once, x
-read, a written, ids and segment records) over its mean launch time taken
-from HIP events recorded around it on its own stream during the timed
-steps. `cpu_baseline` is the fp64 oracle on a bounded sample of the same
+Prints one JSON line. `roofline` is the gather/aggregate step, two kernels
+(seg_fwd for ids with few rows, seg_group for ids with many rows in large
+batches): algorithmic bytes per launch (each distinct id's K_t and V_t rows
+once, x read, a written, ids and segment records) over the mean launch
+times taken from HIP events recorded around each kernel on its own stream
+during the timed steps. `cpu_baseline` is the fp64 oracle on a bounded sample of the same
 batch on the host CPU.
 """
 from __future__ import annotations
@@ -31,17 +32,21 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 
 
-def algorithmic_bytes(w, plan) -> dict:
-    """Bytes the gather/aggregate step must move, per launch."""
+def algorithmic_bytes(w, plan, group_min_rows: int) -> dict:
+    """Bytes the gather/aggregate step must move, per launch, split by the
+    kernel that handles each id: every distinct id's K_t and V_t rows once,
+    its tokens' x rows read and a rows written, the token index and the
+    segment record."""
     e = 2 if w.spec.dtype == "bf16" else 4
-    d, d_e, B = w.spec.d, w.spec.d_e, w.batch
+    d, d_e = w.spec.d, w.spec.d_e
     n = np.asarray(plan["seg_n"], np.int64)
-    table = int(n.sum()) * (d + d_e) * e
-    x_read = B * d * e
-    a_write = B * d_e * e
-    misc = B * 4 + plan["S"] * 16
-    return dict(total=table + x_read + a_write + misc, table=table,
-                x=x_read, a=a_write, misc=misc)
+    m = np.diff(np.asarray(plan["seg_tok_start"], np.int64))
+    per_seg = n * (d + d_e) * e + m * (d * e + d_e * e + 4) + 16
+    grp = (n >= group_min_rows) if group_min_rows > 0 else np.zeros_like(n, bool)
+    out = dict(group=int(per_seg[grp].sum()), wave=int(per_seg[~grp].sum()))
+    out["total"] = out["group"] + out["wave"]
+    out["table"] = int((n * (d + d_e) * e).sum())
+    return out
 
 
 def gemm_flops(w) -> dict:
@@ -114,6 +119,7 @@ def main():
     layer.make_plan(ids, offsets)
     assert L.l3_plan_check(layer.plan) == L.L3_OK
     plan_np = L.l3_plan_export(layer.plan)
+    info = L.l3_plan_info(layer.plan)
 
     def step():
         layer.make_plan(ids, offsets)
@@ -135,13 +141,17 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = w.batch * args.steps / (t1 - t0)
 
-    ab = algorithmic_bytes(w, plan_np)
-    seg_ms, seg_n = stages["seg_fwd"]
-    seg_avg_ms = seg_ms / max(seg_n, 1)
-    achieved = ab["total"] / (seg_avg_ms * 1e-3) / 1e9
-    fl = gemm_flops(w)
+    ab = algorithmic_bytes(w, plan_np, info["group_min_rows"])
     stage_avg = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in stages.items()
                  if v[1]}
+    # the gather/aggregate step: wave kernel (+ row-chunk combine) for ids
+    # with few rows, group kernel for ids with many rows
+    t_wave = stage_avg.get("seg_fwd", 0.0) + stage_avg.get("seg_combine", 0.0)
+    t_group = stage_avg.get("seg_group", 0.0)
+    gather_ms = t_wave + t_group
+    achieved = ab["total"] / (gather_ms * 1e-3) / 1e9
+    gbs = lambda b, t: round(b / (t * 1e-3) / 1e9, 1) if t > 0 else None
+    fl = gemm_flops(w)
     mfma = {}
     for k in ("up_proj", "mix_proj"):
         if k in stage_avg and stage_avg[k] > 0:
@@ -166,12 +176,21 @@ def main():
                    "vocab": w.spec.vocab, "table_rows": w.rows,
                    "d": w.spec.d, "d_e": w.spec.d_e, "k_max": w.spec.k_max,
                    "distinct_ids": int(plan_np["S"])},
-        "roofline": {"kernel": "seg_fwd", "bound": "hbm",
+        "roofline": {"kernel": "gather (seg_fwd + seg_group)",
+                     "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None,
                      "algorithmic_bytes_per_launch": ab["total"],
-                     "avg_launch_ms": round(seg_avg_ms, 4)},
+                     "avg_launch_ms": round(gather_ms, 4),
+                     "per_kernel": {
+                         "seg_fwd": {"bytes": ab["wave"],
+                                     "ms": round(t_wave, 4),
+                                     "GB/s": gbs(ab["wave"], t_wave)},
+                         "seg_group": {"bytes": ab["group"],
+                                       "ms": round(t_group, 4),
+                                       "GB/s": gbs(ab["group"], t_group)}}},
+        "plan_info": info,
         "stage_ms": {k: round(v, 4) for k, v in stage_avg.items()},
         "mfma": mfma,
     }

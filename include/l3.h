@@ -192,6 +192,15 @@ l3_status l3_plan_export(l3_plan_t plan, int32_t* perm, int32_t* S,
                          int32_t* seg_id, int32_t* seg_tok_start,
                          int64_t* seg_row_off, int32_t* seg_n, void* stream);
 
+/*
+ * l3_plan_info -- how the forward pass will split the planned batch (waits
+ * for the stream). info (host int64) receives up to n of:
+ *   [0] B, [1] S (distinct ids), [2] wave-kernel work items,
+ *   [3] group-kernel work items, [4] rows per wave-kernel item,
+ *   [5] rows from which an id goes to the group kernel (0: group kernel off)
+ */
+l3_status l3_plan_info(l3_plan_t plan, int64_t* info, int n, void* stream);
+
 /* Free a plan handle (not its workspace). NULL is ignored. */
 void l3_plan_release(l3_plan_t plan);
 

@@ -65,6 +65,7 @@ def _load():
                                 P, P, P, P, P, P, c_size_t, P]),
         "l3_plan_check": (c_int, [P, P]),
         "l3_plan_export": (c_int, [P, P, P, P, P, P, P, P]),
+        "l3_plan_info": (c_int, [P, POINTER(c_int64), c_int, P]),
         "l3_plan_release": (None, [P]),
         "l3_plan_tokens": (c_int64, [P]),
         "l3_timing_enable": (c_int, [P, c_int]),
@@ -80,7 +81,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("l3_workspace_size", "l3_plan", "l3_replan", "l3_forward",
-            "l3_backward", "l3_plan_check", "l3_plan_export",
+            "l3_backward", "l3_plan_check", "l3_plan_export", "l3_plan_info",
             "l3_plan_release", "l3_plan_tokens", "l3_status_str",
             "l3_timing_enable", "l3_timing_read", "l3_stage_name")
 
@@ -223,6 +224,15 @@ def l3_plan_export(plan: Plan, stream=None) -> dict:
     return dict(perm=perm[:B].copy(), S=n, seg_id=seg_id[:n].copy(),
                 seg_tok_start=seg_tok_start[:n + 1].copy(),
                 seg_row_off=seg_row_off[:n].copy(), seg_n=seg_n[:n].copy())
+
+
+def l3_plan_info(plan: Plan, stream=None) -> dict:
+    v = (c_int64 * 6)()
+    _check(_lib.l3_plan_info(plan.handle, v, 6, _stream(stream)),
+           "l3_plan_info")
+    keys = ("B", "S", "wave_items", "group_items", "chunk_rows",
+            "group_min_rows")
+    return {k: int(v[i]) for i, k in enumerate(keys)}
 
 
 def l3_timing_enable(plan: Plan, enable: bool = True) -> None:

@@ -28,7 +28,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
 
-SOURCES = ["plan.hip", "seg_fwd.hip", "gemm.hip", "bwd.hip", "api.cpp"]
+SOURCES = ["plan.hip", "seg_fwd.hip", "seg_group.hip", "gemm.hip", "bwd.hip",
+           "api.cpp"]
 
 
 def _run(cmd):

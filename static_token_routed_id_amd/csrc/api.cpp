@@ -48,11 +48,13 @@ enum Stage {
   ST_BWD_LN,
   ST_BWD_UP,
   ST_BWD_SEG,
+  ST_GROUP,
   ST_COUNT
 };
 const char* const kStageNames[ST_COUNT] = {
-    "plan",    "seg_fwd",   "seg_combine",   "up_proj", "layernorm",
-    "mix_proj", "bwd_mix",  "bwd_layernorm", "bwd_up",  "bwd_seg"};
+    "plan",     "seg_fwd", "seg_combine",   "up_proj", "layernorm",
+    "mix_proj", "bwd_mix", "bwd_layernorm", "bwd_up",  "bwd_seg",
+    "seg_group"};
 
 bool debug_sync() {
   static const bool on = [] {
@@ -91,6 +93,17 @@ int nch_for(int64_t B, int k_max) {
   return (k_max + ch - 1) / ch;
 }
 
+// Large bf16 batches send ids with at least this many rows to the group
+// kernel (a workgroup per 64-token tile streams the id's whole K_t, V_t
+// slice); 0 disables it. Small batches keep every id on the wave kernel,
+// whose row chunks spread one id over many wavefronts.
+constexpr int kGroupMinRows = 128;
+int group_min_rows_for(const l3_desc& d, int64_t B) {
+  return (d.dtype == L3_BF16 && B > 2048 && seg_group_ok(d.d, d.d_e))
+             ? kGroupMinRows
+             : 0;
+}
+
 PlanDev carve_plan(Carver& c, int64_t B) {
   const size_t nb = static_cast<size_t>(B);
   const size_t nblk = (nb + kSortTile - 1) / kSortTile;
@@ -103,6 +116,7 @@ PlanDev carve_plan(Carver& c, int64_t B) {
   p.seg_row_off = c.take<int64_t>(nb);
   p.seg_n = c.take<int32_t>(nb);
   p.seg_item_start = c.take<int32_t>(nb + 1);
+  p.seg_gitem_start = c.take<int32_t>(nb + 1);
   p.keys_alt = c.take<int32_t>(nb);
   p.vals_alt = c.take<int32_t>(nb);
   p.hist = c.take<int32_t>(256 * nblk);
@@ -197,6 +211,7 @@ struct l3_plan_s {
   int64_t capacity = 0;  // largest B the workspace holds
   int chunk_rows = 32;
   int nch_max = 1;
+  int group_min_rows = 0;
   PlanDev dev;
   void* ws = nullptr;
   size_t ws_bytes = 0;
@@ -261,6 +276,7 @@ l3_status do_plan(l3_plan_s* p, const int32_t* ids, int64_t B,
   p->saved = nullptr;
   p->chunk_rows = chunk_rows_for(B, p->desc.k_max);
   p->nch_max = nch_for(B, p->desc.k_max);
+  p->group_min_rows = group_min_rows_for(p->desc, B);
   Carver c(p->ws);
   p->dev = carve_plan(c, B);
   if (B == 0) return L3_OK;
@@ -272,6 +288,7 @@ l3_status do_plan(l3_plan_s* p, const int32_t* ids, int64_t B,
   pp.B = static_cast<int>(B);
   pp.k_max = p->desc.k_max;
   pp.chunk_rows = p->chunk_rows;
+  pp.group_min_rows = p->group_min_rows;
   hipError_t e;
   {
     StageTimer t(p, ST_PLAN, s);
@@ -400,6 +417,20 @@ l3_status l3_plan_check(l3_plan_t plan, void* stream) {
   return L3_OK;
 }
 
+l3_status l3_plan_info(l3_plan_t plan, int64_t* info, int n, void* stream) {
+  if (!plan || (!info && n > 0)) return L3_ERR_NULL;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+    return L3_ERR_HIP;
+  int32_t hdr[4] = {0, 0, 0, 0};
+  if (plan->B > 0 && hipMemcpy(hdr, plan->dev.header, sizeof(hdr),
+                               hipMemcpyDeviceToHost) != hipSuccess)
+    return L3_ERR_HIP;
+  const int64_t v[6] = {plan->B, hdr[1], hdr[2], hdr[3], plan->chunk_rows,
+                        plan->group_min_rows};
+  for (int i = 0; i < n && i < 6; ++i) info[i] = v[i];
+  return L3_OK;
+}
+
 l3_status l3_plan_export(l3_plan_t plan, int32_t* perm, int32_t* S,
                          int32_t* seg_id, int32_t* seg_tok_start,
                          int64_t* seg_row_off, int32_t* seg_n, void* stream) {
@@ -487,8 +518,31 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
                          s);
     }
     if (e != hipSuccess) return L3_ERR_HIP;
+    if (plan->group_min_rows > 0) {
+      SegGroupArgs ga;
+      ga.header = pd.header;
+      ga.perm = pd.perm;
+      ga.seg_tok_start = pd.seg_tok_start;
+      ga.seg_row_off = pd.seg_row_off;
+      ga.seg_n = pd.seg_n;
+      ga.seg_gitem_start = pd.seg_gitem_start;
+      ga.x = static_cast<const uint16_t*>(x);
+      ga.K = static_cast<const uint16_t*>(K);
+      ga.V = static_cast<const uint16_t*>(V);
+      ga.d = d.d;
+      ga.d_e = d.d_e;
+      ga.a_out = static_cast<uint16_t*>(f.a_act);
+      ga.a_save = sv.a32;
+      const int64_t gitems_ub = (B + kGroupTok - 1) / kGroupTok + distinct;
+      StageTimer t(plan, ST_GROUP, s);
+      e = seg_group_launch(
+          ga, static_cast<int>(gitems_ub < (1 << 30) ? gitems_ub : (1 << 30)),
+          s);
+      if (e != hipSuccess) return L3_ERR_HIP;
+    }
     if (plan->nch_max > 1) {
       CombineArgs ca;
+      ca.group_min_rows = plan->group_min_rows;
       ca.header = pd.header;
       ca.perm = pd.perm;
       ca.seg_tok_start = pd.seg_tok_start;

@@ -10,9 +10,11 @@
 
 namespace l3 {
 
-// Tokens handled by one work item of the segment forward kernel (the M size
-// of one 16x16 MFMA block).
+// Tokens handled by one work item of the segment forward wave kernel (the M
+// size of one 16x16 MFMA block).
 constexpr int kTokTile = 16;
+// Tokens handled by one item of the group kernel (ids with many rows).
+constexpr int kGroupTok = 64;
 // Largest batch sorted by the single-workgroup plan kernel.
 constexpr int kSmallPlanMax = 8192;
 // Elements per block of the multi-kernel radix sort.
@@ -24,14 +26,16 @@ constexpr int kBadCount = 2;
 
 // Device arrays of one plan, carved out of the caller's plan workspace.
 struct PlanDev {
-  int32_t* header;          // [0] status bits, [1] S, [2] work items
+  int32_t* header;          // [0] status bits, [1] S, [2] wave items,
+                            // [3] group items
   int32_t* perm;            // [B] token index at sorted position
   int32_t* sorted_ids;      // [B]
   int32_t* seg_id;          // [B]
   int32_t* seg_tok_start;   // [B+1]
   int64_t* seg_row_off;     // [B]
   int32_t* seg_n;           // [B]
-  int32_t* seg_item_start;  // [B+1]
+  int32_t* seg_item_start;  // [B+1] wave items
+  int32_t* seg_gitem_start; // [B+1] group items
   int32_t* keys_alt;        // [B] radix ping-pong
   int32_t* vals_alt;        // [B]
   int32_t* hist;            // [256 * ceil(B / kSortTile)]
@@ -45,6 +49,7 @@ struct PlanParams {
   int B;
   int k_max;
   int chunk_rows;  // rows of one forward work item (multiple of 16)
+  int group_min_rows;  // ids with this many rows use the group kernel (0: off)
 };
 
 // Arguments of the segment forward kernel (softmax-attention of each token
@@ -69,6 +74,7 @@ struct SegFwdArgs {
 };
 
 struct CombineArgs {
+  int group_min_rows;
   const int32_t* header;
   const int32_t* perm;
   const int32_t* seg_tok_start;
@@ -135,6 +141,26 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& pp,
 hipError_t seg_fwd_launch(const SegFwdArgs& a, int dtype, int B, int items_ub,
                           hipStream_t s);
 hipError_t seg_combine_launch(const CombineArgs& a, int dtype, hipStream_t s);
+
+// Group kernel: one workgroup per (id, tile of 64 tokens), all of the id's
+// rows; bf16 only, d % 64 == 0, d_e % 128 == 0, d_e <= 512.
+struct SegGroupArgs {
+  const int32_t* header;
+  const int32_t* perm;
+  const int32_t* seg_tok_start;
+  const int64_t* seg_row_off;
+  const int32_t* seg_n;
+  const int32_t* seg_gitem_start;
+  const uint16_t* x;
+  const uint16_t* K;
+  const uint16_t* V;
+  int d, d_e;
+  uint16_t* a_out;  // [B x d_e] bf16, original token order
+  float* a_save;    // [B x d_e] float32 or NULL
+};
+bool seg_group_ok(int d, int d_e);
+hipError_t seg_group_launch(const SegGroupArgs& a, int items_ub,
+                            hipStream_t s);
 hipError_t gemm_launch(const GemmArgs& g, int a_type, int b_type, int c_type,
                        hipStream_t s);
 hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s);

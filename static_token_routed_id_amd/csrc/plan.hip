@@ -16,9 +16,11 @@
 //   * larger batches: LSD radix sort of the 32-bit ids with the position as
 //     payload (stable, 8-bit digits, histogram / scan / ranked scatter per
 //     digit), then segment cut kernels.
-// After the segments, the plan counts the forward pass's work items: segment
-// g with m_g tokens and n_g rows yields ceil(m_g / 16) * ceil(n_g / chunk)
-// items, and seg_item_start is their exclusive prefix sum.
+// After the segments, the plan counts the forward pass's work items: a
+// segment with n_g >= group_min_rows (large batches only) yields
+// ceil(m_g / 64) group items (seg_gitem_start), any other segment
+// ceil(m_g / 32) * ceil(n_g / chunk) wave items (seg_item_start); both are
+// exclusive prefix sums.
 
 #include "l3_device.h"
 #include "l3_internal.h"
@@ -49,8 +51,17 @@ __device__ __forceinline__ bool id_rows(const PlanParams& p, int t,
   return true;
 }
 
-__device__ __forceinline__ int items_of(int m, int n, int chunk) {
-  return ceil_div(m, kTokTile) * ceil_div(n, chunk);
+// Segments with at least group_min_rows rows (when enabled) go to the
+// workgroup-per-item group kernel in tiles of kGroupTok tokens; the others
+// to the wave kernel in tiles of kTokTile tokens times row chunks.
+__device__ __forceinline__ bool is_group(int n, const PlanParams& p) {
+  return p.group_min_rows > 0 && n >= p.group_min_rows;
+}
+__device__ __forceinline__ int items_of(int m, int n, const PlanParams& p) {
+  return is_group(n, p) ? 0 : ceil_div(m, kTokTile) * ceil_div(n, p.chunk_rows);
+}
+__device__ __forceinline__ int gitems_of(int m, int n, const PlanParams& p) {
+  return is_group(n, p) ? ceil_div(m, kGroupTok) : 0;
 }
 
 // ---------------------------------------------------------------- small ---
@@ -127,22 +138,30 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
     pd.header[1] = S;
   }
   __syncthreads();
-  // work items per segment, exclusive scan
+  // work items per segment (wave items and group items), exclusive scans
   const int sper = ceil_div(S, 1024);
   const int s0 = min(S, tid * sper), s1 = min(S, s0 + sper);
-  int icnt = 0;
-  for (int g = s0; g < s1; ++g)
-    icnt += items_of(pd.seg_tok_start[g + 1] - pd.seg_tok_start[g],
-                     pd.seg_n[g], p.chunk_rows);
-  int ibase = block_excl_scan<1024>(icnt, tmp, &total);
+  int icnt = 0, gcnt = 0;
   for (int g = s0; g < s1; ++g) {
+    const int m = pd.seg_tok_start[g + 1] - pd.seg_tok_start[g];
+    icnt += items_of(m, pd.seg_n[g], p);
+    gcnt += gitems_of(m, pd.seg_n[g], p);
+  }
+  int ibase = block_excl_scan<1024>(icnt, tmp, &total);
+  int gtotal;
+  int gbase = block_excl_scan<1024>(gcnt, tmp, &gtotal);
+  for (int g = s0; g < s1; ++g) {
+    const int m = pd.seg_tok_start[g + 1] - pd.seg_tok_start[g];
     pd.seg_item_start[g] = ibase;
-    ibase += items_of(pd.seg_tok_start[g + 1] - pd.seg_tok_start[g],
-                      pd.seg_n[g], p.chunk_rows);
+    pd.seg_gitem_start[g] = gbase;
+    ibase += items_of(m, pd.seg_n[g], p);
+    gbase += gitems_of(m, pd.seg_n[g], p);
   }
   if (tid == 0) {
     pd.seg_item_start[S] = total;
+    pd.seg_gitem_start[S] = gtotal;
     pd.header[2] = total;
+    pd.header[3] = gtotal;
   }
   (void)s_total;
 }
@@ -290,38 +309,46 @@ __global__ __launch_bounds__(256) void seg_write_kernel(PlanDev pd,
   }
 }
 
-// Work items per segment (into seg_item_start, scanned afterwards).
+// Work items per segment (into seg_item_start / seg_gitem_start, scanned
+// afterwards).
 __global__ __launch_bounds__(256) void seg_items_kernel(PlanDev pd,
                                                         PlanParams p) {
   const int S = pd.header[1];
   for (int g = blockIdx.x * 256 + threadIdx.x; g < S;
        g += gridDim.x * 256) {
-    pd.seg_item_start[g] = items_of(
-        pd.seg_tok_start[g + 1] - pd.seg_tok_start[g], pd.seg_n[g],
-        p.chunk_rows);
+    const int m = pd.seg_tok_start[g + 1] - pd.seg_tok_start[g];
+    pd.seg_item_start[g] = items_of(m, pd.seg_n[g], p);
+    pd.seg_gitem_start[g] = gitems_of(m, pd.seg_n[g], p);
   }
 }
 
-// Scan seg_item_start[0..S) in place; the count S is read on the device.
-__global__ __launch_bounds__(1024) void seg_items_scan_kernel(PlanDev pd) {
-  __shared__ int tmp[1024 / 64 + 1];
-  const int n = pd.header[1];
-  int32_t* a = pd.seg_item_start;
+// Exclusive scan of a[0..n) in place, a[n] = total.
+__device__ void scan_inplace_1024(int32_t* a, int n, int* tmp, int* total) {
   const int tid = threadIdx.x;
   const int per = ceil_div(n, 1024);
   const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
   int sum = 0;
   for (int i = i0; i < i1; ++i) sum += a[i];
-  int total;
-  int run = block_excl_scan<1024>(sum, tmp, &total);
+  int run = block_excl_scan<1024>(sum, tmp, total);
   for (int i = i0; i < i1; ++i) {
     int v = a[i];
     a[i] = run;
     run += v;
   }
-  if (tid == 0) {
-    a[n] = total;
+  if (tid == 0) a[n] = *total;
+}
+
+// Scan both item counts in place; the count S is read on the device.
+__global__ __launch_bounds__(1024) void seg_items_scan_kernel(PlanDev pd) {
+  __shared__ int tmp[1024 / 64 + 1];
+  const int n = pd.header[1];
+  int total, gtotal;
+  scan_inplace_1024(pd.seg_item_start, n, tmp, &total);
+  __syncthreads();
+  scan_inplace_1024(pd.seg_gitem_start, n, tmp, &gtotal);
+  if (threadIdx.x == 0) {
     pd.header[2] = total;
+    pd.header[3] = gtotal;
   }
 }
 

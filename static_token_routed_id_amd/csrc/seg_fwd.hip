@@ -1,5 +1,7 @@
-// Segment forward: a_i = V_t^T Softmax(K_t x_i) for every token, with the
-// batch grouped by id so that each id's rows are read once per 16 tokens.
+// Segment forward (wave kernel): a_i = V_t^T Softmax(K_t x_i) for the tokens
+// of ids with few rows (ids with many rows in large batches go to the group
+// kernel), with the batch grouped by id so that each id's rows are read once
+// per 16 tokens.
 //
 // gist.science explainer of "L^3: Large Lookup Layers", Technical Summary,
 // Core Architecture: after the static lookup of K_t and V_t, the hidden
@@ -379,7 +381,9 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(CombineArgs a) {
     else
       hi = mid - 1;
   }
-  const int nch = ceil_div(a.seg_n[lo], a.chunk_rows);
+  const int n_rows = a.seg_n[lo];
+  if (a.group_min_rows > 0 && n_rows >= a.group_min_rows) return;
+  const int nch = ceil_div(n_rows, a.chunk_rows);
   if (nch <= 1) return;
   const int64_t slot0 = static_cast<int64_t>(pos) * a.nch_max;
   float M = -INFINITY;
