@@ -10,9 +10,9 @@
 //
 //   scores   S = X K_t^T (64 tokens x n rows) on 16x16x32 bf16 MFMA. Wave w
 //            owns rows 64w .. 64w+63; its K fragments stream from global
-//            memory straight into registers with one 64-column slice of
-//            look-ahead (each K row is used by exactly one wave, so it never
-//            touches LDS). The X slice (64 tokens x 64 columns) is shared by
+//            memory straight into registers, three 32-column steps ahead of
+//            the multiply (each K row is used by exactly one wave, so it
+//            never touches LDS). The X slice (64 tokens x 128 columns) is shared by
 //            all waves, so it is staged in LDS, double buffered, one barrier
 //            per slice. Both operands use the same lane -> k assignment.
 //   softmax  exact: per-wave row maxima / sums combined through LDS; the
@@ -38,7 +38,8 @@ namespace l3 {
 constexpr int kGW = 8;                 // waves per workgroup
 constexpr int kGT = kGroupTok;         // tokens per item
 constexpr int kGRows = L3_MAX_ROWS_PER_ID;
-constexpr int kXS = 64 + 8;            // X slice row stride (elements)
+constexpr int kSW = 128;               // columns of d per K / X slice
+constexpr int kXS = kSW + 8;           // X slice row stride (elements)
 constexpr int kPS = kGRows + 8;        // P row stride
 constexpr int kVR = 32;                // V rows per value step
 constexpr int kCPWMax = 64;            // value columns per wave at most
@@ -65,15 +66,23 @@ __device__ __forceinline__ void group_item(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int d = a.d;
-  const int nsl = d / 64;
+  const int nsl = d / kSW;
 
   // ------------------------------------------------------------ scores ---
+  // K streams in 32-column steps through a ring of four register slots:
+  // step t's loads are issued three steps before its multiply (the loop is
+  // unrolled by four so every slot index is static, and there is no per-wave
+  // branch), which keeps about 96 KB of K in flight per workgroup. Lane group
+  // g supplies columns 32t + 8g .. 32t + 8g + 7 of its row for both
+  // operands. X is staged in 128-column slices in LDS (double buffered, one
+  // barrier per slice). A wave past the id's last row re-reads that cached
+  // row; its results are masked below.
   const int wrow0 = w * 64;
   const bool has_rows = wrow0 < n;
   int koff[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
-    koff[nb] = min(wrow0 + nb * 16 + r, n - 1) * d + g * 16;
+    koff[nb] = min(wrow0 + nb * 16 + r, n - 1) * d + g * 8;
   const uint16_t* kt = a.K + rowbase * d;
   const int xt = tid >> 3, xc = (tid & 7) * 8;
   const uint16_t* xsrc =
@@ -84,50 +93,56 @@ __device__ __forceinline__ void group_item(
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  u32x4 kcur[4][2];
-  *reinterpret_cast<u32x4*>(&s_x[0][xt * kXS + xc]) = ld16(xsrc);
-  if (has_rows) {
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      kcur[nb][0] = ld16(kt + koff[nb]);
-      kcur[nb][1] = ld16(kt + koff[nb] + 8);
-    }
+
+  const int nsteps = d / 32;
+  u32x4 k0[4], k1[4], k2[4], k3[4];
+#define L3_LOAD_K(dst, t)                                                \
+  {                                                                      \
+    const int col = min((t), nsteps - 1) * 32;                           \
+    _Pragma("unroll") for (int nb = 0; nb < 4; ++nb) dst[nb] =           \
+        ld16(kt + koff[nb] + col);                                       \
   }
-  u32x4 xreg = ld16(xsrc + min(1, nsl - 1) * 64);
+#define L3_MUL(kreg, buf, j)                                             \
+  {                                                                      \
+    u32x4 xf[MB];                                                        \
+    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) xf[mb] =           \
+        *reinterpret_cast<const u32x4*>(                                 \
+            &s_x[buf][(mb * 16 + r) * kXS + (j) * 32 + g * 8]);          \
+    _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                     \
+        _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) acc[mb][nb] =  \
+            mfma16(xf[mb], kreg[nb], acc[mb][nb]);                       \
+  }
+  u32x4 x0 = ld16(xsrc), x1 = ld16(xsrc + 64);
+  *reinterpret_cast<u32x4*>(&s_x[0][xt * kXS + xc]) = x0;
+  *reinterpret_cast<u32x4*>(&s_x[0][xt * kXS + xc + 64]) = x1;
+  L3_LOAD_K(k0, 0)
+  L3_LOAD_K(k1, 1)
+  L3_LOAD_K(k2, 2)
+  {
+    const int nx = min(1, nsl - 1) * kSW;
+    x0 = ld16(xsrc + nx);
+    x1 = ld16(xsrc + nx + 64);
+  }
   __syncthreads();
   for (int sl = 0; sl < nsl; ++sl) {
-    const int cur = sl & 1;
-    u32x4 knext[4][2];
-    const int nx = min(sl + 1, nsl - 1) * 64;
-    if (has_rows) {
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        knext[nb][0] = ld16(kt + koff[nb] + nx);
-        knext[nb][1] = ld16(kt + koff[nb] + nx + 8);
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4 xf[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          xf[mb] = *reinterpret_cast<const u32x4*>(
-              &s_x[cur][(mb * 16 + r) * kXS + g * 16 + h * 8]);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            acc[mb][nb] = mfma16(xf[mb], kcur[nb][h], acc[mb][nb]);
-      }
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        kcur[nb][0] = knext[nb][0];
-        kcur[nb][1] = knext[nb][1];
-      }
-    }
-    *reinterpret_cast<u32x4*>(&s_x[cur ^ 1][xt * kXS + xc]) = xreg;
-    xreg = ld16(xsrc + min(sl + 2, nsl - 1) * 64);
+    const int cur = sl & 1, t = sl * 4;
+    L3_LOAD_K(k3, t + 3)
+    L3_MUL(k0, cur, 0)
+    L3_LOAD_K(k0, t + 4)
+    L3_MUL(k1, cur, 1)
+    L3_LOAD_K(k1, t + 5)
+    L3_MUL(k2, cur, 2)
+    L3_LOAD_K(k2, t + 6)
+    L3_MUL(k3, cur, 3)
+    *reinterpret_cast<u32x4*>(&s_x[cur ^ 1][xt * kXS + xc]) = x0;
+    *reinterpret_cast<u32x4*>(&s_x[cur ^ 1][xt * kXS + xc + 64]) = x1;
+    const int nx = min(sl + 2, nsl - 1) * kSW;
+    x0 = ld16(xsrc + nx);
+    x1 = ld16(xsrc + nx + 64);
     __syncthreads();
   }
+#undef L3_LOAD_K
+#undef L3_MUL
 
   // ----------------------------------------------------------- softmax ---
   // lane holds S[token mb*16 + 4g + i][row wrow0 + nb*16 + r]
@@ -331,7 +346,7 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
 }
 
 bool seg_group_ok(int d, int d_e) {
-  return d % 64 == 0 && d_e % 128 == 0 && d_e <= kGW * kCPWMax;
+  return d % kSW == 0 && d_e % 128 == 0 && d_e <= kGW * kCPWMax;
 }
 
 hipError_t seg_group_launch(const SegGroupArgs& a, int items_ub,
