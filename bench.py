@@ -11,8 +11,11 @@ Prints one JSON line. `roofline` is the gather/aggregate step, two kernels
 batches): algorithmic bytes per launch (each distinct id's K_t and V_t rows
 once, x read, a written, ids and segment records) over the mean launch
 times taken from HIP events recorded around each kernel on its own stream
-during the timed steps. `cpu_baseline` is the fp64 oracle on a bounded sample of the same
-batch on the host CPU.
+during the timed steps; `traffic` is the HBM bytes per launch of the same two
+kernels from the committed FETCH_SIZE / WRITE_SIZE counter summary
+(profiles/traffic_gather_<workload>.md), or null when the kernels changed
+since it was taken. `cpu_baseline` is the fp64 oracle on a bounded sample of
+the same batch on the host CPU.
 """
 from __future__ import annotations
 
@@ -47,6 +50,59 @@ def algorithmic_bytes(w, plan, group_min_rows: int) -> dict:
     out["total"] = out["group"] + out["wave"]
     out["table"] = int((n * (d + d_e) * e).sum())
     return out
+
+
+# Sources whose change invalidates the committed HBM traffic counts of the
+# gather kernels (kernel code, shared device helpers, launch configuration).
+TRAFFIC_SOURCES = ("static_token_routed_id_amd/csrc/seg_fwd.hip",
+                   "static_token_routed_id_amd/csrc/seg_group.hip",
+                   "static_token_routed_id_amd/csrc/l3_device.h",
+                   "static_token_routed_id_amd/csrc/l3_internal.h",
+                   "static_token_routed_id_amd/csrc/api.cpp")
+
+
+def sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the gather kernels from the committed
+    FETCH_SIZE / WRITE_SIZE counter summary of this workload, or None when
+    there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gather_{workload}.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    try:
+        rec = json.loads(text[start + 7:end])
+    except ValueError:
+        return None
+    if rec.get("sources_digest") != sources_digest():
+        return None
+    return rec
+
+
+def calibrate_copy(nbytes: int = 1 << 30, reps: int = 3) -> None:
+    """A plain device-to-device copy of known size, the reference launch for
+    scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
+                      "reps": reps}), flush=True)
 
 
 def gemm_flops(w) -> dict:
@@ -88,7 +144,12 @@ def main():
     ap.add_argument("--workload", default="large_prefill_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not "
               "supported (this build runs on a single MI355X)",
@@ -158,6 +219,7 @@ def main():
             tf = fl[k] / (stage_avg[k] * 1e-3) / 1e12
             mfma[k] = {"tflops": round(tf, 1),
                        "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFS, 4)}
+    traffic = measured_traffic(w.spec.name)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -180,7 +242,8 @@ def main():
                      "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": traffic["bytes_per_launch"] if traffic
+                                else None,
                      "algorithmic_bytes_per_launch": ab["total"],
                      "avg_launch_ms": round(gather_ms, 4),
                      "per_kernel": {

@@ -80,10 +80,12 @@ l3_status check_desc(const l3_desc* d) {
   return L3_OK;
 }
 
-// Rows of one forward work item: small batches split an id's rows so that
-// enough wavefronts stream them; large batches keep every id in one chunk.
+// Rows of one wave-kernel work item: small batches split an id's rows
+// finely so that enough wavefronts stream them; otherwise an item takes up
+// to kWaveMaxRows rows (ids with more rows are split into chunks, or go to
+// the group kernel in large bf16 batches).
 int chunk_rows_for(int64_t B, int k_max) {
-  int ch = B <= 256 ? 32 : (B <= 2048 ? 128 : 512);
+  int ch = B <= 256 ? 32 : kWaveMaxRows;
   int kp = 16;
   while (kp < k_max) kp <<= 1;
   return ch < kp ? ch : kp;
@@ -540,7 +542,12 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
           s);
       if (e != hipSuccess) return L3_ERR_HIP;
     }
-    if (plan->nch_max > 1) {
+    // Row chunks exist only for ids with more rows than one wave item takes;
+    // when all such ids go to the group kernel nothing needs merging.
+    const bool split = plan->nch_max > 1 &&
+                       !(plan->group_min_rows > 0 &&
+                         plan->group_min_rows <= plan->chunk_rows);
+    if (split) {
       CombineArgs ca;
       ca.group_min_rows = plan->group_min_rows;
       ca.header = pd.header;

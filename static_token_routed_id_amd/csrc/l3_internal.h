@@ -13,6 +13,9 @@ namespace l3 {
 // Tokens handled by one work item of the segment forward wave kernel (the M
 // size of one 16x16 MFMA block).
 constexpr int kTokTile = 16;
+// Most rows of one id handled by one wave-kernel work item; ids with more
+// rows are split into row chunks merged by the combine kernel.
+constexpr int kWaveMaxRows = 128;
 // Tokens handled by one item of the group kernel (ids with many rows).
 constexpr int kGroupTok = 64;
 // Largest batch sorted by the single-workgroup plan kernel.

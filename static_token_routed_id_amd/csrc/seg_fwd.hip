@@ -1,7 +1,7 @@
-// Segment forward (wave kernel): a_i = V_t^T Softmax(K_t x_i) for the tokens
-// of ids with few rows (ids with many rows in large batches go to the group
-// kernel), with the batch grouped by id so that each id's rows are read once
-// per 16 tokens.
+// Segment forward, wave kernel: a_i = V_t^T Softmax(K_t x_i) for the tokens
+// of ids with few rows (ids with many rows in large bf16 batches go to the
+// group kernel), the batch grouped by id so that each id's rows are read
+// once per 16 tokens.
 //
 // gist.science explainer of "L^3: Large Lookup Layers", Technical Summary,
 // Core Architecture: after the static lookup of K_t and V_t, the hidden
@@ -10,23 +10,26 @@
 // Design, Batch Sorting: grouping tokens by id makes the mask
 // block-diagonal, so one block of tokens shares one read of K_t, V_t.
 //
-// Work item = (segment, tile of <= 16 of its tokens, chunk of its rows). One
-// wavefront owns one item at a time; the four wavefronts of a workgroup are
-// independent (no workgroup barrier), and wavefronts loop over the items
-// round-robin.
-//   1. scores S = X K_chunk^T with 16x16 MFMA blocks (bf16 16x16x32 or f32
-//      16x16x4), both operands streamed straight from global memory into
-//      registers: lane l reads 16 (bf16) or 4 (f32) consecutive elements of
-//      row l & 15, so each 64-element slice of a row is one full 128-byte
-//      line, and the two (or four) MFMAs of a slice use the same lane->k
-//      assignment for A and B (the contraction does not care which k a slot
-//      holds as long as both operands agree);
+// Work item = (segment, tile of <= 16 of its tokens, chunk of <= 128 of its
+// rows). One wavefront owns one item at a time; the four wavefronts of a
+// workgroup are independent (no workgroup barrier), and wavefronts walk the
+// items round-robin. Many small items per compute unit give the memory
+// system many independent streams, so registers are kept low (several
+// wavefronts per SIMD).
+//   1. scores S = X K_chunk^T on 16x16 MFMA blocks, operands streamed from
+//      global memory into registers. bf16: 32-column steps (lane group g
+//      holds columns 8g .. 8g+7 of row l & 15, the MFMA's own k layout) with
+//      the next step's loads in flight during the current multiply (two
+//      register slots, loop unrolled by two). f32: 16-column steps of the
+//      16x16x4 MFMA (lane group g holds columns 4g .. 4g+3; four MFMAs, one
+//      per element, use the same lane -> k assignment for both operands);
 //   2. exact softmax over the chunk (row max and row sum across the 16 lanes
 //      holding a row), unnormalised weights to this wave's LDS (fp16 for
 //      bf16 inputs, f32 for f32 inputs), laid out [row j][token];
 //   3. aggregation acc[t][e] += p[t][j] * V[j][e] on the vector ALU: lane l
-//      owns columns e = l*EPL .. l*EPL+EPL-1, so every V row is one
-//      coalesced load, and the token loop is bounded by the real tile size;
+//      owns columns e = l*EPL .. l*EPL+EPL-1 of a 64*EPL-column pass, V rows
+//      are loaded 16 at a time (coalesced) before they are used, and the
+//      token loop is bounded by the real tile size;
 //   4. single chunk: a = acc / rowsum, written in original token order;
 //      several chunks: (max, sum, acc) partials, merged by seg_combine in a
 //      fixed chunk order (exact, deterministic).
@@ -36,7 +39,8 @@
 
 namespace l3 {
 
-constexpr int kNBMax = 32;  // 16-row blocks per item: 512 rows
+constexpr int kNBMax = kWaveMaxRows / 16;  // 16-row blocks per item
+constexpr int kVBurst = 16;                // V rows loaded ahead of use
 
 template <bool BF16>
 struct Types;
@@ -51,6 +55,10 @@ struct Types<false> {
   typedef float P;
 };
 
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
 // ---- scores --------------------------------------------------------------
 template <int NB>
 __device__ __forceinline__ void scores_bf16(const uint16_t* __restrict__ xr,
@@ -62,27 +70,31 @@ __device__ __forceinline__ void scores_bf16(const uint16_t* __restrict__ xr,
   int koff[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
-    koff[nb] = min(nb * 16 + r, nc - 1) * d + g * 16;
-  const uint16_t* xp = xr + g * 16;
-  for (int kc = 0; kc < d; kc += 64) {
-    const uint4 x0 = *reinterpret_cast<const uint4*>(xp + kc);
-    const uint4 x1 = *reinterpret_cast<const uint4*>(xp + kc + 8);
-    constexpr int G = NB < 8 ? NB : 8;  // blocks whose loads are in flight
-#pragma unroll
-    for (int nb0 = 0; nb0 < NB; nb0 += G) {
-      uint4 k0[G], k1[G];
-#pragma unroll
-      for (int q = 0; q < G; ++q) {
-        k0[q] = *reinterpret_cast<const uint4*>(kt + koff[nb0 + q] + kc);
-        k1[q] = *reinterpret_cast<const uint4*>(kt + koff[nb0 + q] + kc + 8);
-      }
-#pragma unroll
-      for (int q = 0; q < G; ++q) {
-        acc[nb0 + q] = mfma_bf16(x0, k0[q], acc[nb0 + q]);
-        acc[nb0 + q] = mfma_bf16(x1, k1[q], acc[nb0 + q]);
-      }
-    }
+    koff[nb] = min(nb * 16 + r, nc - 1) * d + g * 8;
+  const uint16_t* xp = xr + g * 8;
+  const int last = d - 32;
+  u32x4 xa, xb, ka[NB], kb[NB];
+#define L3_LOAD(xd, kd, col)                                          \
+  {                                                                   \
+    const int c = (col);                                              \
+    xd = ld16(xp + c);                                                \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) kd[nb] =        \
+        ld16(kt + koff[nb] + c);                                      \
   }
+#define L3_MUL(xs, ks)                                                \
+  _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) acc[nb] =         \
+      __builtin_amdgcn_mfma_f32_16x16x32_bf16(                        \
+          __builtin_bit_cast(bf16x8_t, xs),                           \
+          __builtin_bit_cast(bf16x8_t, ks[nb]), acc[nb], 0, 0, 0);
+  L3_LOAD(xa, ka, 0)
+  for (int kc = 0; kc < d; kc += 64) {
+    L3_LOAD(xb, kb, kc + 32)
+    L3_MUL(xa, ka)
+    L3_LOAD(xa, ka, min(kc + 64, last))
+    L3_MUL(xb, kb)
+  }
+#undef L3_LOAD
+#undef L3_MUL
 }
 
 template <int NB>
@@ -157,67 +169,61 @@ __device__ __forceinline__ void softmax_rows(floatx4 (&acc)[kNBMax], int nc,
   }
 }
 
-// ---- aggregation ------------------------------------------------------------
-template <int EPL>
-__device__ __forceinline__ void load_row(const uint16_t* p, float (&v)[EPL]) {
-  if constexpr (EPL == 8) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[2 * q] = __uint_as_float(w[q] << 16);
-      v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-    }
-  } else if constexpr (EPL == 4) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    v[0] = __uint_as_float(u.x << 16);
-    v[1] = __uint_as_float(u.x & 0xffff0000u);
-    v[2] = __uint_as_float(u.y << 16);
-    v[3] = __uint_as_float(u.y & 0xffff0000u);
-  } else if constexpr (EPL == 2) {
-    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-    v[0] = __uint_as_float(u << 16);
-    v[1] = __uint_as_float(u & 0xffff0000u);
-  } else {
-    v[0] = bf2f(*p);
-  }
+template <int NB, bool BF16>
+__device__ __forceinline__ void scores_softmax(
+    const typename Types<BF16>::T* xr, const typename Types<BF16>::T* kt,
+    int d, int nc, int r, int g, typename Types<BF16>::P* P, float* ml) {
+  floatx4 acc[kNBMax];
+  if constexpr (BF16)
+    scores_bf16<NB>(xr, kt, d, nc, r, g, acc);
+  else
+    scores_f32<NB>(xr, kt, d, nc, r, g, acc);
+  softmax_rows<NB>(acc, nc, r, g, P, ml);
 }
-template <int EPL>
-__device__ __forceinline__ void load_row(const float* p, float (&v)[EPL]) {
-  if constexpr (EPL % 4 == 0) {
-#pragma unroll
-    for (int q = 0; q < EPL / 4; ++q) {
-      const float4 f = reinterpret_cast<const float4*>(p)[q];
-      v[4 * q] = f.x;
-      v[4 * q + 1] = f.y;
-      v[4 * q + 2] = f.z;
-      v[4 * q + 3] = f.w;
+
+// ---- aggregation ------------------------------------------------------------
+// EPL values of one row for this lane, as raw storage words.
+template <int EPL, bool BF16>
+struct RowWords {
+  static constexpr int kWords = BF16 ? (EPL + 1) / 2 : EPL;
+  uint32_t w[kWords];
+};
+
+template <int EPL, bool BF16>
+__device__ __forceinline__ void load_words(
+    const typename Types<BF16>::T* p, RowWords<EPL, BF16>& v) {
+  if constexpr (BF16) {
+    if constexpr (EPL == 4) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      v.w[0] = u.x;
+      v.w[1] = u.y;
+    } else if constexpr (EPL == 2) {
+      v.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+      v.w[0] = *reinterpret_cast<const uint16_t*>(p);
     }
   } else {
+    if constexpr (EPL == 4) {
+      const u32x4 u = ld16(p);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) v[e] = p[e];
+      for (int e = 0; e < 4; ++e) v.w[e] = u[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        v.w[e] = __float_as_uint(reinterpret_cast<const float*>(p)[e]);
+    }
   }
 }
 
-template <int MTOK, int EPL, typename T, typename PT>
-__device__ __forceinline__ void aggregate(const T* __restrict__ vt, int d_e,
-                                          int nc, const PT* P,
-                                          float (&acc)[16][EPL]) {
-#pragma unroll
-  for (int t = 0; t < MTOK; ++t)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
-#pragma unroll 4
-  for (int j = 0; j < nc; ++j) {
-    float v[EPL];
-    load_row<EPL>(vt + static_cast<int64_t>(j) * d_e, v);
-    const PT* pj = P + j * kTokTile;
-#pragma unroll
-    for (int t = 0; t < MTOK; ++t) {
-      const float p = static_cast<float>(pj[t]);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[t][e] = fmaf(p, v[e], acc[t][e]);
-    }
+template <int EPL, bool BF16>
+__device__ __forceinline__ float word_value(const RowWords<EPL, BF16>& v,
+                                            int e) {
+  if constexpr (BF16) {
+    if constexpr (EPL == 1) return __uint_as_float(v.w[0] << 16);
+    const uint32_t u = v.w[e >> 1];
+    return __uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16));
+  } else {
+    return __uint_as_float(v.w[e]);
   }
 }
 
@@ -241,11 +247,39 @@ __device__ __forceinline__ void aggregate_and_store(
     const typename Types<BF16>::P* P, const float* ml, int tok0, int mcount,
     int nch, int chunk, int lane) {
   typedef typename Types<BF16>::T T;
+  typedef typename Types<BF16>::P PT;
   const int passes = a.d_e / (64 * EPL);
   for (int ps = 0; ps < passes; ++ps) {
     const int e0 = ps * 64 * EPL + lane * EPL;
-    float acc[16][EPL];
-    aggregate<MTOK, EPL>(vt + e0, a.d_e, nc, P, acc);
+    const T* vp = vt + e0;
+    float acc[MTOK][EPL];
+#pragma unroll
+    for (int t = 0; t < MTOK; ++t)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
+    for (int j0 = 0; j0 < nc; j0 += kVBurst) {
+      // a burst of V rows in flight before any is used (rows past the
+      // chunk repeat its last row; their weights are never read)
+      RowWords<EPL, BF16> v[kVBurst];
+#pragma unroll
+      for (int q = 0; q < kVBurst; ++q)
+        load_words<EPL, BF16>(
+            vp + static_cast<int64_t>(min(j0 + q, nc - 1)) * a.d_e, v[q]);
+      const int jn = min(kVBurst, nc - j0);
+#pragma unroll
+      for (int q = 0; q < kVBurst; ++q) {
+        if (q < jn) {
+          const PT* pj = P + (j0 + q) * kTokTile;
+#pragma unroll
+          for (int t = 0; t < MTOK; ++t) {
+            const float p = static_cast<float>(pj[t]);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+              acc[t][e] = fmaf(p, word_value<EPL, BF16>(v[q], e), acc[t][e]);
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int t = 0; t < MTOK; ++t) {
       if (t < mcount) {
@@ -270,18 +304,6 @@ __device__ __forceinline__ void aggregate_and_store(
       }
     }
   }
-}
-
-template <int NB, bool BF16>
-__device__ __forceinline__ void scores_softmax(
-    const typename Types<BF16>::T* xr, const typename Types<BF16>::T* kt,
-    int d, int nc, int r, int g, typename Types<BF16>::P* P, float* ml) {
-  floatx4 acc[kNBMax];
-  if constexpr (BF16)
-    scores_bf16<NB>(xr, kt, d, nc, r, g, acc);
-  else
-    scores_f32<NB>(xr, kt, d, nc, r, g, acc);
-  softmax_rows<NB>(acc, nc, r, g, P, ml);
 }
 
 template <bool BF16, int EPL>
@@ -335,30 +357,25 @@ __global__ __launch_bounds__(256) void seg_fwd_kernel(SegFwdArgs a) {
       scores_softmax<2, BF16>(xr, kt, a.d, nc, r, g, P, ml);
     else if (nbc <= 4)
       scores_softmax<4, BF16>(xr, kt, a.d, nc, r, g, P, ml);
-    else if (nbc <= 8)
-      scores_softmax<8, BF16>(xr, kt, a.d, nc, r, g, P, ml);
-    else if (nbc <= 16)
-      scores_softmax<16, BF16>(xr, kt, a.d, nc, r, g, P, ml);
     else
-      scores_softmax<32, BF16>(xr, kt, a.d, nc, r, g, P, ml);
+      scores_softmax<8, BF16>(xr, kt, a.d, nc, r, g, P, ml);
     __builtin_amdgcn_wave_barrier();
 
     const T* vt = V + rowbase * a.d_e;
+#define L3_AGG(N)                                                           \
+  aggregate_and_store<N, EPL, BF16>(a, vt, nc, P, ml, tok0, mcount, nch,    \
+                                    chunk, lane)
     if (mcount <= 1)
-      aggregate_and_store<1, EPL, BF16>(a, vt, nc, P, ml, tok0, mcount, nch,
-                                        chunk, lane);
+      L3_AGG(1);
     else if (mcount <= 2)
-      aggregate_and_store<2, EPL, BF16>(a, vt, nc, P, ml, tok0, mcount, nch,
-                                        chunk, lane);
+      L3_AGG(2);
     else if (mcount <= 4)
-      aggregate_and_store<4, EPL, BF16>(a, vt, nc, P, ml, tok0, mcount, nch,
-                                        chunk, lane);
+      L3_AGG(4);
     else if (mcount <= 8)
-      aggregate_and_store<8, EPL, BF16>(a, vt, nc, P, ml, tok0, mcount, nch,
-                                        chunk, lane);
+      L3_AGG(8);
     else
-      aggregate_and_store<16, EPL, BF16>(a, vt, nc, P, ml, tok0, mcount, nch,
-                                         chunk, lane);
+      L3_AGG(16);
+#undef L3_AGG
   }
 }
 
@@ -407,12 +424,10 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(CombineArgs a) {
 template <bool BF16>
 static hipError_t seg_fwd_dispatch(const SegFwdArgs& a, int grid,
                                    hipStream_t s) {
+  // EPL: value columns per lane per pass (at most 4, the rest in passes)
   const int q = a.d_e / 64;  // d_e is a multiple of 64
-  const int epl = q % 8 == 0 ? 8 : q % 4 == 0 ? 4 : q % 2 == 0 ? 2 : 1;
+  const int epl = q % 4 == 0 ? 4 : q % 2 == 0 ? 2 : 1;
   switch (epl) {
-    case 8:
-      seg_fwd_kernel<BF16, 8><<<grid, 256, 0, s>>>(a);
-      break;
     case 4:
       seg_fwd_kernel<BF16, 4><<<grid, 256, 0, s>>>(a);
       break;
@@ -430,7 +445,7 @@ hipError_t seg_fwd_launch(const SegFwdArgs& a, int dtype, int B, int items_ub,
                           hipStream_t s) {
   (void)B;
   int grid = ceil_div(items_ub, 4);
-  if (grid > 2048) grid = 2048;
+  if (grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;
   return dtype == kBF16 ? seg_fwd_dispatch<true>(a, grid, s)
                         : seg_fwd_dispatch<false>(a, grid, s);
