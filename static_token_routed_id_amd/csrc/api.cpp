@@ -147,7 +147,6 @@ struct FwdBufs {
   void* h_act;  // [B x d] dtype
   float* part;
   float* part_ml;
-  float* stats;  // [B x d/128 x 2] LayerNorm partials (inference, bf16)
 };
 FwdBufs carve_fwd(Carver& c, const l3_desc& d, int64_t B) {
   FwdBufs f;
@@ -155,7 +154,6 @@ FwdBufs carve_fwd(Carver& c, const l3_desc& d, int64_t B) {
   f.a_act = c.take<char>(B * d.d_e * es);
   f.U = c.take<float>(B * d.d);
   f.h_act = c.take<char>(B * d.d * es);
-  f.stats = c.take<float>(B * (d.d / 128 + 1) * 2);
   const int nch = nch_for(B, d.k_max);
   if (nch > 1) {
     f.part = c.take<float>(B * nch * d.d_e);
@@ -583,28 +581,22 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     up.N = d.d;
     up.K = d.d_e;
     up.header = pd.header;
-    up.row_stats = nullptr;
-    // Inference on bf16 with the 256-tile GEMM: u is written as bf16 and the
-    // epilogue also writes per-row, per-128-column (mean, M2) of the float32
-    // u, from which ln_apply normalises (no float32 round trip of u).
-    const bool fused_ln = !save && d.dtype == L3_BF16 && gemm_nt_256_ok(up);
-    if (fused_ln) {
-      up.row_stats = f.stats;
+    // Inference on bf16 with an MFMA GEMM: u is written as bf16 and
+    // ln_apply normalises each row from it (statistics over the row in
+    // registers). Training and float32 keep u in float32 for the saved state.
+    const bool u_bf16 = !save && d.dtype == L3_BF16 && gemm_nt_mfma_ok(up);
+    {
       StageTimer t(plan, ST_UP, s);
-      e = gemm_nt_mfma_launch(up, kBF16, s);
-    } else {
-      StageTimer t(plan, ST_UP, s);
-      if (!save && d.dtype == L3_BF16 && gemm_nt_mfma_ok(up))
-        e = gemm_nt_mfma_launch(up, kF32, s);
+      if (u_bf16)
+        e = gemm_nt_mfma_launch(up, kBF16, s);
       else
         e = gemm_launch(up, save ? kF32 : d.dtype, d.dtype, kF32, s);
     }
     if (e != hipSuccess) return L3_ERR_HIP;
-    if (fused_ln) {
+    if (u_bf16) {
       LnApplyArgs la;
       la.header = pd.header;
       la.U = reinterpret_cast<const uint16_t*>(f.U);
-      la.stats = f.stats;
       la.gamma = static_cast<const uint16_t*>(gamma);
       la.beta = static_cast<const uint16_t*>(beta);
       la.B = static_cast<int>(B);
@@ -627,7 +619,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     ln.h_save = sv.h32;
     ln.uhat_save = sv.uhat;
     ln.rstd_save = sv.rstd;
-    if (!fused_ln) {
+    if (!u_bf16) {
       StageTimer t(plan, ST_LN, s);
       e = ln_launch(ln, d.dtype, s);
     }

@@ -198,13 +198,21 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmArgs g) {
 // One workgroup (4 waves, one per SIMD) owns a 256 x 256 tile of C; wave
 // (wm, wn) owns rows wm*128.. and columns wn*128.. as 4 x 4 blocks of
 // 32x32x16 MFMA results (256 float accumulators per lane, in AGPRs). The K
-// loop walks 64-wide slices: both operand slices (256 rows x 128 bytes)
-// sit in LDS, double buffered (2 x 2 x 36 KB, rows padded to 72 elements so
-// the 8 lanes served per LDS cycle hit distinct banks), and the slice two
-// steps ahead is loaded from global memory into registers while the current
-// one is multiplied, so one barrier per slice suffices. The prefetch is
-// unconditional (clamped to the last slice) so the staging registers are
-// never demoted to scratch memory.
+// loop walks 64-wide slices, each split into four 16-wide steps:
+//   * both operand slices (256 rows x 128 bytes) sit in LDS, double
+//     buffered, rows padded to 72 elements so that a 16-byte read of 16 rows
+//     touches 64 distinct banks;
+//   * the fragments of step s+1 are read from LDS while the 16 MFMAs of step
+//     s run (two fragment register sets); the first step of the next slice
+//     is read after the workgroup barrier, during the last step's MFMAs;
+//   * the slice after next is fetched from global memory into registers by
+//     buffer loads (scalar base + 32-bit lane offset; rows past the matrix
+//     end read as zero) and its previous contents written to the other LDS
+//     buffer, spread over the first three steps: one load or LDS write
+//     between consecutive MFMAs, never a burst that would stall the wave's
+//     in-order issue behind a full memory queue.
+// Scheduling barriers pin this interleaving; the compiler only inserts the
+// waits each operand needs.
 //
 // Tile order is XCD-aware: workgroup b runs on XCD b % 8, so tiles are
 // renumbered to give each XCD a contiguous range of the logical order, which
@@ -213,7 +221,65 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmArgs g) {
 constexpr int kTM = 256, kTN = 256, kTK = 64, kTL = kTK + 8;
 constexpr int kXcd = 8, kGroupM = 4;
 
-template <typename TC, bool STATS>
+struct Frag256 {
+  u32x4 a[4], b[4];
+};
+
+// Operand source of one K slice: buffer resource, lane offset, row-group
+// stride and slice column (all wave-uniform except the lane offset).
+struct SliceSrc {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  int va, vb, qa, qb, ka, kb;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(
+    const uint16_t* base, int64_t bytes) {
+  // 0x00020000: raw (untyped) 32-bit data format, the usual gfx9 setting
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(base), 0,
+      static_cast<int>(bytes > 0x7fffffff ? 0x7fffffff : bytes), 0x00020000);
+}
+
+// One 16-wide step: 16 MFMAs on FC; after MFMA m, optionally the read of
+// fragment m of the next step (m < 8) and staging operation m - S0 of rows
+// Q0.. (per row group q: LDS write of A, of B, then reload of A, of B).
+template <bool READ, int Q0, int NQ, int S0>
+__device__ __forceinline__ void step256(floatx16 (&acc)[4][4],
+                                        const Frag256& FC, Frag256& FN,
+                                        const uint16_t* rd_a,
+                                        const uint16_t* rd_b, int rd_k,
+                                        u32x4 (&ra)[8], u32x4 (&rb)[8],
+                                        uint16_t* wr_a, uint16_t* wr_b,
+                                        const SliceSrc& src) {
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    acc[m >> 2][m & 3] = mfma32_bf16(FC.a[m >> 2], FC.b[m & 3],
+                                     acc[m >> 2][m & 3]);
+    if (READ && m < 8) {
+      const int f = m >> 1;
+      if (m & 1)
+        FN.b[f] = *reinterpret_cast<const u32x4*>(rd_b + f * 32 * kTL + rd_k);
+      else
+        FN.a[f] = *reinterpret_cast<const u32x4*>(rd_a + f * 32 * kTL + rd_k);
+    }
+    if (m >= S0 && m - S0 < 4 * NQ) {
+      const int q = Q0 + (m - S0) / 4, op = (m - S0) & 3;
+      if (op == 0)
+        *reinterpret_cast<u32x4*>(wr_a + q * 32 * kTL) = ra[q];
+      else if (op == 1)
+        *reinterpret_cast<u32x4*>(wr_b + q * 32 * kTL) = rb[q];
+      else if (op == 2)
+        ra[q] = __builtin_amdgcn_raw_buffer_load_b128(src.ra, src.va,
+                                                      q * src.qa + src.ka, 0);
+      else
+        rb[q] = __builtin_amdgcn_raw_buffer_load_b128(src.rb, src.vb,
+                                                      q * src.qb + src.kb, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <typename TC>
 __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
   __shared__ uint16_t lds[2][2][kTM * kTL];
   if (g.header && g.header[0] != 0) return;
@@ -234,43 +300,50 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
     n_tile = tile % nt;
   }
   const int m0 = m_tile * kTM, n0 = n_tile * kTN;
-  const uint16_t* A1 = static_cast<const uint16_t*>(g.A1);
-  const uint16_t* A2 = static_cast<const uint16_t*>(g.A2);
-  const uint16_t* Bm = static_cast<const uint16_t*>(g.Bm);
+  const int rows = min(kTM, g.M - m0);
 
   // global -> register mapping: 8 lanes per 128-byte row slice, 32 rows per
-  // pass, 8 passes per operand
+  // group, 8 groups per operand; the resources cover only this tile's rows
   const int lr = tid >> 3, lc = (tid & 7) * 8;
-  int64_t aoff1[8], aoff2[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int64_t row = min(m0 + lr + 32 * q, g.M - 1);
-    aoff1[q] = row * g.a1_m + lc;
-    aoff2[q] = row * g.a2_m + lc;
-  }
-  const uint16_t* bbase = Bm + static_cast<int64_t>(n0 + lr) * g.b_n + lc;
-  const int64_t bstep = 32 * g.b_n;
+  const __amdgpu_buffer_rsrc_t rA1 = make_rsrc(
+      static_cast<const uint16_t*>(g.A1) + static_cast<int64_t>(m0) * g.a1_m,
+      static_cast<int64_t>(rows) * g.a1_m * 2);
+  const __amdgpu_buffer_rsrc_t rA2 = make_rsrc(
+      static_cast<const uint16_t*>(g.A2) + static_cast<int64_t>(m0) * g.a2_m,
+      static_cast<int64_t>(rows) * g.a2_m * 2);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(
+      static_cast<const uint16_t*>(g.Bm) + static_cast<int64_t>(n0) * g.b_n,
+      static_cast<int64_t>(kTN) * g.b_n * 2);
+  const int vA1 = static_cast<int>((lr * g.a1_m + lc) * 2);
+  const int vA2 = static_cast<int>((lr * g.a2_m + lc) * 2);
+  const int vB = static_cast<int>((lr * g.b_n + lc) * 2);
+  const int qA1 = static_cast<int>(32 * g.a1_m * 2);
+  const int qA2 = static_cast<int>(32 * g.a2_m * 2);
+  const int qB = static_cast<int>(32 * g.b_n * 2);
+  auto slice_src = [&](int k0) {
+    SliceSrc s;
+    const bool first = k0 < g.K1;
+    s.ra = first ? rA1 : rA2;
+    s.va = first ? vA1 : vA2;
+    s.qa = first ? qA1 : qA2;
+    s.ka = (first ? k0 : k0 - g.K1) * 2;
+    s.rb = rB;
+    s.vb = vB;
+    s.qb = qB;
+    s.kb = k0 * 2;
+    return s;
+  };
+
   u32x4 ra[8], rb[8];
-#define L3_LOAD_SLICE(k0)                                                     \
-  {                                                                           \
-    const int kk0 = (k0);                                                     \
-    const bool first = kk0 < g.K1;                                            \
-    const uint16_t* ab = first ? A1 + kk0 : A2 + (kk0 - g.K1);                \
-    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                           \
-      ra[q] = *reinterpret_cast<const u32x4*>(ab + (first ? aoff1[q]          \
-                                                          : aoff2[q]));       \
-      rb[q] = *reinterpret_cast<const u32x4*>(bbase + q * bstep + kk0);       \
-    }                                                                         \
-  }
-#define L3_STORE_SLICE(buf)                                                   \
-  {                                                                           \
-    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                           \
-      *reinterpret_cast<u32x4*>(&lds[buf][0][(lr + 32 * q) * kTL + lc]) =     \
-          ra[q];                                                              \
-      *reinterpret_cast<u32x4*>(&lds[buf][1][(lr + 32 * q) * kTL + lc]) =     \
-          rb[q];                                                              \
-    }                                                                         \
-  }
+  auto load_all = [&](const SliceSrc& s) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      ra[q] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, s.va, q * s.qa + s.ka,
+                                                    0);
+      rb[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, s.vb, q * s.qb + s.kb,
+                                                    0);
+    }
+  };
 
   floatx16 acc[4][4];
 #pragma unroll
@@ -280,37 +353,38 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
 
   const int nk = g.K / kTK;
   const int r = lane & 31, kh = (lane >> 5) * 8;
-  L3_LOAD_SLICE(0)
-  L3_STORE_SLICE(0)
-  L3_LOAD_SLICE(min(1, nk - 1) * kTK)
-  __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    const uint16_t* As = lds[it & 1][0] + (wm * 128 + r) * kTL + kh;
-    const uint16_t* Bs = lds[it & 1][1] + (wn * 128 + r) * kTL + kh;
+  const int aoff = (wm * 128 + r) * kTL + kh, boff = (wn * 128 + r) * kTL + kh;
+  const int woff = lr * kTL + lc;
+  load_all(slice_src(0));
 #pragma unroll
-    for (int kk = 0; kk < kTK; kk += 16) {
-      u32x4 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(As + i * 32 * kTL + kk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const u32x4*>(Bs + j * 32 * kTL + kk);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = mfma32_bf16(af[i], bf[j], acc[i][j]);
-    }
-    // the slice after next lands in the buffer just read; its global loads
-    // overlap the next slice's multiplies (clamped: the tail reloads the
-    // last slice into a buffer nobody reads again)
-    L3_STORE_SLICE((it + 1) & 1)
-    L3_LOAD_SLICE(min(it + 2, nk - 1) * kTK)
-    __syncthreads();
+  for (int q = 0; q < 8; ++q) {
+    *reinterpret_cast<u32x4*>(&lds[0][0][woff + q * 32 * kTL]) = ra[q];
+    *reinterpret_cast<u32x4*>(&lds[0][1][woff + q * 32 * kTL]) = rb[q];
   }
-#undef L3_LOAD_SLICE
-#undef L3_STORE_SLICE
+  load_all(slice_src(min(1, nk - 1) * kTK));
+  __syncthreads();
+  Frag256 F0, F1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    F0.a[i] = *reinterpret_cast<const u32x4*>(&lds[0][0][aoff + i * 32 * kTL]);
+    F0.b[i] = *reinterpret_cast<const u32x4*>(&lds[0][1][boff + i * 32 * kTL]);
+  }
+  for (int it = 0; it < nk; ++it) {
+    const int buf = it & 1;
+    // slice it+1 (in registers) goes to the other buffer, slice it+2 is
+    // fetched (clamped: the tail refetches the last slice, never read)
+    const SliceSrc src = slice_src(min(it + 2, nk - 1) * kTK);
+    const uint16_t* rda = &lds[buf][0][aoff];
+    const uint16_t* rdb = &lds[buf][1][boff];
+    uint16_t* wra = &lds[buf ^ 1][0][woff];
+    uint16_t* wrb = &lds[buf ^ 1][1][woff];
+    step256<true, 0, 3, 4>(acc, F0, F1, rda, rdb, 16, ra, rb, wra, wrb, src);
+    step256<true, 3, 3, 4>(acc, F1, F0, rda, rdb, 32, ra, rb, wra, wrb, src);
+    step256<true, 6, 2, 8>(acc, F0, F1, rda, rdb, 48, ra, rb, wra, wrb, src);
+    __syncthreads();
+    step256<true, 0, 0, 16>(acc, F1, F0, &lds[buf ^ 1][0][aoff],
+                            &lds[buf ^ 1][1][boff], 0, ra, rb, wra, wrb, src);
+  }
 
   TC* C = static_cast<TC*>(g.C);
   const int h4 = (lane >> 5) * 4;
@@ -319,32 +393,6 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int gm = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + h4 + (e & 3);
-      if (STATS) {
-        // 128 columns of row gm live in this wave: 4 per lane across the 32
-        // lanes of this half; mean and squared deviations of the float32
-        // values (two passes over registers)
-        float sm = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sm += acc[i][j][e];
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
-        const float mean = sm * (1.0f / 128.0f);
-        float m2 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float c = acc[i][j][e] - mean;
-          m2 += c * c;
-        }
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) m2 += __shfl_xor(m2, o);
-        if (r == 0 && gm < g.M) {
-          const int chunk = (n0 + wn * 128) >> 7;
-          *reinterpret_cast<float2*>(
-              g.row_stats +
-              (static_cast<int64_t>(gm) * (g.N >> 7) + chunk) * 2) =
-              make_float2(mean, m2);
-        }
-      }
       if (gm >= g.M) continue;
       TC* crow = C + static_cast<int64_t>(gm) * g.c_m + n0 + wn * 128 + r;
 #pragma unroll
@@ -354,56 +402,75 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
 }
 
 bool gemm_nt_256_ok(const GemmArgs& g) {
+  // buffer offsets are 32-bit: one tile's rows must span < 2 GiB
   return g.M >= 1024 && g.N % kTN == 0 && g.K % kTK == 0 &&
          g.K1 % kTK == 0 && g.a1_k == 1 && g.a2_k == 1 && g.b_k == 1 &&
-         g.a1_m % 8 == 0 && g.a2_m % 8 == 0 && g.b_n % 8 == 0;
+         g.a1_m % 8 == 0 && g.a2_m % 8 == 0 && g.b_n % 8 == 0 &&
+         static_cast<int64_t>(kTM) * g.a1_m * 2 < (int64_t(1) << 30) &&
+         static_cast<int64_t>(kTM) * g.a2_m * 2 < (int64_t(1) << 30) &&
+         static_cast<int64_t>(kTN) * g.b_n * 2 < (int64_t(1) << 30);
 }
 
-// ------------------------------------------------ LayerNorm from partials ---
-// One wave per row: combine the row's per-128-column (mean, M2) partials with
-// Chan's formula (equal chunk sizes), then h = gamma * (u - mean) * rstd +
-// beta on 8 bf16 elements per lane and step.
+// ------------------------------------------------- LayerNorm of bf16 u ---
+// One wave per row: the row (d bf16 values, d <= 4096) is loaded once into
+// registers, 8 values per lane and 512-column chunk; mean and biased
+// variance in two passes over the registers (wave reductions), then
+// h = gamma * (u - mean) * rstd + beta written as bf16.
 __global__ __launch_bounds__(256) void ln_apply_kernel(LnApplyArgs a) {
   if (a.header[0] != 0) return;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.B) return;
-  const int nch = a.d >> 7;
-  const float* st = a.stats + static_cast<int64_t>(row) * nch * 2;
-  float cm = 0.f, cq = 0.f;
-  if (lane < nch) {
-    const float2 v = *reinterpret_cast<const float2*>(st + 2 * lane);
-    cm = v.x;
-    cq = v.y;
-  }
-  const float mean = wave_sum(cm) / nch;
-  const float dev = lane < nch ? (cm - mean) : 0.f;
-  const float m2 = wave_sum(cq + 128.0f * dev * dev);
-  const float rstd = 1.0f / sqrtf(m2 / a.d + a.eps);
+  constexpr int kMaxChunks = 4096 / 512;
   const int64_t base = static_cast<int64_t>(row) * a.d;
-  for (int e0 = lane * 8; e0 < a.d; e0 += 512) {
-    const uint4 u = *reinterpret_cast<const uint4*>(a.U + base + e0);
-    const uint4 gv = *reinterpret_cast<const uint4*>(a.gamma + e0);
-    const uint4 bv = *reinterpret_cast<const uint4*>(a.beta + e0);
-    const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
-    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-    const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
-    uint32_t ow[4];
+  u32x4 raw[kMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int e0 = c * 512 + lane * 8;
+    raw[c] = e0 < a.d ? *reinterpret_cast<const u32x4*>(a.U + base + e0)
+                      : u32x4{0, 0, 0, 0};
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      s += __uint_as_float(raw[c][q] << 16) +
+           __uint_as_float(raw[c][q] & 0xffff0000u);
+  const float mean = wave_sum(s) / a.d;
+  float m2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    if (c * 512 + lane * 8 < a.d) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float d0 = __uint_as_float(raw[c][q] << 16) - mean;
+        const float d1 = __uint_as_float(raw[c][q] & 0xffff0000u) - mean;
+        m2 += d0 * d0 + d1 * d1;
+      }
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(m2) / a.d + a.eps);
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int e0 = c * 512 + lane * 8;
+    if (e0 >= a.d) continue;
+    const u32x4 gv = *reinterpret_cast<const u32x4*>(a.gamma + e0);
+    const u32x4 bv = *reinterpret_cast<const u32x4*>(a.beta + e0);
+    u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float u0 = __uint_as_float(uw[q] << 16);
-      const float u1 = __uint_as_float(uw[q] & 0xffff0000u);
-      const float g0 = __uint_as_float(gw[q] << 16);
-      const float g1 = __uint_as_float(gw[q] & 0xffff0000u);
-      const float b0 = __uint_as_float(bw[q] << 16);
-      const float b1 = __uint_as_float(bw[q] & 0xffff0000u);
-      const float h0 = g0 * ((u0 - mean) * rstd) + b0;
-      const float h1 = g1 * ((u1 - mean) * rstd) + b1;
-      ow[q] = static_cast<uint32_t>(f2bf(h0)) |
-              (static_cast<uint32_t>(f2bf(h1)) << 16);
+      const float u0 = __uint_as_float(raw[c][q] << 16);
+      const float u1 = __uint_as_float(raw[c][q] & 0xffff0000u);
+      const float h0 = __uint_as_float(gv[q] << 16) * ((u0 - mean) * rstd) +
+                       __uint_as_float(bv[q] << 16);
+      const float h1 =
+          __uint_as_float(gv[q] & 0xffff0000u) * ((u1 - mean) * rstd) +
+          __uint_as_float(bv[q] & 0xffff0000u);
+      o[q] = static_cast<uint32_t>(f2bf(h0)) |
+             (static_cast<uint32_t>(f2bf(h1)) << 16);
     }
-    *reinterpret_cast<uint4*>(a.h + base + e0) =
-        make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    *reinterpret_cast<u32x4*>(a.h + base + e0) = o;
   }
 }
 
@@ -423,17 +490,12 @@ hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
   if (gemm_nt_256_ok(g)) {
     const int grid = ceil_div(g.M, kTM) * (g.N / kTN);
-    if (g.row_stats) {
-      if (c_type != kBF16) return hipErrorInvalidValue;
-      gemm_nt_256_kernel<uint16_t, true><<<grid, 256, 0, s>>>(g);
-    } else if (c_type == kBF16) {
-      gemm_nt_256_kernel<uint16_t, false><<<grid, 256, 0, s>>>(g);
-    } else {
-      gemm_nt_256_kernel<float, false><<<grid, 256, 0, s>>>(g);
-    }
+    if (c_type == kBF16)
+      gemm_nt_256_kernel<uint16_t><<<grid, 256, 0, s>>>(g);
+    else
+      gemm_nt_256_kernel<float><<<grid, 256, 0, s>>>(g);
     return hipGetLastError();
   }
-  if (g.row_stats) return hipErrorInvalidValue;
   dim3 grid(g.N / kBN, ceil_div(g.M, kBM));
   if (c_type == kBF16)
     gemm_nt_mfma_kernel<uint16_t><<<grid, 256, 0, s>>>(g);

@@ -104,9 +104,6 @@ struct GemmArgs {
   int64_t c_m;
   int M, N, K;
   const int32_t* header;  // plan status word (kernel does nothing if set)
-  // Optional epilogue output: per row and per 128-column chunk of C, the
-  // chunk mean and sum of squared deviations (float2), [M x N/128].
-  float* row_stats;
 };
 
 // LayerNorm of float32 rows (one wave per row).
@@ -128,7 +125,6 @@ struct LnArgs {
 struct LnApplyArgs {
   const int32_t* header;
   const uint16_t* U;       // [B x d] bf16
-  const float* stats;      // [B x d/128 x 2]
   const uint16_t* gamma;
   const uint16_t* beta;
   int B, d;
