@@ -123,6 +123,8 @@ PlanDev carve_plan(Carver& c, int64_t B) {
   p.vals_alt = c.take<int32_t>(nb);
   p.hist = c.take<int32_t>(256 * nblk);
   p.blk = c.take<int32_t>(nblk + 1);
+  p.item_map = c.take<int2>(static_cast<size_t>(wave_items_cap(B)));
+  p.gitem_map = c.take<int2>(static_cast<size_t>(group_items_cap(B)));
   return p;
 }
 
@@ -496,6 +498,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     sa.seg_row_off = pd.seg_row_off;
     sa.seg_n = pd.seg_n;
     sa.seg_item_start = pd.seg_item_start;
+    sa.item_map = pd.item_map;
     sa.x = x;
     sa.K = K;
     sa.V = V;
@@ -526,6 +529,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       ga.seg_row_off = pd.seg_row_off;
       ga.seg_n = pd.seg_n;
       ga.seg_gitem_start = pd.seg_gitem_start;
+      ga.gitem_map = pd.gitem_map;
       ga.x = static_cast<const uint16_t*>(x);
       ga.K = static_cast<const uint16_t*>(K);
       ga.V = static_cast<const uint16_t*>(V);

@@ -43,7 +43,17 @@ struct PlanDev {
   int32_t* vals_alt;        // [B]
   int32_t* hist;            // [256 * ceil(B / kSortTile)]
   int32_t* blk;             // [ceil(B / kSortTile) + 1]
+  int2* item_map;           // wave item -> (segment, index within segment)
+  int2* gitem_map;          // group item -> (segment, tile within segment)
 };
+// Capacity of the item maps for a batch of B tokens: a segment of m tokens
+// has at most ceil(m / 16) token tiles times ceil(512 / 32) row chunks.
+__host__ __device__ inline int64_t wave_items_cap(int64_t B) {
+  return (B / kTokTile + B + 1) * (L3_MAX_ROWS_PER_ID / 32);
+}
+__host__ __device__ inline int64_t group_items_cap(int64_t B) {
+  return B / kGroupTok + B + 1;
+}
 
 struct PlanParams {
   const int32_t* ids;
@@ -64,6 +74,7 @@ struct SegFwdArgs {
   const int64_t* seg_row_off;
   const int32_t* seg_n;
   const int32_t* seg_item_start;
+  const int2* item_map;
   const void* x;
   const void* K;
   const void* V;
@@ -150,6 +161,7 @@ struct SegGroupArgs {
   const int64_t* seg_row_off;
   const int32_t* seg_n;
   const int32_t* seg_gitem_start;
+  const int2* gitem_map;
   const uint16_t* x;
   const uint16_t* K;
   const uint16_t* V;

@@ -352,6 +352,21 @@ __global__ __launch_bounds__(1024) void seg_items_scan_kernel(PlanDev pd) {
   }
 }
 
+// Direct maps from a work item to its segment and its index there, so the
+// forward kernels need no search: one thread per segment writes the
+// segment's item range (at most a few thousand entries).
+__global__ __launch_bounds__(256) void item_map_kernel(PlanDev pd) {
+  if (pd.header[0] != 0) return;
+  const int S = pd.header[1];
+  for (int g = blockIdx.x * 256 + threadIdx.x; g < S;
+       g += gridDim.x * 256) {
+    const int i0 = pd.seg_item_start[g], i1 = pd.seg_item_start[g + 1];
+    for (int i = i0; i < i1; ++i) pd.item_map[i] = make_int2(g, i - i0);
+    const int j0 = pd.seg_gitem_start[g], j1 = pd.seg_gitem_start[g + 1];
+    for (int j = j0; j < j1; ++j) pd.gitem_map[j] = make_int2(g, j - j0);
+  }
+}
+
 static int digit_passes(int64_t vocab) {
   int bits = 1;
   while (bits < 32 && (int64_t(1) << bits) < vocab) ++bits;
@@ -363,6 +378,7 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
   const int B = p.B;
   if (B <= kSmallPlanMax) {
     plan_small_kernel<<<1, 1024, 0, s>>>(pd, p);
+    item_map_kernel<<<ceil_div(B, 256), 256, 0, s>>>(pd);
     return hipGetLastError();
   }
   const int nblk = ceil_div(B, kSortTile);
@@ -390,6 +406,7 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
   seg_write_kernel<<<nblk, 256, 0, s>>>(pd, p, nblk);
   seg_items_kernel<<<ceil_div(B, 256), 256, 0, s>>>(pd, p);
   seg_items_scan_kernel<<<1, 1024, 0, s>>>(pd);
+  item_map_kernel<<<ceil_div(B, 256), 256, 0, s>>>(pd);
   return hipGetLastError();
 }
 

@@ -315,7 +315,6 @@ __global__ __launch_bounds__(256) void seg_fwd_kernel(SegFwdArgs a) {
   if (a.header[0] != 0) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int S = a.header[1];
   const int n_items = a.header[2];
   PT* P = s_p[w];
   float* ml = s_ml[w];
@@ -324,21 +323,12 @@ __global__ __launch_bounds__(256) void seg_fwd_kernel(SegFwdArgs a) {
   const T* V = static_cast<const T*>(a.V);
   for (int item = blockIdx.x * 4 + w; item < n_items;
        item += gridDim.x * 4) {
-    // segment owning this item: last s with seg_item_start[s] <= item
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.seg_item_start[mid] <= item)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-    const int s = lo;
+    const int2 im = a.item_map[item];
+    const int s = im.x, local = im.y;
     const int t_begin = a.seg_tok_start[s];
     const int m = a.seg_tok_start[s + 1] - t_begin;
     const int n = a.seg_n[s];
     const int nch = ceil_div(n, a.chunk_rows);
-    const int local = item - a.seg_item_start[s];
     const int tile = local / nch, chunk = local - tile * nch;
     const int tok0 = t_begin + tile * kTokTile;
     const int mcount = min(kTokTile, m - tile * kTokTile);

@@ -9,10 +9,10 @@
 // tokens) and all of the id's rows (at most 512).
 //
 //   scores   S = X K_t^T (64 tokens x n rows) on 16x16x32 bf16 MFMA. Wave w
-//            owns rows 64w .. 64w+63; its K fragments stream from global
-//            memory straight into registers, three 32-column steps ahead of
-//            the multiply (each K row is used by exactly one wave, so it
-//            never touches LDS). The X slice (64 tokens x 128 columns) is shared by
+//            owns an even share of the rows (16, 32 or 64 of them); its K
+//            fragments stream from global memory straight into registers,
+//            up to fifteen 32-column steps ahead of the multiply (each K row
+//            is used by exactly one wave, so it never touches LDS). The X slice (64 tokens x 128 columns) is shared by
 //            all waves, so it is staged in LDS, double buffered, one barrier
 //            per slice. Both operands use the same lane -> k assignment.
 //   softmax  exact: per-wave row maxima / sums combined through LDS; the
@@ -58,7 +58,7 @@ __device__ __forceinline__ floatx4 mfma16(const u32x4& a, const u32x4& b,
       0, 0);
 }
 
-template <int MB, int NBV>
+template <int MB, int NBW, int NBV>
 __device__ __forceinline__ void group_item(
     const SegGroupArgs& a, int tok0, int mcount, int n, int64_t rowbase,
     uint16_t (*s_x)[kGT * kXS], uint16_t* s_p, uint16_t* s_v,
@@ -69,80 +69,82 @@ __device__ __forceinline__ void group_item(
   const int nsl = d / kSW;
 
   // ------------------------------------------------------------ scores ---
-  // K streams in 32-column steps through a ring of four register slots:
-  // step t's loads are issued three steps before its multiply (the loop is
-  // unrolled by four so every slot index is static, and there is no per-wave
-  // branch), which keeps about 96 KB of K in flight per workgroup. Lane group
-  // g supplies columns 32t + 8g .. 32t + 8g + 7 of its row for both
-  // operands. X is staged in 128-column slices in LDS (double buffered, one
-  // barrier per slice). A wave past the id's last row re-reads that cached
-  // row; its results are masked below.
-  const int wrow0 = w * 64;
+  // Wave w owns rows 16*NBW*w .. 16*NBW*(w+1)-1, NBW = 1, 2 or 4 blocks of
+  // 16 rows chosen from n so that the eight waves share the id's rows
+  // evenly. K streams in 32-column steps through a ring of R = 16 / NBW
+  // register slots: step t's loads are issued R-1 steps before its multiply
+  // (the loop is unrolled by R so every slot index is static, and there is
+  // no per-wave branch), which keeps 15 .. 12 KB of K in flight per wave
+  // whatever NBW is. Lane group g supplies columns 32t + 8g .. 32t + 8g + 7
+  // of its row for both operands. X is staged in 128-column slices in LDS
+  // (double buffered, one barrier per slice). A wave past the id's last row
+  // re-reads that cached row; its results are masked below.
+  constexpr int R = 16 / NBW;
+  const int wrow0 = w * 16 * NBW;
   const bool has_rows = wrow0 < n;
-  int koff[4];
+  int koff[NBW];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb = 0; nb < NBW; ++nb)
     koff[nb] = min(wrow0 + nb * 16 + r, n - 1) * d + g * 8;
   const uint16_t* kt = a.K + rowbase * d;
   const int xt = tid >> 3, xc = (tid & 7) * 8;
   const uint16_t* xsrc =
       a.x + static_cast<int64_t>(a.perm[tok0 + min(xt, mcount - 1)]) * d + xc;
 
-  floatx4 acc[MB][4];
+  floatx4 acc[MB][NBW];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = d / 32;
-  u32x4 k0[4], k1[4], k2[4], k3[4];
-#define L3_LOAD_K(dst, t)                                                \
+  const int nsteps = d / 32;  // a multiple of 16 (seg_group_ok)
+  u32x4 kr[R][NBW];
+#define L3_LOAD_K(slot, t)                                               \
   {                                                                      \
     const int col = min((t), nsteps - 1) * 32;                           \
-    _Pragma("unroll") for (int nb = 0; nb < 4; ++nb) dst[nb] =           \
+    _Pragma("unroll") for (int nb = 0; nb < NBW; ++nb) kr[slot][nb] =    \
         ld16(kt + koff[nb] + col);                                       \
-  }
-#define L3_MUL(kreg, buf, j)                                             \
-  {                                                                      \
-    u32x4 xf[MB];                                                        \
-    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) xf[mb] =           \
-        *reinterpret_cast<const u32x4*>(                                 \
-            &s_x[buf][(mb * 16 + r) * kXS + (j) * 32 + g * 8]);          \
-    _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                     \
-        _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) acc[mb][nb] =  \
-            mfma16(xf[mb], kreg[nb], acc[mb][nb]);                       \
   }
   u32x4 x0 = ld16(xsrc), x1 = ld16(xsrc + 64);
   *reinterpret_cast<u32x4*>(&s_x[0][xt * kXS + xc]) = x0;
   *reinterpret_cast<u32x4*>(&s_x[0][xt * kXS + xc + 64]) = x1;
-  L3_LOAD_K(k0, 0)
-  L3_LOAD_K(k1, 1)
-  L3_LOAD_K(k2, 2)
+#pragma unroll
+  for (int q = 0; q < R - 1; ++q) L3_LOAD_K(q, q)
   {
     const int nx = min(1, nsl - 1) * kSW;
     x0 = ld16(xsrc + nx);
     x1 = ld16(xsrc + nx + 64);
   }
   __syncthreads();
-  for (int sl = 0; sl < nsl; ++sl) {
-    const int cur = sl & 1, t = sl * 4;
-    L3_LOAD_K(k3, t + 3)
-    L3_MUL(k0, cur, 0)
-    L3_LOAD_K(k0, t + 4)
-    L3_MUL(k1, cur, 1)
-    L3_LOAD_K(k1, t + 5)
-    L3_MUL(k2, cur, 2)
-    L3_LOAD_K(k2, t + 6)
-    L3_MUL(k3, cur, 3)
-    *reinterpret_cast<u32x4*>(&s_x[cur ^ 1][xt * kXS + xc]) = x0;
-    *reinterpret_cast<u32x4*>(&s_x[cur ^ 1][xt * kXS + xc + 64]) = x1;
-    const int nx = min(sl + 2, nsl - 1) * kSW;
-    x0 = ld16(xsrc + nx);
-    x1 = ld16(xsrc + nx + 64);
-    __syncthreads();
+  for (int base = 0; base < nsteps; base += R) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int t = base + q;
+      L3_LOAD_K((q + R - 1) % R, t + R - 1)
+      const int buf = (t >> 2) & 1;
+      u32x4 xf[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        xf[mb] = *reinterpret_cast<const u32x4*>(
+            &s_x[buf][(mb * 16 + r) * kXS + (q & 3) * 32 + g * 8]);
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb][nb] = mfma16(xf[mb], kr[q][nb], acc[mb][nb]);
+      if ((q & 3) == 3) {
+        // end of X slice t/4: the next slice (in registers) goes to the
+        // other buffer, the one after is fetched
+        *reinterpret_cast<u32x4*>(&s_x[buf ^ 1][xt * kXS + xc]) = x0;
+        *reinterpret_cast<u32x4*>(&s_x[buf ^ 1][xt * kXS + xc + 64]) = x1;
+        const int nx = min((t >> 2) + 2, nsl - 1) * kSW;
+        x0 = ld16(xsrc + nx);
+        x1 = ld16(xsrc + nx + 64);
+        __syncthreads();
+      }
+    }
   }
 #undef L3_LOAD_K
-#undef L3_MUL
 
   // ----------------------------------------------------------- softmax ---
   // lane holds S[token mb*16 + 4g + i][row wrow0 + nb*16 + r]
@@ -154,7 +156,7 @@ __device__ __forceinline__ void group_item(
     for (int i = 0; i < 4; ++i) mx[mb][i] = -INFINITY;
   if (has_rows) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NBW; ++nb)
       if (wrow0 + nb * 16 + r < n) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -187,7 +189,7 @@ __device__ __forceinline__ void group_item(
 #pragma unroll
     for (int i = 0; i < 4; ++i) sm[mb][i] = 0.f;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NBW; ++nb) {
     const int row = wrow0 + nb * 16 + r;
     if (row < n32) {
       const bool valid = row < n;
@@ -313,40 +315,45 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
   __shared__ uint16_t s_v[kGW][kVR * kVS];
   __shared__ float s_red[2][kGW][kGT];
   if (a.header[0] != 0) return;
-  const int S = a.header[1];
   const int n_items = a.header[3];
   const int G = gridDim.x;
   const int vb = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
                               : blockIdx.x;
   uint16_t* my_v = s_v[threadIdx.x >> 6];
   for (int item = vb; item < n_items; item += G) {
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.seg_gitem_start[mid] <= item)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-    const int s = lo;
+    const int2 im = a.gitem_map[item];
+    const int s = im.x, tile = im.y;
     const int t_begin = a.seg_tok_start[s];
     const int m = a.seg_tok_start[s + 1] - t_begin;
-    const int tile = item - a.seg_gitem_start[s];
     const int tok0 = t_begin + tile * kGT;
     const int mcount = min(kGT, m - tile * kGT);
     const int n = a.seg_n[s];
     const int64_t rowbase = a.seg_row_off[s];
-    if (mcount <= 16)
-      group_item<1, NBV>(a, tok0, mcount, n, rowbase, s_x, s_p, my_v, s_red);
-    else if (mcount <= 32)
-      group_item<2, NBV>(a, tok0, mcount, n, rowbase, s_x, s_p, my_v, s_red);
-    else
-      group_item<4, NBV>(a, tok0, mcount, n, rowbase, s_x, s_p, my_v, s_red);
+#define L3_ITEM(MB, NBW) \
+  group_item<MB, NBW, NBV>(a, tok0, mcount, n, rowbase, s_x, s_p, my_v, s_red)
+#define L3_ROWS(MB)        \
+  if (n <= 128)            \
+    L3_ITEM(MB, 1);        \
+  else if (n <= 256)       \
+    L3_ITEM(MB, 2);        \
+  else                     \
+    L3_ITEM(MB, 4);
+    if (mcount <= 16) {
+      L3_ROWS(1)
+    } else if (mcount <= 32) {
+      L3_ROWS(2)
+    } else {
+      L3_ROWS(4)
+    }
+#undef L3_ROWS
+#undef L3_ITEM
   }
 }
 
 bool seg_group_ok(int d, int d_e) {
-  return d % kSW == 0 && d_e % 128 == 0 && d_e <= kGW * kCPWMax;
+  // d: whole 16-step K rings (32 columns a step); d_e: whole 16-column
+  // value blocks per wave
+  return d % 512 == 0 && d_e % 128 == 0 && d_e <= kGW * kCPWMax;
 }
 
 hipError_t seg_group_launch(const SegGroupArgs& a, int items_ub,
