@@ -74,9 +74,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
   const int B = p.B;
   int B2 = 1;
   while (B2 < B) B2 <<= 1;
-  if (tid == 0) {
-    pd.header[0] = 0;
-  }
+  if (tid < 16) pd.header[tid] = 0;
   __syncthreads();
 
   for (int i = tid; i < B2; i += 1024) {
@@ -168,7 +166,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
 
 // ---------------------------------------------------------------- large ---
 __global__ void header_init_kernel(int32_t* header) {
-  if (threadIdx.x < 4) header[threadIdx.x] = 0;
+  if (threadIdx.x < 16) header[threadIdx.x] = 0;
 }
 
 // Digit histogram of one 1024-key tile; pass 0 also checks the id range.

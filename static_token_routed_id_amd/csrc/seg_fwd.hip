@@ -40,7 +40,7 @@
 namespace l3 {
 
 constexpr int kNBMax = kWaveMaxRows / 16;  // 16-row blocks per item
-constexpr int kVBurst = 16;                // V rows loaded ahead of use
+constexpr int kVHalf = 8;                  // V rows per half burst
 
 template <bool BF16>
 struct Types;
@@ -60,7 +60,7 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 }
 
 // ---- scores --------------------------------------------------------------
-template <int NB>
+template <int NB, int R>
 __device__ __forceinline__ void scores_bf16(const uint16_t* __restrict__ xr,
                                             const uint16_t* __restrict__ kt,
                                             int d, int nc, int r, int g,
@@ -72,29 +72,34 @@ __device__ __forceinline__ void scores_bf16(const uint16_t* __restrict__ xr,
   for (int nb = 0; nb < NB; ++nb)
     koff[nb] = min(nb * 16 + r, nc - 1) * d + g * 8;
   const uint16_t* xp = xr + g * 8;
-  const int last = d - 32;
-  u32x4 xa, xb, ka[NB], kb[NB];
-#define L3_LOAD(xd, kd, col)                                          \
+  const int nsteps = d / 32;  // a multiple of R
+  // ring of R register slots: step t's loads are issued R-1 steps ahead of
+  // its multiply; the loop is unrolled by R so slot indices are static
+  u32x4 xs[R], ks[R][NB];
+#define L3_LOAD(slot, t)                                              \
   {                                                                   \
-    const int c = (col);                                              \
-    xd = ld16(xp + c);                                                \
-    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) kd[nb] =        \
+    const int c = min((t), nsteps - 1) * 32;                          \
+    xs[slot] = ld16(xp + c);                                          \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) ks[slot][nb] =  \
         ld16(kt + koff[nb] + c);                                      \
   }
-#define L3_MUL(xs, ks)                                                \
-  _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) acc[nb] =         \
-      __builtin_amdgcn_mfma_f32_16x16x32_bf16(                        \
-          __builtin_bit_cast(bf16x8_t, xs),                           \
-          __builtin_bit_cast(bf16x8_t, ks[nb]), acc[nb], 0, 0, 0);
-  L3_LOAD(xa, ka, 0)
-  for (int kc = 0; kc < d; kc += 64) {
-    L3_LOAD(xb, kb, kc + 32)
-    L3_MUL(xa, ka)
-    L3_LOAD(xa, ka, min(kc + 64, last))
-    L3_MUL(xb, kb)
+#pragma unroll
+  for (int q = 0; q < R - 1; ++q) L3_LOAD(q, q)
+  for (int base = 0; base < nsteps; base += R) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      L3_LOAD((q + R - 1) % R, base + q + R - 1)
+      // keep the loads ahead of this step's multiplies: left alone, the
+      // scheduler sinks them past the MFMAs and the ring drains each step
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, xs[q]),
+            __builtin_bit_cast(bf16x8_t, ks[q][nb]), acc[nb], 0, 0, 0);
+    }
   }
 #undef L3_LOAD
-#undef L3_MUL
 }
 
 template <int NB>
@@ -174,9 +179,14 @@ __device__ __forceinline__ void scores_softmax(
     const typename Types<BF16>::T* xr, const typename Types<BF16>::T* kt,
     int d, int nc, int r, int g, typename Types<BF16>::P* P, float* ml) {
   floatx4 acc[kNBMax];
-  if constexpr (BF16)
-    scores_bf16<NB>(xr, kt, d, nc, r, g, acc);
-  else
+  if constexpr (BF16) {
+    // deeper rings where few rows leave registers free
+    constexpr int R = NB == 1 ? 8 : (NB == 2 ? 4 : 2);
+    if (R > 2 && (d / 32) % R == 0)
+      scores_bf16<NB, R>(xr, kt, d, nc, r, g, acc);
+    else
+      scores_bf16<NB, 2>(xr, kt, d, nc, r, g, acc);
+  } else
     scores_f32<NB>(xr, kt, d, nc, r, g, acc);
   softmax_rows<NB>(acc, nc, r, g, P, ml);
 }
@@ -257,29 +267,40 @@ __device__ __forceinline__ void aggregate_and_store(
     for (int t = 0; t < MTOK; ++t)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
-    for (int j0 = 0; j0 < nc; j0 += kVBurst) {
-      // a burst of V rows in flight before any is used (rows past the
-      // chunk repeat its last row; their weights are never read)
-      RowWords<EPL, BF16> v[kVBurst];
-#pragma unroll
-      for (int q = 0; q < kVBurst; ++q)
-        load_words<EPL, BF16>(
-            vp + static_cast<int64_t>(min(j0 + q, nc - 1)) * a.d_e, v[q]);
-      const int jn = min(kVBurst, nc - j0);
-#pragma unroll
-      for (int q = 0; q < kVBurst; ++q) {
-        if (q < jn) {
-          const PT* pj = P + (j0 + q) * kTokTile;
-#pragma unroll
-          for (int t = 0; t < MTOK; ++t) {
-            const float p = static_cast<float>(pj[t]);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e)
-              acc[t][e] = fmaf(p, word_value<EPL, BF16>(v[q], e), acc[t][e]);
-          }
-        }
-      }
+    // V rows in two half bursts: the next half is in flight while the
+    // current one is used (rows past the chunk repeat its last row; their
+    // weights are never read)
+    RowWords<EPL, BF16> va[kVHalf], vb[kVHalf];
+#define L3_VLOAD(dst, j)                                                  \
+  _Pragma("unroll") for (int q = 0; q < kVHalf; ++q) load_words<EPL, BF16>( \
+      vp + static_cast<int64_t>(min((j) + q, nc - 1)) * a.d_e, dst[q]);
+#define L3_VUSE(src, j)                                                   \
+  {                                                                       \
+    const int jn = min(kVHalf, nc - (j));                                 \
+    _Pragma("unroll") for (int q = 0; q < kVHalf; ++q) {                  \
+      if (q < jn) {                                                       \
+        const PT* pj = P + ((j) + q) * kTokTile;                          \
+        _Pragma("unroll") for (int t = 0; t < MTOK; ++t) {                \
+          const float p = static_cast<float>(pj[t]);                      \
+          _Pragma("unroll") for (int e = 0; e < EPL; ++e) acc[t][e] =     \
+              fmaf(p, word_value<EPL, BF16>(src[q], e), acc[t][e]);       \
+        }                                                                 \
+      }                                                                   \
+    }                                                                     \
+  }
+    L3_VLOAD(va, 0)
+    for (int j0 = 0; j0 < nc; j0 += 2 * kVHalf) {
+      L3_VLOAD(vb, j0 + kVHalf)
+      __builtin_amdgcn_sched_barrier(0);
+      L3_VUSE(va, j0)
+      __builtin_amdgcn_sched_barrier(0);
+      L3_VLOAD(va, j0 + 2 * kVHalf)
+      __builtin_amdgcn_sched_barrier(0);
+      L3_VUSE(vb, j0 + kVHalf)
+      __builtin_amdgcn_sched_barrier(0);
     }
+#undef L3_VLOAD
+#undef L3_VUSE
 #pragma unroll
     for (int t = 0; t < MTOK; ++t) {
       if (t < mcount) {
@@ -307,7 +328,7 @@ __device__ __forceinline__ void aggregate_and_store(
 }
 
 template <bool BF16, int EPL>
-__global__ __launch_bounds__(256) void seg_fwd_kernel(SegFwdArgs a) {
+__global__ __launch_bounds__(256, 2) void seg_fwd_kernel(SegFwdArgs a) {
   typedef typename Types<BF16>::T T;
   typedef typename Types<BF16>::P PT;
   __shared__ PT s_p[4][kNBMax * 16 * kTokTile];

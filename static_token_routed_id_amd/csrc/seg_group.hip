@@ -121,6 +121,9 @@ __device__ __forceinline__ void group_item(
     for (int q = 0; q < R; ++q) {
       const int t = base + q;
       L3_LOAD_K((q + R - 1) % R, t + R - 1)
+      // keep the loads ahead of this step's multiplies: left alone, the
+      // scheduler sinks them past the MFMAs and the ring drains each step
+      __builtin_amdgcn_sched_barrier(0);
       const int buf = (t >> 2) & 1;
       u32x4 xf[MB];
 #pragma unroll
@@ -141,6 +144,7 @@ __device__ __forceinline__ void group_item(
         x0 = ld16(xsrc + nx);
         x1 = ld16(xsrc + nx + 64);
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -282,6 +286,7 @@ __device__ __forceinline__ void group_item(
     for (int q = 0; q < SPL; ++q)
       vreg[q] = ld16(vt + static_cast<int64_t>(min(nr + vrow[q], n - 1)) *
                               a.d_e + vcol[q]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ------------------------------------------------------------ output ---
