@@ -189,24 +189,40 @@ __global__ __launch_bounds__(256) void radix_hist_kernel(
   hist[tid * nblk + blockIdx.x] = h[tid];
 }
 
-// In-place exclusive scan of n ints by one 1024-thread workgroup; the total
-// goes to *total_out when given.
+// In-place exclusive scan of a[0..n) by one 1024-thread workgroup: rounds
+// of 16384 values, each thread taking 16 consecutive ones (all loads of a
+// round in flight together), one workgroup scan per round. Returns the total.
+__device__ int scan_excl_1024(int32_t* a, int n, int* tmp) {
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int base = 0; base < n; base += 16 * 1024) {
+    const int i0 = base + tid * 16;
+    int v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = i0 + j < n ? a[i0 + j] : 0;
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int t = v[j];
+      v[j] = sum;
+      sum += t;
+    }
+    int total;
+    const int off = block_excl_scan<1024>(sum, tmp, &total) + carry;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (i0 + j < n) a[i0 + j] = v[j] + off;
+    carry += total;
+  }
+  return carry;
+}
+
+// In-place exclusive scan of n ints; the total goes to *total_out when given.
 __global__ __launch_bounds__(1024) void scan_single_kernel(int32_t* a, int n,
                                                            int32_t* total_out) {
   __shared__ int tmp[1024 / 64 + 1];
-  const int tid = threadIdx.x;
-  const int per = ceil_div(n, 1024);
-  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
-  int sum = 0;
-  for (int i = i0; i < i1; ++i) sum += a[i];
-  int total;
-  int run = block_excl_scan<1024>(sum, tmp, &total);
-  for (int i = i0; i < i1; ++i) {
-    int v = a[i];
-    a[i] = run;
-    run += v;
-  }
-  if (tid == 0 && total_out) *total_out = total;
+  const int total = scan_excl_1024(a, n, tmp);
+  if (threadIdx.x == 0 && total_out) *total_out = total;
 }
 
 // Stable scatter of one 1024-key tile by one digit. Keys of a tile are taken
@@ -320,31 +336,15 @@ __global__ __launch_bounds__(256) void seg_items_kernel(PlanDev pd,
   }
 }
 
-// Exclusive scan of a[0..n) in place, a[n] = total.
-__device__ void scan_inplace_1024(int32_t* a, int n, int* tmp, int* total) {
-  const int tid = threadIdx.x;
-  const int per = ceil_div(n, 1024);
-  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
-  int sum = 0;
-  for (int i = i0; i < i1; ++i) sum += a[i];
-  int run = block_excl_scan<1024>(sum, tmp, total);
-  for (int i = i0; i < i1; ++i) {
-    int v = a[i];
-    a[i] = run;
-    run += v;
-  }
-  if (tid == 0) a[n] = *total;
-}
-
-// Scan both item counts in place; the count S is read on the device.
+// Scan both item counts in place (a[S] = total); S is read on the device.
 __global__ __launch_bounds__(1024) void seg_items_scan_kernel(PlanDev pd) {
   __shared__ int tmp[1024 / 64 + 1];
   const int n = pd.header[1];
-  int total, gtotal;
-  scan_inplace_1024(pd.seg_item_start, n, tmp, &total);
-  __syncthreads();
-  scan_inplace_1024(pd.seg_gitem_start, n, tmp, &gtotal);
+  const int total = scan_excl_1024(pd.seg_item_start, n, tmp);
+  const int gtotal = scan_excl_1024(pd.seg_gitem_start, n, tmp);
   if (threadIdx.x == 0) {
+    pd.seg_item_start[n] = total;
+    pd.seg_gitem_start[n] = gtotal;
     pd.header[2] = total;
     pd.header[3] = gtotal;
   }
