@@ -18,6 +18,9 @@ constexpr int kTokTile = 16;
 constexpr int kWaveMaxRows = 128;
 // Tokens handled by one item of the group kernel (ids with many rows).
 constexpr int kGroupTok = 64;
+// Ids of the group kernel with more than kGroupTok tokens are cut into
+// items of this many tokens (K_t and V_t are read once per item).
+constexpr int kHotTok = 128;
 // Largest batch sorted by the single-workgroup plan kernel.
 constexpr int kSmallPlanMax = 8192;
 // Elements per block of the multi-kernel radix sort.

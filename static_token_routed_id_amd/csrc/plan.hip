@@ -52,8 +52,9 @@ __device__ __forceinline__ bool id_rows(const PlanParams& p, int t,
 }
 
 // Segments with at least group_min_rows rows (when enabled) go to the
-// workgroup-per-item group kernel in tiles of kGroupTok tokens; the others
-// to the wave kernel in tiles of kTokTile tokens times row chunks.
+// workgroup-per-item group kernel: one item if they have at most kGroupTok
+// tokens, else items of kHotTok tokens; the others go to the wave kernel in
+// tiles of kTokTile tokens times row chunks.
 __device__ __forceinline__ bool is_group(int n, const PlanParams& p) {
   return p.group_min_rows > 0 && n >= p.group_min_rows;
 }
@@ -61,7 +62,8 @@ __device__ __forceinline__ int items_of(int m, int n, const PlanParams& p) {
   return is_group(n, p) ? 0 : ceil_div(m, kTokTile) * ceil_div(n, p.chunk_rows);
 }
 __device__ __forceinline__ int gitems_of(int m, int n, const PlanParams& p) {
-  return is_group(n, p) ? ceil_div(m, kGroupTok) : 0;
+  if (!is_group(n, p)) return 0;
+  return m > kGroupTok ? ceil_div(m, kHotTok) : 1;
 }
 
 // ---------------------------------------------------------------- small ---

@@ -313,29 +313,305 @@ __device__ __forceinline__ void group_item(
   __syncthreads();
 }
 
+// ---------------------------------------------------------------- busy ids ---
+// Items of ids with more than kGroupTok tokens hold up to kHotTok tokens, so
+// the id's K_t and V_t are read once per 128 tokens. Layout of the shared
+// buffer: scores phase {X slice [128][72], K slice [512][72]}, then values
+// phase {P [128][520], V staging [8 waves][16][72]} in the same bytes.
+//
+//   scores  S = X K_t^T as a small GEMM on 32x32x16 bf16 MFMA: wave w owns
+//           rows 64w .. 64w+63 of K_t (two 32-row blocks) for all tokens
+//           (MB32 blocks of 32). Both operands go through LDS in 64-column
+//           slices loaded with whole 128-byte lines per row (8 lanes per
+//           row): the MFMA register layout would fetch 16 rows x 64 bytes
+//           per load, which halves what the L1 delivers when K_t comes from
+//           L2, as it does for the later items of a busy id. The next slice
+//           is fetched into registers while the current one is multiplied.
+//   softmax exact, as in the 64-token path (per-wave maxima and sums through
+//           LDS); weights bf16 in P.
+//   values  A = P V_t on 16x16x16 bf16 MFMA, wave w owning d_e/8 columns for
+//           all tokens; V_t rows reach the B operand through a wave-private
+//           16-row staging buffer and the transposing LDS read, the rows of
+//           the next three steps in flight in registers.
+constexpr int kHT = kHotTok;           // tokens per busy-id item
+constexpr int kHS = 64;                // columns per X / K slice
+constexpr int kHL = kHS + 8;           // slice row stride (elements)
+constexpr int kHPS = kGRows + 8;       // P row stride
+constexpr int kHVR = 16;               // V rows per value step
+constexpr int kHRV = 4;                // value steps in flight
+constexpr size_t kHotScoreBytes = (size_t)(kHT + kGRows) * kHL * 2;
+constexpr size_t kHotValueBytes =
+    (size_t)kHT * kHPS * 2 + (size_t)kGW * kHVR * kVS * 2;
+constexpr size_t kGroupBytes = (size_t)2 * kGT * kXS * 2 +
+                               (size_t)kGT * kPS * 2 +
+                               (size_t)kGW * kVR * kVS * 2;
+constexpr size_t kSmemBytes =
+    kHotValueBytes > kGroupBytes ? kHotValueBytes : kGroupBytes;
+static_assert(kHotScoreBytes <= kSmemBytes, "scores staging must fit");
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t group_rsrc(
+    const uint16_t* base, int64_t bytes) {
+  // 0x00020000: raw (untyped) 32-bit data format, the usual gfx9 setting
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(base), 0,
+      static_cast<int>(bytes > 0x7fffffff ? 0x7fffffff : bytes), 0x00020000);
+}
+
+// The thread index through an empty asm: addresses derived from it are
+// recomputed per item instead of being hoisted out of the item loop (where
+// the hundred-odd lane addresses of the softmax would be spilled).
+__device__ __forceinline__ int opaque_int(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+template <int MB32, int NBV>
+__device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
+                                         int mcount, int n, int64_t rowbase,
+                                         uint8_t* smem,
+                                         float (*red)[kGW][kHT]) {
+  const int tid = opaque_int(threadIdx.x), lane = tid & 63, w = tid >> 6;
+  const int d = a.d;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* ks = xs + kHT * kHL;
+
+  // ------------------------------------------------------------ scores ---
+  // staging: thread -> rows lr + 64q, 16-byte chunk lc of the slice
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
+  const __amdgpu_buffer_rsrc_t rk =
+      group_rsrc(a.K + rowbase * d, static_cast<int64_t>(n) * d * 2);
+  int kvo[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) kvo[q] = (min(lr + 64 * q, n - 1) * d + lc) * 2;
+  const uint16_t* xp[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    xp[q] = a.x +
+            static_cast<int64_t>(a.perm[tok0 + min(lr + 64 * q, mcount - 1)]) *
+                d + lc;
+  u32x4 sx[2], sk[8];
+  auto load_slice = [&](int c0) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) sx[q] = ld16(xp[q] + c0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      sk[q] = __builtin_amdgcn_raw_buffer_load_b128(rk, kvo[q], c0 * 2, 0);
+  };
+  floatx16 acc[MB32][2];
+#pragma unroll
+  for (int i = 0; i < MB32; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+  const int nsl = d / kHS;
+  const int r = lane & 31, kh = (lane >> 5) * 8;
+  load_slice(0);
+  for (int sl = 0; sl < nsl; ++sl) {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      *reinterpret_cast<u32x4*>(&xs[(lr + 64 * q) * kHL + lc]) = sx[q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      *reinterpret_cast<u32x4*>(&ks[(lr + 64 * q) * kHL + lc]) = sk[q];
+    __syncthreads();
+    load_slice(min(sl + 1, nsl - 1) * kHS);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < kHS; kk += 16) {
+      u32x4 af[MB32], bq[2];
+#pragma unroll
+      for (int i = 0; i < MB32; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(
+            &xs[(32 * i + r) * kHL + kk + kh]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bq[j] = *reinterpret_cast<const u32x4*>(
+            &ks[(64 * w + 32 * j + r) * kHL + kk + kh]);
+#pragma unroll
+      for (int i = 0; i < MB32; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = mfma32_bf16(af[i], bq[j], acc[i][j]);
+    }
+  }
+
+  // ----------------------------------------------------------- softmax ---
+  // acc[i][j][e]: token 32i + 8(e/4) + 4h + e%4, row 64w + 32j + r (h, r:
+  // lane half and lane within the half)
+  const int h4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < MB32; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float v = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (64 * w + 32 * j + r < n) v = fmaxf(v, acc[i][j][e]);
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+      if (r == 0) red[0][w][32 * i + 8 * (e >> 2) + h4 + (e & 3)] = v;
+    }
+  __syncthreads();
+  uint16_t* P = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+  for (int i = 0; i < MB32; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int t = 32 * i + 8 * (e >> 2) + h4 + (e & 3);
+      float mxv = red[0][0][t];
+#pragma unroll
+      for (int v = 1; v < kGW; ++v) mxv = fmaxf(mxv, red[0][v][t]);
+      float sm = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = 64 * w + 32 * j + r;
+        const float pv = row < n ? __expf(acc[i][j][e] - mxv) : 0.f;
+        sm += pv;
+        P[t * kHPS + row] = f2bf(pv);
+      }
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
+      if (r == 0) red[1][w][t] = sm;
+    }
+  __syncthreads();
+
+  // ------------------------------------------------------------ values ---
+  constexpr int TB = MB32 * 2;          // 16-token blocks
+  constexpr int CPW = NBV * 16;         // value columns of this wave
+  constexpr int CPR = CPW / 8;          // 16-byte chunks per staged row
+  constexpr int NCH = kHVR * CPR;       // chunks per step
+  constexpr int SPL = (NCH + 63) / 64;  // chunks per lane
+  uint16_t* vs = P + kHT * kHPS + w * (kHVR * kVS);
+  const int col0 = w * CPW;
+  const uint16_t* vt = a.V + rowbase * a.d_e + col0;
+  int vrow[SPL], vcol[SPL];
+#pragma unroll
+  for (int q = 0; q < SPL; ++q) {
+    const int id = min(q * 64 + lane, NCH - 1);
+    vrow[q] = id / CPR;
+    vcol[q] = (id % CPR) * 8;
+  }
+  // steps of 16 rows, padded to a multiple of kHRV (P is zero past row n)
+  const int nst = ceil_div(ceil_div(n, kHVR), kHRV) * kHRV;
+  u32x4 vr[kHRV][SPL];
+#define L3_VLOAD(slot, st)                                                  \
+  {                                                                         \
+    const int slot_ = (slot), row_ = (st) * kHVR;                           \
+    _Pragma("unroll") for (int c_ = 0; c_ < SPL; ++c_) vr[slot_][c_] =      \
+        ld16(vt + static_cast<int64_t>(min(row_ + vrow[c_], n - 1)) *       \
+                      a.d_e + vcol[c_]);                                    \
+  }
+#pragma unroll
+  for (int q = 0; q < kHRV - 1; ++q) L3_VLOAD(q, q)
+  floatx4 acc2[TB][NBV];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int cb = 0; cb < NBV; ++cb) acc2[tb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int r16 = lane & 15, g16 = lane >> 4;
+  // transposing-read source of this lane: row 4*g16 + r16/4, columns
+  // 4 * (r16 % 4) of each 16-column block
+  const int trow = 4 * g16 + (r16 >> 2), tcol = 4 * (r16 & 3);
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  for (int base = 0; base < nst; base += kHRV) {
+#pragma unroll
+    for (int q = 0; q < kHRV; ++q) {
+      const int st = base + q;
+      L3_VLOAD((q + kHRV - 1) % kHRV, st + kHRV - 1)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int c = 0; c < SPL; ++c)
+        *reinterpret_cast<u32x4*>(&vs[vrow[c] * kVS + vcol[c]]) = vr[q][c];
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      v4i16 bq[NBV];
+#pragma unroll
+      for (int cb = 0; cb < NBV; ++cb)
+        bq[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(&vs[trow * kVS + cb * 16 + tcol]));
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const v4i16 pa = *reinterpret_cast<const v4i16*>(
+            &P[(tb * 16 + r16) * kHPS + st * kHVR + 4 * g16]);
+#pragma unroll
+        for (int cb = 0; cb < NBV; ++cb)
+          acc2[tb][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              pa, bq[cb], acc2[tb][cb], 0, 0, 0);
+      }
+    }
+  }
+#undef L3_VLOAD
+
+  // ------------------------------------------------------------ output ---
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = tb * 16 + 4 * g16 + i;
+      if (t < mcount) {
+        float l = 0.f;
+#pragma unroll
+        for (int v = 0; v < kGW; ++v) l += red[1][v][t];
+        const float inv = 1.0f / l;
+        const int64_t orig = a.perm[tok0 + t];
+#pragma unroll
+        for (int cb = 0; cb < NBV; ++cb) {
+          const float o = acc2[tb][cb][i] * inv;
+          const int64_t idx = orig * a.d_e + col0 + cb * 16 + r16;
+          a.a_out[idx] = f2bf(o);
+          if (a.a_save) a.a_save[idx] = o;
+        }
+      }
+    }
+  __syncthreads();
+}
+
+
 template <int NBV>
 __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
-  __shared__ uint16_t s_x[2][kGT * kXS];
-  __shared__ uint16_t s_p[kGT * kPS];
-  __shared__ uint16_t s_v[kGW][kVR * kVS];
-  __shared__ float s_red[2][kGW][kGT];
+  __shared__ __align__(16) uint8_t smem[kSmemBytes];
+  __shared__ float s_red[2][kGW][kHT];
   if (a.header[0] != 0) return;
+  // 64-token path: X slices, P and V staging carved from the same bytes
+  uint16_t (*s_x)[kGT * kXS] = reinterpret_cast<uint16_t (*)[kGT * kXS]>(smem);
+  uint16_t* s_p = reinterpret_cast<uint16_t*>(smem) + 2 * kGT * kXS;
+  uint16_t* s_v = s_p + kGT * kPS;
+  float (*red64)[kGW][kGT] = reinterpret_cast<float (*)[kGW][kGT]>(&s_red[0][0][0]);
   const int n_items = a.header[3];
   const int G = gridDim.x;
   const int vb = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
                               : blockIdx.x;
-  uint16_t* my_v = s_v[threadIdx.x >> 6];
+  uint16_t* my_v = s_v + (threadIdx.x >> 6) * (kVR * kVS);
+  // Two passes over this workgroup's items: first the 128-token items of
+  // ids with more than kGroupTok tokens, then the others (separate loops
+  // keep the two paths' registers apart).
   for (int item = vb; item < n_items; item += G) {
     const int2 im = a.gitem_map[item];
     const int s = im.x, tile = im.y;
     const int t_begin = a.seg_tok_start[s];
     const int m = a.seg_tok_start[s + 1] - t_begin;
-    const int tok0 = t_begin + tile * kGT;
-    const int mcount = min(kGT, m - tile * kGT);
+    if (m <= kGT) continue;
     const int n = a.seg_n[s];
     const int64_t rowbase = a.seg_row_off[s];
+    const int tok0 = t_begin + tile * kHT;
+    const int mcount = min(kHT, m - tile * kHT);
+    if (mcount > 64)
+      hot_item<4, NBV>(a, tok0, mcount, n, rowbase, smem, s_red);
+    else
+      hot_item<2, NBV>(a, tok0, mcount, n, rowbase, smem, s_red);
+  }
+  for (int item = vb; item < n_items; item += G) {
+    const int2 im = a.gitem_map[item];
+    const int s = im.x;
+    const int t_begin = a.seg_tok_start[s];
+    const int m = a.seg_tok_start[s + 1] - t_begin;
+    if (m > kGT) continue;
+    const int n = a.seg_n[s];
+    const int64_t rowbase = a.seg_row_off[s];
+    const int tok0 = t_begin;
+    const int mcount = m;
 #define L3_ITEM(MB, NBW) \
-  group_item<MB, NBW, NBV>(a, tok0, mcount, n, rowbase, s_x, s_p, my_v, s_red)
+  group_item<MB, NBW, NBV>(a, tok0, mcount, n, rowbase, s_x, s_p, my_v, red64)
 #define L3_ROWS(MB)        \
   if (n <= 128)            \
     L3_ITEM(MB, 1);        \
@@ -356,9 +632,9 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
 }
 
 bool seg_group_ok(int d, int d_e) {
-  // d: whole 16-step K rings (32 columns a step); d_e: whole 16-column
-  // value blocks per wave
-  return d % 512 == 0 && d_e % 128 == 0 && d_e <= kGW * kCPWMax;
+  // d: whole 16-step K rings (32 columns a step); d_e: one, two or four
+  // 16-column value blocks per wave
+  return d % 512 == 0 && (d_e == 128 || d_e == 256 || d_e == 512);
 }
 
 hipError_t seg_group_launch(const SegGroupArgs& a, int items_ub,
