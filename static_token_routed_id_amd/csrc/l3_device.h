@@ -73,26 +73,56 @@ __device__ __forceinline__ floatx4 mfma_f32(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// Cross-lane reductions on DPP moves (no trip through the LDS crossbar).
+// Controls (gfx9 encoding): quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140, row_bcast15 = 0x142,
+// row_bcast31 = 0x143.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                         __builtin_bit_cast(int, v), CTRL,
+                                         ROW_MASK, 0xF, false));
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-// Reductions over the 16 lanes that share (lane >> 4).
+// Every lane of each 16-lane row gets the row's sum / maximum: after the two
+// quad permutations each quad holds its total, the half mirror pairs the two
+// quads of each 8 lanes, the mirror pairs the two halves of the row.
 __device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  v += dpp_f<0xB1>(v, v);
+  v += dpp_f<0x4E>(v, v);
+  v += dpp_f<0x141>(v, v);
+  v += dpp_f<0x140>(v, v);
   return v;
 }
 __device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  v = fmaxf(v, dpp_f<0xB1>(v, v));
+  v = fmaxf(v, dpp_f<0x4E>(v, v));
+  v = fmaxf(v, dpp_f<0x141>(v, v));
+  v = fmaxf(v, dpp_f<0x140>(v, v));
   return v;
+}
+// 32-lane groups (lanes 0-31, 32-63): the total lands in lanes 16-31 and
+// 48-63 (row 1 / row 3 receive lane 15 of the row below).
+__device__ __forceinline__ float group32_sum_hi(float v) {
+  v = group16_sum(v);
+  return v + dpp_f<0x142, 0xA>(0.f, v);
+}
+__device__ __forceinline__ float group32_max_hi(float v) {
+  v = group16_max(v);
+  return fmaxf(v, dpp_f<0x142, 0xA>(-INFINITY, v));
+}
+// Whole-wave reductions, result in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group32_sum_hi(v);
+  v = v + dpp_f<0x143, 0xC>(0.f, v);
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = group32_max_hi(v);
+  v = fmaxf(v, dpp_f<0x143, 0xC>(-INFINITY, v));
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // Inclusive prefix sum over a wave.

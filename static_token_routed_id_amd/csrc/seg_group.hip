@@ -447,9 +447,8 @@ __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         if (64 * w + 32 * j + r < n) v = fmaxf(v, acc[i][j][e]);
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-      if (r == 0) red[0][w][32 * i + 8 * (e >> 2) + h4 + (e & 3)] = v;
+      v = group32_max_hi(v);
+      if (r == 31) red[0][w][32 * i + 8 * (e >> 2) + h4 + (e & 3)] = v;
     }
   __syncthreads();
   uint16_t* P = reinterpret_cast<uint16_t*>(smem);
@@ -469,9 +468,8 @@ __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
         sm += pv;
         P[t * kHPS + row] = f2bf(pv);
       }
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
-      if (r == 0) red[1][w][t] = sm;
+      sm = group32_sum_hi(sm);
+      if (r == 31) red[1][w][t] = sm;
     }
   __syncthreads();
 
