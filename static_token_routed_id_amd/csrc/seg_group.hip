@@ -51,6 +51,20 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Maximum / sum of the eight per-wave partials of one token, stored
+// contiguously ([token][wave]) so two 16-byte LDS reads fetch them.
+__device__ __forceinline__ float max8(const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  return fmaxf(fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)),
+               fmaxf(fmaxf(b.x, b.y), fmaxf(b.z, b.w)));
+}
+__device__ __forceinline__ float sum8(const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  return ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+}
+
 __device__ __forceinline__ floatx4 mfma16(const u32x4& a, const u32x4& b,
                                           floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -62,7 +76,7 @@ template <int MB, int NBW, int NBV>
 __device__ __forceinline__ void group_item(
     const SegGroupArgs& a, int tok0, int mcount, int n, int64_t rowbase,
     uint16_t (*s_x)[kGT * kXS], uint16_t* s_p, uint16_t* s_v,
-    float (*red)[kGW][kGT]) {
+    float (*red)[kGT][kGW]) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int d = a.d;
@@ -174,7 +188,7 @@ __device__ __forceinline__ void group_item(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float m = group16_max(mx[mb][i]);
-      if (r == 0) red[0][w][mb * 16 + 4 * g + i] = m;
+      if (r == 0) red[0][mb * 16 + 4 * g + i][w] = m;
     }
   __syncthreads();
 #pragma unroll
@@ -182,9 +196,7 @@ __device__ __forceinline__ void group_item(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = mb * 16 + 4 * g + i;
-      float m = red[0][0][t];
-#pragma unroll
-      for (int v = 1; v < kGW; ++v) m = fmaxf(m, red[0][v][t]);
+      const float m = max8(&red[0][t][0]);
       mx[mb][i] = m;
     }
   float sm[MB][4];
@@ -212,7 +224,7 @@ __device__ __forceinline__ void group_item(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float s = group16_sum(sm[mb][i]);
-      if (r == 0) red[1][w][mb * 16 + 4 * g + i] = s;
+      if (r == 0) red[1][mb * 16 + 4 * g + i][w] = s;
     }
   __syncthreads();
 
@@ -296,9 +308,7 @@ __device__ __forceinline__ void group_item(
     for (int i = 0; i < 4; ++i) {
       const int t = mb * 16 + 4 * g + i;
       if (t < mcount) {
-        float l = 0.f;
-#pragma unroll
-        for (int v = 0; v < kGW; ++v) l += red[1][v][t];
+        const float l = sum8(&red[1][t][0]);
         const float inv = 1.0f / l;
         const int64_t orig = a.perm[tok0 + t];
 #pragma unroll
@@ -369,7 +379,7 @@ template <int MB32, int NBV>
 __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
                                          int mcount, int n, int64_t rowbase,
                                          uint8_t* smem,
-                                         float (*red)[kGW][kHT]) {
+                                         float (*red)[kHT][kGW]) {
   const int tid = opaque_int(threadIdx.x), lane = tid & 63, w = tid >> 6;
   const int d = a.d;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
@@ -448,7 +458,7 @@ __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
       for (int j = 0; j < 2; ++j)
         if (64 * w + 32 * j + r < n) v = fmaxf(v, acc[i][j][e]);
       v = group32_max_hi(v);
-      if (r == 31) red[0][w][32 * i + 8 * (e >> 2) + h4 + (e & 3)] = v;
+      if (r == 31) red[0][32 * i + 8 * (e >> 2) + h4 + (e & 3)][w] = v;
     }
   __syncthreads();
   uint16_t* P = reinterpret_cast<uint16_t*>(smem);
@@ -457,9 +467,7 @@ __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int t = 32 * i + 8 * (e >> 2) + h4 + (e & 3);
-      float mxv = red[0][0][t];
-#pragma unroll
-      for (int v = 1; v < kGW; ++v) mxv = fmaxf(mxv, red[0][v][t]);
+      const float mxv = max8(&red[0][t][0]);
       float sm = 0.f;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -469,7 +477,7 @@ __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
         P[t * kHPS + row] = f2bf(pv);
       }
       sm = group32_sum_hi(sm);
-      if (r == 31) red[1][w][t] = sm;
+      if (r == 31) red[1][t][w] = sm;
     }
   __syncthreads();
 
@@ -547,9 +555,7 @@ __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
     for (int i = 0; i < 4; ++i) {
       const int t = tb * 16 + 4 * g16 + i;
       if (t < mcount) {
-        float l = 0.f;
-#pragma unroll
-        for (int v = 0; v < kGW; ++v) l += red[1][v][t];
+        const float l = sum8(&red[1][t][0]);
         const float inv = 1.0f / l;
         const int64_t orig = a.perm[tok0 + t];
 #pragma unroll
@@ -568,13 +574,13 @@ __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
 template <int NBV>
 __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
   __shared__ __align__(16) uint8_t smem[kSmemBytes];
-  __shared__ float s_red[2][kGW][kHT];
+  __shared__ __align__(16) float s_red[2][kHT][kGW];
   if (a.header[0] != 0) return;
   // 64-token path: X slices, P and V staging carved from the same bytes
   uint16_t (*s_x)[kGT * kXS] = reinterpret_cast<uint16_t (*)[kGT * kXS]>(smem);
   uint16_t* s_p = reinterpret_cast<uint16_t*>(smem) + 2 * kGT * kXS;
   uint16_t* s_v = s_p + kGT * kPS;
-  float (*red64)[kGW][kGT] = reinterpret_cast<float (*)[kGW][kGT]>(&s_red[0][0][0]);
+  float (*red64)[kGT][kGW] = reinterpret_cast<float (*)[kGT][kGW]>(&s_red[0][0][0]);
   const int n_items = a.header[3];
   const int G = gridDim.x;
   const int vb = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
