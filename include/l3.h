@@ -138,6 +138,9 @@ l3_status l3_replan(l3_plan_t plan, const int32_t* ids, int64_t B,
  *   scratch device scratch workspace (scratch_bytes)
  * Errors: L3_ERR_NULL, L3_ERR_WORKSPACE, L3_ERR_HIP. Device-detected input
  * errors of the plan make this a no-op (see l3_plan).
+ * Forward and backward calls on one plan must not run concurrently (queue
+ * them on one stream or synchronise): the plan workspace also holds the
+ * forward kernels' work-queue counters, and the scratch workspace is shared.
  */
 l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
                      const void* V, const void* W_up, const void* gamma,

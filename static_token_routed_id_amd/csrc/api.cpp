@@ -530,6 +530,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       ga.seg_n = pd.seg_n;
       ga.seg_gitem_start = pd.seg_gitem_start;
       ga.gitem_map = pd.gitem_map;
+      ga.work = pd.header + 4;
       ga.x = static_cast<const uint16_t*>(x);
       ga.K = static_cast<const uint16_t*>(K);
       ga.V = static_cast<const uint16_t*>(V);

@@ -33,7 +33,8 @@ constexpr int kBadCount = 2;
 // Device arrays of one plan, carved out of the caller's plan workspace.
 struct PlanDev {
   int32_t* header;          // [0] status bits, [1] S, [2] wave items,
-                            // [3] group items
+                            // [3] group items, [4..5] group-kernel work
+                            // queue (zero between launches)
   int32_t* perm;            // [B] token index at sorted position
   int32_t* sorted_ids;      // [B]
   int32_t* seg_id;          // [B]
@@ -165,6 +166,7 @@ struct SegGroupArgs {
   const int32_t* seg_n;
   const int32_t* seg_gitem_start;
   const int2* gitem_map;
+  int* work;        // two ints, zero between launches: queue, finished WGs
   const uint16_t* x;
   const uint16_t* K;
   const uint16_t* V;

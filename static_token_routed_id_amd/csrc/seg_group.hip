@@ -586,9 +586,9 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
   const int vb = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
                               : blockIdx.x;
   uint16_t* my_v = s_v + (threadIdx.x >> 6) * (kVR * kVS);
-  // Two passes over this workgroup's items: first the 128-token items of
-  // ids with more than kGroupTok tokens, then the others (separate loops
-  // keep the two paths' registers apart).
+  // Two passes: first this workgroup's 128-token items of ids with more than
+  // kGroupTok tokens (a static share, XCD-major), then the others (separate
+  // loops keep the two paths' registers apart).
   for (int item = vb; item < n_items; item += G) {
     const int2 im = a.gitem_map[item];
     const int s = im.x, tile = im.y;
@@ -604,12 +604,26 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
     else
       hot_item<2, NBV>(a, tok0, mcount, n, rowbase, smem, s_red);
   }
-  for (int item = vb; item < n_items; item += G) {
+  // Second pass from a device-wide queue: each workgroup takes the next item
+  // when it finishes one (items are in id order, so the ids with most rows
+  // come first), which evens out the workgroups' finishing times. The next
+  // index is requested at the start of an item and read at its end, so the
+  // atomic's latency overlaps the work. The last workgroup out resets the
+  // counters for the next launch.
+  __shared__ int s_next;
+  int* work = a.work;
+  if (threadIdx.x == 0) s_next = atomicAdd(&work[0], 1);
+  __syncthreads();
+  int item = s_next;
+  while (item < n_items) {
+    __syncthreads();  // every wave has read s_next
+    int next = 0;
+    if (threadIdx.x == 0) next = atomicAdd(&work[0], 1);
     const int2 im = a.gitem_map[item];
     const int s = im.x;
     const int t_begin = a.seg_tok_start[s];
     const int m = a.seg_tok_start[s + 1] - t_begin;
-    if (m > kGT) continue;
+    if (m <= kGT) {
     const int n = a.seg_n[s];
     const int64_t rowbase = a.seg_row_off[s];
     const int tok0 = t_begin;
@@ -632,6 +646,17 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
     }
 #undef L3_ROWS
 #undef L3_ITEM
+    }
+    if (threadIdx.x == 0) s_next = next;
+    __syncthreads();
+    item = s_next;
+  }
+  if (threadIdx.x == 0) {
+    const int left = atomicAdd(&work[1], 1);
+    if (left == static_cast<int>(gridDim.x) - 1) {
+      atomicExch(&work[0], 0);
+      atomicExch(&work[1], 0);
+    }
   }
 }
 
