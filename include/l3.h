@@ -90,6 +90,8 @@ typedef struct l3_plan_s* l3_plan_t;
  *   plan_ws    -- written by l3_plan, read by l3_forward / l3_backward;
  *   save_ws    -- written by l3_forward when training, read by l3_backward;
  *   scratch_ws -- temporary; its content is never needed between calls.
+ * Every workspace must start on a 256-byte boundary (device allocations
+ * do); a misaligned one is rejected with L3_ERR_WORKSPACE.
  * Any output pointer may be NULL. Errors: L3_ERR_NULL, L3_ERR_SHAPE,
  * L3_ERR_DTYPE.
  */

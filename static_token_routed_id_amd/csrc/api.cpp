@@ -21,6 +21,9 @@ namespace {
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned(const void* p) {
+  return reinterpret_cast<uintptr_t>(p) % kAlign == 0;
+}
 
 // Bump allocator over a caller workspace (base == nullptr only measures).
 struct Carver {
@@ -356,7 +359,8 @@ l3_status l3_plan(const l3_desc* desc, const int32_t* ids, int64_t B,
     if (st != L3_OK) return st;
     if (B < 0 || B >= (int64_t(1) << 31)) return L3_ERR_SHAPE;
     if (!plan_ws) return L3_ERR_NULL;
-    if (plan_ws_bytes < plan_bytes(B)) return L3_ERR_WORKSPACE;
+    if (plan_ws_bytes < plan_bytes(B) || !aligned(plan_ws))
+      return L3_ERR_WORKSPACE;
     // capacity: the largest batch whose plan fits this workspace
     int64_t lo = B, hi = (int64_t(1) << 31) - 1;
     while (lo < hi) {
@@ -478,8 +482,10 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
         !scratch)
       return L3_ERR_NULL;
     const l3_desc& d = plan->desc;
-    if (scratch_bytes < fwd_bytes_for(d, B)) return L3_ERR_WORKSPACE;
-    if (save && save_bytes < save_bytes_for(d, B)) return L3_ERR_WORKSPACE;
+    if (scratch_bytes < fwd_bytes_for(d, B) || !aligned(scratch))
+      return L3_ERR_WORKSPACE;
+    if (save && (save_bytes < save_bytes_for(d, B) || !aligned(save)))
+      return L3_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     Carver cs(scratch);
     FwdBufs f = carve_fwd(cs, d, B);
@@ -690,8 +696,10 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
       return finish(plan, e, s);
     }
     if (plan->saved != save) return L3_ERR_STATE;
-    if (save_bytes < save_bytes_for(d, B)) return L3_ERR_WORKSPACE;
-    if (scratch_bytes < bwd_bytes_for(d, B)) return L3_ERR_WORKSPACE;
+    if (save_bytes < save_bytes_for(d, B) || !aligned(save))
+      return L3_ERR_WORKSPACE;
+    if (scratch_bytes < bwd_bytes_for(d, B) || !aligned(scratch))
+      return L3_ERR_WORKSPACE;
     Carver cv(const_cast<void*>(save));
     SaveBufs sv = carve_save(cv, d, B);
     Carver cs(scratch);

@@ -200,8 +200,20 @@ __device__ int scan_excl_1024(int32_t* a, int n, int* tmp) {
   for (int base = 0; base < n; base += 16 * 1024) {
     const int i0 = base + tid * 16;
     int v[16];
+    if (i0 + 16 <= n) {
+      // whole run of 16: four 16-byte loads (a is 256-byte aligned)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = i0 + j < n ? a[i0 + j] : 0;
+      for (int j = 0; j < 4; ++j) {
+        const int4 q = *reinterpret_cast<const int4*>(a + i0 + 4 * j);
+        v[4 * j] = q.x;
+        v[4 * j + 1] = q.y;
+        v[4 * j + 2] = q.z;
+        v[4 * j + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = i0 + j < n ? a[i0 + j] : 0;
+    }
     int sum = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -211,9 +223,17 @@ __device__ int scan_excl_1024(int32_t* a, int n, int* tmp) {
     }
     int total;
     const int off = block_excl_scan<1024>(sum, tmp, &total) + carry;
+    if (i0 + 16 <= n) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (i0 + j < n) a[i0 + j] = v[j] + off;
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<int4*>(a + i0 + 4 * j) =
+            make_int4(v[4 * j] + off, v[4 * j + 1] + off, v[4 * j + 2] + off,
+                      v[4 * j + 3] + off);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (i0 + j < n) a[i0 + j] = v[j] + off;
+    }
     carry += total;
   }
   return carry;

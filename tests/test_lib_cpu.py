@@ -88,10 +88,15 @@ def test_plan_host_checks(L):
                        ctypes.byref(out)) == L.L3_ERR_WORKSPACE
     assert lib.l3_plan(ctypes.byref(dsc), None, -3, None, buf, 64, None,
                        ctypes.byref(out)) == L.L3_ERR_SHAPE
+    # workspaces must start on a 256-byte boundary
+    raw = ctypes.create_string_buffer(p + 512)
+    base = (ctypes.addressof(raw) + 255) // 256 * 256
+    assert lib.l3_plan(ctypes.byref(dsc), None, 0, None,
+                       ctypes.c_void_p(base + 16), p, None,
+                       ctypes.byref(out)) == L.L3_ERR_WORKSPACE
     # an empty batch needs no device work: the handle is made, B = 0
-    big = ctypes.create_string_buffer(p)
-    assert lib.l3_plan(ctypes.byref(dsc), None, 0, None, big, p, None,
-                       ctypes.byref(out)) == L.L3_OK
+    assert lib.l3_plan(ctypes.byref(dsc), None, 0, None, ctypes.c_void_p(base),
+                       p, None, ctypes.byref(out)) == L.L3_OK
     assert lib.l3_plan_tokens(out) == 0
     # ids missing for a non-empty batch
     assert lib.l3_replan(out, None, 5, None, None) == L.L3_ERR_NULL
