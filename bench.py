@@ -8,10 +8,12 @@ d = 2048, d_e = 512, bf16 inputs, float32 accumulation and output).
 
 Prints one JSON line. `roofline` is the gather/aggregate step, two kernels
 (seg_fwd for ids with few rows, seg_group for ids with many rows in large
-batches): algorithmic bytes per launch (each distinct id's K_t and V_t rows
-once, x read, a written, ids and segment records) over the mean launch
-times taken from HIP events recorded around each kernel on its own stream
-during the timed steps; `traffic` is the HBM bytes per launch of the same two
+batches) that run concurrently on two streams: algorithmic bytes per launch
+(each distinct id's K_t and V_t rows once, x read, a written, ids and
+segment records) over the mean time from the fork to the join of the two
+streams, taken from HIP events on the caller's stream during the timed steps
+(each kernel's own mean duration, from events on its stream, is listed
+beside it); `traffic` is the HBM bytes per launch of the same two
 kernels from the committed FETCH_SIZE / WRITE_SIZE counter summary
 (profiles/traffic_gather_<workload>.md), or null when the kernels changed
 since it was taken. `cpu_baseline` is the fp64 oracle on a bounded sample of
@@ -209,7 +211,8 @@ def main():
     # with few rows, group kernel for ids with many rows
     t_wave = stage_avg.get("seg_fwd", 0.0) + stage_avg.get("seg_combine", 0.0)
     t_group = stage_avg.get("seg_group", 0.0)
-    gather_ms = t_wave + t_group
+    # the two kernels run on two streams; "gather" spans both (fork to join)
+    gather_ms = stage_avg.get("gather", t_wave + t_group)
     achieved = ab["total"] / (gather_ms * 1e-3) / 1e9
     gbs = lambda b, t: round(b / (t * 1e-3) / 1e9, 1) if t > 0 else None
     fl = gemm_flops(w)

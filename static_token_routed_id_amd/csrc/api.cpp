@@ -52,12 +52,13 @@ enum Stage {
   ST_BWD_UP,
   ST_BWD_SEG,
   ST_GROUP,
+  ST_GATHER,
   ST_COUNT
 };
 const char* const kStageNames[ST_COUNT] = {
     "plan",     "seg_fwd", "seg_combine",   "up_proj", "layernorm",
     "mix_proj", "bwd_mix", "bwd_layernorm", "bwd_up",  "bwd_seg",
-    "seg_group"};
+    "seg_group", "gather"};
 
 bool debug_sync() {
   static const bool on = [] {
@@ -128,6 +129,7 @@ PlanDev carve_plan(Carver& c, int64_t B) {
   p.blk = c.take<int32_t>(nblk + 1);
   p.item_map = c.take<int2>(static_cast<size_t>(wave_items_cap(B)));
   p.gitem_map = c.take<int2>(static_cast<size_t>(group_items_cap(B)));
+  p.hitem_map = c.take<int2>(static_cast<size_t>(group_items_cap(B)));
   return p;
 }
 
@@ -227,6 +229,10 @@ struct l3_plan_s {
   };
   std::vector<Ev> events;
   const void* saved = nullptr;  // save workspace of the last training forward
+  // second stream for the group kernel, forked from and joined back into the
+  // caller's stream (made on first use, on the device current then)
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
 };
 
 namespace {
@@ -255,6 +261,18 @@ struct StageTimer {
     }
   }
 };
+
+// The group kernel's stream and the fork / join events (default priority,
+// non-blocking with respect to the null stream).
+hipError_t side_stream(l3_plan_s* p) {
+  if (p->side) return hipSuccess;
+  hipError_t e = hipEventCreateWithFlags(&p->fork, hipEventDisableTiming);
+  if (e == hipSuccess)
+    e = hipEventCreateWithFlags(&p->join, hipEventDisableTiming);
+  if (e == hipSuccess)
+    e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
+  return e;
+}
 
 l3_status finish(l3_plan_s* p, hipError_t e, hipStream_t s) {
   if (e != hipSuccess) return L3_ERR_HIP;
@@ -404,6 +422,9 @@ void l3_plan_release(l3_plan_t plan) {
     hipEventDestroy(e.a);
     hipEventDestroy(e.b);
   }
+  if (plan->fork) hipEventDestroy(plan->fork);
+  if (plan->join) hipEventDestroy(plan->join);
+  if (plan->side) hipStreamDestroy(plan->side);
   delete plan;
 }
 
@@ -519,6 +540,20 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     const int64_t distinct = B < d.vocab ? B : d.vocab;
     const int64_t items_ub = ((B + kTokTile - 1) / kTokTile + distinct) *
                              static_cast<int64_t>(plan->nch_max);
+    // The wave kernel (caller's stream) and the group kernel (side stream)
+    // run concurrently: their tails overlap and the GPU mixes the wave
+    // kernel's latency-bound small items with the group kernel's streaming.
+    const bool fork = plan->group_min_rows > 0;
+    StageTimer* gather = new StageTimer(plan, ST_GATHER, s);
+    if (fork) {
+      e = side_stream(plan);
+      if (e == hipSuccess) e = hipEventRecord(plan->fork, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(plan->side, plan->fork, 0);
+      if (e != hipSuccess) {
+        delete gather;
+        return L3_ERR_HIP;
+      }
+    }
     {
       StageTimer t(plan, ST_SEG, s);
       e = seg_fwd_launch(sa, d.dtype, static_cast<int>(B),
@@ -526,8 +561,12 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
                                                                : (1 << 30)),
                          s);
     }
-    if (e != hipSuccess) return L3_ERR_HIP;
-    if (plan->group_min_rows > 0) {
+    if (e != hipSuccess) {
+      delete gather;
+      return L3_ERR_HIP;
+    }
+    if (fork) {
+      hipStream_t gs = plan->side;
       SegGroupArgs ga;
       ga.header = pd.header;
       ga.perm = pd.perm;
@@ -536,6 +575,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       ga.seg_n = pd.seg_n;
       ga.seg_gitem_start = pd.seg_gitem_start;
       ga.gitem_map = pd.gitem_map;
+      ga.hitem_map = pd.hitem_map;
       ga.work = pd.header + 4;
       ga.x = static_cast<const uint16_t*>(x);
       ga.K = static_cast<const uint16_t*>(K);
@@ -545,12 +585,21 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       ga.a_out = static_cast<uint16_t*>(f.a_act);
       ga.a_save = sv.a32;
       const int64_t gitems_ub = (B + kGroupTok - 1) / kGroupTok + distinct;
-      StageTimer t(plan, ST_GROUP, s);
-      e = seg_group_launch(
-          ga, static_cast<int>(gitems_ub < (1 << 30) ? gitems_ub : (1 << 30)),
-          s);
-      if (e != hipSuccess) return L3_ERR_HIP;
+      {
+        StageTimer t(plan, ST_GROUP, gs);
+        e = seg_group_launch(
+            ga,
+            static_cast<int>(gitems_ub < (1 << 30) ? gitems_ub : (1 << 30)),
+            gs);
+      }
+      if (e == hipSuccess) e = hipEventRecord(plan->join, gs);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, plan->join, 0);
+      if (e != hipSuccess) {
+        delete gather;
+        return L3_ERR_HIP;
+      }
     }
+    delete gather;
     // Row chunks exist only for ids with more rows than one wave item takes;
     // when all such ids go to the group kernel nothing needs merging.
     const bool split = plan->nch_max > 1 &&

@@ -33,8 +33,9 @@ constexpr int kBadCount = 2;
 // Device arrays of one plan, carved out of the caller's plan workspace.
 struct PlanDev {
   int32_t* header;          // [0] status bits, [1] S, [2] wave items,
-                            // [3] group items, [4..5] group-kernel work
-                            // queue (zero between launches)
+                            // [3] group items, [4], [5], [7] group-kernel
+                            // work queues (zero between launches),
+                            // [6] 128-token group items
   int32_t* perm;            // [B] token index at sorted position
   int32_t* sorted_ids;      // [B]
   int32_t* seg_id;          // [B]
@@ -49,6 +50,8 @@ struct PlanDev {
   int32_t* blk;             // [ceil(B / kSortTile) + 1]
   int2* item_map;           // wave item -> (segment, index within segment)
   int2* gitem_map;          // group item -> (segment, tile within segment)
+  int2* hitem_map;          // the 128-token group items only, any order;
+                            // their count in header[6]
 };
 // Capacity of the item maps for a batch of B tokens: a segment of m tokens
 // has at most ceil(m / 16) token tiles times ceil(512 / 32) row chunks.
@@ -166,7 +169,9 @@ struct SegGroupArgs {
   const int32_t* seg_n;
   const int32_t* seg_gitem_start;
   const int2* gitem_map;
-  int* work;        // two ints, zero between launches: queue, finished WGs
+  const int2* hitem_map;
+  int* work;        // header[4..7]: queue of the 64-token pass, finished
+                    // workgroups, count of 128-token items, their queue
   const uint16_t* x;
   const uint16_t* K;
   const uint16_t* V;

@@ -384,6 +384,12 @@ __global__ __launch_bounds__(256) void item_map_kernel(PlanDev pd) {
     for (int i = i0; i < i1; ++i) pd.item_map[i] = make_int2(g, i - i0);
     const int j0 = pd.seg_gitem_start[g], j1 = pd.seg_gitem_start[g + 1];
     for (int j = j0; j < j1; ++j) pd.gitem_map[j] = make_int2(g, j - j0);
+    // the 128-token items also go to a compact list of their own (its order
+    // depends on timing; the items' results do not)
+    if (j1 > j0 && pd.seg_tok_start[g + 1] - pd.seg_tok_start[g] > kGroupTok) {
+      const int h0 = atomicAdd(&pd.header[6], j1 - j0);
+      for (int j = j0; j < j1; ++j) pd.hitem_map[h0 + j - j0] = make_int2(g, j - j0);
+    }
   }
 }
 

@@ -64,6 +64,7 @@ template <int NB, int R>
 __device__ __forceinline__ void scores_bf16(const uint16_t* __restrict__ xr,
                                             const uint16_t* __restrict__ kt,
                                             int d, int nc, int r, int g,
+                                            int rot,
                                             floatx4 (&acc)[kNBMax]) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -76,9 +77,12 @@ __device__ __forceinline__ void scores_bf16(const uint16_t* __restrict__ xr,
   // ring of R register slots: step t's loads are issued R-1 steps ahead of
   // its multiply; the loop is unrolled by R so slot indices are static
   u32x4 xs[R], ks[R][NB];
+  // the item walks d from step rot (items reading the same column offset
+  // of their rows at once crowd a few memory channels)
 #define L3_LOAD(slot, t)                                              \
   {                                                                   \
-    const int c = min((t), nsteps - 1) * 32;                          \
+    const int t_ = min((t), nsteps - 1) + rot;                        \
+    const int c = (t_ < nsteps ? t_ : t_ - nsteps) * 32;              \
     xs[slot] = ld16(xp + c);                                          \
     _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) ks[slot][nb] =  \
         ld16(kt + koff[nb] + c);                                      \
@@ -177,15 +181,16 @@ __device__ __forceinline__ void softmax_rows(floatx4 (&acc)[kNBMax], int nc,
 template <int NB, bool BF16>
 __device__ __forceinline__ void scores_softmax(
     const typename Types<BF16>::T* xr, const typename Types<BF16>::T* kt,
-    int d, int nc, int r, int g, typename Types<BF16>::P* P, float* ml) {
+    int d, int nc, int r, int g, int rot, typename Types<BF16>::P* P,
+    float* ml) {
   floatx4 acc[kNBMax];
   if constexpr (BF16) {
     // deeper rings where few rows leave registers free
     constexpr int R = NB == 1 ? 8 : (NB == 2 ? 4 : 2);
     if (R > 2 && (d / 32) % R == 0)
-      scores_bf16<NB, R>(xr, kt, d, nc, r, g, acc);
+      scores_bf16<NB, R>(xr, kt, d, nc, r, g, rot, acc);
     else
-      scores_bf16<NB, 2>(xr, kt, d, nc, r, g, acc);
+      scores_bf16<NB, 2>(xr, kt, d, nc, r, g, rot, acc);
   } else
     scores_f32<NB>(xr, kt, d, nc, r, g, acc);
   softmax_rows<NB>(acc, nc, r, g, P, ml);
@@ -361,15 +366,16 @@ __global__ __launch_bounds__(256, 2) void seg_fwd_kernel(SegFwdArgs a) {
     const T* xr = X + xrow * a.d;
     const T* kt = K + rowbase * a.d;
     const int nbc = ceil_div(nc, 16);
+    const int rot = (s * 13 + local * 5) % (a.d / 32);
     __builtin_amdgcn_wave_barrier();
     if (nbc <= 1)
-      scores_softmax<1, BF16>(xr, kt, a.d, nc, r, g, P, ml);
+      scores_softmax<1, BF16>(xr, kt, a.d, nc, r, g, rot, P, ml);
     else if (nbc <= 2)
-      scores_softmax<2, BF16>(xr, kt, a.d, nc, r, g, P, ml);
+      scores_softmax<2, BF16>(xr, kt, a.d, nc, r, g, rot, P, ml);
     else if (nbc <= 4)
-      scores_softmax<4, BF16>(xr, kt, a.d, nc, r, g, P, ml);
+      scores_softmax<4, BF16>(xr, kt, a.d, nc, r, g, rot, P, ml);
     else
-      scores_softmax<8, BF16>(xr, kt, a.d, nc, r, g, P, ml);
+      scores_softmax<8, BF16>(xr, kt, a.d, nc, r, g, rot, P, ml);
     __builtin_amdgcn_wave_barrier();
 
     const T* vt = V + rowbase * a.d_e;

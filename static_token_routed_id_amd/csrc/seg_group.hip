@@ -27,8 +27,11 @@
 //            consecutive columns of rows 8G + s/4 hand every lane eight
 //            consecutive rows of one column -- the B operand layout.
 //   output   a = A / rowsum, bf16 (and float32 when saving), original order.
-// Items are walked in an XCD-major order so the tiles of one id run on
-// workgroups of one XCD and share its L2.
+// Workgroups take items from two device-wide queues (first the 128-token
+// items of the busiest ids, then the rest in id order), and every item walks
+// the key width from a column slice of its own so that concurrent items do
+// not all read the same column offset of their rows (which crowds a few
+// memory channels).
 
 #include "l3_device.h"
 #include "l3_internal.h"
@@ -75,6 +78,7 @@ __device__ __forceinline__ floatx4 mfma16(const u32x4& a, const u32x4& b,
 template <int MB, int NBW, int NBV>
 __device__ __forceinline__ void group_item(
     const SegGroupArgs& a, int tok0, int mcount, int n, int64_t rowbase,
+    int rot,
     uint16_t (*s_x)[kGT * kXS], uint16_t* s_p, uint16_t* s_v,
     float (*red)[kGT][kGW]) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -113,19 +117,27 @@ __device__ __forceinline__ void group_item(
 
   const int nsteps = d / 32;  // a multiple of 16 (seg_group_ok)
   u32x4 kr[R][NBW];
+  // Items walk d from a slice of their own (rot): when every item reads the
+  // same column offset of its rows at once, the accesses pile onto a few
+  // memory channels (a probe loses a fifth of the bandwidth that way).
+  auto rcol = [&](int sl) {
+    const int rs = sl + rot;
+    return (rs < nsl ? rs : rs - nsl) * kSW;
+  };
 #define L3_LOAD_K(slot, t)                                               \
   {                                                                      \
-    const int col = min((t), nsteps - 1) * 32;                           \
+    const int tt_ = min((t), nsteps - 1);                                \
+    const int col = rcol(tt_ >> 2) + (tt_ & 3) * 32;                     \
     _Pragma("unroll") for (int nb = 0; nb < NBW; ++nb) kr[slot][nb] =    \
         ld16(kt + koff[nb] + col);                                       \
   }
-  u32x4 x0 = ld16(xsrc), x1 = ld16(xsrc + 64);
+  u32x4 x0 = ld16(xsrc + rcol(0)), x1 = ld16(xsrc + rcol(0) + 64);
   *reinterpret_cast<u32x4*>(&s_x[0][xt * kXS + xc]) = x0;
   *reinterpret_cast<u32x4*>(&s_x[0][xt * kXS + xc + 64]) = x1;
 #pragma unroll
   for (int q = 0; q < R - 1; ++q) L3_LOAD_K(q, q)
   {
-    const int nx = min(1, nsl - 1) * kSW;
+    const int nx = rcol(min(1, nsl - 1));
     x0 = ld16(xsrc + nx);
     x1 = ld16(xsrc + nx + 64);
   }
@@ -154,7 +166,7 @@ __device__ __forceinline__ void group_item(
         // other buffer, the one after is fetched
         *reinterpret_cast<u32x4*>(&s_x[buf ^ 1][xt * kXS + xc]) = x0;
         *reinterpret_cast<u32x4*>(&s_x[buf ^ 1][xt * kXS + xc + 64]) = x1;
-        const int nx = min((t >> 2) + 2, nsl - 1) * kSW;
+        const int nx = rcol(min((t >> 2) + 2, nsl - 1));
         x0 = ld16(xsrc + nx);
         x1 = ld16(xsrc + nx + 64);
         __syncthreads();
@@ -379,7 +391,7 @@ template <int MB32, int NBV>
 __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
                                          int mcount, int n, int64_t rowbase,
                                          uint8_t* smem,
-                                         float (*red)[kHT][kGW]) {
+                                         float (*red)[kHT][kGW], int rot) {
   const int tid = opaque_int(threadIdx.x), lane = tid & 63, w = tid >> 6;
   const int d = a.d;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
@@ -414,7 +426,12 @@ __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
     for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
   const int nsl = d / kHS;
   const int r = lane & 31, kh = (lane >> 5) * 8;
-  load_slice(0);
+  // each item walks d from its own slice (rot), spreading channels
+  auto rslice = [&](int sl) {
+    const int rs = sl + rot;
+    return (rs < nsl ? rs : rs - nsl) * kHS;
+  };
+  load_slice(rslice(0));
   for (int sl = 0; sl < nsl; ++sl) {
     __syncthreads();
 #pragma unroll
@@ -424,7 +441,7 @@ __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
     for (int q = 0; q < 8; ++q)
       *reinterpret_cast<u32x4*>(&ks[(lr + 64 * q) * kHL + lc]) = sk[q];
     __syncthreads();
-    load_slice(min(sl + 1, nsl - 1) * kHS);
+    load_slice(rslice(min(sl + 1, nsl - 1)));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < kHS; kk += 16) {
@@ -582,36 +599,42 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
   uint16_t* s_v = s_p + kGT * kPS;
   float (*red64)[kGT][kGW] = reinterpret_cast<float (*)[kGT][kGW]>(&s_red[0][0][0]);
   const int n_items = a.header[3];
-  const int G = gridDim.x;
-  const int vb = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
-                              : blockIdx.x;
   uint16_t* my_v = s_v + (threadIdx.x >> 6) * (kVR * kVS);
-  // Two passes: first this workgroup's 128-token items of ids with more than
-  // kGroupTok tokens (a static share, XCD-major), then the others (separate
-  // loops keep the two paths' registers apart).
-  for (int item = vb; item < n_items; item += G) {
-    const int2 im = a.gitem_map[item];
+  // Two passes, each from a device-wide work queue: first the 128-token
+  // items of ids with more than kGroupTok tokens (compact list), then the
+  // 64-token items (separate loops keep the two paths' registers apart).
+  // A workgroup requests its next item when it starts one and reads the
+  // answer when it ends, so the atomic's latency overlaps the work; the last
+  // workgroup out resets the queues for the next launch.
+  __shared__ int s_next;
+  int* work = a.work;
+  const int n_hot = work[2];
+  if (threadIdx.x == 0) s_next = atomicAdd(&work[3], 1);
+  __syncthreads();
+  for (int hi = s_next; hi < n_hot;) {
+    __syncthreads();  // every wave has read s_next
+    int next = 0;
+    if (threadIdx.x == 0) next = atomicAdd(&work[3], 1);
+    const int2 im = a.hitem_map[hi];
     const int s = im.x, tile = im.y;
     const int t_begin = a.seg_tok_start[s];
     const int m = a.seg_tok_start[s + 1] - t_begin;
-    if (m <= kGT) continue;
     const int n = a.seg_n[s];
     const int64_t rowbase = a.seg_row_off[s];
     const int tok0 = t_begin + tile * kHT;
     const int mcount = min(kHT, m - tile * kHT);
+    const int rot = (s * 7 + tile * 3) % (a.d / kHS);
     if (mcount > 64)
-      hot_item<4, NBV>(a, tok0, mcount, n, rowbase, smem, s_red);
+      hot_item<4, NBV>(a, tok0, mcount, n, rowbase, smem, s_red, rot);
     else
-      hot_item<2, NBV>(a, tok0, mcount, n, rowbase, smem, s_red);
+      hot_item<2, NBV>(a, tok0, mcount, n, rowbase, smem, s_red, rot);
+    if (threadIdx.x == 0) s_next = next;
+    __syncthreads();
+    hi = s_next;
   }
-  // Second pass from a device-wide queue: each workgroup takes the next item
-  // when it finishes one (items are in id order, so the ids with most rows
-  // come first), which evens out the workgroups' finishing times. The next
-  // index is requested at the start of an item and read at its end, so the
-  // atomic's latency overlaps the work. The last workgroup out resets the
-  // counters for the next launch.
-  __shared__ int s_next;
-  int* work = a.work;
+  __syncthreads();
+  // 64-token items in id order (the ids with most rows first); the
+  // 128-token items met on the way are skipped
   if (threadIdx.x == 0) s_next = atomicAdd(&work[0], 1);
   __syncthreads();
   int item = s_next;
@@ -628,8 +651,10 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
     const int64_t rowbase = a.seg_row_off[s];
     const int tok0 = t_begin;
     const int mcount = m;
+    const int rot = (s * 7) % (a.d / kSW);
 #define L3_ITEM(MB, NBW) \
-  group_item<MB, NBW, NBV>(a, tok0, mcount, n, rowbase, s_x, s_p, my_v, red64)
+  group_item<MB, NBW, NBV>(a, tok0, mcount, n, rowbase, rot, s_x, s_p, my_v, \
+                           red64)
 #define L3_ROWS(MB)        \
   if (n <= 128)            \
     L3_ITEM(MB, 1);        \
@@ -656,6 +681,7 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
     if (left == static_cast<int>(gridDim.x) - 1) {
       atomicExch(&work[0], 0);
       atomicExch(&work[1], 0);
+      atomicExch(&work[3], 0);
     }
   }
 }
