@@ -117,9 +117,10 @@ __device__ __forceinline__ void group_item(
 
   const int nsteps = d / 32;  // a multiple of 16 (seg_group_ok)
   u32x4 kr[R][NBW];
-  // Items walk d from a slice of their own (rot): when every item reads the
-  // same column offset of its rows at once, the accesses pile onto a few
-  // memory channels (a probe loses a fifth of the bandwidth that way).
+  // Items walk d from a slice of their own (rot), and within a slice wave w
+  // starts at step w % 4: when every wave reads the same column offset of
+  // its rows at once, the accesses pile onto a few memory channels (a probe
+  // loses a fifth of the bandwidth that way).
   auto rcol = [&](int sl) {
     const int rs = sl + rot;
     return (rs < nsl ? rs : rs - nsl) * kSW;
@@ -127,7 +128,7 @@ __device__ __forceinline__ void group_item(
 #define L3_LOAD_K(slot, t)                                               \
   {                                                                      \
     const int tt_ = min((t), nsteps - 1);                                \
-    const int col = rcol(tt_ >> 2) + (tt_ & 3) * 32;                     \
+    const int col = rcol(tt_ >> 2) + ((tt_ + w) & 3) * 32;               \
     _Pragma("unroll") for (int nb = 0; nb < NBW; ++nb) kr[slot][nb] =    \
         ld16(kt + koff[nb] + col);                                       \
   }
@@ -155,7 +156,7 @@ __device__ __forceinline__ void group_item(
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
         xf[mb] = *reinterpret_cast<const u32x4*>(
-            &s_x[buf][(mb * 16 + r) * kXS + (q & 3) * 32 + g * 8]);
+            &s_x[buf][(mb * 16 + r) * kXS + ((q + w) & 3) * 32 + g * 8]);
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
