@@ -130,6 +130,8 @@ PlanDev carve_plan(Carver& c, int64_t B) {
   p.item_map = c.take<int2>(static_cast<size_t>(wave_items_cap(B)));
   p.gitem_map = c.take<int2>(static_cast<size_t>(group_items_cap(B)));
   p.hitem_map = c.take<int2>(static_cast<size_t>(group_items_cap(B)));
+  p.seg_aitem_start = c.take<int32_t>(nb + 1);
+  p.aitem_map = c.take<int2>(static_cast<size_t>(wave_items_cap(B)));
   return p;
 }
 
@@ -524,8 +526,13 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     sa.seg_tok_start = pd.seg_tok_start;
     sa.seg_row_off = pd.seg_row_off;
     sa.seg_n = pd.seg_n;
-    sa.seg_item_start = pd.seg_item_start;
-    sa.item_map = pd.item_map;
+    // Training runs every id through the wave kernel, whose weights then
+    // stay float32 (the group kernel multiplies bf16 weights on MFMA, too
+    // coarse for the saved aggregate the gradients are built from).
+    const bool all_wave = save != nullptr && plan->group_min_rows > 0;
+    sa.seg_item_start = all_wave ? pd.seg_aitem_start : pd.seg_item_start;
+    sa.item_map = all_wave ? pd.aitem_map : pd.item_map;
+    sa.count_slot = all_wave ? 8 : 2;
     sa.x = x;
     sa.K = K;
     sa.V = V;
@@ -543,7 +550,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     // The wave kernel (caller's stream) and the group kernel (side stream)
     // run concurrently: their tails overlap and the GPU mixes the wave
     // kernel's latency-bound small items with the group kernel's streaming.
-    const bool fork = plan->group_min_rows > 0;
+    const bool fork = plan->group_min_rows > 0 && !all_wave;
     StageTimer* gather = new StageTimer(plan, ST_GATHER, s);
     if (fork) {
       e = side_stream(plan);
@@ -602,12 +609,13 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     delete gather;
     // Row chunks exist only for ids with more rows than one wave item takes;
     // when all such ids go to the group kernel nothing needs merging.
-    const bool split = plan->nch_max > 1 &&
-                       !(plan->group_min_rows > 0 &&
-                         plan->group_min_rows <= plan->chunk_rows);
+    const bool split =
+        plan->nch_max > 1 &&
+        (all_wave || !(plan->group_min_rows > 0 &&
+                       plan->group_min_rows <= plan->chunk_rows));
     if (split) {
       CombineArgs ca;
-      ca.group_min_rows = plan->group_min_rows;
+      ca.group_min_rows = all_wave ? 0 : plan->group_min_rows;
       ca.header = pd.header;
       ca.perm = pd.perm;
       ca.seg_tok_start = pd.seg_tok_start;

@@ -35,7 +35,8 @@ struct PlanDev {
   int32_t* header;          // [0] status bits, [1] S, [2] wave items,
                             // [3] group items, [4], [5], [7] group-kernel
                             // work queues (zero between launches),
-                            // [6] 128-token group items
+                            // [6] 128-token group items, [8] wave items
+                            // of every segment
   int32_t* perm;            // [B] token index at sorted position
   int32_t* sorted_ids;      // [B]
   int32_t* seg_id;          // [B]
@@ -52,6 +53,11 @@ struct PlanDev {
   int2* gitem_map;          // group item -> (segment, tile within segment)
   int2* hitem_map;          // the 128-token group items only, any order;
                             // their count in header[6]
+  // Wave items of every segment (the training forward runs all ids through
+  // the wave kernel); count in header[8]. Only filled when the group kernel
+  // is enabled (else the wave items are already all of them).
+  int32_t* seg_aitem_start; // [B+1]
+  int2* aitem_map;
 };
 // Capacity of the item maps for a batch of B tokens: a segment of m tokens
 // has at most ceil(m / 16) token tiles times ceil(512 / 32) row chunks.
@@ -82,6 +88,7 @@ struct SegFwdArgs {
   const int32_t* seg_n;
   const int32_t* seg_item_start;
   const int2* item_map;
+  int count_slot;   // header slot holding the number of items
   const void* x;
   const void* K;
   const void* V;

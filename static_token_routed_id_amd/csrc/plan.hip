@@ -61,6 +61,10 @@ __device__ __forceinline__ bool is_group(int n, const PlanParams& p) {
 __device__ __forceinline__ int items_of(int m, int n, const PlanParams& p) {
   return is_group(n, p) ? 0 : ceil_div(m, kTokTile) * ceil_div(n, p.chunk_rows);
 }
+// wave items of a segment when every id goes to the wave kernel
+__device__ __forceinline__ int aitems_of(int m, int n, const PlanParams& p) {
+  return ceil_div(m, kTokTile) * ceil_div(n, p.chunk_rows);
+}
 __device__ __forceinline__ int gitems_of(int m, int n, const PlanParams& p) {
   if (!is_group(n, p)) return 0;
   return m > kGroupTok ? ceil_div(m, kHotTok) : 1;
@@ -141,27 +145,33 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
   // work items per segment (wave items and group items), exclusive scans
   const int sper = ceil_div(S, 1024);
   const int s0 = min(S, tid * sper), s1 = min(S, s0 + sper);
-  int icnt = 0, gcnt = 0;
+  int icnt = 0, gcnt = 0, acnt = 0;
   for (int g = s0; g < s1; ++g) {
     const int m = pd.seg_tok_start[g + 1] - pd.seg_tok_start[g];
     icnt += items_of(m, pd.seg_n[g], p);
     gcnt += gitems_of(m, pd.seg_n[g], p);
+    acnt += aitems_of(m, pd.seg_n[g], p);
   }
   int ibase = block_excl_scan<1024>(icnt, tmp, &total);
-  int gtotal;
+  int gtotal, atotal;
   int gbase = block_excl_scan<1024>(gcnt, tmp, &gtotal);
+  int abase = block_excl_scan<1024>(acnt, tmp, &atotal);
   for (int g = s0; g < s1; ++g) {
     const int m = pd.seg_tok_start[g + 1] - pd.seg_tok_start[g];
     pd.seg_item_start[g] = ibase;
     pd.seg_gitem_start[g] = gbase;
+    if (p.group_min_rows > 0) pd.seg_aitem_start[g] = abase;
     ibase += items_of(m, pd.seg_n[g], p);
     gbase += gitems_of(m, pd.seg_n[g], p);
+    abase += aitems_of(m, pd.seg_n[g], p);
   }
   if (tid == 0) {
     pd.seg_item_start[S] = total;
     pd.seg_gitem_start[S] = gtotal;
+    if (p.group_min_rows > 0) pd.seg_aitem_start[S] = atotal;
     pd.header[2] = total;
     pd.header[3] = gtotal;
+    pd.header[8] = atotal;
   }
   (void)s_total;
 }
@@ -355,42 +365,77 @@ __global__ __launch_bounds__(256) void seg_items_kernel(PlanDev pd,
     const int m = pd.seg_tok_start[g + 1] - pd.seg_tok_start[g];
     pd.seg_item_start[g] = items_of(m, pd.seg_n[g], p);
     pd.seg_gitem_start[g] = gitems_of(m, pd.seg_n[g], p);
+    if (p.group_min_rows > 0)
+      pd.seg_aitem_start[g] = aitems_of(m, pd.seg_n[g], p);
   }
 }
 
-// Scan both item counts in place (a[S] = total); S is read on the device.
-__global__ __launch_bounds__(1024) void seg_items_scan_kernel(PlanDev pd) {
+// Scan the item counts in place (a[S] = total); S is read on the device.
+__global__ __launch_bounds__(1024) void seg_items_scan_kernel(PlanDev pd,
+                                                              int with_all) {
   __shared__ int tmp[1024 / 64 + 1];
   const int n = pd.header[1];
   const int total = scan_excl_1024(pd.seg_item_start, n, tmp);
   const int gtotal = scan_excl_1024(pd.seg_gitem_start, n, tmp);
+  const int atotal = with_all ? scan_excl_1024(pd.seg_aitem_start, n, tmp) : total;
   if (threadIdx.x == 0) {
     pd.seg_item_start[n] = total;
     pd.seg_gitem_start[n] = gtotal;
+    if (with_all) pd.seg_aitem_start[n] = atotal;
     pd.header[2] = total;
     pd.header[3] = gtotal;
+    pd.header[8] = atotal;
   }
 }
 
 // Direct maps from a work item to its segment and its index there, so the
-// forward kernels need no search: one thread per segment writes the
-// segment's item range (at most a few thousand entries).
-__global__ __launch_bounds__(256) void item_map_kernel(PlanDev pd) {
+// forward kernels need no search: one thread per item finds its segment by
+// binary search over the segments' first items (parallel over items, so a
+// segment with thousands of items costs no more than one with one).
+__device__ __forceinline__ int seg_of(const int32_t* start, int S, int i) {
+  int lo = 0, hi = S - 1;  // last g with start[g] <= i
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (start[mid] <= i)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void item_map_kernel(PlanDev pd,
+                                                       int with_all) {
   if (pd.header[0] != 0) return;
   const int S = pd.header[1];
-  for (int g = blockIdx.x * 256 + threadIdx.x; g < S;
-       g += gridDim.x * 256) {
-    const int i0 = pd.seg_item_start[g], i1 = pd.seg_item_start[g + 1];
-    for (int i = i0; i < i1; ++i) pd.item_map[i] = make_int2(g, i - i0);
-    const int j0 = pd.seg_gitem_start[g], j1 = pd.seg_gitem_start[g + 1];
-    for (int j = j0; j < j1; ++j) pd.gitem_map[j] = make_int2(g, j - j0);
-    // the 128-token items also go to a compact list of their own (its order
-    // depends on timing; the items' results do not)
-    if (j1 > j0 && pd.seg_tok_start[g + 1] - pd.seg_tok_start[g] > kGroupTok) {
-      const int h0 = atomicAdd(&pd.header[6], j1 - j0);
-      for (int j = j0; j < j1; ++j) pd.hitem_map[h0 + j - j0] = make_int2(g, j - j0);
+  const int n_wave = pd.header[2], n_group = pd.header[3];
+  const int n_all = with_all ? pd.header[8] : 0;
+  const int n = max(n_wave, max(n_group, n_all));
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    if (i < n_wave) {
+      const int g = seg_of(pd.seg_item_start, S, i);
+      pd.item_map[i] = make_int2(g, i - pd.seg_item_start[g]);
+    }
+    if (i < n_group) {
+      const int g = seg_of(pd.seg_gitem_start, S, i);
+      const int j = i - pd.seg_gitem_start[g];
+      pd.gitem_map[i] = make_int2(g, j);
+      // the 128-token items also go to a compact list of their own (its
+      // order depends on timing; the items' results do not)
+      if (pd.seg_tok_start[g + 1] - pd.seg_tok_start[g] > kGroupTok)
+        pd.hitem_map[atomicAdd(&pd.header[6], 1)] = make_int2(g, j);
+    }
+    if (i < n_all) {
+      const int g = seg_of(pd.seg_aitem_start, S, i);
+      pd.aitem_map[i] = make_int2(g, i - pd.seg_aitem_start[g]);
     }
   }
+}
+
+static int item_map_grid(int B) {
+  const int64_t cap = wave_items_cap(B);
+  const int64_t g = (cap + 255) / 256;
+  return static_cast<int>(g < 2048 ? (g > 0 ? g : 1) : 2048);
 }
 
 static int digit_passes(int64_t vocab) {
@@ -404,7 +449,7 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
   const int B = p.B;
   if (B <= kSmallPlanMax) {
     plan_small_kernel<<<1, 1024, 0, s>>>(pd, p);
-    item_map_kernel<<<ceil_div(B, 256), 256, 0, s>>>(pd);
+    item_map_kernel<<<item_map_grid(B), 256, 0, s>>>(pd, p.group_min_rows > 0);
     return hipGetLastError();
   }
   const int nblk = ceil_div(B, kSortTile);
@@ -431,8 +476,8 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
   scan_single_kernel<<<1, 1024, 0, s>>>(pd.blk, nblk, pd.blk + nblk);
   seg_write_kernel<<<nblk, 256, 0, s>>>(pd, p, nblk);
   seg_items_kernel<<<ceil_div(B, 256), 256, 0, s>>>(pd, p);
-  seg_items_scan_kernel<<<1, 1024, 0, s>>>(pd);
-  item_map_kernel<<<ceil_div(B, 256), 256, 0, s>>>(pd);
+  seg_items_scan_kernel<<<1, 1024, 0, s>>>(pd, p.group_min_rows > 0);
+  item_map_kernel<<<item_map_grid(B), 256, 0, s>>>(pd, p.group_min_rows > 0);
   return hipGetLastError();
 }
 

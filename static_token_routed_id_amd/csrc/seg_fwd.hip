@@ -34,6 +34,8 @@
 //      several chunks: (max, sum, acc) partials, merged by seg_combine in a
 //      fixed chunk order (exact, deterministic).
 
+#include <type_traits>
+
 #include "l3_device.h"
 #include "l3_internal.h"
 
@@ -42,15 +44,18 @@ namespace l3 {
 constexpr int kNBMax = kWaveMaxRows / 16;  // 16-row blocks per item
 constexpr int kVHalf = 8;                  // V rows per half burst
 
-template <bool BF16>
+// Storage of the inputs (T) and of the unnormalised weights in LDS (P):
+// fp16 weights for bf16 inputs, float32 for float32 inputs and whenever the
+// float32 aggregate is saved for the backward pass (P32).
+template <bool BF16, bool P32 = false>
 struct Types;
-template <>
-struct Types<true> {
+template <bool P32>
+struct Types<true, P32> {
   typedef uint16_t T;
-  typedef _Float16 P;
+  typedef typename std::conditional<P32, float, _Float16>::type P;
 };
-template <>
-struct Types<false> {
+template <bool P32>
+struct Types<false, P32> {
   typedef float T;
   typedef float P;
 };
@@ -178,11 +183,10 @@ __device__ __forceinline__ void softmax_rows(floatx4 (&acc)[kNBMax], int nc,
   }
 }
 
-template <int NB, bool BF16>
+template <int NB, bool BF16, typename PT>
 __device__ __forceinline__ void scores_softmax(
     const typename Types<BF16>::T* xr, const typename Types<BF16>::T* kt,
-    int d, int nc, int r, int g, int rot, typename Types<BF16>::P* P,
-    float* ml) {
+    int d, int nc, int r, int g, int rot, PT* P, float* ml) {
   floatx4 acc[kNBMax];
   if constexpr (BF16) {
     // deeper rings where few rows leave registers free
@@ -256,13 +260,12 @@ __device__ __forceinline__ void store_row(float* dst, const float (&v)[EPL]) {
   for (int e = 0; e < EPL; ++e) dst[e] = v[e];
 }
 
-template <int MTOK, int EPL, bool BF16>
+template <int MTOK, int EPL, bool BF16, typename PT>
 __device__ __forceinline__ void aggregate_and_store(
     const SegFwdArgs& a, const typename Types<BF16>::T* vt, int nc,
-    const typename Types<BF16>::P* P, const float* ml, int tok0, int mcount,
+    const PT* P, const float* ml, int tok0, int mcount,
     int nch, int chunk, int lane) {
   typedef typename Types<BF16>::T T;
-  typedef typename Types<BF16>::P PT;
   const int passes = a.d_e / (64 * EPL);
   for (int ps = 0; ps < passes; ++ps) {
     const int e0 = ps * 64 * EPL + lane * EPL;
@@ -332,16 +335,16 @@ __device__ __forceinline__ void aggregate_and_store(
   }
 }
 
-template <bool BF16, int EPL>
+template <bool BF16, int EPL, bool P32>
 __global__ __launch_bounds__(256, 2) void seg_fwd_kernel(SegFwdArgs a) {
   typedef typename Types<BF16>::T T;
-  typedef typename Types<BF16>::P PT;
+  typedef typename Types<BF16, P32>::P PT;
   __shared__ PT s_p[4][kNBMax * 16 * kTokTile];
   __shared__ float s_ml[4][2 * kTokTile];
   if (a.header[0] != 0) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int n_items = a.header[2];
+  const int n_items = a.header[a.count_slot];
   PT* P = s_p[w];
   float* ml = s_ml[w];
   const T* X = static_cast<const T*>(a.x);
@@ -369,19 +372,19 @@ __global__ __launch_bounds__(256, 2) void seg_fwd_kernel(SegFwdArgs a) {
     const int rot = (s * 13 + local * 5) % (a.d / 32);
     __builtin_amdgcn_wave_barrier();
     if (nbc <= 1)
-      scores_softmax<1, BF16>(xr, kt, a.d, nc, r, g, rot, P, ml);
+      scores_softmax<1, BF16, PT>(xr, kt, a.d, nc, r, g, rot, P, ml);
     else if (nbc <= 2)
-      scores_softmax<2, BF16>(xr, kt, a.d, nc, r, g, rot, P, ml);
+      scores_softmax<2, BF16, PT>(xr, kt, a.d, nc, r, g, rot, P, ml);
     else if (nbc <= 4)
-      scores_softmax<4, BF16>(xr, kt, a.d, nc, r, g, rot, P, ml);
+      scores_softmax<4, BF16, PT>(xr, kt, a.d, nc, r, g, rot, P, ml);
     else
-      scores_softmax<8, BF16>(xr, kt, a.d, nc, r, g, rot, P, ml);
+      scores_softmax<8, BF16, PT>(xr, kt, a.d, nc, r, g, rot, P, ml);
     __builtin_amdgcn_wave_barrier();
 
     const T* vt = V + rowbase * a.d_e;
 #define L3_AGG(N)                                                           \
-  aggregate_and_store<N, EPL, BF16>(a, vt, nc, P, ml, tok0, mcount, nch,    \
-                                    chunk, lane)
+  aggregate_and_store<N, EPL, BF16, PT>(a, vt, nc, P, ml, tok0, mcount,     \
+                                        nch, chunk, lane)
     if (mcount <= 1)
       L3_AGG(1);
     else if (mcount <= 2)
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(CombineArgs a) {
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool P32>
 static hipError_t seg_fwd_dispatch(const SegFwdArgs& a, int grid,
                                    hipStream_t s) {
   // EPL: value columns per lane per pass (at most 4, the rest in passes)
@@ -446,13 +449,13 @@ static hipError_t seg_fwd_dispatch(const SegFwdArgs& a, int grid,
   const int epl = q % 4 == 0 ? 4 : q % 2 == 0 ? 2 : 1;
   switch (epl) {
     case 4:
-      seg_fwd_kernel<BF16, 4><<<grid, 256, 0, s>>>(a);
+      seg_fwd_kernel<BF16, 4, P32><<<grid, 256, 0, s>>>(a);
       break;
     case 2:
-      seg_fwd_kernel<BF16, 2><<<grid, 256, 0, s>>>(a);
+      seg_fwd_kernel<BF16, 2, P32><<<grid, 256, 0, s>>>(a);
       break;
     default:
-      seg_fwd_kernel<BF16, 1><<<grid, 256, 0, s>>>(a);
+      seg_fwd_kernel<BF16, 1, P32><<<grid, 256, 0, s>>>(a);
       break;
   }
   return hipGetLastError();
@@ -464,8 +467,10 @@ hipError_t seg_fwd_launch(const SegFwdArgs& a, int dtype, int B, int items_ub,
   int grid = ceil_div(items_ub, 4);
   if (grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;
-  return dtype == kBF16 ? seg_fwd_dispatch<true>(a, grid, s)
-                        : seg_fwd_dispatch<false>(a, grid, s);
+  if (dtype != kBF16) return seg_fwd_dispatch<false, true>(a, grid, s);
+  // float32 weights when the aggregate is saved for the backward pass
+  return a.a_save ? seg_fwd_dispatch<true, true>(a, grid, s)
+                  : seg_fwd_dispatch<true, false>(a, grid, s);
 }
 
 hipError_t seg_combine_launch(const CombineArgs& a, int dtype,

@@ -72,3 +72,24 @@ def test_backward_without_save_is_an_error():
     with pytest.raises(L.L3Error) as e:
         layer.backward(dev.dy, *dev.params())
     assert e.value.status == L.L3_ERR_STATE
+
+
+@pytest.mark.timeout(900)
+def test_prefill_shapes_bf16_backward():
+    """The training step at prefill shapes (d = 1024, d_e = 256, a table of
+    171,462 rows, ids with up to 512 rows): the first 1024 tokens of the
+    prefill id stream with a drawn upstream gradient."""
+    import dataclasses
+    from static_token_routed_id_amd import workloads as wl
+    base = gu.workload("prefill_bf16")
+    w = wl.with_ids(base, base.ids[:1024])
+    g = np.random.default_rng(5).standard_normal((1024, base.spec.d))
+    w = dataclasses.replace(w, dy=wl.store(g, "bf16"))
+    res = gu.run(w, training=True)
+    ref = gu.oracle_backward(w)
+    for k in NAMES:
+        got = gu.f64(res["grads"][k])
+        e = gu.max_abs(got, ref[k])
+        print(f"prefill shapes {k}: max abs {e:.3e} (max |ref| "
+              f"{np.abs(ref[k]).max():.2f})")
+        assert e <= 2e-2, k
