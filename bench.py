@@ -6,15 +6,14 @@ batch, all resident in HBM before timing starts. Default workload: the
 large-prefill configuration (65536 tokens, vocab 131072, 2^22-row budget,
 d = 2048, d_e = 512, bf16 inputs, float32 accumulation and output).
 
-Prints one JSON line. `roofline` is the gather/aggregate step, two kernels
-(seg_fwd for ids with few rows, seg_group for ids with many rows in large
-batches) that run concurrently on two streams: algorithmic bytes per launch
-(each distinct id's K_t and V_t rows once, x read, a written, ids and
-segment records) over the mean time from the fork to the join of the two
-streams, taken from HIP events on the caller's stream during the timed steps
-(each kernel's own mean duration, from events on its stream, is listed
-beside it); `traffic` is the HBM bytes per launch of the same two
-kernels from the committed FETCH_SIZE / WRITE_SIZE counter summary
+Prints one JSON line. `roofline` is the gather/aggregate step: on large
+bf16 batches one launch of seg_group_kernel (it also runs the wave items of
+the ids with few rows), else seg_fwd_kernel (+ seg_combine for split rows):
+algorithmic bytes per launch (each distinct id's K_t and V_t rows once, x
+read, a written, ids and segment records) over the mean launch time, taken
+from HIP events recorded on the launch stream around the step during the
+timed steps; `traffic` is the HBM bytes per launch from the committed
+FETCH_SIZE / WRITE_SIZE counter summary
 (profiles/traffic_gather_<workload>.md), or null when the kernels changed
 since it was taken. `cpu_baseline` is the fp64 oracle on a bounded sample of
 the same batch on the host CPU.
@@ -58,6 +57,7 @@ def algorithmic_bytes(w, plan, group_min_rows: int) -> dict:
 # gather kernels (kernel code, shared device helpers, launch configuration).
 TRAFFIC_SOURCES = ("static_token_routed_id_amd/csrc/seg_fwd.hip",
                    "static_token_routed_id_amd/csrc/seg_group.hip",
+                   "static_token_routed_id_amd/csrc/seg_wave.h",
                    "static_token_routed_id_amd/csrc/l3_device.h",
                    "static_token_routed_id_amd/csrc/l3_internal.h",
                    "static_token_routed_id_amd/csrc/api.cpp")
@@ -207,11 +207,11 @@ def main():
     ab = algorithmic_bytes(w, plan_np, info["group_min_rows"])
     stage_avg = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in stages.items()
                  if v[1]}
-    # the gather/aggregate step: wave kernel (+ row-chunk combine) for ids
-    # with few rows, group kernel for ids with many rows
+    # the gather/aggregate step: one group-kernel launch on large bf16
+    # batches (it takes the wave items too), else the wave kernel (+ the
+    # row-chunk combine); "gather" spans whichever ran
     t_wave = stage_avg.get("seg_fwd", 0.0) + stage_avg.get("seg_combine", 0.0)
     t_group = stage_avg.get("seg_group", 0.0)
-    # the two kernels run on two streams; "gather" spans both (fork to join)
     gather_ms = stage_avg.get("gather", t_wave + t_group)
     achieved = ab["total"] / (gather_ms * 1e-3) / 1e9
     gbs = lambda b, t: round(b / (t * 1e-3) / 1e9, 1) if t > 0 else None
@@ -241,7 +241,8 @@ def main():
                    "vocab": w.spec.vocab, "table_rows": w.rows,
                    "d": w.spec.d, "d_e": w.spec.d_e, "k_max": w.spec.k_max,
                    "distinct_ids": int(plan_np["S"])},
-        "roofline": {"kernel": "gather (seg_fwd + seg_group)",
+        "roofline": {"kernel": "gather (seg_group_kernel)" if t_group > 0
+                               else "gather (seg_fwd_kernel)",
                      "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -249,13 +250,8 @@ def main():
                                 else None,
                      "algorithmic_bytes_per_launch": ab["total"],
                      "avg_launch_ms": round(gather_ms, 4),
-                     "per_kernel": {
-                         "seg_fwd": {"bytes": ab["wave"],
-                                     "ms": round(t_wave, 4),
-                                     "GB/s": gbs(ab["wave"], t_wave)},
-                         "seg_group": {"bytes": ab["group"],
-                                       "ms": round(t_group, 4),
-                                       "GB/s": gbs(ab["group"], t_group)}}},
+                     "bytes_by_item_kind": {"wave_items": ab["wave"],
+                                            "group_items": ab["group"]}},
         "plan_info": info,
         "stage_ms": {k: round(v, 4) for k, v in stage_avg.items()},
         "mfma": mfma,

@@ -231,10 +231,6 @@ struct l3_plan_s {
   };
   std::vector<Ev> events;
   const void* saved = nullptr;  // save workspace of the last training forward
-  // second stream for the group kernel, forked from and joined back into the
-  // caller's stream (made on first use, on the device current then)
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
 };
 
 namespace {
@@ -263,18 +259,6 @@ struct StageTimer {
     }
   }
 };
-
-// The group kernel's stream and the fork / join events (default priority,
-// non-blocking with respect to the null stream).
-hipError_t side_stream(l3_plan_s* p) {
-  if (p->side) return hipSuccess;
-  hipError_t e = hipEventCreateWithFlags(&p->fork, hipEventDisableTiming);
-  if (e == hipSuccess)
-    e = hipEventCreateWithFlags(&p->join, hipEventDisableTiming);
-  if (e == hipSuccess)
-    e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
-  return e;
-}
 
 l3_status finish(l3_plan_s* p, hipError_t e, hipStream_t s) {
   if (e != hipSuccess) return L3_ERR_HIP;
@@ -424,9 +408,6 @@ void l3_plan_release(l3_plan_t plan) {
     hipEventDestroy(e.a);
     hipEventDestroy(e.b);
   }
-  if (plan->fork) hipEventDestroy(plan->fork);
-  if (plan->join) hipEventDestroy(plan->join);
-  if (plan->side) hipStreamDestroy(plan->side);
   delete plan;
 }
 
@@ -547,33 +528,19 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     const int64_t distinct = B < d.vocab ? B : d.vocab;
     const int64_t items_ub = ((B + kTokTile - 1) / kTokTile + distinct) *
                              static_cast<int64_t>(plan->nch_max);
-    // The wave kernel (caller's stream) and the group kernel (side stream)
-    // run concurrently: their tails overlap and the GPU mixes the wave
-    // kernel's latency-bound small items with the group kernel's streaming.
-    const bool fork = plan->group_min_rows > 0 && !all_wave;
+    // With the group kernel enabled (inference), one launch of it runs every
+    // item: its workgroups take the busy ids' items, then the 64-token
+    // items, then the wave items one per wavefront, all from device-wide
+    // queues, so no workgroup idles while another still has work.
+    const bool merged = plan->group_min_rows > 0 && !all_wave;
     StageTimer* gather = new StageTimer(plan, ST_GATHER, s);
-    if (fork) {
-      e = side_stream(plan);
-      if (e == hipSuccess) e = hipEventRecord(plan->fork, s);
-      if (e == hipSuccess) e = hipStreamWaitEvent(plan->side, plan->fork, 0);
-      if (e != hipSuccess) {
-        delete gather;
-        return L3_ERR_HIP;
-      }
-    }
-    {
+    if (!merged) {
       StageTimer t(plan, ST_SEG, s);
       e = seg_fwd_launch(sa, d.dtype, static_cast<int>(B),
                          static_cast<int>(items_ub < (1 << 30) ? items_ub
                                                                : (1 << 30)),
                          s);
-    }
-    if (e != hipSuccess) {
-      delete gather;
-      return L3_ERR_HIP;
-    }
-    if (fork) {
-      hipStream_t gs = plan->side;
+    } else {
       SegGroupArgs ga;
       ga.header = pd.header;
       ga.perm = pd.perm;
@@ -591,20 +558,17 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       ga.d_e = d.d_e;
       ga.a_out = static_cast<uint16_t*>(f.a_act);
       ga.a_save = sv.a32;
-      const int64_t gitems_ub = (B + kGroupTok - 1) / kGroupTok + distinct;
-      {
-        StageTimer t(plan, ST_GROUP, gs);
-        e = seg_group_launch(
-            ga,
-            static_cast<int>(gitems_ub < (1 << 30) ? gitems_ub : (1 << 30)),
-            gs);
-      }
-      if (e == hipSuccess) e = hipEventRecord(plan->join, gs);
-      if (e == hipSuccess) e = hipStreamWaitEvent(s, plan->join, 0);
-      if (e != hipSuccess) {
-        delete gather;
-        return L3_ERR_HIP;
-      }
+      ga.wave = sa;
+      const int64_t gitems_ub =
+          (B + kGroupTok - 1) / kGroupTok + distinct + items_ub;
+      StageTimer t(plan, ST_GROUP, s);
+      e = seg_group_launch(
+          ga, static_cast<int>(gitems_ub < (1 << 30) ? gitems_ub : (1 << 30)),
+          s);
+    }
+    if (e != hipSuccess) {
+      delete gather;
+      return L3_ERR_HIP;
     }
     delete gather;
     // Row chunks exist only for ids with more rows than one wave item takes;

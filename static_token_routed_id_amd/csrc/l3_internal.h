@@ -33,7 +33,7 @@ constexpr int kBadCount = 2;
 // Device arrays of one plan, carved out of the caller's plan workspace.
 struct PlanDev {
   int32_t* header;          // [0] status bits, [1] S, [2] wave items,
-                            // [3] group items, [4], [5], [7] group-kernel
+                            // [3] group items, [4], [5], [7], [9] group-kernel
                             // work queues (zero between launches),
                             // [6] 128-token group items, [8] wave items
                             // of every segment
@@ -177,14 +177,17 @@ struct SegGroupArgs {
   const int32_t* seg_gitem_start;
   const int2* gitem_map;
   const int2* hitem_map;
-  int* work;        // header[4..7]: queue of the 64-token pass, finished
-                    // workgroups, count of 128-token items, their queue
+  int* work;        // header[4..9]: queue of the 64-token pass, finished
+                    // workgroups, count of 128-token items, their queue,
+                    // (wave-item count), queue of the wave-item pass
   const uint16_t* x;
   const uint16_t* K;
   const uint16_t* V;
   int d, d_e;
   uint16_t* a_out;  // [B x d_e] bf16, original token order
   float* a_save;    // [B x d_e] float32 or NULL
+  // wave items taken in a last pass (header NULL: none); bf16 inference
+  SegFwdArgs wave;
 };
 bool seg_group_ok(int d, int d_e);
 hipError_t seg_group_launch(const SegGroupArgs& a, int items_ub,

@@ -27,17 +27,26 @@
 //            consecutive columns of rows 8G + s/4 hand every lane eight
 //            consecutive rows of one column -- the B operand layout.
 //   output   a = A / rowsum, bf16 (and float32 when saving), original order.
-// Workgroups take items from two device-wide queues (first the 128-token
-// items of the busiest ids, then the rest in id order), and every item walks
-// the key width from a column slice of its own so that concurrent items do
-// not all read the same column offset of their rows (which crowds a few
-// memory channels).
+// One launch of this kernel runs the whole segment forward of the batch:
+// workgroups take items from three device-wide queues (the 128-token items
+// of the busiest ids; the 64-token items in id order; the wave items of the
+// ids with fewer rows, one per wavefront, run by the same code as the wave
+// kernel), half of the workgroups starting with the wave items and half with
+// the others, every workgroup then visiting the remaining queues. Every item
+// walks the key width from a column slice of its own so that concurrent
+// items do not all read the same column offset of their rows (which crowds
+// a few memory channels).
 
 #include "l3_device.h"
 #include "l3_internal.h"
+#include "seg_wave.h"
 
 namespace l3 {
 
+#ifndef L3_WAVE_FIRST_EVERY
+#define L3_WAVE_FIRST_EVERY 2
+#endif
+constexpr int kWaveFirstEvery = L3_WAVE_FIRST_EVERY;
 constexpr int kGW = 8;                 // waves per workgroup
 constexpr int kGT = kGroupTok;         // tokens per item
 constexpr int kGRows = L3_MAX_ROWS_PER_ID;
@@ -368,6 +377,9 @@ constexpr size_t kHotValueBytes =
 constexpr size_t kGroupBytes = (size_t)2 * kGT * kXS * 2 +
                                (size_t)kGT * kPS * 2 +
                                (size_t)kGW * kVR * kVS * 2;
+static_assert(kGW * kNBMax * 16 * kTokTile * 2 + kGW * 2 * kTokTile * 4 <=
+                  kGT * kXS * 2 * 2,
+              "wave item buffers fit in the shared bytes");
 constexpr size_t kSmemBytes =
     kHotValueBytes > kGroupBytes ? kHotValueBytes : kGroupBytes;
 static_assert(kHotScoreBytes <= kSmemBytes, "scores staging must fit");
@@ -589,6 +601,27 @@ __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
 }
 
 
+// The wave items (ids with fewer rows), one per wavefront from their own
+// queue, biggest first, on a workgroup's eight waves (each wave takes its
+// next item as soon as its current one is done).
+template <int NBV>
+__device__ __forceinline__ void wave_pass(const SegGroupArgs& a,
+                                          uint8_t* smem, int* work) {
+  typedef Types<true, false>::P PT;
+  constexpr int kEPL = NBV == 1 ? 2 : 4;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  PT* P = reinterpret_cast<PT*>(smem) + wv * (kNBMax * 16 * kTokTile);
+  float* ml = reinterpret_cast<float*>(
+                  smem + kGW * kNBMax * 16 * kTokTile * sizeof(PT)) +
+              wv * 2 * kTokTile;
+  const int n_wave = a.wave.header[a.wave.count_slot];
+  int wi = 0;
+  if (lane == 0) wi = atomicAdd(&work[5], 1);
+  wi = __shfl(wi, 0);
+  while (wi < n_wave)
+    wi = wave_item<true, kEPL, false>(a.wave, wi, lane, P, ml, &work[5]);
+}
+
 template <int NBV>
 __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
   __shared__ __align__(16) uint8_t smem[kSmemBytes];
@@ -610,6 +643,16 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
   __shared__ int s_next;
   int* work = a.work;
   const int n_hot = work[2];
+  // Half of the workgroups (alternate groups of eight: every XCD gets its
+  // share) start with the wave items, the rest with the busy ids' and the
+  // 64-token items; every workgroup then visits the other queues. The wave
+  // items' latency-bound tail (ids with a few rows) so runs beside the
+  // streaming 64-token items instead of after them.
+  const bool wave_first = a.wave.header && ((blockIdx.x >> 3) % kWaveFirstEvery) == 0;
+  if (wave_first) {
+    wave_pass<NBV>(a, smem, work);
+    __syncthreads();
+  }
   if (threadIdx.x == 0) s_next = atomicAdd(&work[3], 1);
   __syncthreads();
   for (int hi = s_next; hi < n_hot;) {
@@ -677,12 +720,18 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
     __syncthreads();
     item = s_next;
   }
+  __syncthreads();
+  if (a.wave.header && !wave_first) {
+    wave_pass<NBV>(a, smem, work);
+    __syncthreads();
+  }
   if (threadIdx.x == 0) {
     const int left = atomicAdd(&work[1], 1);
     if (left == static_cast<int>(gridDim.x) - 1) {
       atomicExch(&work[0], 0);
       atomicExch(&work[1], 0);
       atomicExch(&work[3], 0);
+      atomicExch(&work[5], 0);
     }
   }
 }
