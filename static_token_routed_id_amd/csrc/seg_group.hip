@@ -89,7 +89,7 @@ __device__ __forceinline__ void group_item(
     const SegGroupArgs& a, int tok0, int mcount, int n, int64_t rowbase,
     int rot,
     uint16_t (*s_x)[kGT * kXS], uint16_t* s_p, uint16_t* s_v,
-    float (*red)[kGT][kGW]) {
+    float (*red)[kGT][kGW], int* queue, int& next) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int d = a.d;
@@ -185,6 +185,10 @@ __device__ __forceinline__ void group_item(
     }
   }
 #undef L3_LOAD_K
+
+  // the workgroup's next item is requested here: the atomic's latency hides
+  // behind the rest of this item, and no item waits behind a whole one
+  if (tid == 0) next = atomicAdd(queue, 1);
 
   // ----------------------------------------------------------- softmax ---
   // lane holds S[token mb*16 + 4g + i][row wrow0 + nb*16 + r]
@@ -634,12 +638,13 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
   float (*red64)[kGT][kGW] = reinterpret_cast<float (*)[kGT][kGW]>(&s_red[0][0][0]);
   const int n_items = a.header[3];
   uint16_t* my_v = s_v + (threadIdx.x >> 6) * (kVR * kVS);
-  // Two passes, each from a device-wide work queue: first the 128-token
-  // items of ids with more than kGroupTok tokens (compact list), then the
-  // 64-token items (separate loops keep the two paths' registers apart).
-  // A workgroup requests its next item when it starts one and reads the
-  // answer when it ends, so the atomic's latency overlaps the work; the last
-  // workgroup out resets the queues for the next launch.
+  // Passes over device-wide work queues: the 128-token items of ids with
+  // more than kGroupTok tokens (compact list), the 64-token items, the wave
+  // items (separate loops keep the paths' registers apart). A workgroup
+  // requests its next 128-token item when it starts one, its next 64-token
+  // or wave item once the current item's scores are done, and reads the
+  // answer when the item ends, so the atomic's latency overlaps the work;
+  // the last workgroup out resets the queues for the next launch.
   __shared__ int s_next;
   int* work = a.work;
   const int n_hot = work[2];
@@ -685,7 +690,6 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
   while (item < n_items) {
     __syncthreads();  // every wave has read s_next
     int next = 0;
-    if (threadIdx.x == 0) next = atomicAdd(&work[0], 1);
     const int2 im = a.gitem_map[item];
     const int s = im.x;
     const int t_begin = a.seg_tok_start[s];
@@ -698,7 +702,7 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
     const int rot = (s * 7) % (a.d / kSW);
 #define L3_ITEM(MB, NBW) \
   group_item<MB, NBW, NBV>(a, tok0, mcount, n, rowbase, rot, s_x, s_p, my_v, \
-                           red64)
+                           red64, &work[0], next)
 #define L3_ROWS(MB)        \
   if (n <= 128)            \
     L3_ITEM(MB, 1);        \
@@ -715,6 +719,8 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
     }
 #undef L3_ROWS
 #undef L3_ITEM
+    } else if (threadIdx.x == 0) {
+      next = atomicAdd(&work[0], 1);
     }
     if (threadIdx.x == 0) s_next = next;
     __syncthreads();
