@@ -209,10 +209,10 @@ def main():
                  if v[1]}
     # the gather/aggregate step: one group-kernel launch on large bf16
     # batches (it takes the wave items too), else the wave kernel (+ the
-    # row-chunk combine); "gather" spans whichever ran
+    # row-chunk combine)
     t_wave = stage_avg.get("seg_fwd", 0.0) + stage_avg.get("seg_combine", 0.0)
     t_group = stage_avg.get("seg_group", 0.0)
-    gather_ms = stage_avg.get("gather", t_wave + t_group)
+    gather_ms = t_wave + t_group
     achieved = ab["total"] / (gather_ms * 1e-3) / 1e9
     gbs = lambda b, t: round(b / (t * 1e-3) / 1e9, 1) if t > 0 else None
     fl = gemm_flops(w)

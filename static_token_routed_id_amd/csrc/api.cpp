@@ -52,13 +52,12 @@ enum Stage {
   ST_BWD_UP,
   ST_BWD_SEG,
   ST_GROUP,
-  ST_GATHER,
   ST_COUNT
 };
 const char* const kStageNames[ST_COUNT] = {
     "plan",     "seg_fwd", "seg_combine",   "up_proj", "layernorm",
     "mix_proj", "bwd_mix", "bwd_layernorm", "bwd_up",  "bwd_seg",
-    "seg_group", "gather"};
+    "seg_group"};
 
 bool debug_sync() {
   static const bool on = [] {
@@ -529,11 +528,10 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     const int64_t items_ub = ((B + kTokTile - 1) / kTokTile + distinct) *
                              static_cast<int64_t>(plan->nch_max);
     // With the group kernel enabled (inference), one launch of it runs every
-    // item: its workgroups take the busy ids' items, then the 64-token
-    // items, then the wave items one per wavefront, all from device-wide
-    // queues, so no workgroup idles while another still has work.
+    // item: the busy ids' 128-token items, the 64-token items and the wave
+    // items (one per wavefront), all from device-wide queues, so no
+    // workgroup idles while another still has work.
     const bool merged = plan->group_min_rows > 0 && !all_wave;
-    StageTimer* gather = new StageTimer(plan, ST_GATHER, s);
     if (!merged) {
       StageTimer t(plan, ST_SEG, s);
       e = seg_fwd_launch(sa, d.dtype, static_cast<int>(B),
@@ -566,11 +564,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
           ga, static_cast<int>(gitems_ub < (1 << 30) ? gitems_ub : (1 << 30)),
           s);
     }
-    if (e != hipSuccess) {
-      delete gather;
-      return L3_ERR_HIP;
-    }
-    delete gather;
+    if (e != hipSuccess) return L3_ERR_HIP;
     // Row chunks exist only for ids with more rows than one wave item takes;
     // when all such ids go to the group kernel nothing needs merging.
     const bool split =
