@@ -5,6 +5,9 @@ softmax-aggregate, W_up projection, LayerNorm, W_mix projection) of one
 batch, all resident in HBM before timing starts. Default workload: the
 large-prefill configuration (65536 tokens, vocab 131072, 2^22-row budget,
 d = 2048, d_e = 512, bf16 inputs, float32 accumulation and output).
+`--train` times a training step instead: plan + forward keeping the saved
+state + backward with a seeded upstream gradient (fwd+bwd tokens/s, every
+stage's mean ms), e.g. `--train --workload train_skew_bf16`.
 
 Prints one JSON line. `roofline` is the gather/aggregate step: on large
 bf16 batches one launch of seg_group_kernel (it also runs the wave items of
@@ -32,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "L3 layer fwd tokens/sec + achieved HBM GB/s of K/V gather vs peak, bf16"
+METRIC_TRAIN = "L3 layer fwd+bwd tokens/sec (training step) + per-stage ms"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 
@@ -112,6 +116,38 @@ def gemm_flops(w) -> dict:
     return dict(up_proj=2.0 * B * d * d_e, mix_proj=2.0 * B * d * 2 * d)
 
 
+def cpu_baseline_train(w, dy, budget_s: float) -> dict:
+    """The oracle's forward + backward (as it stands) on a bounded sample of
+    the batch (the first n tokens as a batch of their own), or None when its
+    dense float64 dK would not fit comfortably in host memory."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import l3_oracle
+    from static_token_routed_id_amd import workloads as wl
+    if w.rows * w.spec.d * 8 > (4 << 30):
+        return None
+    dd = wl.decoded(w)
+    dyd = wl.decode(dy)
+
+    def run(n):
+        args = [dd["x"][:n], dd["ids"][:n], dd["K"], dd["V"], dd["offsets"],
+                dd["W_up"], dd["gamma"], dd["beta"], dd["W_mix"]]
+        t0 = time.perf_counter()
+        l3_oracle.forward(*args)
+        l3_oracle.backward(*args, dyd[:n])
+        return time.perf_counter() - t0
+
+    with threadpool_limits(limits=1):
+        n = min(w.batch, 16)
+        dt = run(n)
+        n = int(min(w.batch, max(16, budget_s / max(dt / n, 1e-6))))
+        dt = run(n)
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {n} tokens of the {w.batch}-token batch as "
+                      f"a batch of their own, forward and backward in "
+                      f"float64, one thread, {dt:.1f} s"}
+
+
 def cpu_baseline(w, budget_s: float) -> dict:
     """The oracle (as it stands) on a bounded sample of the batch."""
     from threadpoolctl import threadpool_limits
@@ -146,6 +182,8 @@ def main():
     ap.add_argument("--workload", default="large_prefill_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--train", action="store_true",
+                    help="time plan + saving forward + backward instead")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -177,16 +215,29 @@ def main():
     offsets = torch.from_numpy(w.offsets).cuda()
     params = [dev[k] for k in ("x", "K", "V", "W_up", "gamma", "beta",
                                "W_mix")]
-    layer = L3Layer(desc, w.batch)
+    layer = L3Layer(desc, w.batch, training=args.train)
     y = torch.empty((w.batch, w.spec.d), dtype=torch.float32, device="cuda")
     layer.make_plan(ids, offsets)
     assert L.l3_plan_check(layer.plan) == L.L3_OK
     plan_np = L.l3_plan_export(layer.plan)
     info = L.l3_plan_info(layer.plan)
+    if args.train:
+        dy_np = wl.upstream_grad(w)
+        dy = to_device(dy_np)
+        f32 = dict(dtype=torch.float32, device="cuda")
+        d, d_e = w.spec.d, w.spec.d_e
+        grads = [torch.empty((w.batch, d), **f32),
+                 torch.empty((w.rows, d), **f32),
+                 torch.empty((w.rows, d_e), **f32),
+                 torch.empty((d, d_e), **f32), torch.empty(d, **f32),
+                 torch.empty(d, **f32), torch.empty((d, 2 * d), **f32)]
 
     def step():
         layer.make_plan(ids, offsets)
         layer.forward(*params, y=y)
+        if args.train:
+            L.l3_backward(layer.plan, dy, *params, layer.save, *grads,
+                          layer.scratch)
 
     for _ in range(args.warmup):
         step()
@@ -224,7 +275,7 @@ def main():
                        "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFS, 4)}
     traffic = measured_traffic(w.spec.name)
     out = {
-        "metric": METRIC,
+        "metric": METRIC_TRAIN if args.train else METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -240,7 +291,9 @@ def main():
         "config": {"workload": w.spec.name, "tokens": w.batch,
                    "vocab": w.spec.vocab, "table_rows": w.rows,
                    "d": w.spec.d, "d_e": w.spec.d_e, "k_max": w.spec.k_max,
-                   "distinct_ids": int(plan_np["S"])},
+                   "distinct_ids": int(plan_np["S"]),
+                   "step": "plan + forward (saved state) + backward"
+                           if args.train else "plan + forward"},
         "roofline": {"kernel": "gather (seg_group_kernel)" if t_group > 0
                                else "gather (seg_fwd_kernel)",
                      "bound": "hbm",
@@ -257,7 +310,12 @@ def main():
         "mfma": mfma,
     }
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        if args.train:
+            cb = cpu_baseline_train(w, dy_np, args.cpu_seconds)
+            if cb is not None:
+                out["cpu_baseline"] = cb
+        else:
+            out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

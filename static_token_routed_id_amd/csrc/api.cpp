@@ -177,12 +177,19 @@ struct BwdBufs {
   float* dH;
   float* dU;
   float* dA;
+  float* P;   // [B x bwd_kst] softmax weights, sorted token order
+  float* dS;  // [B x bwd_kst] score gradients
 };
+// Row stride of the segment backward's p / dS arrays: k_max rounded up to
+// its 64-row blocks.
+int bwd_kst(const l3_desc& d) { return (d.k_max + 63) / 64 * 64; }
 BwdBufs carve_bwd(Carver& c, const l3_desc& d, int64_t B) {
   BwdBufs b;
   b.dH = c.take<float>(B * d.d);
   b.dU = c.take<float>(B * d.d);
   b.dA = c.take<float>(B * d.d_e);
+  b.P = c.take<float>(B * bwd_kst(d));
+  b.dS = c.take<float>(B * bwd_kst(d));
   return b;
 }
 
@@ -795,6 +802,13 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
     ba.dgamma = dgamma;
     ba.dbeta = dbeta;
     ba.rows = d.rows;
+    // the work items of the saving forward: every id's wave items
+    ba.item_map = plan->group_min_rows > 0 ? pd.aitem_map : pd.item_map;
+    ba.count_slot = plan->group_min_rows > 0 ? 8 : 2;
+    ba.chunk_rows = plan->chunk_rows;
+    ba.kst = bwd_kst(d);
+    ba.Pbuf = bb.P;
+    ba.DSbuf = bb.dS;
     {
       StageTimer t(plan, ST_BWD_LN, s);
       e = ln_bwd_launch(ba, d.dtype, s);
@@ -842,7 +856,15 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
       StageTimer t(plan, ST_BWD_SEG, s);
       e = fill_zero_launch(dK, d.rows * D, s);
       if (e == hipSuccess) e = fill_zero_launch(dV, d.rows * DE, s);
-      if (e == hipSuccess) e = seg_bwd_launch(ba, d.dtype, Bi, s);
+      const int64_t distinct = B < d.vocab ? B : d.vocab;
+      const int64_t items_ub =
+          ((B + kTokTile - 1) / kTokTile + distinct) *
+          static_cast<int64_t>(plan->nch_max);
+      if (e == hipSuccess)
+        e = seg_bwd_launch(
+            ba, d.dtype,
+            static_cast<int>(items_ub < (1 << 30) ? items_ub : (1 << 30)),
+            static_cast<int>(distinct), s);
     }
     return finish(plan, e, s);
   } catch (...) {

@@ -6,13 +6,14 @@
 //
 // Determinism: nothing here uses floating-point atomics. LayerNorm column
 // sums (dgamma, dbeta) are taken by one thread per column over the rows in
-// order. The segment backward gives each id (segment) to one workgroup,
-// which walks that id's tokens in sorted order and is the only writer of the
-// id's dK / dV rows (Systems-Friendly Design, Batch Sorting: the sorted
-// batch makes the mask block-diagonal, so ids never share rows).
+// order. In the segment backward every element of dK, dV has one writer
+// that sums the id's tokens in sorted order, and every dx row one writer
+// (Systems-Friendly Design, Batch Sorting: the sorted batch makes the mask
+// block-diagonal, so ids never share rows and tokens never share ids).
 
 #include "l3_device.h"
 #include "l3_internal.h"
+#include "seg_wave.h"
 
 namespace l3 {
 
@@ -81,100 +82,346 @@ hipError_t ln_bwd_launch(const BwdArgs& a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Fixed-order reduction over the 256 threads of a workgroup.
-__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  v = is_max ? wave_max(v) : wave_sum(v);
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int q = 1; q < 4; ++q) r = is_max ? fmaxf(r, red[q]) : r + red[q];
-  __syncthreads();
-  return r;
-}
+// ---------------------------------------------------------- segment bwd ---
+// Two passes, both over the id-sorted batch, neither with atomics:
+//
+// Tiles (one wavefront per tile of <= 16 tokens of one id, all n <= k_max
+// of its rows, the training forward's own work items): recompute the
+// scores S = X K_t^T (the forward's MFMA code) and dP = dA V_t^T (16x16x4
+// float32 MFMA), both as float32, in row chunks of 128; then per token the
+// exact softmax p, dS = p * (dP - p . dP); p and dS go to two
+// [B x k] float32 scratch arrays (token in sorted order, row j); finally
+// dX_att = dS K_t, added to the token's dx row (each token belongs to one
+// tile, so it has one writer).
+//
+// Rows (one workgroup per (id, block of 64 rows, block of 256 columns of
+// [K | V])): dK_t[j, c] = sum_i dS[i, j] x_i[c] and dV_t[j, c] =
+// sum_i p[i, j] dA_i[c] over the id's tokens in sorted order, one thread
+// per column with the 64 rows in registers; each table element has exactly
+// one writer, which stores the whole sum.
 
-// One workgroup per id. For each of the id's tokens i in sorted order:
-// recompute p = Softmax(K_t x_i), dp = V_t da_i, ds = p * (dp - p . dp);
-// dV_t += p da_i^T, dK_t += ds x_i^T (this workgroup owns those rows);
-// dx_i += K_t^T ds.
-template <typename T>
-__global__ __launch_bounds__(256) void seg_bwd_kernel(BwdArgs a) {
-  __shared__ float xs[4096];
-  __shared__ float das[4096];
-  __shared__ float ps[L3_MAX_ROWS_PER_ID];
-  __shared__ float dss[L3_MAX_ROWS_PER_ID];
-  __shared__ float red[4];
-  if (a.header[0] != 0) return;
-  const int S = a.header[1];
-  const int tid = threadIdx.x;
-  const T* X = static_cast<const T*>(a.x);
-  const T* K = static_cast<const T*>(a.K);
-  const T* V = static_cast<const T*>(a.V);
-  for (int s = blockIdx.x; s < S; s += gridDim.x) {
-    const int t0 = a.seg_tok_start[s], t1 = a.seg_tok_start[s + 1];
-    const int n = a.seg_n[s];
-    const int64_t r0 = a.seg_row_off[s];
-    for (int tk = t0; tk < t1; ++tk) {
-      const int64_t i = a.perm[tk];
-      for (int c = tid; c < a.d; c += 256) xs[c] = ld<T>(X, i * a.d + c);
-      for (int c = tid; c < a.d_e; c += 256) das[c] = a.dA[i * a.d_e + c];
-      __syncthreads();
-      float mx = -INFINITY;
-      for (int j = tid; j < n; j += 256) {
-        const int64_t rk = (r0 + j) * a.d, rv = (r0 + j) * a.d_e;
-        float sc = 0.f, dp = 0.f;
-        for (int c = 0; c < a.d; ++c) sc = fmaf(ld<T>(K, rk + c), xs[c], sc);
-        for (int c = 0; c < a.d_e; ++c) dp = fmaf(ld<T>(V, rv + c), das[c], dp);
-        ps[j] = sc;
-        dss[j] = dp;
-        mx = fmaxf(mx, sc);
+constexpr int kBwdRowBlk = 64;
+constexpr int kBwdColBlk = 256;
+
+template <typename T, int NB>
+__device__ __forceinline__ void bwd_chunk(const BwdArgs& a, const T* xr,
+                                          const float* dar, int64_t rowbase,
+                                          int nc, int r, int g, int pbase,
+                                          int c0, int mcount, float (&mx)[4]) {
+  floatx4 sacc[kNBMax], dacc[kNBMax];
+  const T* kt = static_cast<const T*>(a.K) + rowbase * a.d;
+  if constexpr (sizeof(T) == 2) {
+    constexpr int R = NB == 1 ? 8 : (NB == 2 ? 4 : 2);
+    if (R > 2 && (a.d / 32) % R == 0)
+      scores_bf16<NB, R>(xr, kt, a.d, nc, r, g, 0, sacc);
+    else
+      scores_bf16<NB, 2>(xr, kt, a.d, nc, r, g, 0, sacc);
+  } else {
+    scores_f32<NB>(xr, kt, a.d, nc, r, g, sacc);
+  }
+  // dP = dA V^T on 16x16x4 float32 MFMA, 16 columns of d_e a step (lane
+  // group g supplies columns 4g .. 4g + 3, one MFMA per element)
+  const T* vt = static_cast<const T*>(a.V) + rowbase * a.d_e;
+  int voff[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    dacc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    voff[nb] = min(nb * 16 + r, nc - 1) * a.d_e + g * 4;
+  }
+  for (int kc = 0; kc < a.d_e; kc += 16) {
+    const float4 dv = *reinterpret_cast<const float4*>(dar + kc + g * 4);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float vv[4];
+      if constexpr (sizeof(T) == 2) {
+        const uint2 u = *reinterpret_cast<const uint2*>(vt + voff[nb] + kc);
+        vv[0] = __uint_as_float(u.x << 16);
+        vv[1] = __uint_as_float(u.x & 0xffff0000u);
+        vv[2] = __uint_as_float(u.y << 16);
+        vv[3] = __uint_as_float(u.y & 0xffff0000u);
+      } else {
+        const float4 f = *reinterpret_cast<const float4*>(vt + voff[nb] + kc);
+        vv[0] = f.x;
+        vv[1] = f.y;
+        vv[2] = f.z;
+        vv[3] = f.w;
       }
-      mx = block_reduce(mx, red, true);
-      float sum = 0.f;
-      for (int j = tid; j < n; j += 256) {
-        const float e = __expf(ps[j] - mx);
-        ps[j] = e;
-        sum += e;
+      dacc[nb] = mfma_f32(dv.x, vv[0], dacc[nb]);
+      dacc[nb] = mfma_f32(dv.y, vv[1], dacc[nb]);
+      dacc[nb] = mfma_f32(dv.z, vv[2], dacc[nb]);
+      dacc[nb] = mfma_f32(dv.w, vv[3], dacc[nb]);
+    }
+  }
+  // lane holds (token 4g + i, row c0 + nb * 16 + r): raw S and dP out
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int j = nb * 16 + r;
+    if (j < nc) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * g + i;
+        if (t < mcount) {
+          const int64_t o = static_cast<int64_t>(pbase + t) * a.kst + c0 + j;
+          a.Pbuf[o] = sacc[nb][i];
+          a.DSbuf[o] = dacc[nb][i];
+          mx[i] = fmaxf(mx[i], sacc[nb][i]);
+        }
       }
-      sum = block_reduce(sum, red, false);
-      const float inv = 1.0f / sum;
-      float pdp = 0.f;
-      for (int j = tid; j < n; j += 256) {
-        const float p = ps[j] * inv;
-        ps[j] = p;
-        pdp = fmaf(p, dss[j], pdp);
-      }
-      pdp = block_reduce(pdp, red, false);
-      for (int j = tid; j < n; j += 256) dss[j] = ps[j] * (dss[j] - pdp);
-      __syncthreads();
-      for (int idx = tid; idx < n * a.d_e; idx += 256) {
-        const int j = idx / a.d_e, c = idx - j * a.d_e;
-        a.dV[(r0 + j) * a.d_e + c] += ps[j] * das[c];
-      }
-      for (int idx = tid; idx < n * a.d; idx += 256) {
-        const int j = idx / a.d, c = idx - j * a.d;
-        a.dK[(r0 + j) * a.d + c] += dss[j] * xs[c];
-      }
-      for (int c = tid; c < a.d; c += 256) {
-        float acc = 0.f;
-        for (int j = 0; j < n; ++j)
-          acc = fmaf(dss[j], ld<T>(K, (r0 + j) * a.d + c), acc);
-        a.dx[i * a.d + c] += acc;
-      }
-      __syncthreads();
     }
   }
 }
 
-hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int S_ub,
+template <typename T>
+__device__ __forceinline__ void bwd_tile(const BwdArgs& a, int s, int tile,
+                                         int lane, float* lds) {
+  const int r = lane & 15, g = lane >> 4;
+  const int t_begin = a.seg_tok_start[s];
+  const int m = a.seg_tok_start[s + 1] - t_begin;
+  const int n = a.seg_n[s];
+  const int64_t r0 = a.seg_row_off[s];
+  const int tok0 = t_begin + tile * kTokTile;
+  const int mcount = min(kTokTile, m - tile * kTokTile);
+  const int64_t xi = a.perm[tok0 + min(r, mcount - 1)];
+  const T* xr = static_cast<const T*>(a.x) + xi * a.d;
+  const float* dar = a.dA + xi * a.d_e;
+  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int c0 = 0; c0 < n; c0 += kWaveMaxRows) {
+    const int nc = min(kWaveMaxRows, n - c0);
+    const int nbc = ceil_div(nc, 16);
+#define L3_CHUNK(NB)                                                        \
+  bwd_chunk<T, NB>(a, xr, dar, r0 + c0, nc, r, g, tok0, c0, mcount, mx)
+    if (nbc <= 1)
+      L3_CHUNK(1);
+    else if (nbc <= 2)
+      L3_CHUNK(2);
+    else if (nbc <= 4)
+      L3_CHUNK(4);
+    else
+      L3_CHUNK(8);
+#undef L3_CHUNK
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mx[i] = group16_max(mx[i]);
+  // the raw values were written by other lanes of this wave
+  __threadfence_block();
+  // per token: p = exp(S - max) / sum, dS = p * (dP - p . dP)
+#pragma unroll
+  for (int t = 0; t < kTokTile; ++t) {
+    if (t < mcount) {
+      const float m_t = __shfl(mx[t & 3], (t >> 2) * 16);
+      const int64_t base = static_cast<int64_t>(tok0 + t) * a.kst;
+      float sum = 0.f, pdp = 0.f;
+      for (int j = lane; j < n; j += 64) {
+        const float e = __expf(a.Pbuf[base + j] - m_t);
+        sum += e;
+        pdp = fmaf(e, a.DSbuf[base + j], pdp);
+      }
+      sum = wave_sum(sum);
+      pdp = wave_sum(pdp);
+      const float inv = 1.0f / sum;
+      const float pd = pdp * inv;
+      for (int j = lane; j < n; j += 64) {
+        const float p = __expf(a.Pbuf[base + j] - m_t) * inv;
+        const float dsv = p * (a.DSbuf[base + j] - pd);
+        a.Pbuf[base + j] = p;
+        a.DSbuf[base + j] = dsv;
+      }
+    }
+  }
+  __threadfence_block();
+  // dX_att = dS K_t: lane owns 4 columns of a 256-column pass, all 16
+  // tokens; dS of 16 rows at a time staged transposed in this wave's LDS
+  // ([row][token]) so each row's 16 weights are 4 broadcast reads
+  const T* K = static_cast<const T*>(a.K);
+  for (int cc = 0; cc < a.d; cc += 256) {
+    const int c = cc + lane * 4;
+    const bool active = c < a.d;
+    float acc[kTokTile][4];
+#pragma unroll
+    for (int t = 0; t < kTokTile; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[t][q] = 0.f;
+    for (int j0 = 0; j0 < n; j0 += 16) {
+      {
+        const int t = lane >> 2, jq = (lane & 3) * 4;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (t < mcount) {
+          const float4 f = *reinterpret_cast<const float4*>(
+              a.DSbuf + static_cast<int64_t>(tok0 + t) * a.kst + j0 + jq);
+          v[0] = f.x;
+          v[1] = f.y;
+          v[2] = f.z;
+          v[3] = f.w;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          lds[(jq + q) * kTokTile + t] = j0 + jq + q < n ? v[q] : 0.f;
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int jn = min(16, n - j0);
+      for (int jj = 0; jj < jn; ++jj) {
+        float kv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (active) {
+          const int64_t o = (r0 + j0 + jj) * a.d + c;
+          if constexpr (sizeof(T) == 2) {
+            const uint2 u = *reinterpret_cast<const uint2*>(K + o);
+            kv[0] = __uint_as_float(u.x << 16);
+            kv[1] = __uint_as_float(u.x & 0xffff0000u);
+            kv[2] = __uint_as_float(u.y << 16);
+            kv[3] = __uint_as_float(u.y & 0xffff0000u);
+          } else {
+            const float4 f = *reinterpret_cast<const float4*>(K + o);
+            kv[0] = f.x;
+            kv[1] = f.y;
+            kv[2] = f.z;
+            kv[3] = f.w;
+          }
+        }
+        const float4* w4 = reinterpret_cast<const float4*>(lds + jj * kTokTile);
+#pragma unroll
+        for (int tq = 0; tq < 4; ++tq) {
+          const float4 wv = w4[tq];
+          const float wt[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              acc[tq * 4 + u][q] = fmaf(wt[u], kv[q], acc[tq * 4 + u][q]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < kTokTile; ++t) {
+        if (t < mcount) {
+          float* dst = a.dx + static_cast<int64_t>(a.perm[tok0 + t]) * a.d + c;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dst[q] += acc[t][q];
+        }
+      }
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void seg_bwd_tile_kernel(BwdArgs a) {
+  __shared__ __align__(16) float s_ds[4][16 * kTokTile];
+  if (a.header[0] != 0) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n_items = a.header[a.count_slot];
+  for (int item = blockIdx.x * 4 + w; item < n_items;
+       item += gridDim.x * 4) {
+    const int2 im = a.item_map[item];
+    const int s = im.x;
+    const int nch = ceil_div(a.seg_n[s], a.chunk_rows);
+    // the forward's items are (token tile, row chunk): take each tile once
+    if (im.y % nch != 0) continue;
+    bwd_tile<T>(a, s, im.y / nch, lane, s_ds[w]);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void seg_bwd_rows_kernel(BwdArgs a) {
+  __shared__ __align__(16) float s_ds[kTokTile][kBwdRowBlk];
+  __shared__ __align__(16) float s_p[kTokTile][kBwdRowBlk];
+  __shared__ int s_tok[kTokTile];
+  if (a.header[0] != 0) return;
+  const int S = a.header[1];
+  const int tid = threadIdx.x;
+  const int ncb = ceil_div(a.d + a.d_e, kBwdColBlk);
+  const int nrb = ceil_div(a.kst, kBwdRowBlk);
+  const int64_t total = static_cast<int64_t>(S) * ncb * nrb;
+  const T* X = static_cast<const T*>(a.x);
+  for (int64_t idx = blockIdx.x; idx < total; idx += gridDim.x) {
+    // index = (row block, column block, segment): a busy id's blocks land on
+    // different workgroups
+    const int s = static_cast<int>(idx % S);
+    const int64_t rest = idx / S;
+    const int cb = static_cast<int>(rest % ncb);
+    const int jb = static_cast<int>(rest / ncb);
+    const int n = a.seg_n[s];
+    const int j0 = jb * kBwdRowBlk;
+    if (j0 >= n) continue;
+    const int t_begin = a.seg_tok_start[s];
+    const int t_end = a.seg_tok_start[s + 1];
+    const int64_t r0 = a.seg_row_off[s];
+    const int c = cb * kBwdColBlk + tid;
+    const bool active = c < a.d + a.d_e;
+    const bool isK = c < a.d;
+    const int col = isK ? c : c - a.d;
+    float acc[kBwdRowBlk];
+#pragma unroll
+    for (int jj = 0; jj < kBwdRowBlk; ++jj) acc[jj] = 0.f;
+    for (int p0 = t_begin; p0 < t_end; p0 += kTokTile) {
+      const int cnt = min(kTokTile, t_end - p0);
+      __syncthreads();  // the previous batch is consumed
+      {
+        // 16 tokens x 64 rows of dS and p: one float4 of each per thread
+        const int t = tid >> 4, jq = (tid & 15) * 4;
+        float4 dv = {0.f, 0.f, 0.f, 0.f}, pv = {0.f, 0.f, 0.f, 0.f};
+        if (t < cnt) {
+          const int64_t o = static_cast<int64_t>(p0 + t) * a.kst + j0 + jq;
+          dv = *reinterpret_cast<const float4*>(a.DSbuf + o);
+          pv = *reinterpret_cast<const float4*>(a.Pbuf + o);
+        }
+        *reinterpret_cast<float4*>(&s_ds[t][jq]) = dv;
+        *reinterpret_cast<float4*>(&s_p[t][jq]) = pv;
+        if (tid < kTokTile) s_tok[tid] = tid < cnt ? a.perm[p0 + tid] : 0;
+      }
+      __syncthreads();
+      if (active) {
+        for (int t = 0; t < cnt; ++t) {
+          const int64_t i = s_tok[t];
+          const float v = isK ? ld<T>(X, i * a.d + col) : a.dA[i * a.d_e + col];
+          const float4* w4 = reinterpret_cast<const float4*>(
+              isK ? &s_ds[t][0] : &s_p[t][0]);
+#pragma unroll
+          for (int q = 0; q < kBwdRowBlk / 4; ++q) {
+            const float4 wv = w4[q];
+            acc[4 * q] = fmaf(wv.x, v, acc[4 * q]);
+            acc[4 * q + 1] = fmaf(wv.y, v, acc[4 * q + 1]);
+            acc[4 * q + 2] = fmaf(wv.z, v, acc[4 * q + 2]);
+            acc[4 * q + 3] = fmaf(wv.w, v, acc[4 * q + 3]);
+          }
+        }
+      }
+    }
+    if (active) {
+      const int jn = min(kBwdRowBlk, n - j0);
+#pragma unroll
+      for (int jj = 0; jj < kBwdRowBlk; ++jj) {
+        if (jj < jn) {
+          const int64_t row = r0 + j0 + jj;
+          if (isK)
+            a.dK[row * a.d + col] = acc[jj];
+          else
+            a.dV[row * a.d_e + col] = acc[jj];
+        }
+      }
+    }
+  }
+}
+
+hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int items_ub, int S_ub,
                           hipStream_t s) {
-  if (S_ub <= 0) return hipSuccess;
-  const int grid = S_ub < 4096 ? S_ub : 4096;
+  if (items_ub <= 0 || S_ub <= 0) return hipSuccess;
+  int grid = ceil_div(items_ub, 4);
+  if (grid > 8192) grid = 8192;
   if (dtype == kBF16)
-    seg_bwd_kernel<uint16_t><<<grid, 256, 0, s>>>(a);
+    seg_bwd_tile_kernel<uint16_t><<<grid, 256, 0, s>>>(a);
   else
-    seg_bwd_kernel<float><<<grid, 256, 0, s>>>(a);
+    seg_bwd_tile_kernel<float><<<grid, 256, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t blocks = static_cast<int64_t>(S_ub) *
+                         ceil_div(a.d + a.d_e, kBwdColBlk) *
+                         ceil_div(a.kst, kBwdRowBlk);
+  const int grid2 = static_cast<int>(blocks < 8192 ? blocks : 8192);
+  if (dtype == kBF16)
+    seg_bwd_rows_kernel<uint16_t><<<grid2, 256, 0, s>>>(a);
+  else
+    seg_bwd_rows_kernel<float><<<grid2, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

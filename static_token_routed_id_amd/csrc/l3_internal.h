@@ -223,10 +223,18 @@ struct BwdArgs {
   float* dgamma;
   float* dbeta;
   int64_t rows;
+  // segment backward: the training forward's work items (token tile, row
+  // chunk) and two [B x kst] float32 arrays for p and dS (sorted order)
+  const int2* item_map;
+  int count_slot;
+  int chunk_rows;
+  int kst;             // row stride of Pbuf / DSbuf: k_max rounded up to 16
+  float* Pbuf;
+  float* DSbuf;
 };
 hipError_t fill_zero_launch(float* p, int64_t n, hipStream_t s);
 hipError_t ln_bwd_launch(const BwdArgs& a, int dtype, hipStream_t s);
-hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int S_ub,
-                          hipStream_t s);
+hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int items_ub,
+                          int S_ub, hipStream_t s);
 
 }  // namespace l3

@@ -306,6 +306,15 @@ def make(name_or_index, batch: Optional[int] = None, ln_perturb: bool = False,
                     W_mix, dy)
 
 
+def upstream_grad(w: Workload) -> np.ndarray:
+    """dy for a training step: the workload's own, else drawn from the same
+    seeded stream a training workload of this configuration would use."""
+    if w.dy is not None:
+        return w.dy
+    return store(_rng(w.cfg, S_DY).standard_normal((w.batch, w.spec.d)),
+                 w.spec.dtype)
+
+
 def with_ids(w: Workload, ids: np.ndarray, x: Optional[np.ndarray] = None,
              dy: Optional[np.ndarray] = None) -> Workload:
     """Same tables and weights, a different id stream (and optionally x, dy)."""
