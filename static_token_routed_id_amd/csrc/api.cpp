@@ -179,7 +179,16 @@ struct BwdBufs {
   float* dA;
   float* P;   // [B x bwd_kst] softmax weights, sorted token order
   float* dS;  // [B x bwd_kst] score gradients
+  float* ln_part;  // [ceil(B / 256) x 2 x d] dgamma / dbeta partials
+  float* gpart;    // split-K partial products of the weight gradients
+  int64_t gpart_floats;
 };
+// Room for split-K partials: eight d x max(d, d_e) products, at most 16 MB.
+int64_t gpart_floats_for(const l3_desc& d) {
+  const int64_t w = static_cast<int64_t>(d.d) * (d.d > d.d_e ? d.d : d.d_e);
+  const int64_t f = 8 * w;
+  return f < (int64_t(1) << 22) ? f : (int64_t(1) << 22);
+}
 // Row stride of the segment backward's p / dS arrays: k_max rounded up to
 // its 64-row blocks.
 int bwd_kst(const l3_desc& d) { return (d.k_max + 63) / 64 * 64; }
@@ -190,6 +199,9 @@ BwdBufs carve_bwd(Carver& c, const l3_desc& d, int64_t B) {
   b.dA = c.take<float>(B * d.d_e);
   b.P = c.take<float>(B * bwd_kst(d));
   b.dS = c.take<float>(B * bwd_kst(d));
+  b.ln_part = c.take<float>((B + 255) / 256 * 2 * d.d);
+  b.gpart_floats = gpart_floats_for(d);
+  b.gpart = c.take<float>(b.gpart_floats);
   return b;
 }
 
@@ -769,11 +781,12 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
         w.N = d.d;
         w.K = Bi;
         w.header = pd.header;
-        e = gemm_launch(w, d.dtype, kF32, kF32, s);
+        e = gemm_launch(w, d.dtype, kF32, kF32, s, bb.gpart, bb.gpart_floats);
         if (e == hipSuccess) {
           w.Bm = x;
           w.C = dW_mix + D;
-          e = gemm_launch(w, d.dtype, d.dtype, kF32, s);
+          e = gemm_launch(w, d.dtype, d.dtype, kF32, s, bb.gpart,
+                          bb.gpart_floats);
         }
       }
     }
@@ -809,6 +822,7 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
     ba.kst = bwd_kst(d);
     ba.Pbuf = bb.P;
     ba.DSbuf = bb.dS;
+    ba.ln_part = bb.ln_part;
     {
       StageTimer t(plan, ST_BWD_LN, s);
       e = ln_bwd_launch(ba, d.dtype, s);
@@ -831,7 +845,7 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
       w.N = d.d_e;
       w.K = Bi;
       w.header = pd.header;
-      e = gemm_launch(w, kF32, kF32, kF32, s);
+      e = gemm_launch(w, kF32, kF32, kF32, s, bb.gpart, bb.gpart_floats);
       // dA = dU W_up
       if (e == hipSuccess) {
         GemmArgs g{};

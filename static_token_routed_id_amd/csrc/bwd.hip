@@ -56,16 +56,48 @@ __global__ __launch_bounds__(256) void ln_bwd_rows_kernel(BwdArgs a) {
   }
 }
 
-// dgamma[j] = sum_i dh[i, j] * uhat[i, j], dbeta[j] = sum_i dh[i, j].
+// dgamma[j] = sum_i dh[i, j] * uhat[i, j], dbeta[j] = sum_i dh[i, j], in a
+// fixed order: each workgroup sums a block of 256 rows for 64 columns (four
+// row phases of 64 rows, combined in order), then one thread per column
+// adds the blocks in order.
+constexpr int kLnRowBlk = 256;
+
 __global__ __launch_bounds__(256) void ln_bwd_cols_kernel(BwdArgs a) {
+  __shared__ float s_g[4][64], s_b[4][64];
+  if (a.header[0] != 0) return;
+  const int c = threadIdx.x & 63, ph = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + c;
+  const int rb = blockIdx.y;
+  float sg = 0.f, sb = 0.f;
+  if (j < a.d) {
+    const int i0 = rb * kLnRowBlk + ph * 64;
+    const int i1 = min(i0 + 64, a.B);
+    for (int i = i0; i < i1; ++i) {
+      const int64_t o = static_cast<int64_t>(i) * a.d + j;
+      sg = fmaf(a.dH[o], a.uhat[o], sg);
+      sb += a.dH[o];
+    }
+  }
+  s_g[ph][c] = sg;
+  s_b[ph][c] = sb;
+  __syncthreads();
+  if (ph == 0 && j < a.d) {
+    const int64_t o = (static_cast<int64_t>(rb) * 2) * a.d + j;
+    a.ln_part[o] = ((s_g[0][c] + s_g[1][c]) + s_g[2][c]) + s_g[3][c];
+    a.ln_part[o + a.d] = ((s_b[0][c] + s_b[1][c]) + s_b[2][c]) + s_b[3][c];
+  }
+}
+
+__global__ __launch_bounds__(256) void ln_bwd_cols_sum_kernel(BwdArgs a,
+                                                              int nrb) {
   if (a.header[0] != 0) return;
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= a.d) return;
   float sg = 0.f, sb = 0.f;
-  for (int i = 0; i < a.B; ++i) {
-    const int64_t o = static_cast<int64_t>(i) * a.d + j;
-    sg += a.dH[o] * a.uhat[o];
-    sb += a.dH[o];
+  for (int rb = 0; rb < nrb; ++rb) {
+    const int64_t o = (static_cast<int64_t>(rb) * 2) * a.d + j;
+    sg += a.ln_part[o];
+    sb += a.ln_part[o + a.d];
   }
   a.dgamma[j] = sg;
   a.dbeta[j] = sb;
@@ -77,8 +109,12 @@ hipError_t ln_bwd_launch(const BwdArgs& a, int dtype, hipStream_t s) {
       ln_bwd_rows_kernel<uint16_t><<<ceil_div(a.B, 4), 256, 0, s>>>(a);
     else
       ln_bwd_rows_kernel<float><<<ceil_div(a.B, 4), 256, 0, s>>>(a);
+    const int nrb = ceil_div(a.B, kLnRowBlk);
+    ln_bwd_cols_kernel<<<dim3(ceil_div(a.d, 64), nrb), 256, 0, s>>>(a);
+    ln_bwd_cols_sum_kernel<<<ceil_div(a.d, 256), 256, 0, s>>>(a, nrb);
+  } else {
+    ln_bwd_cols_sum_kernel<<<ceil_div(a.d, 256), 256, 0, s>>>(a, 0);
   }
-  ln_bwd_cols_kernel<<<ceil_div(a.d, 256), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -103,11 +139,21 @@ hipError_t ln_bwd_launch(const BwdArgs& a, int dtype, hipStream_t s) {
 constexpr int kBwdRowBlk = 64;
 constexpr int kBwdColBlk = 256;
 
+// Per-token softmax statistics of one tile, merged over row chunks: running
+// max M, L = sum_j exp(S_j - M), Q = sum_j exp(S_j - M) dP_j. Lane group g
+// holds tokens 4g .. 4g + 3 (element i); all 16 lanes of a group agree.
+struct TileStats {
+  float M[4], L[4], Q[4];
+};
+
+// Scores and dP of rows c0 .. c0 + nc - 1 of one tile: the raw values go to
+// the p / dS arrays (each lane writes, and later rereads, only its own
+// entries) and the chunk is folded into the statistics.
 template <typename T, int NB>
 __device__ __forceinline__ void bwd_chunk(const BwdArgs& a, const T* xr,
                                           const float* dar, int64_t rowbase,
                                           int nc, int r, int g, int pbase,
-                                          int c0, int mcount, float (&mx)[4]) {
+                                          int c0, int mcount, TileStats& st) {
   floatx4 sacc[kNBMax], dacc[kNBMax];
   const T* kt = static_cast<const T*>(a.K) + rowbase * a.d;
   if constexpr (sizeof(T) == 2) {
@@ -152,23 +198,109 @@ __device__ __forceinline__ void bwd_chunk(const BwdArgs& a, const T* xr,
       dacc[nb] = mfma_f32(dv.w, vv[3], dacc[nb]);
     }
   }
-  // lane holds (token 4g + i, row c0 + nb * 16 + r): raw S and dP out
+  // lane holds (token 4g + i, row c0 + nb * 16 + r)
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int j = nb * 16 + r;
-    if (j < nc) {
+  for (int i = 0; i < 4; ++i) {
+    const int t = 4 * g + i;
+    float cm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * g + i;
+    for (int nb = 0; nb < NB; ++nb)
+      if (nb * 16 + r < nc) cm = fmaxf(cm, sacc[nb][i]);
+    cm = group16_max(cm);
+    const float m_new = fmaxf(st.M[i], cm);
+    float l = 0.f, q = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int j = nb * 16 + r;
+      if (j < nc) {
+        const float e = __expf(sacc[nb][i] - m_new);
+        l += e;
+        q = fmaf(e, dacc[nb][i], q);
         if (t < mcount) {
           const int64_t o = static_cast<int64_t>(pbase + t) * a.kst + c0 + j;
           a.Pbuf[o] = sacc[nb][i];
           a.DSbuf[o] = dacc[nb][i];
-          mx[i] = fmaxf(mx[i], sacc[nb][i]);
+        }
+      }
+    }
+    l = group16_sum(l);
+    q = group16_sum(q);
+    const float sc = __expf(st.M[i] - m_new);  // 0 on the first chunk
+    st.L[i] = fmaf(st.L[i], sc, l);
+    st.Q[i] = fmaf(st.Q[i], sc, q);
+    st.M[i] = m_new;
+  }
+}
+
+// Second sweep over the same lane's entries: p = exp(S - M) / L,
+// dS = p * (dP - Q / L).
+template <int NB>
+__device__ __forceinline__ void bwd_chunk_finish(const BwdArgs& a, int nc,
+                                                 int r, int g, int pbase,
+                                                 int c0, int mcount,
+                                                 const TileStats& st) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 4 * g + i;
+    if (t < mcount) {
+      const float inv = 1.0f / st.L[i];
+      const float pd = st.Q[i] * inv;
+      float sv[NB], dv[NB];
+      const int64_t base = static_cast<int64_t>(pbase + t) * a.kst + c0 + r;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if (nb * 16 + r < nc) {
+          sv[nb] = a.Pbuf[base + nb * 16];
+          dv[nb] = a.DSbuf[base + nb * 16];
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if (nb * 16 + r < nc) {
+          const float p = __expf(sv[nb] - st.M[i]) * inv;
+          a.Pbuf[base + nb * 16] = p;
+          a.DSbuf[base + nb * 16] = p * (dv[nb] - pd);
         }
       }
     }
   }
+}
+
+// K rows j0 .. j0 + 15 of this lane's 4 columns (c) and the 16 tokens' dS of
+// those rows (one float4 per lane: token lane >> 2, rows 4 (lane & 3) ..)
+template <typename T>
+struct DxBlock {
+  uint32_t k[16][sizeof(T) == 2 ? 2 : 4];
+  float4 ds;
+};
+
+template <typename T>
+__device__ __forceinline__ void dx_block_load(const BwdArgs& a, int64_t r0,
+                                              int n, int j0, int c,
+                                              bool active, int lane, int tok0,
+                                              int mcount, DxBlock<T>& b) {
+  const T* K = static_cast<const T*>(a.K);
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const int j = min(j0 + jj, n - 1);
+    if (active) {
+      const int64_t o = (r0 + j) * a.d + c;
+      if constexpr (sizeof(T) == 2) {
+        const uint2 u = *reinterpret_cast<const uint2*>(K + o);
+        b.k[jj][0] = u.x;
+        b.k[jj][1] = u.y;
+      } else {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(K + o);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) b.k[jj][q] = u[q];
+      }
+    }
+  }
+  const int t = lane >> 2, jq = (lane & 3) * 4;
+  b.ds = float4{0.f, 0.f, 0.f, 0.f};
+  if (t < mcount)
+    b.ds = *reinterpret_cast<const float4*>(
+        a.DSbuf + static_cast<int64_t>(tok0 + t) * a.kst + j0 + jq);
 }
 
 template <typename T>
@@ -184,55 +316,45 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int s, int tile,
   const int64_t xi = a.perm[tok0 + min(r, mcount - 1)];
   const T* xr = static_cast<const T*>(a.x) + xi * a.d;
   const float* dar = a.dA + xi * a.d_e;
-  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  TileStats st;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    st.M[i] = -INFINITY;
+    st.L[i] = 0.f;
+    st.Q[i] = 0.f;
+  }
+#define L3_NB_DISPATCH(CALL)  \
+  if (nbc <= 1) {             \
+    CALL(1);                  \
+  } else if (nbc <= 2) {      \
+    CALL(2);                  \
+  } else if (nbc <= 4) {      \
+    CALL(4);                  \
+  } else {                    \
+    CALL(8);                  \
+  }
   for (int c0 = 0; c0 < n; c0 += kWaveMaxRows) {
     const int nc = min(kWaveMaxRows, n - c0);
     const int nbc = ceil_div(nc, 16);
-#define L3_CHUNK(NB)                                                        \
-  bwd_chunk<T, NB>(a, xr, dar, r0 + c0, nc, r, g, tok0, c0, mcount, mx)
-    if (nbc <= 1)
-      L3_CHUNK(1);
-    else if (nbc <= 2)
-      L3_CHUNK(2);
-    else if (nbc <= 4)
-      L3_CHUNK(4);
-    else
-      L3_CHUNK(8);
+#define L3_CHUNK(NB) \
+  bwd_chunk<T, NB>(a, xr, dar, r0 + c0, nc, r, g, tok0, c0, mcount, st)
+    L3_NB_DISPATCH(L3_CHUNK)
 #undef L3_CHUNK
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) mx[i] = group16_max(mx[i]);
-  // the raw values were written by other lanes of this wave
-  __threadfence_block();
-  // per token: p = exp(S - max) / sum, dS = p * (dP - p . dP)
-#pragma unroll
-  for (int t = 0; t < kTokTile; ++t) {
-    if (t < mcount) {
-      const float m_t = __shfl(mx[t & 3], (t >> 2) * 16);
-      const int64_t base = static_cast<int64_t>(tok0 + t) * a.kst;
-      float sum = 0.f, pdp = 0.f;
-      for (int j = lane; j < n; j += 64) {
-        const float e = __expf(a.Pbuf[base + j] - m_t);
-        sum += e;
-        pdp = fmaf(e, a.DSbuf[base + j], pdp);
-      }
-      sum = wave_sum(sum);
-      pdp = wave_sum(pdp);
-      const float inv = 1.0f / sum;
-      const float pd = pdp * inv;
-      for (int j = lane; j < n; j += 64) {
-        const float p = __expf(a.Pbuf[base + j] - m_t) * inv;
-        const float dsv = p * (a.DSbuf[base + j] - pd);
-        a.Pbuf[base + j] = p;
-        a.DSbuf[base + j] = dsv;
-      }
-    }
+  for (int c0 = 0; c0 < n; c0 += kWaveMaxRows) {
+    const int nc = min(kWaveMaxRows, n - c0);
+    const int nbc = ceil_div(nc, 16);
+#define L3_FIN(NB) bwd_chunk_finish<NB>(a, nc, r, g, tok0, c0, mcount, st)
+    L3_NB_DISPATCH(L3_FIN)
+#undef L3_FIN
   }
+#undef L3_NB_DISPATCH
+  // dS was written by other lanes of this wave
   __threadfence_block();
   // dX_att = dS K_t: lane owns 4 columns of a 256-column pass, all 16
-  // tokens; dS of 16 rows at a time staged transposed in this wave's LDS
-  // ([row][token]) so each row's 16 weights are 4 broadcast reads
-  const T* K = static_cast<const T*>(a.K);
+  // tokens; per 16-row block the tokens' dS are staged transposed in this
+  // wave's LDS ([row][token]: 4 broadcast reads a row), the next block's K
+  // rows and dS already in flight while the current one is used
   for (int cc = 0; cc < a.d; cc += 256) {
     const int c = cc + lane * 4;
     const bool active = c < a.d;
@@ -241,42 +363,33 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int s, int tile,
     for (int t = 0; t < kTokTile; ++t)
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[t][q] = 0.f;
+    DxBlock<T> cur, nxt;
+    dx_block_load<T>(a, r0, n, 0, c, active, lane, tok0, mcount, cur);
     for (int j0 = 0; j0 < n; j0 += 16) {
+      if (j0 + 16 < n)
+        dx_block_load<T>(a, r0, n, j0 + 16, c, active, lane, tok0, mcount,
+                         nxt);
       {
         const int t = lane >> 2, jq = (lane & 3) * 4;
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-        if (t < mcount) {
-          const float4 f = *reinterpret_cast<const float4*>(
-              a.DSbuf + static_cast<int64_t>(tok0 + t) * a.kst + j0 + jq);
-          v[0] = f.x;
-          v[1] = f.y;
-          v[2] = f.z;
-          v[3] = f.w;
-        }
+        const float v[4] = {cur.ds.x, cur.ds.y, cur.ds.z, cur.ds.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           lds[(jq + q) * kTokTile + t] = j0 + jq + q < n ? v[q] : 0.f;
       }
       __builtin_amdgcn_wave_barrier();
-      const int jn = min(16, n - j0);
-      for (int jj = 0; jj < jn; ++jj) {
-        float kv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (active) {
-          const int64_t o = (r0 + j0 + jj) * a.d + c;
-          if constexpr (sizeof(T) == 2) {
-            const uint2 u = *reinterpret_cast<const uint2*>(K + o);
-            kv[0] = __uint_as_float(u.x << 16);
-            kv[1] = __uint_as_float(u.x & 0xffff0000u);
-            kv[2] = __uint_as_float(u.y << 16);
-            kv[3] = __uint_as_float(u.y & 0xffff0000u);
-          } else {
-            const float4 f = *reinterpret_cast<const float4*>(K + o);
-            kv[0] = f.x;
-            kv[1] = f.y;
-            kv[2] = f.z;
-            kv[3] = f.w;
-          }
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        float kv[4];
+        if constexpr (sizeof(T) == 2) {
+          kv[0] = __uint_as_float(cur.k[jj][0] << 16);
+          kv[1] = __uint_as_float(cur.k[jj][0] & 0xffff0000u);
+          kv[2] = __uint_as_float(cur.k[jj][1] << 16);
+          kv[3] = __uint_as_float(cur.k[jj][1] & 0xffff0000u);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) kv[q] = __uint_as_float(cur.k[jj][q]);
         }
+        // rows past n have zero weights
         const float4* w4 = reinterpret_cast<const float4*>(lds + jj * kTokTile);
 #pragma unroll
         for (int tq = 0; tq < 4; ++tq) {
@@ -290,6 +403,7 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int s, int tile,
         }
       }
       __builtin_amdgcn_wave_barrier();
+      cur = nxt;
     }
     if (active) {
 #pragma unroll
@@ -371,18 +485,31 @@ __global__ __launch_bounds__(256) void seg_bwd_rows_kernel(BwdArgs a) {
       }
       __syncthreads();
       if (active) {
-        for (int t = 0; t < cnt; ++t) {
-          const int64_t i = s_tok[t];
-          const float v = isK ? ld<T>(X, i * a.d + col) : a.dA[i * a.d_e + col];
-          const float4* w4 = reinterpret_cast<const float4*>(
-              isK ? &s_ds[t][0] : &s_p[t][0]);
+        // this column's value of every token of the batch, all loads issued
+        // before the first use
+        float vals[kTokTile];
 #pragma unroll
-          for (int q = 0; q < kBwdRowBlk / 4; ++q) {
-            const float4 wv = w4[q];
-            acc[4 * q] = fmaf(wv.x, v, acc[4 * q]);
-            acc[4 * q + 1] = fmaf(wv.y, v, acc[4 * q + 1]);
-            acc[4 * q + 2] = fmaf(wv.z, v, acc[4 * q + 2]);
-            acc[4 * q + 3] = fmaf(wv.w, v, acc[4 * q + 3]);
+        for (int t = 0; t < kTokTile; ++t) {
+          vals[t] = 0.f;
+          if (t < cnt) {
+            const int64_t i = s_tok[t];
+            vals[t] = isK ? ld<T>(X, i * a.d + col) : a.dA[i * a.d_e + col];
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < kTokTile; ++t) {
+          if (t < cnt) {
+            const float v = vals[t];
+            const float4* w4 = reinterpret_cast<const float4*>(
+                isK ? &s_ds[t][0] : &s_p[t][0]);
+#pragma unroll
+            for (int q = 0; q < kBwdRowBlk / 4; ++q) {
+              const float4 wv = w4[q];
+              acc[4 * q] = fmaf(wv.x, v, acc[4 * q]);
+              acc[4 * q + 1] = fmaf(wv.y, v, acc[4 * q + 1]);
+              acc[4 * q + 2] = fmaf(wv.z, v, acc[4 * q + 2]);
+              acc[4 * q + 3] = fmaf(wv.w, v, acc[4 * q + 3]);
+            }
           }
         }
       }

@@ -17,71 +17,162 @@
 //   used for small shapes, float32 inputs and the backward pass.
 // * layernorm_rows: one wave per row, two-pass mean / biased variance.
 
+#include <algorithm>
+
 #include "l3_device.h"
 #include "l3_internal.h"
 
 namespace l3 {
 
 // ---------------------------------------------------------------- generic ---
+// Any strides, any mix of bf16 / float32 operands, float32 accumulation on
+// 16x16x4 float32 MFMA. 64 x 64 tile per workgroup (four waves, 32 x 32
+// each as 2 x 2 MFMA blocks), K in steps of 16 through double-buffered LDS;
+// the next step's operands are loaded into registers while the current one
+// is multiplied. Each operand is read along whichever of its dimensions is
+// contiguous (16 consecutive k of a row, or 64 consecutive rows of a k).
+// With nsplit > 1, workgroup z of the grid's third dimension takes the z-th
+// share of K and writes its float32 partial product to part; gemm_reduce
+// then adds the shares in order (the result does not depend on timing).
 template <typename TA, typename TB, typename TC>
 __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmArgs g) {
-  __shared__ float As[16][64 + 4];
-  __shared__ float Bs[16][64 + 4];
+  __shared__ float As[2][16][64 + 4];
+  __shared__ float Bs[2][16][64 + 4];
   if (g.header && g.header[0] != 0) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int r = lane & 15, gq = lane >> 4;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  const int tm = tid >> 4, tn = tid & 15;
   const TA* A1 = static_cast<const TA*>(g.A1);
   const TA* A2 = static_cast<const TA*>(g.A2);
   const TB* Bm = static_cast<const TB*>(g.Bm);
-  float acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int k0 = 0; k0 < g.K; k0 += 16) {
+  // this workgroup's share of K: [kbeg, kend), whole 16-steps
+  const int kshare = ceil_div(ceil_div(g.K, g.nsplit), 16) * 16;
+  const int kbeg = static_cast<int>(blockIdx.z) * kshare;
+  const int kend = min(g.K, kbeg + kshare);
+  // element q of this thread's share of a 16 x 64 operand slice
+  const bool a_kfast = g.a1_k == 1 && g.a2_k == 1;
+  const bool b_kfast = g.b_k == 1;
+  auto a_pos = [&](int q, int& kk, int& mm) {
+    const int e = tid + q * 256;
+    if (a_kfast) {
+      kk = e & 15;
+      mm = e >> 4;
+    } else {
+      kk = e >> 6;
+      mm = e & 63;
+    }
+  };
+  auto b_pos = [&](int q, int& kk, int& nn) {
+    const int e = tid + q * 256;
+    if (b_kfast) {
+      kk = e & 15;
+      nn = e >> 4;
+    } else {
+      kk = e >> 6;
+      nn = e & 63;
+    }
+  };
+  float ra[4], rb[4];
+  auto load = [&](int k0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int e = tid + q * 256;
-      const int kk = e >> 6, mm = e & 63;
+      int kk, mm;
+      a_pos(q, kk, mm);
       const int gm = m0 + mm, gk = k0 + kk;
       float v = 0.f;
-      if (gm < g.M && gk < g.K) {
-        v = gk < g.K1 ? ld<TA>(A1, gm * g.a1_m + gk * g.a1_k)
-                      : ld<TA>(A2, gm * g.a2_m + (gk - g.K1) * g.a2_k);
+      if (gm < g.M && gk < kend) {
+        v = gk < g.K1
+                ? ld<TA>(A1, static_cast<int64_t>(gm) * g.a1_m +
+                                 static_cast<int64_t>(gk) * g.a1_k)
+                : ld<TA>(A2, static_cast<int64_t>(gm) * g.a2_m +
+                                 static_cast<int64_t>(gk - g.K1) * g.a2_k);
       }
-      As[kk][mm] = v;
-      const int gn = n0 + mm;
-      float b = 0.f;
-      if (gn < g.N && gk < g.K) b = ld<TB>(Bm, gk * g.b_k + gn * g.b_n);
-      Bs[kk][mm] = b;
+      ra[q] = v;
+      int kb, nn;
+      b_pos(q, kb, nn);
+      const int gn = n0 + nn, gkb = k0 + kb;
+      float bv = 0.f;
+      if (gn < g.N && gkb < kend)
+        bv = ld<TB>(Bm, static_cast<int64_t>(gkb) * g.b_k +
+                            static_cast<int64_t>(gn) * g.b_n);
+      rb[q] = bv;
     }
-    __syncthreads();
+  };
+  auto store = [&](int buf) {
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][tm * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tn * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    for (int q = 0; q < 4; ++q) {
+      int kk, mm;
+      a_pos(q, kk, mm);
+      As[buf][kk][mm] = ra[q];
+      int kb, nn;
+      b_pos(q, kb, nn);
+      Bs[buf][kb][nn] = rb[q];
     }
+  };
+  floatx4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  load(kbeg);
+  store(0);
+  __syncthreads();
+  const int nk = kend > kbeg ? ceil_div(kend - kbeg, 16) : 0;
+  for (int it = 0; it < nk; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < nk) load(kbeg + (it + 1) * 16);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k = ks * 4 + gq;
+      float av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) av[i] = As[buf][k][wm * 32 + i * 16 + r];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bv[j] = Bs[buf][k][wn * 32 + j * 16 + r];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f32(av[i], bv[j], acc[i][j]);
+    }
+    if (it + 1 < nk) store(buf ^ 1);
     __syncthreads();
   }
+  // D[4 gq + e][r] of block (i, j)
   TC* C = static_cast<TC*>(g.C);
+  float* P = g.nsplit > 1
+                 ? g.part + static_cast<int64_t>(blockIdx.z) * g.M * g.N
+                 : nullptr;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gm = m0 + tm * 4 + i;
-    if (gm >= g.M) continue;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gn = n0 + tn * 4 + j;
-      if (gn < g.N) st<TC>(C, gm * g.c_m + gn, acc[i][j]);
+    for (int e = 0; e < 4; ++e) {
+      const int gm = m0 + wm * 32 + i * 16 + 4 * gq + e;
+      if (gm >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int gn = n0 + wn * 32 + j * 16 + r;
+        if (gn < g.N) {
+          if (P)
+            P[static_cast<int64_t>(gm) * g.N + gn] = acc[i][j][e];
+          else
+            st<TC>(C, static_cast<int64_t>(gm) * g.c_m + gn, acc[i][j][e]);
+        }
+      }
     }
-  }
+}
+
+// C = the nsplit partial products added in order.
+template <typename TC>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g) {
+  if (g.header && g.header[0] != 0) return;
+  const int64_t mn = static_cast<int64_t>(g.M) * g.N;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= mn) return;
+  float v = 0.f;
+  for (int z = 0; z < g.nsplit; ++z) v += g.part[z * mn + i];
+  const int64_t m = i / g.N, n = i - m * g.N;
+  st<TC>(static_cast<TC*>(g.C), m * g.c_m + n, v);
 }
 
 template <typename TA, typename TB>
@@ -93,10 +184,28 @@ static void gemm_generic_c(const GemmArgs& g, int c_type, dim3 grid,
     gemm_generic_kernel<TA, TB, float><<<grid, 256, 0, s>>>(g);
 }
 
-hipError_t gemm_launch(const GemmArgs& g, int a_type, int b_type, int c_type,
-                       hipStream_t s) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  dim3 grid(ceil_div(g.N, 64), ceil_div(g.M, 64));
+hipError_t gemm_launch(const GemmArgs& g0, int a_type, int b_type, int c_type,
+                       hipStream_t s, float* part, int64_t part_floats) {
+  if (g0.M <= 0 || g0.N <= 0) return hipSuccess;
+  GemmArgs g = g0;
+  g.part = nullptr;
+  g.nsplit = 1;
+  // few output tiles and a long K (the weight gradients, K = tokens):
+  // split K so that the GPU has enough workgroups
+  const int64_t tiles =
+      static_cast<int64_t>(ceil_div(g.N, 64)) * ceil_div(g.M, 64);
+  const int64_t mn = static_cast<int64_t>(g.M) * g.N;
+  if (part && tiles < 1024 && g.K >= 256) {
+    int64_t ns = (1024 + tiles - 1) / tiles;
+    ns = std::min<int64_t>(ns, g.K / 128);
+    ns = std::min<int64_t>(ns, part_floats / mn);
+    ns = std::min<int64_t>(ns, 64);
+    if (ns >= 2) {
+      g.part = part;
+      g.nsplit = static_cast<int>(ns);
+    }
+  }
+  dim3 grid(ceil_div(g.N, 64), ceil_div(g.M, 64), g.nsplit);
   if (a_type == kBF16) {
     if (b_type == kBF16)
       gemm_generic_c<uint16_t, uint16_t>(g, c_type, grid, s);
@@ -107,6 +216,15 @@ hipError_t gemm_launch(const GemmArgs& g, int a_type, int b_type, int c_type,
       gemm_generic_c<float, uint16_t>(g, c_type, grid, s);
     else
       gemm_generic_c<float, float>(g, c_type, grid, s);
+  }
+  if (g.nsplit > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int rgrid = static_cast<int>((mn + 255) / 256);
+    if (c_type == kBF16)
+      gemm_reduce_kernel<uint16_t><<<rgrid, 256, 0, s>>>(g);
+    else
+      gemm_reduce_kernel<float><<<rgrid, 256, 0, s>>>(g);
   }
   return hipGetLastError();
 }

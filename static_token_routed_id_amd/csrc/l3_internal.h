@@ -129,6 +129,10 @@ struct GemmArgs {
   int64_t c_m;
   int M, N, K;
   const int32_t* header;  // plan status word (kernel does nothing if set)
+  // generic kernel only: split of K over workgroups, partial M x N float32
+  // products in part (nsplit of them), summed in order by a second kernel
+  float* part = nullptr;
+  int nsplit = 1;
 };
 
 // LayerNorm of float32 rows (one wave per row).
@@ -193,7 +197,8 @@ bool seg_group_ok(int d, int d_e);
 hipError_t seg_group_launch(const SegGroupArgs& a, int items_ub,
                             hipStream_t s);
 hipError_t gemm_launch(const GemmArgs& g, int a_type, int b_type, int c_type,
-                       hipStream_t s);
+                       hipStream_t s, float* part = nullptr,
+                       int64_t part_floats = 0);
 hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s);
 bool gemm_nt_mfma_ok(const GemmArgs& g);
 // The 256 x 256 tile kernel (needed for the row-statistics epilogue).
@@ -231,6 +236,7 @@ struct BwdArgs {
   int kst;             // row stride of Pbuf / DSbuf: k_max rounded up to 16
   float* Pbuf;
   float* DSbuf;
+  float* ln_part;      // [ceil(B / 256) x 2 x d] LayerNorm column partials
 };
 hipError_t fill_zero_launch(float* p, int64_t n, hipStream_t s);
 hipError_t ln_bwd_launch(const BwdArgs& a, int dtype, hipStream_t s);
