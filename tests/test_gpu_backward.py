@@ -75,15 +75,17 @@ def test_backward_without_save_is_an_error():
 
 
 @pytest.mark.timeout(900)
-def test_prefill_shapes_bf16_backward():
+@pytest.mark.parametrize("tokens", [1024, 777])
+def test_prefill_shapes_bf16_backward(tokens):
     """The training step at prefill shapes (d = 1024, d_e = 256, a table of
     171,462 rows, ids with up to 512 rows): the first 1024 tokens of the
-    prefill id stream with a drawn upstream gradient."""
+    prefill id stream with a drawn upstream gradient, and a ragged 777
+    (no multiple of the 16-token tiles or the 256-row LayerNorm blocks)."""
     import dataclasses
     from static_token_routed_id_amd import workloads as wl
     base = gu.workload("prefill_bf16")
-    w = wl.with_ids(base, base.ids[:1024])
-    g = np.random.default_rng(5).standard_normal((1024, base.spec.d))
+    w = wl.with_ids(base, base.ids[:tokens])
+    g = np.random.default_rng(5).standard_normal((tokens, base.spec.d))
     w = dataclasses.replace(w, dy=wl.store(g, "bf16"))
     res = gu.run(w, training=True)
     ref = gu.oracle_backward(w)
