@@ -11,8 +11,9 @@
 //   scores   S = X K_t^T (64 tokens x n rows) on 16x16x32 bf16 MFMA. Wave w
 //            owns an even share of the rows (16, 32 or 64 of them); its K
 //            fragments stream from global memory straight into registers,
-//            up to fifteen 32-column steps ahead of the multiply (each K row
-//            is used by exactly one wave, so it never touches LDS). The X slice (64 tokens x 128 columns) is shared by
+//            a few 32-column steps ahead of the multiply (each K row is used
+//            by exactly one wave, so it never touches LDS). The X slice
+//            (64 tokens x 128 columns) is shared by
 //            all waves, so it is staged in LDS, double buffered, one barrier
 //            per slice. Both operands use the same lane -> k assignment.
 //   softmax  exact: per-wave row maxima / sums combined through LDS; the
@@ -98,15 +99,18 @@ __device__ __forceinline__ void group_item(
   // ------------------------------------------------------------ scores ---
   // Wave w owns rows 16*NBW*w .. 16*NBW*(w+1)-1, NBW = 1, 2 or 4 blocks of
   // 16 rows chosen from n so that the eight waves share the id's rows
-  // evenly. K streams in 32-column steps through a ring of R = 16 / NBW
-  // register slots: step t's loads are issued R-1 steps before its multiply
-  // (the loop is unrolled by R so every slot index is static, and there is
-  // no per-wave branch), which keeps 15 .. 12 KB of K in flight per wave
-  // whatever NBW is. Lane group g supplies columns 32t + 8g .. 32t + 8g + 7
+  // evenly. K streams in 32-column steps through a ring of R = 4, 2, 2
+  // register slots (NBW = 1, 2, 4): step t's loads are issued R-1 steps
+  // before its multiply (the loop is unrolled by R so every slot index is
+  // static, and there is no per-wave branch), 1 - 4 KB of K in flight per
+  // wave. Deeper rings (up to 16 KB a wave) were slower: they pushed the
+  // kernel past 256 registers into spills, and with eight such waves on
+  // every CU the memory system is already saturated. Lane group g supplies
+  // columns 32t + 8g .. 32t + 8g + 7
   // of its row for both operands. X is staged in 128-column slices in LDS
   // (double buffered, one barrier per slice). A wave past the id's last row
   // re-reads that cached row; its results are masked below.
-  constexpr int R = 16 / NBW;
+  constexpr int R = 4 / NBW > 1 ? 4 / NBW : 2;
   const int wrow0 = w * 16 * NBW;
   const bool has_rows = wrow0 < n;
   int koff[NBW];
@@ -160,18 +164,20 @@ __device__ __forceinline__ void group_item(
       // keep the loads ahead of this step's multiplies: left alone, the
       // scheduler sinks them past the MFMAs and the ring drains each step
       __builtin_amdgcn_sched_barrier(0);
+      // step t is step t % 4 of X slice t / 4 (R need not be a multiple
+      // of 4: the slice position comes from t, not from the ring slot)
       const int buf = (t >> 2) & 1;
       u32x4 xf[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
         xf[mb] = *reinterpret_cast<const u32x4*>(
-            &s_x[buf][(mb * 16 + r) * kXS + ((q + w) & 3) * 32 + g * 8]);
+            &s_x[buf][(mb * 16 + r) * kXS + ((t + w) & 3) * 32 + g * 8]);
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           acc[mb][nb] = mfma16(xf[mb], kr[q][nb], acc[mb][nb]);
-      if ((q & 3) == 3) {
+      if ((t & 3) == 3) {
         // end of X slice t/4: the next slice (in registers) goes to the
         // other buffer, the one after is fetched
         *reinterpret_cast<u32x4*>(&s_x[buf ^ 1][xt * kXS + xc]) = x0;
