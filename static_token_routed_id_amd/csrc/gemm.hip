@@ -514,7 +514,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
       if (gm >= g.M) continue;
       TC* crow = C + static_cast<int64_t>(gm) * g.c_m + n0 + wn * 128 + r;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st<TC>(crow, j * 32, acc[i][j][e]);
+      for (int j = 0; j < 4; ++j) {
+        // streaming (non-temporal) stores: C is read much later or by a
+        // kernel that streams it once; kept out of the caches, it does not
+        // evict operands, and the write-back does not delay what follows
+        if constexpr (sizeof(TC) == 4)
+          __builtin_nontemporal_store(acc[i][j][e],
+                                      reinterpret_cast<float*>(crow) + j * 32);
+        else
+          __builtin_nontemporal_store(
+              f2bf(acc[i][j][e]), reinterpret_cast<uint16_t*>(crow) + j * 32);
+      }
     }
   }
 }
@@ -588,7 +598,8 @@ __global__ __launch_bounds__(256) void ln_apply_kernel(LnApplyArgs a) {
       o[q] = static_cast<uint32_t>(f2bf(h0)) |
              (static_cast<uint32_t>(f2bf(h1)) << 16);
     }
-    *reinterpret_cast<u32x4*>(a.h + base + e0) = o;
+    // streaming store (h is read once, by the W_mix GEMM)
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.h + base + e0));
   }
 }
 

@@ -347,7 +347,7 @@ __device__ __forceinline__ void group_item(
         for (int nb = 0; nb < NBV; ++nb) {
           const float o = acc2[mb][nb][i] * inv;
           const int64_t idx = orig * a.d_e + col0 + nb * 16 + r;
-          a.a_out[idx] = f2bf(o);
+          __builtin_nontemporal_store(f2bf(o), a.a_out + idx);
           if (a.a_save) a.a_save[idx] = o;
         }
       }
@@ -602,7 +602,7 @@ __device__ __forceinline__ void hot_item(const SegGroupArgs& a, int tok0,
         for (int cb = 0; cb < NBV; ++cb) {
           const float o = acc2[tb][cb][i] * inv;
           const int64_t idx = orig * a.d_e + col0 + cb * 16 + r16;
-          a.a_out[idx] = f2bf(o);
+          __builtin_nontemporal_store(f2bf(o), a.a_out + idx);
           if (a.a_save) a.a_save[idx] = o;
         }
       }

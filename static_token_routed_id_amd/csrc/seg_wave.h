@@ -310,6 +310,8 @@ __device__ __forceinline__ float word_value(const RowWords<EPL, BF16>& v,
 
 template <int EPL, typename T>
 __device__ __forceinline__ void store_row(T* dst, const float (&v)[EPL]);
+// bf16 rows of a are written with streaming (non-temporal) stores: the W_up
+// GEMM reads them once, much later.
 template <int EPL>
 __device__ __forceinline__ void store_row(uint16_t* dst,
                                           const float (&v)[EPL]) {
@@ -319,10 +321,11 @@ __device__ __forceinline__ void store_row(uint16_t* dst,
     for (int e = 0; e < 4; ++e)
       o[e] = static_cast<uint32_t>(f2bf(v[2 * e])) |
              (static_cast<uint32_t>(f2bf(v[2 * e + 1])) << 16);
-    *reinterpret_cast<u32x4*>(dst) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst));
   } else {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) dst[e] = f2bf(v[e]);
+    for (int e = 0; e < EPL; ++e)
+      __builtin_nontemporal_store(f2bf(v[e]), dst + e);
   }
 }
 template <int EPL>
