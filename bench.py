@@ -7,7 +7,9 @@ large-prefill configuration (65536 tokens, vocab 131072, 2^22-row budget,
 d = 2048, d_e = 512, bf16 inputs, float32 accumulation and output).
 `--train` times a training step instead: plan + forward keeping the saved
 state + backward with a seeded upstream gradient (fwd+bwd tokens/s, every
-stage's mean ms), e.g. `--train --workload train_skew_bf16`.
+stage's mean ms), e.g. `--train --workload train_skew_bf16`. `--layers L`
+times plan + L layer forwards (each layer its own tables and weights over
+the same offsets, one plan for the stack): tokens/s through the stack.
 
 Prints one JSON line. `roofline` is the gather/aggregate step: on large
 bf16 batches one launch of seg_group_kernel (it also runs the wave items of
@@ -36,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "L3 layer fwd tokens/sec + achieved HBM GB/s of K/V gather vs peak, bf16"
 METRIC_TRAIN = "L3 layer fwd+bwd tokens/sec (training step) + per-stage ms"
+METRIC_STACK = "L3 stack fwd tokens/sec (one plan shared by every layer)"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 
@@ -184,6 +187,9 @@ def main():
                     help="time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--train", action="store_true",
                     help="time plan + saving forward + backward instead")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="forward a stack of this many layers (own tables "
+                         "and weights, same offsets) with one plan a step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -209,8 +215,19 @@ def main():
     dtype = L.L3_BF16 if w.spec.dtype == "bf16" else L.L3_F32
     desc = L.make_desc(w.spec.vocab, w.rows, w.spec.d, w.spec.d_e,
                        w.spec.k_max, dtype, L.L3_F32)
+    if args.layers < 1 or (args.layers > 1 and args.train):
+        print("--layers takes a positive count, without --train",
+              file=sys.stderr)
+        sys.exit(2)
     dev = {k: to_device(getattr(w, k)) for k in
            ("x", "K", "V", "W_up", "gamma", "beta", "W_mix")}
+    stack = []
+    for li in range(1, args.layers):
+        wl_i = wl.layer_params(w, li)
+        stack.append([dev["x"]] + [to_device(getattr(wl_i, k)) for k in
+                                   ("K", "V", "W_up")] +
+                     [dev["gamma"], dev["beta"], to_device(wl_i.W_mix)])
+        del wl_i
     ids = torch.from_numpy(w.ids).cuda()
     offsets = torch.from_numpy(w.offsets).cuda()
     params = [dev[k] for k in ("x", "K", "V", "W_up", "gamma", "beta",
@@ -235,6 +252,8 @@ def main():
     def step():
         layer.make_plan(ids, offsets)
         layer.forward(*params, y=y)
+        for p_i in stack:
+            layer.forward(*p_i, y=y)
         if args.train:
             L.l3_backward(layer.plan, dy, *params, layer.save, *grads,
                           layer.scratch)
@@ -275,7 +294,8 @@ def main():
                        "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFS, 4)}
     traffic = measured_traffic(w.spec.name)
     out = {
-        "metric": METRIC_TRAIN if args.train else METRIC,
+        "metric": (METRIC_TRAIN if args.train else
+                   METRIC_STACK if args.layers > 1 else METRIC),
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -293,7 +313,9 @@ def main():
                    "d": w.spec.d, "d_e": w.spec.d_e, "k_max": w.spec.k_max,
                    "distinct_ids": int(plan_np["S"]),
                    "step": "plan + forward (saved state) + backward"
-                           if args.train else "plan + forward"},
+                           if args.train else
+                           f"plan + {args.layers} layer forwards"
+                           if args.layers > 1 else "plan + forward"},
         "roofline": {"kernel": "gather (seg_group_kernel)" if t_group > 0
                                else "gather (seg_fwd_kernel)",
                      "bound": "hbm",

@@ -151,9 +151,12 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
                      void* stream);
 
 /*
- * l3_backward -- gradients of sum(y * dy) for the batch of the last
- * l3_forward that was given `save` with this plan (the pages print no
- * gradients; these are the chain rule of the forward formula).
+ * l3_backward -- gradients of sum(y * dy) for the planned batch, from the
+ * state a saving l3_forward on this plan (since its last l3_plan /
+ * l3_replan) left in `save` (the pages print no gradients; these are the
+ * chain rule of the forward formula). One plan serves every layer that
+ * shares the batch's ids and the offsets: each layer calls l3_forward with
+ * its own tables, weights and save workspace, and l3_backward with the same.
  *   dy      device [B x d] (dtype)
  *   x, K, V, W_up, gamma, beta, W_mix: the forward's inputs
  *   save    the forward's save workspace (save_bytes)
@@ -162,11 +165,12 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
  *           every row is written; rows of ids absent from the batch are 0
  *   dW_up   device float32 [d x d_e]; dgamma, dbeta device float32 [d];
  *   dW_mix  device float32 [d x 2d]
- * Every output is overwritten (never accumulated). Table gradients are
- * reduced per id in sorted-batch order by the single workgroup owning that
- * id, and every other reduction has a fixed order, so results are bitwise
- * reproducible run to run.
- * Errors: L3_ERR_NULL, L3_ERR_WORKSPACE, L3_ERR_STATE, L3_ERR_HIP.
+ * Every output is overwritten (never accumulated). Every element of dK, dV
+ * and every row of dx has one writer, table gradients sum an id's tokens in
+ * sorted-batch order, and every other reduction has a fixed order, so
+ * results are bitwise reproducible run to run.
+ * Errors: L3_ERR_NULL, L3_ERR_WORKSPACE, L3_ERR_HIP, L3_ERR_STATE (`save` was
+ * not written by a saving forward on this plan since it was last planned).
  */
 l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
                       const void* K, const void* V, const void* W_up,

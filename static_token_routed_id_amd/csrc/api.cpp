@@ -248,7 +248,9 @@ struct l3_plan_s {
     int stage;
   };
   std::vector<Ev> events;
-  const void* saved = nullptr;  // save workspace of the last training forward
+  // save workspaces written by saving forwards since the last (re)plan: one
+  // plan can serve several layers, each with its own save workspace
+  std::vector<const void*> saved;
 };
 
 namespace {
@@ -300,7 +302,7 @@ l3_status do_plan(l3_plan_s* p, const int32_t* ids, int64_t B,
   if (B > p->capacity) return L3_ERR_WORKSPACE;
   if (B > 0 && (!ids || !offsets)) return L3_ERR_NULL;
   p->B = B;
-  p->saved = nullptr;
+  p->saved.clear();
   p->chunk_rows = chunk_rows_for(B, p->desc.k_max);
   p->nch_max = nch_for(B, p->desc.k_max);
   p->group_min_rows = group_min_rows_for(p->desc, B);
@@ -497,7 +499,6 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
                      void* stream) {
   try {
     if (!plan) return L3_ERR_NULL;
-    plan->saved = nullptr;
     const int64_t B = plan->B;
     if (B == 0) return L3_OK;
     if (!x || !K || !V || !W_up || !gamma || !beta || !W_mix || !y ||
@@ -693,7 +694,14 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
         e = gemm_launch(mx, d.dtype, d.dtype, d.y_dtype, s);
     }
     l3_status st = finish(plan, e, s);
-    if (st == L3_OK && save) plan->saved = save;
+    if (st == L3_OK && save) {
+      bool known = false;
+      for (const void* p : plan->saved) known = known || p == save;
+      if (!known) {
+        if (plan->saved.size() >= 1024) plan->saved.erase(plan->saved.begin());
+        plan->saved.push_back(save);
+      }
+    }
     return st;
   } catch (...) {
     return L3_ERR_HIP;
@@ -729,7 +737,9 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
       if (e == hipSuccess) e = fill_zero_launch(dW_mix, int64_t(d.d) * 2 * d.d, s);
       return finish(plan, e, s);
     }
-    if (plan->saved != save) return L3_ERR_STATE;
+    bool known = false;
+    for (const void* p : plan->saved) known = known || p == save;
+    if (!known) return L3_ERR_STATE;
     if (save_bytes < save_bytes_for(d, B) || !aligned(save))
       return L3_ERR_WORKSPACE;
     if (scratch_bytes < bwd_bytes_for(d, B) || !aligned(scratch))

@@ -315,6 +315,25 @@ def upstream_grad(w: Workload) -> np.ndarray:
                  w.spec.dtype)
 
 
+def layer_params(w: Workload, layer: int,
+                 threads: Optional[int] = None) -> Workload:
+    """Layer `layer` of a stack sharing this batch's ids and offsets: its own
+    K, V, W_up, W_mix drawn from streams of their own (layer 0 is w itself);
+    x, gamma, beta and dy are w's."""
+    if layer == 0:
+        return w
+    spec, cfg, dt = w.spec, w.cfg, w.spec.dtype
+    off = 16 * layer
+    K = draw_table(cfg, S_K + off, w.rows, spec.d, spec.sigma_k, dt, threads)
+    V = draw_table(cfg, S_V + off, w.rows, spec.d_e, spec.sigma_v, dt,
+                   threads)
+    W_up = store(_rng(cfg, S_WUP + off).standard_normal((spec.d, spec.d_e))
+                 / np.sqrt(spec.d_e), dt)
+    W_mix = store(_rng(cfg, S_WMIX + off).standard_normal((spec.d, 2 * spec.d))
+                  / np.sqrt(2 * spec.d), dt)
+    return dataclasses.replace(w, K=K, V=V, W_up=W_up, W_mix=W_mix)
+
+
 def with_ids(w: Workload, ids: np.ndarray, x: Optional[np.ndarray] = None,
              dy: Optional[np.ndarray] = None) -> Workload:
     """Same tables and weights, a different id stream (and optionally x, dy)."""
