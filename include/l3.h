@@ -181,8 +181,37 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
                       size_t scratch_bytes, void* stream);
 
 /*
+ * l3_stage_rows -- for tables kept in host memory (gist.science explainer,
+ * Systems-Friendly Design: the tables may live in CPU memory because a
+ * token's rows follow from its id alone, Core Architecture, Static
+ * Routing): copy the rows of every id in the planned batch into compact
+ * device tables and point the plan at them. Stream-ordered after the plan;
+ * it may run on another stream than the layers before it (order it with an
+ * event) so the copy overlaps their work.
+ *   K_host   pinned host memory (hipHostMalloc, or a pinned torch
+ *            tensor) [rows x d] (dtype), the full key table; device memory
+ *            is accepted too; pageable host memory is refused (L3_ERR_NULL)
+ *   V_host   the same for the value table [rows x d_e]
+ *   K_stage  device [stage_rows x d] (dtype); V_stage device
+ *            [stage_rows x d_e]: receive the batch's rows, id by id in
+ *            ascending id order
+ *   stage_rows capacity in rows; B * k_max always suffices
+ * Afterwards l3_forward must be given K_stage, V_stage in place of the full
+ * tables, until the next l3_plan / l3_replan of this handle. A staged plan
+ * serves inference only: l3_backward returns L3_ERR_STATE, and staging twice
+ * without replanning returns L3_ERR_STATE. If the batch's rows exceed
+ * stage_rows, nothing is copied, every later kernel of the plan does
+ * nothing, and l3_plan_check reports L3_ERR_WORKSPACE.
+ * Errors: L3_ERR_NULL, L3_ERR_SHAPE, L3_ERR_STATE, L3_ERR_HIP.
+ */
+l3_status l3_stage_rows(l3_plan_t plan, const void* K_host,
+                        const void* V_host, void* K_stage, void* V_stage,
+                        int64_t stage_rows, void* stream);
+
+/*
  * l3_plan_check -- wait for the stream, then report the device-side
- * validation of the plan: L3_OK, L3_ERR_TOKEN_RANGE or L3_ERR_COUNT
+ * validation of the plan: L3_OK, L3_ERR_TOKEN_RANGE, L3_ERR_COUNT or
+ * L3_ERR_WORKSPACE (staged rows beyond the staging capacity)
  * (L3_ERR_HIP if the stream itself failed).
  */
 l3_status l3_plan_check(l3_plan_t plan, void* stream);

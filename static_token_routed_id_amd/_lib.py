@@ -64,6 +64,7 @@ def _load():
         "l3_backward": (c_int, [P, P, P, P, P, P, P, P, P, P, c_size_t, P, P,
                                 P, P, P, P, P, P, c_size_t, P]),
         "l3_plan_check": (c_int, [P, P]),
+        "l3_stage_rows": (c_int, [P, P, P, P, P, c_int64, P]),
         "l3_plan_export": (c_int, [P, P, P, P, P, P, P, P]),
         "l3_plan_info": (c_int, [P, POINTER(c_int64), c_int, P]),
         "l3_plan_release": (None, [P]),
@@ -83,7 +84,8 @@ _lib = _load()
 EXPORTED = ("l3_workspace_size", "l3_plan", "l3_replan", "l3_forward",
             "l3_backward", "l3_plan_check", "l3_plan_export", "l3_plan_info",
             "l3_plan_release", "l3_plan_tokens", "l3_status_str",
-            "l3_timing_enable", "l3_timing_read", "l3_stage_name")
+            "l3_timing_enable", "l3_timing_read", "l3_stage_name",
+            "l3_stage_rows")
 
 
 def lib():
@@ -199,9 +201,19 @@ def l3_backward(plan: Plan, dy, x, K, V, W_up, gamma, beta, W_mix, save, dx,
                             _stream(stream)), "l3_backward")
 
 
+def l3_stage_rows(plan: Plan, K_host, V_host, K_stage, V_stage,
+                  stream=None) -> None:
+    """Copy the batch's rows of host-resident tables into K_stage / V_stage
+    (device, capacity = K_stage's rows) and point the plan at them."""
+    rows = int(K_stage.shape[0]) if K_stage is not None else 0
+    _check(_lib.l3_stage_rows(plan.handle, _ptr(K_host), _ptr(V_host),
+                              _ptr(K_stage), _ptr(V_stage), rows,
+                              _stream(stream)), "l3_stage_rows")
+
+
 def l3_plan_check(plan: Plan, stream=None) -> int:
     """Returns the plan's device-side status (0, or L3_ERR_TOKEN_RANGE /
-    L3_ERR_COUNT); raises only on a HIP failure."""
+    L3_ERR_COUNT / L3_ERR_WORKSPACE); raises only on a HIP failure."""
     st = _lib.l3_plan_check(plan.handle, _stream(stream))
     if st == L3_ERR_HIP or st == L3_ERR_NULL:
         raise L3Error(st, "l3_plan_check")

@@ -29,6 +29,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wno-unused-command-line-argument"]
 
 SOURCES = ["plan.hip", "seg_fwd.hip", "seg_group.hip", "gemm.hip", "bwd.hip",
+           "stage.hip",
            "api.cpp"]
 
 

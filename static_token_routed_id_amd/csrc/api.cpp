@@ -131,6 +131,7 @@ PlanDev carve_plan(Carver& c, int64_t B) {
   p.hitem_map = c.take<int2>(static_cast<size_t>(group_items_cap(B)));
   p.seg_aitem_start = c.take<int32_t>(nb + 1);
   p.aitem_map = c.take<int2>(static_cast<size_t>(wave_items_cap(B)));
+  p.stage_off = c.take<int64_t>(nb);
   return p;
 }
 
@@ -251,6 +252,8 @@ struct l3_plan_s {
   // save workspaces written by saving forwards since the last (re)plan: one
   // plan can serve several layers, each with its own save workspace
   std::vector<const void*> saved;
+  // l3_stage_rows pointed the segments at staged tables (inference only)
+  bool staged = false;
 };
 
 namespace {
@@ -291,6 +294,7 @@ l3_status finish(l3_plan_s* p, hipError_t e, hipStream_t s) {
         return L3_ERR_HIP;
       if (h & kBadId) return L3_ERR_TOKEN_RANGE;
       if (h & kBadCount) return L3_ERR_COUNT;
+      if (h & kBadStage) return L3_ERR_WORKSPACE;
     }
   }
   return L3_OK;
@@ -303,6 +307,7 @@ l3_status do_plan(l3_plan_s* p, const int32_t* ids, int64_t B,
   if (B > 0 && (!ids || !offsets)) return L3_ERR_NULL;
   p->B = B;
   p->saved.clear();
+  p->staged = false;
   p->chunk_rows = chunk_rows_for(B, p->desc.k_max);
   p->nch_max = nch_for(B, p->desc.k_max);
   p->group_min_rows = group_min_rows_for(p->desc, B);
@@ -444,7 +449,69 @@ l3_status l3_plan_check(l3_plan_t plan, void* stream) {
     return L3_ERR_HIP;
   if (h & kBadId) return L3_ERR_TOKEN_RANGE;
   if (h & kBadCount) return L3_ERR_COUNT;
+  if (h & kBadStage) return L3_ERR_WORKSPACE;
   return L3_OK;
+}
+
+namespace {
+// The device address of memory the GPU may read: pinned host memory known
+// to HIP (its mapped address), or device / managed memory (itself). Plain
+// pageable host memory is refused (the copy kernel would fault on it).
+bool device_readable(const void* p, const void** out) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (attr.type == hipMemoryTypeHost) {
+    *out = attr.devicePointer;
+    return *out != nullptr;
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+    *out = p;
+    return true;
+  }
+  return false;
+}
+}  // namespace
+
+l3_status l3_stage_rows(l3_plan_t plan, const void* K_host,
+                        const void* V_host, void* K_stage, void* V_stage,
+                        int64_t stage_rows, void* stream) {
+  try {
+    if (!plan) return L3_ERR_NULL;
+    if (plan->B == 0) return L3_OK;
+    if (!K_host || !V_host || !K_stage || !V_stage) return L3_ERR_NULL;
+    const void* K_src = nullptr;
+    const void* V_src = nullptr;
+    if (!device_readable(K_host, &K_src) || !device_readable(V_host, &V_src))
+      return L3_ERR_NULL;
+    if (stage_rows < 0) return L3_ERR_SHAPE;
+    if (plan->staged) return L3_ERR_STATE;
+    const l3_desc& d = plan->desc;
+    StageArgs a;
+    a.header = plan->dev.header;
+    a.seg_n = plan->dev.seg_n;
+    a.seg_row_off = plan->dev.seg_row_off;
+    a.stage_off = plan->dev.stage_off;
+    a.d = d.d;
+    a.d_e = d.d_e;
+    a.elem = static_cast<int>(elem_bytes(d.dtype));
+    a.stage_rows = stage_rows;
+    a.K_host = static_cast<const uint8_t*>(K_src);
+    a.V_host = static_cast<const uint8_t*>(V_src);
+    a.K_stage = static_cast<uint8_t*>(K_stage);
+    a.V_stage = static_cast<uint8_t*>(V_stage);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t S_ub = plan->B < d.vocab ? plan->B : d.vocab;
+    hipError_t e = stage_rows_launch(a, static_cast<int>(S_ub), s);
+    if (e != hipSuccess) return L3_ERR_HIP;
+    plan->staged = true;
+    plan->saved.clear();
+    return finish(plan, e, s);
+  } catch (...) {
+    return L3_ERR_HIP;
+  }
 }
 
 l3_status l3_plan_info(l3_plan_t plan, int64_t* info, int n, void* stream) {
@@ -739,7 +806,7 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
     }
     bool known = false;
     for (const void* p : plan->saved) known = known || p == save;
-    if (!known) return L3_ERR_STATE;
+    if (!known || plan->staged) return L3_ERR_STATE;
     if (save_bytes < save_bytes_for(d, B) || !aligned(save))
       return L3_ERR_WORKSPACE;
     if (scratch_bytes < bwd_bytes_for(d, B) || !aligned(scratch))

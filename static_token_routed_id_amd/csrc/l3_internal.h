@@ -29,6 +29,7 @@ constexpr int kSortTile = 1024;
 // Bits of the device-side validation word of a plan.
 constexpr int kBadId = 1;
 constexpr int kBadCount = 2;
+constexpr int kBadStage = 4;  // staged rows exceed the staging tables
 
 // Device arrays of one plan, carved out of the caller's plan workspace.
 struct PlanDev {
@@ -58,6 +59,7 @@ struct PlanDev {
   // is enabled (else the wave items are already all of them).
   int32_t* seg_aitem_start; // [B+1]
   int2* aitem_map;
+  int64_t* stage_off;       // [B] first row of each segment in staged tables
 };
 // Capacity of the item maps for a batch of B tokens: a segment of m tokens
 // has at most ceil(m / 16) token tiles times ceil(512 / 32) row chunks.
@@ -193,6 +195,21 @@ struct SegGroupArgs {
   // wave items taken in a last pass (header NULL: none); bf16 inference
   SegFwdArgs wave;
 };
+// Staging of the batch's rows from host-resident tables (stage.hip).
+struct StageArgs {
+  int32_t* header;
+  const int32_t* seg_n;
+  int64_t* seg_row_off;   // rewritten to the staged offsets
+  int64_t* stage_off;
+  int d, d_e, elem;       // row widths, element bytes
+  int64_t stage_rows;     // capacity of K_stage / V_stage in rows
+  const uint8_t* K_host;
+  const uint8_t* V_host;
+  uint8_t* K_stage;
+  uint8_t* V_stage;
+};
+hipError_t stage_rows_launch(const StageArgs& a, int S_ub, hipStream_t s);
+
 bool seg_group_ok(int d, int d_e);
 hipError_t seg_group_launch(const SegGroupArgs& a, int items_ub,
                             hipStream_t s);
