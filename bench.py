@@ -7,7 +7,10 @@ large-prefill configuration (65536 tokens, vocab 131072, 2^22-row budget,
 d = 2048, d_e = 512, bf16 inputs, float32 accumulation and output).
 `--train` times a training step instead: plan + forward keeping the saved
 state + backward with a seeded upstream gradient (fwd+bwd tokens/s, every
-stage's mean ms), e.g. `--train --workload train_skew_bf16`. `--layers L`
+stage's mean ms), e.g. `--train --workload train_skew_bf16`. `--offload
+--workload decode_bf16` keeps the tables in pinned host memory and stages
+the batch's rows into HBM beside a stand-in for the preceding layers,
+against the same step with the tables in HBM. `--layers L`
 times plan + L layer forwards (each layer its own tables and weights over
 the same offsets, one plan for the stack): tokens/s through the stack.
 
@@ -177,6 +180,134 @@ def cpu_baseline(w, budget_s: float) -> dict:
                       f"one thread, {dt:.1f} s"}
 
 
+def run_offload(args) -> None:
+    """Decode with the tables in pinned host memory: per step the plan, then
+    the batch's rows staged into HBM on a side stream while a stand-in for
+    the preceding layers (bf16 GEMMs streaming --prelayer-gb of weights)
+    runs on the main stream, then the layer's forward on the staged rows.
+    Compared with the same step with the tables in HBM."""
+    import torch
+
+    from static_token_routed_id_amd import _lib as L
+    from static_token_routed_id_amd import workloads as wl
+    from static_token_routed_id_amd.layer import L3Layer, to_device
+
+    w = wl.make(args.workload)
+    dtype = L.L3_BF16 if w.spec.dtype == "bf16" else L.L3_F32
+    desc = L.make_desc(w.spec.vocab, w.rows, w.spec.d, w.spec.d_e,
+                       w.spec.k_max, dtype, L.L3_F32)
+    dev = {k: to_device(getattr(w, k)) for k in
+           ("x", "K", "V", "W_up", "gamma", "beta", "W_mix")}
+
+    def pinned(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).pin_memory()
+
+    K_host, V_host = pinned(w.K), pinned(w.V)
+    ids = torch.from_numpy(w.ids).cuda()
+    offsets = torch.from_numpy(w.offsets).cuda()
+    B, d, d_e = w.batch, w.spec.d, w.spec.d_e
+    stage_rows = min(w.rows, B * w.spec.k_max)
+    tdt = dev["K"].dtype
+    K_stage = torch.empty((stage_rows, d), dtype=tdt, device="cuda")
+    V_stage = torch.empty((stage_rows, d_e), dtype=tdt, device="cuda")
+    u = np.unique(w.ids)
+    rows = int((w.offsets[u + 1] - w.offsets[u]).sum())
+    stage_bytes = rows * (d + d_e) * (2 if w.spec.dtype == "bf16" else 4)
+    # stand-in for the layers before this one: weight-streaming GEMMs
+    width = 4096
+    n_w = max(1, int(args.prelayer_gb * 1e9 / (2 * width * 8192)))
+    W_pre = [torch.randn(width, 8192, device="cuda").to(torch.bfloat16)
+             for _ in range(n_w)]
+    x_pre = torch.randn(B, width, device="cuda").to(torch.bfloat16)
+
+    def prelayers():
+        for Wp in W_pre:
+            torch.mm(x_pre, Wp)
+
+    layer = L3Layer(desc, B)
+    y = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    params = [dev[k] for k in ("x", "K", "V", "W_up", "gamma", "beta",
+                               "W_mix")]
+    staged = [dev["x"], K_stage, V_stage, dev["W_up"], dev["gamma"],
+              dev["beta"], dev["W_mix"]]
+    side = torch.cuda.Stream()
+    main_s = torch.cuda.current_stream()
+
+    def step_hbm():
+        layer.make_plan(ids, offsets)
+        prelayers()
+        layer.forward(*params, y=y)
+
+    def step_offload():
+        layer.make_plan(ids, offsets)
+        side.wait_stream(main_s)
+        with torch.cuda.stream(side):
+            L.l3_stage_rows(layer.plan, K_host, V_host, K_stage, V_stage,
+                            stream=side)
+        prelayers()
+        main_s.wait_stream(side)
+        layer.forward(*staged, y=y)
+
+    def step_stage_only():
+        layer.make_plan(ids, offsets)
+        L.l3_stage_rows(layer.plan, K_host, V_host, K_stage, V_stage)
+
+    def step_pre_only():
+        prelayers()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    ms_hbm = timed(step_hbm)
+    ms_off = timed(step_offload)
+    ms_stage = timed(step_stage_only)
+    ms_pre = timed(step_pre_only)
+    layer.make_plan(ids, offsets)
+    L.l3_stage_rows(layer.plan, K_host, V_host, K_stage, V_stage)
+    assert L.l3_plan_check(layer.plan) == L.L3_OK
+    out = {
+        "metric": "L3 decode step with tables in pinned host memory (rows "
+                  "staged beside the preceding layers) vs tables in HBM",
+        "value": round(B / (ms_off * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_off, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.spec.dtype,
+        "data": "synthetic (seeded Zipf ids and allocation, Gaussian tables "
+                "and weights)",
+        "config": {"workload": w.spec.name, "tokens": B,
+                   "table_rows": w.rows, "d": d, "d_e": d_e,
+                   "step": "plan + preceding-layer stand-in + forward",
+                   "prelayer_weight_gb": round(n_w * 2 * width * 8192 / 1e9,
+                                               2)},
+        "offload": {
+            "ms_step_tables_in_hbm": round(ms_hbm, 4),
+            "ms_step_tables_in_host": round(ms_off, 4),
+            "overhead_frac": round(ms_off / ms_hbm - 1.0, 4),
+            "ms_stage_alone": round(ms_stage, 4),
+            "ms_prelayers_alone": round(ms_pre, 4),
+            "staged_rows": rows,
+            "staged_bytes": stage_bytes,
+            "host_link_GBs": round(stage_bytes / (ms_stage * 1e-3) / 1e9, 1),
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +321,13 @@ def main():
     ap.add_argument("--layers", type=int, default=1,
                     help="forward a stack of this many layers (own tables "
                          "and weights, same offsets) with one plan a step")
+    ap.add_argument("--offload", action="store_true",
+                    help="decode with the tables in pinned host memory, "
+                         "their rows staged beside a stand-in for the "
+                         "preceding layers (use with --workload decode_bf16)")
+    ap.add_argument("--prelayer-gb", type=float, default=5.2,
+                    help="weights the preceding-layer stand-in streams a step "
+                         "(5.2 GB: a 2.6B-parameter model in bf16)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -201,6 +339,9 @@ def main():
               "supported (this build runs on a single MI355X)",
               file=sys.stderr)
         sys.exit(2)
+    if args.offload:
+        run_offload(args)
+        return
 
     import torch
 

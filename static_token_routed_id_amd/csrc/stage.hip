@@ -14,15 +14,21 @@
 //                         total exceeds the staging capacity the plan's
 //                         status word gets kBadStage and every later kernel
 //                         of the plan does nothing;
-//   stage_copy_kernel     one workgroup per segment at a time: copies the
-//                         id's K and V rows (contiguous on both sides, read
-//                         across the host link in 16-byte pieces, many in
-//                         flight), then points the segment at its copy.
+//   stage_copy_kernel     a few workgroups, one segment each at a time:
+//                         copies the id's K and V rows (contiguous on both
+//                         sides, read across the host link in 16-byte
+//                         pieces, eight a thread in flight), then points the
+//                         segment at its copy.
 
 #include "l3_device.h"
 #include "l3_internal.h"
 
 namespace l3 {
+
+#ifndef L3_STAGE_WGS
+#define L3_STAGE_WGS 16
+#endif
+constexpr int kStageWGs = L3_STAGE_WGS;
 
 __global__ __launch_bounds__(1024) void stage_offsets_kernel(StageArgs a) {
   __shared__ int64_t s_part[1024];
@@ -72,13 +78,12 @@ __global__ __launch_bounds__(256) void stage_copy_kernel(StageArgs a) {
                                            dst * rb);
       const int64_t q = n * rb / 16;
       int64_t i = tid;
-      for (; i + 3 * 256 < q; i += 4 * 256) {
-        const u32x4 v0 = from[i], v1 = from[i + 256], v2 = from[i + 512],
-                    v3 = from[i + 768];
-        to[i] = v0;
-        to[i + 256] = v1;
-        to[i + 512] = v2;
-        to[i + 768] = v3;
+      for (; i + 7 * 256 < q; i += 8 * 256) {
+        u32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = from[i + k * 256];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) to[i + k * 256] = v[k];
       }
       for (; i < q; i += 256) to[i] = from[i];
     }
@@ -91,7 +96,10 @@ __global__ __launch_bounds__(256) void stage_copy_kernel(StageArgs a) {
 hipError_t stage_rows_launch(const StageArgs& a, int S_ub, hipStream_t s) {
   if (S_ub <= 0) return hipSuccess;
   stage_offsets_kernel<<<1, 1024, 0, s>>>(a);
-  const int grid = S_ub < 2048 ? S_ub : 2048;
+  // few workgroups (each with 32 KB of reads in flight): the host link,
+  // not the CUs, bounds the copy, and the CUs stay free for the layers the
+  // copy is meant to overlap
+  const int grid = S_ub < kStageWGs ? S_ub : kStageWGs;
   stage_copy_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
