@@ -209,6 +209,25 @@ l3_status l3_stage_rows(l3_plan_t plan, const void* K_host,
                         int64_t stage_rows, void* stream);
 
 /*
+ * l3_stage_rows_dma -- the same result as l3_stage_rows, with the copies
+ * made by the DMA engines (no compute unit is used, so the copy overlaps
+ * kernels on other streams): waits for `stream` (which the caller orders
+ * after the plan, e.g. with an event, and before nothing else it needs
+ * soon), reads the plan's segments to the host, then queues on `stream`
+ * one host-to-device copy of K rows and one of V rows per run of ids with
+ * adjacent rows, and a small kernel that points the plan at the copies.
+ * A pinned host buffer of 32 B per token is allocated with the plan on
+ * first use and freed by l3_plan_release; a later call on the plan reuses
+ * it, so calls on one plan must not overlap.
+ * Errors: as l3_stage_rows, and L3_ERR_WORKSPACE at once (nothing queued)
+ * when the rows exceed stage_rows; L3_ERR_TOKEN_RANGE / L3_ERR_COUNT for a
+ * plan that failed its device-side checks.
+ */
+l3_status l3_stage_rows_dma(l3_plan_t plan, const void* K_host,
+                            const void* V_host, void* K_stage, void* V_stage,
+                            int64_t stage_rows, void* stream);
+
+/*
  * l3_plan_check -- wait for the stream, then report the device-side
  * validation of the plan: L3_OK, L3_ERR_TOKEN_RANGE, L3_ERR_COUNT or
  * L3_ERR_WORKSPACE (staged rows beyond the staging capacity)

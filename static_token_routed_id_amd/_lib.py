@@ -65,6 +65,7 @@ def _load():
                                 P, P, P, P, P, P, c_size_t, P]),
         "l3_plan_check": (c_int, [P, P]),
         "l3_stage_rows": (c_int, [P, P, P, P, P, c_int64, P]),
+        "l3_stage_rows_dma": (c_int, [P, P, P, P, P, c_int64, P]),
         "l3_plan_export": (c_int, [P, P, P, P, P, P, P, P]),
         "l3_plan_info": (c_int, [P, POINTER(c_int64), c_int, P]),
         "l3_plan_release": (None, [P]),
@@ -85,7 +86,7 @@ EXPORTED = ("l3_workspace_size", "l3_plan", "l3_replan", "l3_forward",
             "l3_backward", "l3_plan_check", "l3_plan_export", "l3_plan_info",
             "l3_plan_release", "l3_plan_tokens", "l3_status_str",
             "l3_timing_enable", "l3_timing_read", "l3_stage_name",
-            "l3_stage_rows")
+            "l3_stage_rows", "l3_stage_rows_dma")
 
 
 def lib():
@@ -202,13 +203,15 @@ def l3_backward(plan: Plan, dy, x, K, V, W_up, gamma, beta, W_mix, save, dx,
 
 
 def l3_stage_rows(plan: Plan, K_host, V_host, K_stage, V_stage,
-                  stream=None) -> None:
+                  stream=None, dma=False) -> None:
     """Copy the batch's rows of host-resident tables into K_stage / V_stage
-    (device, capacity = K_stage's rows) and point the plan at them."""
+    (device, capacity = K_stage's rows) and point the plan at them; with
+    dma=True the DMA engines copy (the call waits for `stream`)."""
     rows = int(K_stage.shape[0]) if K_stage is not None else 0
-    _check(_lib.l3_stage_rows(plan.handle, _ptr(K_host), _ptr(V_host),
-                              _ptr(K_stage), _ptr(V_stage), rows,
-                              _stream(stream)), "l3_stage_rows")
+    fn = _lib.l3_stage_rows_dma if dma else _lib.l3_stage_rows
+    _check(fn(plan.handle, _ptr(K_host), _ptr(V_host), _ptr(K_stage),
+              _ptr(V_stage), rows, _stream(stream)),
+           "l3_stage_rows_dma" if dma else "l3_stage_rows")
 
 
 def l3_plan_check(plan: Plan, stream=None) -> int:

@@ -254,6 +254,10 @@ struct l3_plan_s {
   std::vector<const void*> saved;
   // l3_stage_rows pointed the segments at staged tables (inference only)
   bool staged = false;
+  // pinned host mirror of the segments for l3_stage_rows_dma (made on
+  // first use): S, then (row offset, rows) per segment, then staged offsets
+  int64_t* host_seg = nullptr;
+  size_t host_seg_count = 0;
 };
 
 namespace {
@@ -433,6 +437,7 @@ void l3_plan_release(l3_plan_t plan) {
     hipEventDestroy(e.a);
     hipEventDestroy(e.b);
   }
+  if (plan->host_seg) (void)hipHostFree(plan->host_seg);
   delete plan;
 }
 
@@ -505,6 +510,102 @@ l3_status l3_stage_rows(l3_plan_t plan, const void* K_host,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t S_ub = plan->B < d.vocab ? plan->B : d.vocab;
     hipError_t e = stage_rows_launch(a, static_cast<int>(S_ub), s);
+    if (e != hipSuccess) return L3_ERR_HIP;
+    plan->staged = true;
+    plan->saved.clear();
+    return finish(plan, e, s);
+  } catch (...) {
+    return L3_ERR_HIP;
+  }
+}
+
+namespace {
+__global__ void copy_i64_kernel(int64_t* dst, const int64_t* src, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+}  // namespace
+
+l3_status l3_stage_rows_dma(l3_plan_t plan, const void* K_host,
+                            const void* V_host, void* K_stage, void* V_stage,
+                            int64_t stage_rows, void* stream) {
+  try {
+    if (!plan) return L3_ERR_NULL;
+    if (plan->B == 0) return L3_OK;
+    if (!K_host || !V_host || !K_stage || !V_stage) return L3_ERR_NULL;
+    const void* K_src = nullptr;
+    const void* V_src = nullptr;
+    if (!device_readable(K_host, &K_src) || !device_readable(V_host, &V_src))
+      return L3_ERR_NULL;
+    if (stage_rows < 0) return L3_ERR_SHAPE;
+    if (plan->staged) return L3_ERR_STATE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const l3_desc& d = plan->desc;
+    const int64_t B = plan->B;
+    const size_t need = static_cast<size_t>(4 * B + 2);
+    if (plan->host_seg_count < need) {
+      if (plan->host_seg) (void)hipHostFree(plan->host_seg);
+      plan->host_seg = nullptr;
+      plan->host_seg_count = 0;
+      if (hipHostMalloc(reinterpret_cast<void**>(&plan->host_seg),
+                        need * sizeof(int64_t), hipHostMallocDefault) !=
+          hipSuccess)
+        return L3_ERR_HIP;
+      plan->host_seg_count = need;
+    }
+    int64_t* h = plan->host_seg;
+    const PlanDev& pd = plan->dev;
+    // the segments, once the plan is done (the caller orders `stream` after
+    // the plan, e.g. with an event)
+    int32_t hdr[2] = {0, 0};
+    hipError_t e = hipMemcpyAsync(hdr, pd.header, sizeof(hdr),
+                                  hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(h + 2, pd.seg_row_off, B * sizeof(int64_t),
+                         hipMemcpyDeviceToHost, s);
+    std::vector<int32_t> n_host(static_cast<size_t>(B));
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(n_host.data(), pd.seg_n, B * sizeof(int32_t),
+                         hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return L3_ERR_HIP;
+    if (hdr[0] & kBadId) return L3_ERR_TOKEN_RANGE;
+    if (hdr[0] & kBadCount) return L3_ERR_COUNT;
+    if (hdr[0] != 0) return L3_ERR_STATE;
+    const int S = hdr[1];
+    const int64_t* src = h + 2;
+    int64_t* staged = h + 2 + B;
+    int64_t total = 0;
+    for (int g = 0; g < S; ++g) {
+      staged[g] = total;
+      total += n_host[g];
+    }
+    if (total > stage_rows) return L3_ERR_WORKSPACE;
+    const int64_t es = static_cast<int64_t>(elem_bytes(d.dtype));
+    const int64_t kb = d.d * es, vb = d.d_e * es;
+    // one DMA copy per run of ids whose rows are adjacent in the table
+    for (int g = 0; g < S && e == hipSuccess;) {
+      int g1 = g + 1;
+      while (g1 < S && src[g1] == src[g1 - 1] + n_host[g1 - 1]) ++g1;
+      const int64_t rows = staged[g1 - 1] + n_host[g1 - 1] - staged[g];
+      e = hipMemcpyAsync(static_cast<uint8_t*>(K_stage) + staged[g] * kb,
+                         static_cast<const uint8_t*>(K_host) + src[g] * kb,
+                         rows * kb, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(static_cast<uint8_t*>(V_stage) + staged[g] * vb,
+                           static_cast<const uint8_t*>(V_host) + src[g] * vb,
+                           rows * vb, hipMemcpyHostToDevice, s);
+      g = g1;
+    }
+    // the plan's row offsets now point into the staged tables (a kernel
+    // reading the pinned mirror: no memset or copy node in the stream)
+    if (e == hipSuccess) {
+      const void* staged_dev = nullptr;
+      if (!device_readable(staged, &staged_dev)) return L3_ERR_HIP;
+      copy_i64_kernel<<<(S + 255) / 256, 256, 0, s>>>(
+          pd.seg_row_off, static_cast<const int64_t*>(staged_dev), S);
+      e = hipGetLastError();
+    }
     if (e != hipSuccess) return L3_ERR_HIP;
     plan->staged = true;
     plan->saved.clear();

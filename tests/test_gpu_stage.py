@@ -19,7 +19,7 @@ def _host_copy(a: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(a)).pin_memory()
 
 
-def _stage_forward(w, dev, stage_rows, K_host, V_host):
+def _stage_forward(w, dev, stage_rows, K_host, V_host, dma=False):
     torch = gu.torch_cuda()
     L = gu.lib()
     desc = gu.desc_of(w)
@@ -31,7 +31,7 @@ def _stage_forward(w, dev, stage_rows, K_host, V_host):
                           device="cuda")
     V_stage = torch.empty((stage_rows, w.spec.d_e), dtype=dev.V.dtype,
                           device="cuda")
-    L.l3_stage_rows(plan, K_host, V_host, K_stage, V_stage)
+    L.l3_stage_rows(plan, K_host, V_host, K_stage, V_stage, dma=dma)
     y = torch.full((w.batch, w.spec.d), float("nan"), dtype=torch.float32,
                    device="cuda")
     L.l3_forward(plan, dev.x, K_stage, V_stage, dev.W_up, dev.gamma,
@@ -40,8 +40,9 @@ def _stage_forward(w, dev, stage_rows, K_host, V_host):
     return plan, y, (pws, scr, K_stage, V_stage)
 
 
+@pytest.mark.parametrize("dma", [False, True])
 @pytest.mark.parametrize("name", ["decode_bf16", "prefill_bf16", "tiny_fp32"])
-def test_staged_forward_equals_device_tables(name):
+def test_staged_forward_equals_device_tables(name, dma):
     torch = gu.torch_cuda()
     L = gu.lib()
     w = gu.workload(name)
@@ -50,7 +51,7 @@ def test_staged_forward_equals_device_tables(name):
     K_host, V_host = _host_copy(w.K), _host_copy(w.V)
     u = np.unique(w.ids)
     rows = int((w.offsets[u + 1] - w.offsets[u]).sum())
-    plan, y, _keep = _stage_forward(w, dev, rows, K_host, V_host)
+    plan, y, _keep = _stage_forward(w, dev, rows, K_host, V_host, dma)
     assert L.l3_plan_check(plan) == L.L3_OK
     assert torch.equal(y, ref)
 
@@ -101,3 +102,16 @@ def test_stage_errors():
     torch.cuda.synchronize()
     assert L.l3_plan_check(plan) == L.L3_OK
     assert torch.equal(y2, y)
+
+
+def test_stage_dma_capacity_error():
+    """The DMA path knows the row count on the host: too small a staging
+    table is refused before anything is queued."""
+    torch = gu.torch_cuda()
+    L = gu.lib()
+    w = gu.workload("decode_bf16")
+    dev = gu.Dev(w)
+    K_host, V_host = _host_copy(w.K), _host_copy(w.V)
+    with pytest.raises(L.L3Error) as e:
+        _stage_forward(w, dev, 16, K_host, V_host, dma=True)
+    assert e.value.status == L.L3_ERR_WORKSPACE
