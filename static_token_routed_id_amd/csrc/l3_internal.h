@@ -21,8 +21,10 @@ constexpr int kGroupTok = 64;
 // Ids of the group kernel with more than kGroupTok tokens are cut into
 // items of this many tokens (K_t and V_t are read once per item).
 constexpr int kHotTok = 128;
-// Largest batch sorted by the single-workgroup plan kernel.
-constexpr int kSmallPlanMax = 8192;
+// Largest batch sorted by the single-workgroup plan kernel (measured: at
+// 4096 tokens both paths take 0.053 ms, at 8192 the radix path 0.055 ms
+// against 0.10).
+constexpr int kSmallPlanMax = 4096;
 // Elements per block of the multi-kernel radix sort.
 constexpr int kSortTile = 1024;
 

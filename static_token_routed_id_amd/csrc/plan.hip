@@ -10,7 +10,7 @@
 //
 // The sort key is (id, position), unique, so every correct sort gives the
 // same permutation. Two implementations:
-//   * batches up to 8192 tokens: one 1024-thread workgroup, bitonic sort of
+//   * batches up to 4096 tokens: one 1024-thread workgroup, bitonic sort of
 //     64-bit keys in LDS, then segment cut and work-item count in the same
 //     launch (one launch: decode-sized batches are latency bound);
 //   * larger batches: LSD radix sort of the 32-bit ids with the position as

@@ -1,7 +1,8 @@
 """GPU plan (sort by id + segments) against the oracle, bit for bit.
 
-Covers both device paths: the single-workgroup sort (up to 8192 tokens) and
-the multi-kernel radix sort (larger batches, 1 to 3 digit passes)."""
+Covers both device paths: the single-workgroup sort (up to 4096 tokens) and
+the multi-kernel radix sort (larger batches, 1 to 3 digit passes), with
+batches on both sides of the boundary."""
 import numpy as np
 import pytest
 
@@ -52,7 +53,12 @@ ADVERSARIAL = {
     "all_same_small": lambda: (np.full(3000, 7, np.int32), 50),
     "all_same_large": lambda: (np.full(20000, 7, np.int32), 50),
     "all_distinct_small": lambda: (
-        np.random.default_rng(1).permutation(8192).astype(np.int32), 8192),
+        np.random.default_rng(1).permutation(4096).astype(np.int32), 4096),
+    "all_distinct_8192": lambda: (
+        np.random.default_rng(8).permutation(8192).astype(np.int32), 8192),
+    "ragged_4097": lambda: (
+        np.random.default_rng(9).integers(0, 3000, 4097).astype(np.int32),
+        3000),
     "all_distinct_large": lambda: (
         np.random.default_rng(2).permutation(40000).astype(np.int32), 40000),
     "max_id_only": lambda: (np.full(17, 99, np.int32), 100),
