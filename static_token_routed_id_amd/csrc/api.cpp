@@ -150,12 +150,21 @@ SaveBufs carve_save(Carver& c, const l3_desc& d, int64_t B) {
   return s;
 }
 
+// Room for split-K partials: eight d x max(d, d_e) products, at most 16 MB.
+int64_t gpart_floats_for(const l3_desc& d) {
+  const int64_t w = static_cast<int64_t>(d.d) * (d.d > d.d_e ? d.d : d.d_e);
+  const int64_t f = 8 * w;
+  return f < (int64_t(1) << 22) ? f : (int64_t(1) << 22);
+}
+
 struct FwdBufs {
   void* a_act;  // [B x d_e] dtype
   float* U;     // [B x d]
   void* h_act;  // [B x d] dtype
   float* part;
   float* part_ml;
+  float* gpart;  // split-K partial products of small-batch GEMMs
+  int64_t gpart_floats;
 };
 FwdBufs carve_fwd(Carver& c, const l3_desc& d, int64_t B) {
   FwdBufs f;
@@ -171,6 +180,9 @@ FwdBufs carve_fwd(Carver& c, const l3_desc& d, int64_t B) {
     f.part = nullptr;
     f.part_ml = nullptr;
   }
+  // small batches split K of the projections (few output tiles)
+  f.gpart_floats = B < 1024 ? gpart_floats_for(d) : 0;
+  f.gpart = f.gpart_floats ? c.take<float>(f.gpart_floats) : nullptr;
   return f;
 }
 
@@ -184,12 +196,7 @@ struct BwdBufs {
   float* gpart;    // split-K partial products of the weight gradients
   int64_t gpart_floats;
 };
-// Room for split-K partials: eight d x max(d, d_e) products, at most 16 MB.
-int64_t gpart_floats_for(const l3_desc& d) {
-  const int64_t w = static_cast<int64_t>(d.d) * (d.d > d.d_e ? d.d : d.d_e);
-  const int64_t f = 8 * w;
-  return f < (int64_t(1) << 22) ? f : (int64_t(1) << 22);
-}
+
 // Row stride of the segment backward's p / dS arrays: k_max rounded up to
 // its 64-row blocks.
 int bwd_kst(const l3_desc& d) { return (d.k_max + 63) / 64 * 64; }
@@ -802,7 +809,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     {
       StageTimer t(plan, ST_UP, s);
       if (u_bf16)
-        e = gemm_nt_mfma_launch(up, kBF16, s);
+        e = gemm_nt_mfma_launch(up, kBF16, s, f.gpart, f.gpart_floats);
       else
         e = gemm_launch(up, save ? kF32 : d.dtype, d.dtype, kF32, s);
     }
@@ -857,7 +864,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     {
       StageTimer t(plan, ST_MIX, s);
       if (d.dtype == L3_BF16 && gemm_nt_mfma_ok(mx))
-        e = gemm_nt_mfma_launch(mx, d.y_dtype, s);
+        e = gemm_nt_mfma_launch(mx, d.y_dtype, s, f.gpart, f.gpart_floats);
       else
         e = gemm_launch(mx, d.dtype, d.dtype, d.y_dtype, s);
     }

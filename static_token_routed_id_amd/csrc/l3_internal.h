@@ -218,7 +218,9 @@ hipError_t seg_group_launch(const SegGroupArgs& a, int items_ub,
 hipError_t gemm_launch(const GemmArgs& g, int a_type, int b_type, int c_type,
                        hipStream_t s, float* part = nullptr,
                        int64_t part_floats = 0);
-hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s);
+hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s,
+                               float* part = nullptr,
+                               int64_t part_floats = 0);
 bool gemm_nt_mfma_ok(const GemmArgs& g);
 // The 256 x 256 tile kernel (needed for the row-statistics epilogue).
 bool gemm_nt_256_ok(const GemmArgs& g);
