@@ -38,6 +38,9 @@
 
 namespace l3 {
 
+// Most row chunks of one id: k_max <= 512 rows in chunks of >= 32.
+constexpr int kMaxChunks = 16;
+
 template <bool BF16, int EPL, bool P32>
 __global__ __launch_bounds__(256, 2) void seg_fwd_kernel(SegFwdArgs a) {
   typedef typename Types<BF16, P32>::P PT;
@@ -75,21 +78,51 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(CombineArgs a) {
   const int nch = ceil_div(n_rows, a.chunk_rows);
   if (nch <= 1) return;
   const int64_t slot0 = static_cast<int64_t>(pos) * a.nch_max;
+  // chunk weights w_c = e^(m_c - M) / L, all chunks' loads issued together
+  float m[kMaxChunks], l[kMaxChunks], w[kMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    m[c] = -INFINITY;
+    l[c] = 0.f;
+    if (c < nch) {
+      const float2 v =
+          *reinterpret_cast<const float2*>(a.part_ml + (slot0 + c) * 2);
+      m[c] = v.x;
+      l[c] = v.y;
+    }
+  }
   float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, a.part_ml[(slot0 + c) * 2]);
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, m[c]);
   float L = 0.f;
-  for (int c = 0; c < nch; ++c)
-    L += a.part_ml[(slot0 + c) * 2 + 1] * __expf(a.part_ml[(slot0 + c) * 2] - M);
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    w[c] = c < nch ? __expf(m[c] - M) : 0.f;
+    L += l[c] * w[c];
+  }
   const float invL = 1.0f / L;
   const int64_t orig = a.perm[pos];
-  for (int e = lane; e < a.d_e; e += 64) {
-    float acc = 0.f;
-    for (int c = 0; c < nch; ++c)
-      acc += a.part[(slot0 + c) * a.d_e + e] *
-             __expf(a.part_ml[(slot0 + c) * 2] - M);
-    const float v = acc * invL;
-    st<T>(static_cast<T*>(a.a_out), orig * a.d_e + e, v);
-    if (a.a_save) a.a_save[orig * a.d_e + e] = v;
+  // 4 columns a lane, the chunks' partial rows loaded together
+  for (int e = lane * 4; e < a.d_e; e += 256) {
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      if (c < nch) {
+        const float4 v = *reinterpret_cast<const float4*>(
+            a.part + (slot0 + c) * a.d_e + e);
+        acc.x = fmaf(v.x, w[c], acc.x);
+        acc.y = fmaf(v.y, w[c], acc.y);
+        acc.z = fmaf(v.z, w[c], acc.z);
+        acc.w = fmaf(v.w, w[c], acc.w);
+      }
+    }
+    const float o[4] = {acc.x * invL, acc.y * invL, acc.z * invL,
+                        acc.w * invL};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      st<T>(static_cast<T*>(a.a_out), orig * a.d_e + e + q, o[q]);
+      if (a.a_save) a.a_save[orig * a.d_e + e + q] = o[q];
+    }
   }
 }
 
