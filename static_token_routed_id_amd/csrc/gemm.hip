@@ -197,7 +197,7 @@ hipError_t gemm_launch(const GemmArgs& g0, int a_type, int b_type, int c_type,
   const int64_t mn = static_cast<int64_t>(g.M) * g.N;
   if (part && tiles < 1024 && g.K >= 256) {
     int64_t ns = (1024 + tiles - 1) / tiles;
-    ns = std::min<int64_t>(ns, g.K / 128);
+    ns = std::min<int64_t>(ns, g.K / 64);
     ns = std::min<int64_t>(ns, part_floats / mn);
     ns = std::min<int64_t>(ns, 64);
     if (ns >= 2) {
