@@ -1,7 +1,10 @@
-// Segment forward, wave kernel: a_i = V_t^T Softmax(K_t x_i) for the tokens
-// of ids with few rows (ids with many rows in large bf16 batches go to the
-// group kernel), the batch grouped by id so that each id's rows are read
-// once per 16 tokens.
+// Segment forward, wave kernel: a_i = V_t^T Softmax(K_t x_i) for every
+// token, one wave item (segment, tile of <= 16 of its tokens, chunk of
+// <= 128 of its rows; seg_wave.h) per wavefront. It serves everything the
+// one-launch group kernel does not: float32 inputs, batches of up to 2048
+// tokens, and the saving forward of training (float32 weights). Four
+// independent wavefronts a workgroup (no workgroup barrier), items taken
+// round-robin, two workgroups a CU.
 //
 // gist.science explainer of "L^3: Large Lookup Layers", Technical Summary,
 // Core Architecture: after the static lookup of K_t and V_t, the hidden
@@ -10,29 +13,9 @@
 // Design, Batch Sorting: grouping tokens by id makes the mask
 // block-diagonal, so one block of tokens shares one read of K_t, V_t.
 //
-// Work item = (segment, tile of <= 16 of its tokens, chunk of <= 128 of its
-// rows). One wavefront owns one item at a time; the four wavefronts of a
-// workgroup are independent (no workgroup barrier), and wavefronts walk the
-// items round-robin. Many small items per compute unit give the memory
-// system many independent streams, so registers are kept low (several
-// wavefronts per SIMD).
-//   1. scores S = X K_chunk^T on 16x16 MFMA blocks, operands streamed from
-//      global memory into registers. bf16: 32-column steps (lane group g
-//      holds columns 8g .. 8g+7 of row l & 15, the MFMA's own k layout) with
-//      the next step's loads in flight during the current multiply (two
-//      register slots, loop unrolled by two). f32: 16-column steps of the
-//      16x16x4 MFMA (lane group g holds columns 4g .. 4g+3; four MFMAs, one
-//      per element, use the same lane -> k assignment for both operands);
-//   2. exact softmax over the chunk (row max and row sum across the 16 lanes
-//      holding a row), unnormalised weights to this wave's LDS (fp16 for
-//      bf16 inputs, f32 for f32 inputs), laid out [row j][token];
-//   3. aggregation acc[t][e] += p[t][j] * V[j][e] on the vector ALU: lane l
-//      owns columns e = l*EPL .. l*EPL+EPL-1 of a 64*EPL-column pass, V rows
-//      are loaded 16 at a time (coalesced) before they are used, and the
-//      token loop is bounded by the real tile size;
-//   4. single chunk: a = acc / rowsum, written in original token order;
-//      several chunks: (max, sum, acc) partials, merged by seg_combine in a
-//      fixed chunk order (exact, deterministic).
+// Ids whose rows span several chunks leave (max, sum, acc) partials per
+// chunk; seg_combine_kernel merges them per token in chunk order (exact,
+// deterministic).
 
 #include "seg_wave.h"
 

@@ -1,6 +1,25 @@
 // Wave work items of the segment forward (a_i = V_t^T Softmax(K_t x_i) for
 // up to 16 tokens of one id and up to 128 of its rows on one wavefront),
-// shared by the wave kernel and the group kernel's last pass.
+// shared by the wave kernel and the group kernel's wave-item pass.
+//
+//   1. scores S = X K_chunk^T on 16x16 MFMA blocks, operands streamed from
+//      global memory into registers. bf16: 32-column steps (lane group g
+//      holds columns 8g .. 8g+7 of row l & 15, the MFMA's own k layout)
+//      through a ring of 8 / 4 / 2 steps for chunks of <= 16 / <= 32 / more
+//      rows. f32: 16-column steps of the 16x16x4 MFMA (lane group g holds
+//      columns 4g .. 4g+3; four MFMAs, one per element, the same lane -> k
+//      assignment for both operands). A single token with d = 512, 1024 or
+//      2048 takes whole-row loads instead (scores_softmax_1tok);
+//   2. exact softmax over the chunk (row max and row sum across the 16
+//      lanes holding a row), unnormalised weights to this wave's LDS (fp16
+//      for bf16 inputs, f32 for f32 inputs and the saving forward), laid
+//      out [row j][token];
+//   3. aggregation acc[t][e] += p[t][j] * V[j][e] on the vector ALU: lane l
+//      owns columns e = l*EPL .. l*EPL+EPL-1 of a 64*EPL-column pass, V
+//      rows in two 8-row half bursts, the token loop bounded by the tile;
+//   4. single chunk: a = acc / rowsum, written in original token order
+//      (bf16 rows with streaming stores); several chunks: (max, sum, acc)
+//      partials for the combine kernel.
 //
 // gist.science explainer of "L^3: Large Lookup Layers", Technical Summary,
 // Core Architecture, Mathematical Formulation (the attention of x over

@@ -107,6 +107,10 @@ def test_plan_host_checks(L):
                           None, 0, None, 0, None) == L.L3_OK
     assert lib.l3_forward(None, None, None, None, None, None, None, None,
                           None, None, 0, None, 0, None) == L.L3_ERR_NULL
+    # staging: a NULL plan is refused; an empty batch has nothing to stage
+    for fn in (lib.l3_stage_rows, lib.l3_stage_rows_dma):
+        assert fn(None, None, None, None, None, 0, None) == L.L3_ERR_NULL
+        assert fn(out, None, None, None, None, 0, None) == L.L3_OK
     lib.l3_plan_release(out)
     lib.l3_plan_release(None)
     assert lib.l3_plan_tokens(None) == -1
