@@ -595,8 +595,7 @@ __global__ __launch_bounds__(256) void ln_apply_kernel(LnApplyArgs a) {
       const float h1 =
           __uint_as_float(gv[q] & 0xffff0000u) * ((u1 - mean) * rstd) +
           __uint_as_float(bv[q] & 0xffff0000u);
-      o[q] = static_cast<uint32_t>(f2bf(h0)) |
-             (static_cast<uint32_t>(f2bf(h1)) << 16);
+      o[q] = f2bf2(h0, h1);
     }
     // streaming store (h is read once, by the W_mix GEMM)
     __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.h + base + e0));

@@ -18,11 +18,16 @@ __device__ __forceinline__ float bf2f(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float32 -> bfloat16, round to nearest, ties to even (inputs are finite).
+// float32 -> bfloat16, round to nearest, ties to even: gfx950 converts in
+// hardware (v_cvt_pk_bf16_f32, two values an instruction).
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// Two values into one word, lo in the low half.
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Element access for the two storage types.

@@ -338,8 +338,7 @@ __device__ __forceinline__ void store_row(uint16_t* dst,
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      o[e] = static_cast<uint32_t>(f2bf(v[2 * e])) |
-             (static_cast<uint32_t>(f2bf(v[2 * e + 1])) << 16);
+      o[e] = f2bf2(v[2 * e], v[2 * e + 1]);
     __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst));
   } else {
 #pragma unroll
