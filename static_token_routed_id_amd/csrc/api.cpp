@@ -802,10 +802,69 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     up.N = d.d;
     up.K = d.d_e;
     up.header = pd.header;
-    // Inference on bf16 with an MFMA GEMM: u is written as bf16 and
-    // ln_apply normalises each row from it (statistics over the row in
-    // registers). Training and float32 keep u in float32 for the saved state.
+    // y = [h ; x] W_mix^T, the A operand switching from h to x at k = d
+    GemmArgs mx{};
+    mx.A1 = f.h_act;
+    mx.A2 = x;
+    mx.a1_m = mx.a2_m = d.d;
+    mx.a1_k = mx.a2_k = 1;
+    mx.K1 = d.d;
+    mx.Bm = W_mix;
+    mx.b_k = 1;
+    mx.b_n = 2 * static_cast<int64_t>(d.d);
+    mx.C = y;
+    mx.c_m = d.d;
+    mx.M = static_cast<int>(B);
+    mx.N = d.d;
+    mx.K = 2 * d.d;
+    mx.header = pd.header;
+    // Inference on bf16 with an MFMA GEMM: u is written as bf16. With both
+    // projections on 256 x 256 tiles, LayerNorm is folded into W_mix: the
+    // W_up epilogue writes per-row partial statistics, gamma and beta are
+    // folded into a bf16 copy of W_mix's first d columns, and W_mix reads u
+    // itself (h is never written). Otherwise ln_apply normalises each row
+    // (statistics over the row in registers). Training and float32 keep u
+    // in float32 for the saved state.
     const bool u_bf16 = !save && d.dtype == L3_BF16 && gemm_nt_mfma_ok(up);
+    const int64_t fold_w1 = static_cast<int64_t>(d.d) * d.d * 2;
+    const int64_t fold_c = static_cast<int64_t>(d.d) * 8;
+    const int64_t fold_st = B * (d.d / 256) * 8;
+    const int64_t fold_rows = B * 8;
+    const bool fold = u_bf16 && !f.gpart && d.d % 256 == 0 &&
+                      gemm_nt_256_ok(up) && gemm_nt_256_ok(mx) &&
+                      fold_w1 + fold_c + fold_st + fold_rows <= B * d.d * 2;
+    LnRowsArgs lr{};
+    if (fold) {
+      char* base = static_cast<char*>(f.h_act);
+      LnFoldArgs fa;
+      fa.header = pd.header;
+      fa.W = static_cast<const uint16_t*>(W_mix);
+      fa.w_n = 2 * static_cast<int64_t>(d.d);
+      fa.gamma = static_cast<const uint16_t*>(gamma);
+      fa.beta = static_cast<const uint16_t*>(beta);
+      fa.n = d.d;
+      fa.d = d.d;
+      fa.W1 = reinterpret_cast<uint16_t*>(base);
+      fa.c12 = reinterpret_cast<float*>(base + fold_w1);
+      float* stats = reinterpret_cast<float*>(base + fold_w1 + fold_c);
+      float* rows = reinterpret_cast<float*>(base + fold_w1 + fold_c + fold_st);
+      up.ln_stats_out = stats;
+      lr.header = pd.header;
+      lr.part = stats;
+      lr.nparts = d.d / 256;
+      lr.B = static_cast<int>(B);
+      lr.d = d.d;
+      lr.eps = d.ln_eps;
+      lr.rows = rows;
+      mx.A1 = f.U;
+      mx.B1 = fa.W1;
+      mx.b1_n = d.d;
+      mx.ln_rows = rows;
+      mx.ln_c12 = fa.c12;
+      StageTimer t(plan, ST_LN, s);
+      e = ln_fold_launch(fa, s);
+      if (e != hipSuccess) return L3_ERR_HIP;
+    }
     {
       StageTimer t(plan, ST_UP, s);
       if (u_bf16)
@@ -814,7 +873,12 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
         e = gemm_launch(up, save ? kF32 : d.dtype, d.dtype, kF32, s);
     }
     if (e != hipSuccess) return L3_ERR_HIP;
-    if (u_bf16) {
+    if (fold) {
+      StageTimer t(plan, ST_LN, s);
+      e = ln_rows_launch(lr, s);
+    }
+    if (e != hipSuccess) return L3_ERR_HIP;
+    if (u_bf16 && !fold) {
       LnApplyArgs la;
       la.header = pd.header;
       la.U = reinterpret_cast<const uint16_t*>(f.U);
@@ -845,22 +909,6 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       e = ln_launch(ln, d.dtype, s);
     }
     if (e != hipSuccess) return L3_ERR_HIP;
-    // y = [h ; x] W_mix^T, the A operand switching from h to x at k = d
-    GemmArgs mx{};
-    mx.A1 = f.h_act;
-    mx.A2 = x;
-    mx.a1_m = mx.a2_m = d.d;
-    mx.a1_k = mx.a2_k = 1;
-    mx.K1 = d.d;
-    mx.Bm = W_mix;
-    mx.b_k = 1;
-    mx.b_n = 2 * static_cast<int64_t>(d.d);
-    mx.C = y;
-    mx.c_m = d.d;
-    mx.M = static_cast<int>(B);
-    mx.N = d.d;
-    mx.K = 2 * d.d;
-    mx.header = pd.header;
     {
       StageTimer t(plan, ST_MIX, s);
       if (d.dtype == L3_BF16 && gemm_nt_mfma_ok(mx))

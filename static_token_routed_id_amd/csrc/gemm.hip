@@ -397,9 +397,13 @@ __device__ __forceinline__ void step256(floatx16 (&acc)[4][4],
   }
 }
 
-template <typename TC>
+template <typename TC, bool FOLD>
 __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
-  __shared__ uint16_t lds[2][2][kTM * kTL];
+  __shared__ __align__(16) uint16_t lds[2][2][kTM * kTL];
+  // LayerNorm fold (consumer): per tile row (rstd, -mean * rstd), per tile
+  // column (c1, c2)
+  __shared__ __align__(16) float2 s_rs[kTM];
+  __shared__ __align__(16) float2 s_c[kTN];
   if (g.header && g.header[0] != 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -432,12 +436,22 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(
       static_cast<const uint16_t*>(g.Bm) + static_cast<int64_t>(n0) * g.b_n,
       static_cast<int64_t>(kTN) * g.b_n * 2);
+  // B operand of the k < K1 part (B1 if given, else Bm)
+  const bool has_b1 = g.B1 != nullptr;
+  const int64_t b1_n = has_b1 ? g.b1_n : g.b_n;
+  const __amdgpu_buffer_rsrc_t rB1 =
+      has_b1 ? make_rsrc(static_cast<const uint16_t*>(g.B1) +
+                             static_cast<int64_t>(n0) * b1_n,
+                         static_cast<int64_t>(kTN) * b1_n * 2)
+             : rB;
   const int vA1 = static_cast<int>((lr * g.a1_m + lc) * 2);
   const int vA2 = static_cast<int>((lr * g.a2_m + lc) * 2);
   const int vB = static_cast<int>((lr * g.b_n + lc) * 2);
+  const int vB1 = static_cast<int>((lr * b1_n + lc) * 2);
   const int qA1 = static_cast<int>(32 * g.a1_m * 2);
   const int qA2 = static_cast<int>(32 * g.a2_m * 2);
   const int qB = static_cast<int>(32 * g.b_n * 2);
+  const int qB1 = static_cast<int>(32 * b1_n * 2);
   auto slice_src = [&](int k0) {
     SliceSrc s;
     const bool first = k0 < g.K1;
@@ -445,12 +459,22 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
     s.va = first ? vA1 : vA2;
     s.qa = first ? qA1 : qA2;
     s.ka = (first ? k0 : k0 - g.K1) * 2;
-    s.rb = rB;
-    s.vb = vB;
-    s.qb = qB;
+    s.rb = first ? rB1 : rB;
+    s.vb = first ? vB1 : vB;
+    s.qb = first ? qB1 : qB;
     s.kb = k0 * 2;
     return s;
   };
+
+  // LayerNorm fold (consumer): the row's (rstd, -mean * rstd) and the
+  // column's (c1, c2), loaded before the first operand slice
+  constexpr bool fold = FOLD;
+  float2 lnr = make_float2(0.f, 0.f), lnc = make_float2(0.f, 0.f);
+  if constexpr (FOLD) {
+    if (m0 + tid < g.M)
+      lnr = reinterpret_cast<const float2*>(g.ln_rows)[m0 + tid];
+    lnc = reinterpret_cast<const float2*>(g.ln_c12)[n0 + tid];
+  }
 
   u32x4 ra[8], rb[8];
   auto load_all = [&](const SliceSrc& s) {
@@ -479,6 +503,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
     *reinterpret_cast<u32x4*>(&lds[0][0][woff + q * 32 * kTL]) = ra[q];
     *reinterpret_cast<u32x4*>(&lds[0][1][woff + q * 32 * kTL]) = rb[q];
   }
+  if constexpr (FOLD) {
+    s_rs[tid] = lnr;
+    s_c[tid] = lnc;
+  }
   load_all(slice_src(min(1, nk - 1) * kTK));
   __syncthreads();
   Frag256 F0, F1;
@@ -487,7 +515,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
     F0.a[i] = *reinterpret_cast<const u32x4*>(&lds[0][0][aoff + i * 32 * kTL]);
     F0.b[i] = *reinterpret_cast<const u32x4*>(&lds[0][1][boff + i * 32 * kTL]);
   }
-  for (int it = 0; it < nk; ++it) {
+  auto kslice = [&](int it) __attribute__((always_inline)) {
     const int buf = it & 1;
     // slice it+1 (in registers) goes to the other buffer, slice it+2 is
     // fetched (clamped: the tail refetches the last slice, never read)
@@ -502,10 +530,51 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
     __syncthreads();
     step256<true, 0, 0, 16>(acc, F1, F0, &lds[buf ^ 1][0][aoff],
                             &lds[buf ^ 1][1][boff], 0, ra, rb, wra, wrb, src);
+  };
+  // with the fold, the k < K1 part runs first, then the accumulators take
+  // the LayerNorm terms, then the rest
+  const int nk1 = FOLD ? g.K1 / kTK : nk;
+  int it = 0;
+  for (; it < nk1; ++it) kslice(it);
+  if constexpr (FOLD) {
+    // acc = rstd * acc - mean * rstd * c1 + c2, four rows of a 32 x 32
+    // block at a time; each value is moved out of its AGPR and back by
+    // explicit moves (left to the register allocator, the rescaled values
+    // crowd the VGPRs and spill)
+    float2 c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = s_c[wn * 128 + j * 32 + r];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int eg = 0; eg < 4; ++eg) {
+        // rows wm*128 + i*32 + 8*eg + h .. +3 (h = 0 or 4 by lane half)
+        const float4* rs4 = reinterpret_cast<const float4*>(
+            &s_rs[wm * 128 + i * 32 + 8 * eg + (lane >> 5) * 4]);
+        const float4 r01 = rs4[0], r23 = rs4[1];
+        const float ra4[4] = {r01.x, r01.z, r23.x, r23.z};
+        const float rb4[4] = {r01.y, r01.w, r23.y, r23.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int ee = 0; ee < 4; ++ee) {
+            float v;
+            asm volatile("v_accvgpr_read_b32 %0, %1"
+                         : "=v"(v)
+                         : "a"(acc[i][j][4 * eg + ee]));
+            v = fmaf(ra4[ee], v, fmaf(rb4[ee], c[j].x, c[j].y));
+            float o;
+            asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(o) : "v"(v));
+            acc[i][j][4 * eg + ee] = o;
+          }
+        }
+      }
   }
+  for (; it < nk; ++it) kslice(it);
+
+  const int h4 = (lane >> 5) * 4;
 
   TC* C = static_cast<TC*>(g.C);
-  const int h4 = (lane >> 5) * 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -526,6 +595,57 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
               f2bf(acc[i][j][e]), reinterpret_cast<uint16_t*>(crow) + j * 32);
       }
     }
+  }
+
+  if (!FOLD && g.ln_stats_out) {
+    // LayerNorm fold (producer): sum and sum of squares of each tile row
+    // over the tile's 256 columns, then (mean, M2 = sum of squares - sum *
+    // mean) in float32 (one pass; M2 is exact to float32 rounding of the
+    // sums while |mean| / std stays well below 2^12). Each lane first adds
+    // up its four columns of a row; the 64 lane sums of a row (32 lanes x
+    // 2 waves) meet in LDS as [slot][row] (row stride padded by 4 floats:
+    // the float4 writes of 8 lanes fall in distinct banks) and one thread
+    // a row adds them up.
+    constexpr int kSP = kTM + 4;
+    float* sp = reinterpret_cast<float*>(&lds[0][0][0]);
+    float* sq = sp + 64 * kSP;
+    const int wo = (wn * 32 + r) * kSP + wm * 128 + h4;
+    __syncthreads();  // every wave is done with the operand buffers
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int eg = 0; eg < 4; ++eg) {
+        float4 v, w;
+        float* vp = reinterpret_cast<float*>(&v);
+        float* wp = reinterpret_cast<float*>(&w);
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) {
+          float a = 0.f, b = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x = acc[i][j][4 * eg + ee];
+            a += x;
+            b = fmaf(x, x, b);
+          }
+          vp[ee] = a;
+          wp[ee] = b;
+        }
+        *reinterpret_cast<float4*>(sp + wo + i * 32 + 8 * eg) = v;
+        *reinterpret_cast<float4*>(sq + wo + i * 32 + 8 * eg) = w;
+      }
+    __syncthreads();
+    float sum = 0.f, sum2 = 0.f;
+#pragma unroll 16
+    for (int sl = 0; sl < 64; ++sl) {
+      sum += sp[sl * kSP + tid];
+      sum2 += sq[sl * kSP + tid];
+    }
+    const float mean = sum * (1.0f / kTN);
+    const float m2 = fmaxf(sum2 - sum * mean, 0.f);
+    if (m0 + tid < g.M)
+      reinterpret_cast<float2*>(g.ln_stats_out)[static_cast<int64_t>(m0 + tid) *
+                                                    nt + n_tile] =
+          make_float2(mean, m2);
   }
 }
 
@@ -608,6 +728,86 @@ hipError_t ln_apply_launch(const LnApplyArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------- LayerNorm fold into W_mix ---
+// LayerNorm followed by a product, sum_k W[n, k] h[m, k] with
+// h = gamma * (u - mean) * rstd + beta, equals
+//   rstd * (sum_k W1[n, k] u[m, k] - mean * c1[n]) + c2[n],
+//   W1[n, k] = W[n, k] gamma[k], c1[n] = sum_k W1[n, k],
+//   c2[n] = sum_k W[n, k] beta[k].
+// W1 is rounded to bf16 (the GEMM operand) and c1 is summed from the rounded
+// values, so the mean term cancels against the rounded product exactly (up
+// to float32 rounding): the error follows the deviations u - mean, not u.
+// One wave per output column n, 8 elements a lane and step.
+__global__ __launch_bounds__(256) void ln_fold_kernel(LnFoldArgs a) {
+  if (a.header[0] != 0) return;
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= a.n) return;
+  const uint16_t* w = a.W + static_cast<int64_t>(n) * a.w_n;
+  uint16_t* w1 = a.W1 + static_cast<int64_t>(n) * a.d;
+  float c1 = 0.f, c2 = 0.f;
+  for (int e0 = lane * 8; e0 < a.d; e0 += 512) {
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(w + e0);
+    const u32x4 gv = *reinterpret_cast<const u32x4*>(a.gamma + e0);
+    const u32x4 bv = *reinterpret_cast<const u32x4*>(a.beta + e0);
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float w0 = __uint_as_float(wv[q] << 16);
+      const float w1v = __uint_as_float(wv[q] & 0xffff0000u);
+      o[q] = f2bf2(w0 * __uint_as_float(gv[q] << 16),
+                   w1v * __uint_as_float(gv[q] & 0xffff0000u));
+      c1 += __uint_as_float(o[q] << 16) + __uint_as_float(o[q] & 0xffff0000u);
+      c2 = fmaf(w0, __uint_as_float(bv[q] << 16), c2);
+      c2 = fmaf(w1v, __uint_as_float(bv[q] & 0xffff0000u), c2);
+    }
+    *reinterpret_cast<u32x4*>(w1 + e0) = o;
+  }
+  c1 = wave_sum(c1);
+  c2 = wave_sum(c2);
+  if (lane == 0) {
+    a.c12[2 * n] = c1;
+    a.c12[2 * n + 1] = c2;
+  }
+}
+
+hipError_t ln_fold_launch(const LnFoldArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  ln_fold_kernel<<<ceil_div(a.n, 4), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// Per row: Chan's combination of the nparts equal-sized (256-column)
+// partial (mean, M2) pairs of the W_up epilogue: mean of the means,
+// M2 = sum of the parts' M2 + 256 * sum of squared deviations of the part
+// means; biased variance M2 / d; out (rstd, -mean * rstd).
+__global__ __launch_bounds__(256) void ln_rows_kernel(LnRowsArgs a) {
+  if (a.header[0] != 0) return;
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row >= a.B) return;
+  const float2* p =
+      reinterpret_cast<const float2*>(a.part) + static_cast<int64_t>(row) * a.nparts;
+  float mean = 0.f;
+  for (int q = 0; q < a.nparts; ++q) mean += p[q].x;
+  mean /= a.nparts;
+  float m2 = 0.f, dev = 0.f;
+  for (int q = 0; q < a.nparts; ++q) {
+    const float2 v = p[q];
+    const float c = v.x - mean;
+    m2 += v.y;
+    dev = fmaf(c, c, dev);
+  }
+  m2 = fmaf(256.0f, dev, m2);
+  const float rstd = 1.0f / sqrtf(m2 / a.d + a.eps);
+  reinterpret_cast<float2*>(a.rows)[row] = make_float2(rstd, -mean * rstd);
+}
+
+hipError_t ln_rows_launch(const LnRowsArgs& a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  ln_rows_kernel<<<ceil_div(a.B, 256), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 bool gemm_nt_mfma_ok(const GemmArgs& g) {
   return g.M > 0 && g.N % kBN == 0 && g.K % kBK == 0 && g.K1 % kBK == 0 &&
          g.a1_k == 1 && g.a2_k == 1 && g.b_k == 1 && g.a1_m % 8 == 0 &&
@@ -638,10 +838,15 @@ hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s,
     return gemm_launch(g, kBF16, kBF16, c_type, s, part, part_floats);
   if (gemm_nt_256_ok(g)) {
     const int grid = static_cast<int>(tiles256);
-    if (c_type == kBF16)
-      gemm_nt_256_kernel<uint16_t><<<grid, 256, 0, s>>>(g);
+    // the LayerNorm fold (consumer side) has its own instantiation
+    if (c_type == kBF16 && g.ln_rows)
+      gemm_nt_256_kernel<uint16_t, true><<<grid, 256, 0, s>>>(g);
+    else if (c_type == kBF16)
+      gemm_nt_256_kernel<uint16_t, false><<<grid, 256, 0, s>>>(g);
+    else if (g.ln_rows)
+      gemm_nt_256_kernel<float, true><<<grid, 256, 0, s>>>(g);
     else
-      gemm_nt_256_kernel<float><<<grid, 256, 0, s>>>(g);
+      gemm_nt_256_kernel<float, false><<<grid, 256, 0, s>>>(g);
     return hipGetLastError();
   }
   dim3 grid(g.N / kBN, ceil_div(g.M, kBM));

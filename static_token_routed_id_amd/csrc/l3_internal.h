@@ -137,6 +137,42 @@ struct GemmArgs {
   // products in part (nsplit of them), summed in order by a second kernel
   float* part = nullptr;
   int nsplit = 1;
+  // 256 x 256 kernel only: LayerNorm folded into the GEMM that consumes
+  // its output (h = gamma * (u - mean) * rstd + beta, then y = [h ; x] W^T):
+  //   producer (u = a W_up^T): ln_stats_out[m * (N / 256) + t] = (mean, M2)
+  //     of row m over the 256 columns of tile t (float32 pairs);
+  //   consumer (y): for k < K1 the B operand is B1 (row stride b1_n), W with
+  //     gamma folded in; ln_rows[m] = (rstd, -mean * rstd) of row m and
+  //     ln_c12[n] = (c1, c2) the folded column sums; after the k < K1 part,
+  //     acc = rstd * acc - mean * rstd * c1 + c2.
+  const void* B1 = nullptr;
+  int64_t b1_n = 0;
+  float* ln_stats_out = nullptr;
+  const float* ln_rows = nullptr;
+  const float* ln_c12 = nullptr;
+};
+
+// Row statistics of the fold from the producer's partials.
+struct LnRowsArgs {
+  const int32_t* header;
+  const float* part;   // [B x nparts] (mean, M2) pairs over 256 columns
+  int nparts, B, d;
+  float eps;
+  float* rows;         // [B] (rstd, -mean * rstd) pairs
+};
+
+// Fold of LayerNorm's affine into the first K1 columns of W_mix (rows of W
+// have stride w_n): W1[n, k] = bf16(W[n, k] * gamma[k]) for k < d,
+// c12[n] = (sum_k W1[n, k], sum_k W[n, k] * beta[k]) in float32.
+struct LnFoldArgs {
+  const int32_t* header;
+  const uint16_t* W;
+  int64_t w_n;
+  const uint16_t* gamma;
+  const uint16_t* beta;
+  int n, d;
+  uint16_t* W1;     // [n x d] bf16
+  float* c12;       // [n x 2]
 };
 
 // LayerNorm of float32 rows (one wave per row).
@@ -153,8 +189,7 @@ struct LnArgs {
   float* rstd_save;
 };
 
-// LayerNorm applied to bf16 rows whose per-128-column (mean, M2) partials
-// were written by the producing GEMM.
+// LayerNorm of bf16 rows (statistics from the row itself), h in bf16.
 struct LnApplyArgs {
   const int32_t* header;
   const uint16_t* U;       // [B x d] bf16
@@ -222,8 +257,11 @@ hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s,
                                float* part = nullptr,
                                int64_t part_floats = 0);
 bool gemm_nt_mfma_ok(const GemmArgs& g);
-// The 256 x 256 tile kernel (needed for the row-statistics epilogue).
+// The 256 x 256 tile kernel (the only one with the LayerNorm fold); the
+// launcher above takes it for these shapes when no split-K buffer is given.
 bool gemm_nt_256_ok(const GemmArgs& g);
+hipError_t ln_fold_launch(const LnFoldArgs& a, hipStream_t s);
+hipError_t ln_rows_launch(const LnRowsArgs& a, hipStream_t s);
 hipError_t ln_apply_launch(const LnApplyArgs& a, hipStream_t s);
 hipError_t ln_launch(const LnArgs& a, int dtype, hipStream_t s);
 

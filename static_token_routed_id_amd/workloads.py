@@ -334,6 +334,18 @@ def layer_params(w: Workload, layer: int,
     return dataclasses.replace(w, K=K, V=V, W_up=W_up, W_mix=W_mix)
 
 
+def with_u_offset(w: Workload, ratio: float) -> Workload:
+    """Same inputs, W_up + ratio * 1 w0^T with w0 ~ N(0, 1/d_e) from a stream
+    of its own: every row of W_up gains the same vector, so each token's
+    up-projection gains one common value (a . w0 * ratio) over all d
+    columns, about `ratio` times the spread of its other entries. A LayerNorm
+    input far from zero mean, for checking how the normalisation copes."""
+    spec, dt = w.spec, w.spec.dtype
+    w0 = _rng(w.cfg, S_WUP + 8).standard_normal(spec.d_e) / np.sqrt(spec.d_e)
+    W_up = decode(w.W_up) + ratio * np.outer(np.ones(spec.d), w0)
+    return dataclasses.replace(w, W_up=store(W_up, dt))
+
+
 def with_ids(w: Workload, ids: np.ndarray, x: Optional[np.ndarray] = None,
              dy: Optional[np.ndarray] = None) -> Workload:
     """Same tables and weights, a different id stream (and optionally x, dy)."""

@@ -51,3 +51,14 @@ def test_bf16_rounding_matches_torch():
     back = wl.bf16_bits_to_f32(mine)
     assert np.array_equal(back, torch.from_numpy(v).to(torch.bfloat16)
                           .float().numpy())
+
+
+def test_u_offset_is_a_common_row():
+    """with_u_offset adds the same vector to every row of W_up (up to the
+    storage rounding) and leaves every other input alone."""
+    w = wl.make("tiny_fp32")
+    w2 = wl.with_u_offset(w, 50.0)
+    diff = wl.decode(w2.W_up) - wl.decode(w.W_up)
+    assert np.abs(diff - diff[0]).max() <= 1e-5 * np.abs(diff).max()
+    assert np.abs(diff[0]).max() > 1.0
+    assert w2.x is w.x and w2.K is w.K and w2.W_mix is w.W_mix
