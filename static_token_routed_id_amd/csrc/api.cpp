@@ -157,6 +157,17 @@ int64_t gpart_floats_for(const l3_desc& d) {
   return f < (int64_t(1) << 22) ? f : (int64_t(1) << 22);
 }
 
+// Split-K partials of the bf16 weight-gradient GEMMs of dW_mix (d x d
+// outputs on 256 x 256 tiles, up to 16 shares so that about 256 workgroups
+// run); 0 where those GEMMs do not apply.
+int64_t splitk_floats_for(const l3_desc& d) {
+  if (d.dtype != L3_BF16 || d.d % 256 != 0 || d.d < 1024) return 0;
+  const int64_t tiles = static_cast<int64_t>(d.d / 256) * (d.d / 256);
+  int64_t ns = (256 + tiles - 1) / tiles;
+  if (ns > 16) ns = 16;
+  return ns > 1 ? ns * d.d * d.d : 0;
+}
+
 struct FwdBufs {
   void* a_act;  // [B x d_e] dtype
   float* U;     // [B x d]
@@ -195,6 +206,10 @@ struct BwdBufs {
   float* ln_part;  // [ceil(B / 256) x 2 x d] dgamma / dbeta partials
   float* gpart;    // split-K partial products of the weight gradients
   int64_t gpart_floats;
+  uint16_t* wmixT;  // [2d x d] W_mix transposed (bf16 only)
+  uint16_t* dyT;    // [d x B] dY transposed (bf16 only)
+  uint16_t* xT;     // [d x B] x transposed (bf16 only)
+  uint16_t* hT;     // [d x 2B] saved h transposed, bf16 hi | lo (bf16 only)
 };
 
 // Row stride of the segment backward's p / dS arrays: k_max rounded up to
@@ -208,8 +223,14 @@ BwdBufs carve_bwd(Carver& c, const l3_desc& d, int64_t B) {
   b.P = c.take<float>(B * bwd_kst(d));
   b.dS = c.take<float>(B * bwd_kst(d));
   b.ln_part = c.take<float>((B + 255) / 256 * 2 * d.d);
-  b.gpart_floats = gpart_floats_for(d);
+  b.gpart_floats = std::max(gpart_floats_for(d), splitk_floats_for(d));
   b.gpart = c.take<float>(b.gpart_floats);
+  const bool b16 = d.dtype == L3_BF16;
+  b.wmixT = b16 ? c.take<uint16_t>(static_cast<size_t>(2) * d.d * d.d)
+                : nullptr;
+  b.dyT = b16 ? c.take<uint16_t>(static_cast<size_t>(B) * d.d) : nullptr;
+  b.xT = b16 ? c.take<uint16_t>(static_cast<size_t>(B) * d.d) : nullptr;
+  b.hT = b16 ? c.take<uint16_t>(static_cast<size_t>(2) * B * d.d) : nullptr;
   return b;
 }
 
@@ -976,7 +997,37 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
     const int64_t D = d.d, DE = d.d_e;
     {
       StageTimer t(plan, ST_BWD_MIX, s);
-      // dH = dY W_a  (W_a = W_mix[:, :d]; B(k=j, n) = W_mix[j, n])
+      // dH = dY W_a, dx = dY W_b (W_a = W_mix[:, :d], W_b = W_mix[:, d:]).
+      // bf16: both operands are bf16 inputs, so bf16 MFMA with float32
+      // accumulation forms the same exact products as float32 arithmetic;
+      // it needs W_mix transposed (the reduction index j last).
+      GemmArgs t16{};
+      t16.A1 = t16.A2 = dy;
+      t16.a1_m = t16.a2_m = D;
+      t16.a1_k = t16.a2_k = 1;
+      t16.K1 = d.d;
+      t16.Bm = bb.wmixT;
+      t16.b_k = 1;
+      t16.b_n = D;
+      t16.C = bb.dH;
+      t16.c_m = D;
+      t16.M = Bi;
+      t16.N = d.d;
+      t16.K = d.d;
+      t16.header = pd.header;
+      const bool mfma = bb.wmixT && gemm_nt_mfma_ok(t16);
+      if (mfma) {
+        e = transpose_bf16_launch(pd.header,
+                                  static_cast<const uint16_t*>(W_mix), 2 * D,
+                                  d.d, 2 * d.d, bb.wmixT, s);
+        if (e == hipSuccess) e = gemm_nt_mfma_launch(t16, kF32, s);
+        if (e == hipSuccess) {
+          t16.Bm = bb.wmixT + D * D;
+          t16.C = dx;
+          e = gemm_nt_mfma_launch(t16, kF32, s);
+        }
+      }
+      // otherwise B(k=j, n) = W_mix[j, n] read in place (generic kernel)
       GemmArgs g{};
       g.A1 = g.A2 = dy;
       g.a1_m = g.a2_m = D;
@@ -991,15 +1042,59 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
       g.N = d.d;
       g.K = d.d;
       g.header = pd.header;
-      e = gemm_launch(g, d.dtype, d.dtype, kF32, s);
-      // dx = dY W_b  (W_b = W_mix[:, d:])
-      if (e == hipSuccess) {
-        g.Bm = static_cast<const char*>(W_mix) + D * es;
-        g.C = dx;
+      if (!mfma) {
         e = gemm_launch(g, d.dtype, d.dtype, kF32, s);
+        if (e == hipSuccess) {
+          g.Bm = static_cast<const char*>(W_mix) + D * es;
+          g.C = dx;
+          e = gemm_launch(g, d.dtype, d.dtype, kF32, s);
+        }
       }
-      // dW_mix[:, :d] = dY^T H, dW_mix[:, d:] = dY^T X  (sums over tokens)
-      if (e == hipSuccess) {
+      // dW_mix[:, :d] = dY^T H, dW_mix[:, d:] = dY^T X  (sums over tokens).
+      // bf16: on the 256 x 256 bf16 kernel with K split, from transposed
+      // copies (tokens last): dY^T X has bf16 operands (exact products);
+      // the float32 H enters as hi + lo bf16 halves over a doubled K
+      // (dY^T repeated), i.e. dY^T H_hi + dY^T H_lo in one reduction.
+      bool wmfma = false;
+      GemmArgs wx{};
+      if (e == hipSuccess && bb.dyT) {
+        wx.A1 = wx.A2 = bb.dyT;
+        wx.a1_m = wx.a2_m = B;
+        wx.a1_k = wx.a2_k = 1;
+        wx.K1 = Bi;
+        wx.Bm = bb.xT;
+        wx.b_k = 1;
+        wx.b_n = B;
+        wx.C = dW_mix + D;
+        wx.c_m = 2 * D;
+        wx.M = d.d;
+        wx.N = d.d;
+        wx.K = Bi;
+        wx.header = pd.header;
+        GemmArgs wh = wx;
+        wh.Bm = bb.hT;
+        wh.b_n = 2 * B;
+        wh.K = 2 * Bi;
+        wh.C = dW_mix;
+        wmfma = gemm_nt_256_ok(wx) && gemm_nt_256_ok(wh);
+        if (wmfma) {
+          e = transpose_bf16_launch(pd.header,
+                                    static_cast<const uint16_t*>(dy), D, Bi,
+                                    d.d, bb.dyT, s);
+          if (e == hipSuccess)
+            e = transpose_bf16_launch(pd.header,
+                                      static_cast<const uint16_t*>(x), D, Bi,
+                                      d.d, bb.xT, s);
+          if (e == hipSuccess)
+            e = transpose_split_launch(pd.header, sv.h32, D, Bi, d.d, bb.hT,
+                                       s);
+          if (e == hipSuccess)
+            e = gemm_nt_256_splitk_launch(wh, s, bb.gpart, bb.gpart_floats);
+          if (e == hipSuccess)
+            e = gemm_nt_256_splitk_launch(wx, s, bb.gpart, bb.gpart_floats);
+        }
+      }
+      if (e == hipSuccess && !wmfma) {
         GemmArgs w{};
         w.A1 = w.A2 = dy;
         w.a1_m = w.a2_m = 1;

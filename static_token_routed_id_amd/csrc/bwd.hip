@@ -1,8 +1,9 @@
 // Backward pass of the layer (the chain rule of the forward formula of the
 // gist.science explainer of "L^3: Large Lookup Layers", Technical Summary,
 // Core Architecture, Mathematical Formulation; the pages print no
-// gradients). The projections' gradients run through gemm_generic; this
-// file holds the LayerNorm backward and the per-id segment backward.
+// gradients). The projections' gradients run through the GEMM kernels;
+// this file holds the LayerNorm backward, the per-id segment backward and a
+// bf16 transpose for the GEMMs' operands.
 //
 // Determinism: nothing here uses floating-point atomics. LayerNorm column
 // sums (dgamma, dbeta) are taken by one thread per column over the rows in
@@ -29,6 +30,83 @@ hipError_t fill_zero_launch(float* p, int64_t n, hipStream_t s) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   fill_zero_kernel<<<static_cast<int>(blocks), 256, 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
+// dst[c * rows + r] = src[r * ld + c] for bf16 (the transposed copy that puts
+// a product's reduction index last in both operands, as the bf16 MFMA GEMM
+// reads them): 64 x 64 tiles through LDS (rows padded by two elements), each
+// thread moving 16 elements; partial edge tiles are bounds-checked.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(
+    const int32_t* header, const uint16_t* src, int64_t ld, int rows,
+    int cols, uint16_t* dst) {
+  if (header[0] != 0) return;
+  __shared__ uint16_t t[64][66];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = r0 + ty + 4 * k, c = c0 + tx;
+    if (r < rows && c < cols) t[ty + 4 * k][tx] = src[r * ld + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int c = c0 + ty + 4 * k, r = r0 + tx;
+    if (r < rows && c < cols)
+      dst[static_cast<int64_t>(c) * rows + r] = t[tx][ty + 4 * k];
+  }
+}
+
+hipError_t transpose_bf16_launch(const int32_t* header, const uint16_t* src,
+                                 int64_t ld, int rows, int cols,
+                                 uint16_t* dst, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64);
+  transpose_bf16_kernel<<<grid, 256, 0, s>>>(header, src, ld, rows, cols,
+                                              dst);
+  return hipGetLastError();
+}
+
+// Float32 src [rows x cols] (row stride ld) to its transpose in two bf16
+// halves side by side, dst [cols x 2 rows]: dst[c][r] = hi = bf16(src[r][c]),
+// dst[c][rows + r] = bf16(src[r][c] - hi). hi + lo carries src to about
+// 2^-17 relative, so one bf16 GEMM over the doubled reduction (the other
+// operand repeated) reproduces a float32 operand's product.
+__global__ __launch_bounds__(256) void transpose_split_kernel(
+    const int32_t* header, const float* src, int64_t ld, int rows, int cols,
+    uint16_t* dst) {
+  if (header[0] != 0) return;
+  __shared__ float t[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = r0 + ty + 4 * k, c = c0 + tx;
+    if (r < rows && c < cols) t[ty + 4 * k][tx] = src[r * ld + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int c = c0 + ty + 4 * k, r = r0 + tx;
+    if (r < rows && c < cols) {
+      const float v = t[tx][ty + 4 * k];
+      const uint16_t hi = f2bf(v);
+      const float hv = __uint_as_float(static_cast<uint32_t>(hi) << 16);
+      uint16_t* row = dst + static_cast<int64_t>(c) * 2 * rows;
+      row[r] = hi;
+      row[rows + r] = f2bf(v - hv);
+    }
+  }
+}
+
+hipError_t transpose_split_launch(const int32_t* header, const float* src,
+                                  int64_t ld, int rows, int cols,
+                                  uint16_t* dst, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64);
+  transpose_split_kernel<<<grid, 256, 0, s>>>(header, src, ld, rows, cols,
+                                               dst);
   return hipGetLastError();
 }
 

@@ -409,9 +409,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
   const int wm = w >> 1, wn = w & 1;
   const int mt = ceil_div(g.M, kTM), nt = g.N / kTN;
   const int T = mt * nt;
-  int tile = blockIdx.x;
+  // split K (nsplit > 1, float32 partials): workgroup b takes share b / T
+  // of K for tile b % T
+  const int kz = blockIdx.x / T, bt = blockIdx.x - kz * T;
+  int tile = bt;
   if (T % kXcd == 0 && mt % kGroupM == 0)
-    tile = (blockIdx.x % kXcd) * (T / kXcd) + blockIdx.x / kXcd;
+    tile = (bt % kXcd) * (T / kXcd) + bt / kXcd;
   int m_tile, n_tile;
   if (mt % kGroupM == 0) {
     const int grp = tile / (kGroupM * nt), in = tile % (kGroupM * nt);
@@ -493,11 +496,13 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
-  const int nk = g.K / kTK;
+  const int kshare = g.K / g.nsplit;
+  const int kbeg = kz * kshare;
+  const int nk = kshare / kTK;
   const int r = lane & 31, kh = (lane >> 5) * 8;
   const int aoff = (wm * 128 + r) * kTL + kh, boff = (wn * 128 + r) * kTL + kh;
   const int woff = lr * kTL + lc;
-  load_all(slice_src(0));
+  load_all(slice_src(kbeg));
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     *reinterpret_cast<u32x4*>(&lds[0][0][woff + q * 32 * kTL]) = ra[q];
@@ -507,7 +512,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
     s_rs[tid] = lnr;
     s_c[tid] = lnc;
   }
-  load_all(slice_src(min(1, nk - 1) * kTK));
+  load_all(slice_src(kbeg + min(1, nk - 1) * kTK));
   __syncthreads();
   Frag256 F0, F1;
 #pragma unroll
@@ -519,7 +524,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
     const int buf = it & 1;
     // slice it+1 (in registers) goes to the other buffer, slice it+2 is
     // fetched (clamped: the tail refetches the last slice, never read)
-    const SliceSrc src = slice_src(min(it + 2, nk - 1) * kTK);
+    const SliceSrc src = slice_src(kbeg + min(it + 2, nk - 1) * kTK);
     const uint16_t* rda = &lds[buf][0][aoff];
     const uint16_t* rdb = &lds[buf][1][boff];
     uint16_t* wra = &lds[buf ^ 1][0][woff];
@@ -574,14 +579,19 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
 
   const int h4 = (lane >> 5) * 4;
 
-  TC* C = static_cast<TC*>(g.C);
+  // split K: share kz's partial product, M x N float32 (the launcher takes
+  // this path for float32 C only)
+  TC* C = g.nsplit > 1 ? reinterpret_cast<TC*>(g.part) +
+                             static_cast<int64_t>(kz) * g.M * g.N
+                       : static_cast<TC*>(g.C);
+  const int64_t c_m = g.nsplit > 1 ? g.N : g.c_m;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int gm = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + h4 + (e & 3);
       if (gm >= g.M) continue;
-      TC* crow = C + static_cast<int64_t>(gm) * g.c_m + n0 + wn * 128 + r;
+      TC* crow = C + static_cast<int64_t>(gm) * c_m + n0 + wn * 128 + r;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // streaming (non-temporal) stores: C is read much later or by a
@@ -725,6 +735,34 @@ __global__ __launch_bounds__(256) void ln_apply_kernel(LnApplyArgs a) {
 hipError_t ln_apply_launch(const LnApplyArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   ln_apply_kernel<<<ceil_div(a.B, 4), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// The 256 x 256 kernel with K split over workgroups (few output tiles and a
+// long K: the weight gradients, K = tokens), float32 C: each share writes
+// its partial product to part, then gemm_reduce_kernel adds the shares in
+// order. Returns hipErrorInvalidValue when the shape does not allow it
+// (the caller then takes another path).
+hipError_t gemm_nt_256_splitk_launch(const GemmArgs& g0, hipStream_t s,
+                                     float* part, int64_t part_floats) {
+  if (!gemm_nt_256_ok(g0) || !part) return hipErrorInvalidValue;
+  GemmArgs g = g0;
+  const int64_t tiles =
+      static_cast<int64_t>(ceil_div(g.M, kTM)) * (g.N / kTN);
+  const int64_t mn = static_cast<int64_t>(g.M) * g.N;
+  int ns = static_cast<int>(std::min<int64_t>((256 + tiles - 1) / tiles, 16));
+  // whole 64-wide slices in every share (a share may straddle K1: the
+  // operands switch per slice)
+  while (ns > 1 && ((g.K % (ns * kTK)) != 0 || ns * mn > part_floats))
+    --ns;
+  g.nsplit = ns;
+  g.part = ns > 1 ? part : nullptr;
+  const int grid = static_cast<int>(tiles) * ns;
+  gemm_nt_256_kernel<float, false><<<grid, 256, 0, s>>>(g);
+  if (ns > 1) {
+    const int rgrid = static_cast<int>((mn + 255) / 256);
+    gemm_reduce_kernel<float><<<rgrid, 256, 0, s>>>(g);
+  }
   return hipGetLastError();
 }
 
