@@ -176,6 +176,11 @@ struct FwdBufs {
   float* part_ml;
   float* gpart;  // split-K partial products of small-batch GEMMs
   int64_t gpart_floats;
+  // training, bf16: the float32 aggregate as bf16 hi | lo [B x d_e] each,
+  // and [W_up | W_up] [d x 2 d_e]
+  uint16_t* a_hi;
+  uint16_t* a_lo;
+  uint16_t* wup2;
 };
 FwdBufs carve_fwd(Carver& c, const l3_desc& d, int64_t B) {
   FwdBufs f;
@@ -194,6 +199,12 @@ FwdBufs carve_fwd(Carver& c, const l3_desc& d, int64_t B) {
   // small batches split K of the projections (few output tiles)
   f.gpart_floats = B < 1024 ? gpart_floats_for(d) : 0;
   f.gpart = f.gpart_floats ? c.take<float>(f.gpart_floats) : nullptr;
+  const bool b16 = d.dtype == L3_BF16;
+  const size_t ae = static_cast<size_t>(B) * d.d_e;
+  f.a_hi = b16 ? c.take<uint16_t>(ae) : nullptr;
+  f.a_lo = b16 ? c.take<uint16_t>(ae) : nullptr;
+  f.wup2 = b16 ? c.take<uint16_t>(static_cast<size_t>(2) * d.d * d.d_e)
+               : nullptr;
   return f;
 }
 
@@ -886,12 +897,35 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       e = ln_fold_launch(fa, s);
       if (e != hipSuccess) return L3_ERR_HIP;
     }
+    // Training on bf16: the float32 aggregate enters as bf16 hi | lo halves
+    // over a doubled K against [W_up | W_up] (a_hi W_up^T + a_lo W_up^T in
+    // one reduction) on the 256 x 256 bf16 kernel.
+    GemmArgs u2 = up;
+    u2.A1 = f.a_hi;
+    u2.A2 = f.a_lo;
+    u2.Bm = f.wup2;
+    u2.b_n = 2 * static_cast<int64_t>(d.d_e);
+    u2.K = 2 * d.d_e;
+    const bool u_split = save && f.a_hi && gemm_nt_256_ok(u2);
     {
       StageTimer t(plan, ST_UP, s);
-      if (u_bf16)
+      if (u_bf16) {
         e = gemm_nt_mfma_launch(up, kBF16, s, f.gpart, f.gpart_floats);
-      else
+      } else if (u_split) {
+        const size_t row = static_cast<size_t>(d.d_e) * 2;
+        e = split_bf16_launch(pd.header, sv.a32, B * d.d_e, f.a_hi, f.a_lo,
+                              s);
+        if (e == hipSuccess)
+          e = hipMemcpy2DAsync(f.wup2, 2 * row, W_up, row, row, d.d,
+                               hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess)
+          e = hipMemcpy2DAsync(f.wup2 + d.d_e, 2 * row, W_up, row, row, d.d,
+                               hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess)
+          e = gemm_nt_256_splitk_launch(u2, s, nullptr, 0);
+      } else {
         e = gemm_launch(up, save ? kF32 : d.dtype, d.dtype, kF32, s);
+      }
     }
     if (e != hipSuccess) return L3_ERR_HIP;
     if (fold) {
@@ -1158,7 +1192,37 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
     if (e != hipSuccess) return L3_ERR_HIP;
     {
       StageTimer t(plan, ST_BWD_UP, s);
-      // dW_up = dU^T A (sum over tokens)
+      // dW_up = dU^T A (sum over tokens). bf16: both are float32, so three
+      // bf16 products hi hi + lo hi + hi lo over K = 3B (the lo lo term is
+      // below float32 rounding): A = [dU_hi^T | dU_lo^T] (the h^T buffer,
+      // free by now; for k >= 2B the second operand pointer wraps to the
+      // hi half), B = [A_hi^T | A_hi^T | A_lo^T] (the dY^T buffer), split K.
+      bool wumfma = false;
+      if (bb.hT && 3 * d.d_e <= d.d) {
+        GemmArgs h{};
+        h.A1 = h.A2 = bb.hT;
+        h.a1_m = h.a2_m = 2 * B;
+        h.a1_k = h.a2_k = 1;
+        h.K1 = 2 * Bi;
+        h.Bm = bb.dyT;
+        h.b_k = 1;
+        h.b_n = 3 * B;
+        h.C = dW_up;
+        h.c_m = DE;
+        h.M = d.d;
+        h.N = d.d_e;
+        h.K = 3 * Bi;
+        h.header = pd.header;
+        wumfma = gemm_nt_256_ok(h);
+        if (wumfma) {
+          e = transpose_split_launch(pd.header, bb.dU, D, Bi, d.d, bb.hT, s);
+          if (e == hipSuccess)
+            e = transpose_split_launch(pd.header, sv.a32, DE, Bi, d.d_e,
+                                       bb.dyT, s, 3 * B, 2 * B, B);
+          if (e == hipSuccess)
+            e = gemm_nt_256_splitk_launch(h, s, bb.gpart, bb.gpart_floats, 64);
+        }
+      }
       GemmArgs w{};
       w.A1 = w.A2 = bb.dU;
       w.a1_m = w.a2_m = 1;
@@ -1173,9 +1237,44 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
       w.N = d.d_e;
       w.K = Bi;
       w.header = pd.header;
-      e = gemm_launch(w, kF32, kF32, kF32, s, bb.gpart, bb.gpart_floats);
-      // dA = dU W_up
-      if (e == hipSuccess) {
+      if (!wumfma)
+        e = gemm_launch(w, kF32, kF32, kF32, s, bb.gpart, bb.gpart_floats);
+      // dA = dU W_up. bf16: the float32 dU enters as bf16 hi | lo halves
+      // (in the dY^T / x^T buffers, free by now) over a doubled K, against
+      // [W_up^T | W_up^T] (in the W_mix^T buffer): dU_hi W_up + dU_lo W_up
+      // in one reduction, on the 256 x 256 bf16 kernel.
+      bool amfma = false;
+      if (e == hipSuccess && bb.dyT && d.d_e <= d.d) {
+        GemmArgs h{};
+        h.A1 = bb.dyT;
+        h.A2 = bb.xT;
+        h.a1_m = h.a2_m = D;
+        h.a1_k = h.a2_k = 1;
+        h.K1 = d.d;
+        h.Bm = bb.wmixT;
+        h.b_k = 1;
+        h.b_n = 2 * D;
+        h.C = bb.dA;
+        h.c_m = DE;
+        h.M = Bi;
+        h.N = d.d_e;
+        h.K = 2 * d.d;
+        h.header = pd.header;
+        amfma = gemm_nt_256_ok(h);
+        if (amfma) {
+          e = split_bf16_launch(pd.header, bb.dU, B * D, bb.dyT, bb.xT, s);
+          const uint16_t* wu = static_cast<const uint16_t*>(W_up);
+          if (e == hipSuccess)
+            e = transpose_bf16_launch(pd.header, wu, DE, d.d, d.d_e, bb.wmixT,
+                                      s, 2 * D);
+          if (e == hipSuccess)
+            e = transpose_bf16_launch(pd.header, wu, DE, d.d, d.d_e,
+                                      bb.wmixT + D, s, 2 * D);
+          if (e == hipSuccess)
+            e = gemm_nt_256_splitk_launch(h, s, bb.gpart, bb.gpart_floats);
+        }
+      }
+      if (e == hipSuccess && !amfma) {
         GemmArgs g{};
         g.A1 = g.A2 = bb.dU;
         g.a1_m = g.a2_m = D;

@@ -39,7 +39,7 @@ hipError_t fill_zero_launch(float* p, int64_t n, hipStream_t s) {
 // thread moving 16 elements; partial edge tiles are bounds-checked.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(
     const int32_t* header, const uint16_t* src, int64_t ld, int rows,
-    int cols, uint16_t* dst) {
+    int cols, uint16_t* dst, int64_t ldd) {
   if (header[0] != 0) return;
   __shared__ uint16_t t[64][66];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
@@ -54,28 +54,70 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(
   for (int k = 0; k < 16; ++k) {
     const int c = c0 + ty + 4 * k, r = r0 + tx;
     if (r < rows && c < cols)
-      dst[static_cast<int64_t>(c) * rows + r] = t[tx][ty + 4 * k];
+      dst[static_cast<int64_t>(c) * ldd + r] = t[tx][ty + 4 * k];
   }
 }
 
 hipError_t transpose_bf16_launch(const int32_t* header, const uint16_t* src,
                                  int64_t ld, int rows, int cols,
-                                 uint16_t* dst, hipStream_t s) {
+                                 uint16_t* dst, hipStream_t s, int64_t ldd) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
   dim3 grid((cols + 63) / 64, (rows + 63) / 64);
   transpose_bf16_kernel<<<grid, 256, 0, s>>>(header, src, ld, rows, cols,
-                                              dst);
+                                              dst, ldd > 0 ? ldd : rows);
   return hipGetLastError();
 }
 
-// Float32 src [rows x cols] (row stride ld) to its transpose in two bf16
-// halves side by side, dst [cols x 2 rows]: dst[c][r] = hi = bf16(src[r][c]),
-// dst[c][rows + r] = bf16(src[r][c] - hi). hi + lo carries src to about
-// 2^-17 relative, so one bf16 GEMM over the doubled reduction (the other
-// operand repeated) reproduces a float32 operand's product.
+// Float32 [n] to bf16 hi = bf16(v), lo = bf16(v - hi) (hi + lo carries v
+// to about 2^-17 relative), four elements a thread.
+__global__ __launch_bounds__(256) void split_bf16_kernel(
+    const int32_t* header, const float* src, int64_t n, uint16_t* hi,
+    uint16_t* lo) {
+  if (header[0] != 0) return;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  if (i + 4 <= n) {
+    const float4 v = *reinterpret_cast<const float4*>(src + i);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      h[q] = f2bf(vv[q]);
+      l[q] = f2bf(vv[q] - __uint_as_float(static_cast<uint32_t>(h[q]) << 16));
+    }
+    *reinterpret_cast<uint2*>(hi + i) =
+        make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16),
+                   h[2] | (static_cast<uint32_t>(h[3]) << 16));
+    *reinterpret_cast<uint2*>(lo + i) =
+        make_uint2(l[0] | (static_cast<uint32_t>(l[1]) << 16),
+                   l[2] | (static_cast<uint32_t>(l[3]) << 16));
+  } else {
+    for (int64_t j = i; j < n; ++j) {
+      hi[j] = f2bf(src[j]);
+      lo[j] = f2bf(src[j] - __uint_as_float(static_cast<uint32_t>(hi[j]) << 16));
+    }
+  }
+}
+
+hipError_t split_bf16_launch(const int32_t* header, const float* src,
+                             int64_t n, uint16_t* hi, uint16_t* lo,
+                             hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 1023) / 1024;
+  split_bf16_kernel<<<static_cast<int>(blocks), 256, 0, s>>>(header, src, n,
+                                                             hi, lo);
+  return hipGetLastError();
+}
+
+// Float32 src [rows x cols] (row stride ld) to its transpose in bf16 hi and
+// lo halves: dst row c (stride ldd) holds hi = bf16(src[r][c]) at r, lo =
+// bf16(src[r][c] - hi) at lo_off + r, and hi again at hi2_off + r if
+// hi2_off >= 0. hi + lo carries src to about 2^-17 relative, so one bf16
+// GEMM over the lengthened reduction (the other operand laid out to match)
+// reproduces a float32 operand's product.
 __global__ __launch_bounds__(256) void transpose_split_kernel(
     const int32_t* header, const float* src, int64_t ld, int rows, int cols,
-    uint16_t* dst) {
+    uint16_t* dst, int64_t ldd, int64_t lo_off, int64_t hi2_off) {
   if (header[0] != 0) return;
   __shared__ float t[64][65];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
@@ -93,20 +135,23 @@ __global__ __launch_bounds__(256) void transpose_split_kernel(
       const float v = t[tx][ty + 4 * k];
       const uint16_t hi = f2bf(v);
       const float hv = __uint_as_float(static_cast<uint32_t>(hi) << 16);
-      uint16_t* row = dst + static_cast<int64_t>(c) * 2 * rows;
+      uint16_t* row = dst + static_cast<int64_t>(c) * ldd;
       row[r] = hi;
-      row[rows + r] = f2bf(v - hv);
+      row[lo_off + r] = f2bf(v - hv);
+      if (hi2_off >= 0) row[hi2_off + r] = hi;
     }
   }
 }
 
 hipError_t transpose_split_launch(const int32_t* header, const float* src,
                                   int64_t ld, int rows, int cols,
-                                  uint16_t* dst, hipStream_t s) {
+                                  uint16_t* dst, hipStream_t s, int64_t ldd,
+                                  int64_t lo_off, int64_t hi2_off) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
   dim3 grid((cols + 63) / 64, (rows + 63) / 64);
-  transpose_split_kernel<<<grid, 256, 0, s>>>(header, src, ld, rows, cols,
-                                               dst);
+  transpose_split_kernel<<<grid, 256, 0, s>>>(
+      header, src, ld, rows, cols, dst, ldd > 0 ? ldd : 2 * int64_t(rows),
+      lo_off > 0 ? lo_off : rows, hi2_off);
   return hipGetLastError();
 }
 

@@ -738,19 +738,23 @@ hipError_t ln_apply_launch(const LnApplyArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The 256 x 256 kernel with K split over workgroups (few output tiles and a
-// long K: the weight gradients, K = tokens), float32 C: each share writes
+// The 256 x 256 kernel with K split over up to max_split workgroups (few
+// output tiles and a long K: the weight gradients, K = tokens), about 256
+// workgroups in all, float32 C: each share writes
 // its partial product to part, then gemm_reduce_kernel adds the shares in
 // order. Returns hipErrorInvalidValue when the shape does not allow it
 // (the caller then takes another path).
 hipError_t gemm_nt_256_splitk_launch(const GemmArgs& g0, hipStream_t s,
-                                     float* part, int64_t part_floats) {
-  if (!gemm_nt_256_ok(g0) || !part) return hipErrorInvalidValue;
+                                     float* part, int64_t part_floats,
+                                     int max_split) {
+  if (!gemm_nt_256_ok(g0)) return hipErrorInvalidValue;
+  if (!part) part_floats = 0;
   GemmArgs g = g0;
   const int64_t tiles =
       static_cast<int64_t>(ceil_div(g.M, kTM)) * (g.N / kTN);
   const int64_t mn = static_cast<int64_t>(g.M) * g.N;
-  int ns = static_cast<int>(std::min<int64_t>((256 + tiles - 1) / tiles, 16));
+  int ns = static_cast<int>(
+      std::min<int64_t>((256 + tiles - 1) / tiles, max_split));
   // whole 64-wide slices in every share (a share may straddle K1: the
   // operands switch per slice)
   while (ns > 1 && ((g.K % (ns * kTK)) != 0 || ns * mn > part_floats))

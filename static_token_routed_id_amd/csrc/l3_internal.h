@@ -298,20 +298,31 @@ struct BwdArgs {
   float* ln_part;      // [ceil(B / 256) x 2 x d] LayerNorm column partials
 };
 hipError_t fill_zero_launch(float* p, int64_t n, hipStream_t s);
-// dst [cols x rows] = transpose of src [rows x cols] (row stride ld), bf16.
+// dst [cols x rows] (row stride ldd, default rows) = transpose of src
+// [rows x cols] (row stride ld), bf16.
 hipError_t transpose_bf16_launch(const int32_t* header, const uint16_t* src,
                                  int64_t ld, int rows, int cols,
-                                 uint16_t* dst, hipStream_t s);
-// dst [cols x 2 rows] = transpose of float32 src [rows x cols] as bf16
-// hi / lo halves side by side (dst[c][r] = hi, dst[c][rows + r] = lo).
+                                 uint16_t* dst, hipStream_t s,
+                                 int64_t ldd = 0);
+// Float32 [n] (n a multiple of 4 for whole vectors; any n works) to its
+// bf16 hi and lo halves: hi = bf16(v), lo = bf16(v - hi).
+hipError_t split_bf16_launch(const int32_t* header, const float* src,
+                             int64_t n, uint16_t* hi, uint16_t* lo,
+                             hipStream_t s);
+// Transpose of float32 src [rows x cols] as bf16 hi / lo halves: dst row c
+// (stride ldd, default 2 rows) holds hi at r, lo at lo_off + r (default
+// rows) and, if hi2_off >= 0, hi again at hi2_off + r.
 hipError_t transpose_split_launch(const int32_t* header, const float* src,
                                   int64_t ld, int rows, int cols,
-                                  uint16_t* dst, hipStream_t s);
+                                  uint16_t* dst, hipStream_t s,
+                                  int64_t ldd = 0, int64_t lo_off = 0,
+                                  int64_t hi2_off = -1);
 // The 256 x 256 bf16 kernel with K split over workgroups into float32
 // partials (part), reduced in order into C (float32). hipErrorInvalidValue
 // if the shape rules of the 256 x 256 kernel do not hold.
 hipError_t gemm_nt_256_splitk_launch(const GemmArgs& g, hipStream_t s,
-                                     float* part, int64_t part_floats);
+                                     float* part, int64_t part_floats,
+                                     int max_split = 16);
 hipError_t ln_bwd_launch(const BwdArgs& a, int dtype, hipStream_t s);
 hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int items_ub,
                           int S_ub, hipStream_t s);
