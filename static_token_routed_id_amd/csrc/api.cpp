@@ -176,11 +176,9 @@ struct FwdBufs {
   float* part_ml;
   float* gpart;  // split-K partial products of small-batch GEMMs
   int64_t gpart_floats;
-  // training, bf16: the float32 aggregate as bf16 hi | lo [B x d_e] each,
-  // and [W_up | W_up] [d x 2 d_e]
+  // training, bf16: the float32 aggregate as bf16 hi | lo [B x d_e] each
   uint16_t* a_hi;
   uint16_t* a_lo;
-  uint16_t* wup2;
 };
 FwdBufs carve_fwd(Carver& c, const l3_desc& d, int64_t B) {
   FwdBufs f;
@@ -203,8 +201,6 @@ FwdBufs carve_fwd(Carver& c, const l3_desc& d, int64_t B) {
   const size_t ae = static_cast<size_t>(B) * d.d_e;
   f.a_hi = b16 ? c.take<uint16_t>(ae) : nullptr;
   f.a_lo = b16 ? c.take<uint16_t>(ae) : nullptr;
-  f.wup2 = b16 ? c.take<uint16_t>(static_cast<size_t>(2) * d.d * d.d_e)
-               : nullptr;
   return f;
 }
 
@@ -221,7 +217,14 @@ struct BwdBufs {
   uint16_t* dyT;    // [d x B] dY transposed (bf16 only)
   uint16_t* xT;     // [d x B] x transposed (bf16 only)
   uint16_t* hT;     // [d x 2B] saved h transposed, bf16 hi | lo (bf16 only)
+  int2* rows_map;   // segment backward's column-pass work list
+  int* rows_count;
+  int2* zero_map;   // 64-row pieces of the absent ids' rows
+  int* zero_count;
 };
+int64_t zero_items_for(const l3_desc& d, int64_t B) {
+  return d.rows / 64 + B + 2;
+}
 
 // Row stride of the segment backward's p / dS arrays: k_max rounded up to
 // its 64-row blocks.
@@ -242,6 +245,11 @@ BwdBufs carve_bwd(Carver& c, const l3_desc& d, int64_t B) {
   b.dyT = b16 ? c.take<uint16_t>(static_cast<size_t>(B) * d.d) : nullptr;
   b.xT = b16 ? c.take<uint16_t>(static_cast<size_t>(B) * d.d) : nullptr;
   b.hT = b16 ? c.take<uint16_t>(static_cast<size_t>(2) * B * d.d) : nullptr;
+  b.rows_map = c.take<int2>(static_cast<size_t>(B) *
+                            ((bwd_kst(d) + 63) / 64));
+  b.rows_count = c.take<int>(64);
+  b.zero_map = c.take<int2>(static_cast<size_t>(zero_items_for(d, B)));
+  b.zero_count = c.take<int>(64);
   return b;
 }
 
@@ -898,13 +906,14 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       if (e != hipSuccess) return L3_ERR_HIP;
     }
     // Training on bf16: the float32 aggregate enters as bf16 hi | lo halves
-    // over a doubled K against [W_up | W_up] (a_hi W_up^T + a_lo W_up^T in
-    // one reduction) on the 256 x 256 bf16 kernel.
+    // over a doubled K, W_up read for both halves (a_hi W_up^T + a_lo
+    // W_up^T in one reduction) on the 256 x 256 bf16 kernel.
     GemmArgs u2 = up;
     u2.A1 = f.a_hi;
     u2.A2 = f.a_lo;
-    u2.Bm = f.wup2;
-    u2.b_n = 2 * static_cast<int64_t>(d.d_e);
+    u2.B1 = W_up;
+    u2.b1_n = d.d_e;
+    u2.b2_rel = 1;
     u2.K = 2 * d.d_e;
     const bool u_split = save && f.a_hi && gemm_nt_256_ok(u2);
     {
@@ -912,15 +921,8 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       if (u_bf16) {
         e = gemm_nt_mfma_launch(up, kBF16, s, f.gpart, f.gpart_floats);
       } else if (u_split) {
-        const size_t row = static_cast<size_t>(d.d_e) * 2;
         e = split_bf16_launch(pd.header, sv.a32, B * d.d_e, f.a_hi, f.a_lo,
                               s);
-        if (e == hipSuccess)
-          e = hipMemcpy2DAsync(f.wup2, 2 * row, W_up, row, row, d.d,
-                               hipMemcpyDeviceToDevice, s);
-        if (e == hipSuccess)
-          e = hipMemcpy2DAsync(f.wup2 + d.d_e, 2 * row, W_up, row, row, d.d,
-                               hipMemcpyDeviceToDevice, s);
         if (e == hipSuccess)
           e = gemm_nt_256_splitk_launch(u2, s, nullptr, 0);
       } else {
@@ -1185,6 +1187,10 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
     ba.Pbuf = bb.P;
     ba.DSbuf = bb.dS;
     ba.ln_part = bb.ln_part;
+    ba.rows_map = bb.rows_map;
+    ba.rows_count = bb.rows_count;
+    ba.zero_map = bb.zero_map;
+    ba.zero_count = bb.zero_count;
     {
       StageTimer t(plan, ST_BWD_LN, s);
       e = ln_bwd_launch(ba, d.dtype, s);
@@ -1295,8 +1301,14 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
     if (e != hipSuccess) return L3_ERR_HIP;
     {
       StageTimer t(plan, ST_BWD_SEG, s);
-      e = fill_zero_launch(dK, d.rows * D, s);
-      if (e == hipSuccess) e = fill_zero_launch(dV, d.rows * DE, s);
+      // rows of absent ids only (the column pass writes the present ones);
+      // float4 stores need d, d_e multiples of 4, row indices int32
+      if (D % 4 == 0 && DE % 4 == 0 && d.rows < (int64_t(1) << 31)) {
+        e = zero_absent_launch(ba, zero_items_for(d, B), s);
+      } else {
+        e = fill_zero_launch(dK, d.rows * D, s);
+        if (e == hipSuccess) e = fill_zero_launch(dV, d.rows * DE, s);
+      }
       const int64_t distinct = B < d.vocab ? B : d.vocab;
       const int64_t items_ub =
           ((B + kTokTile - 1) / kTokTile + distinct) *

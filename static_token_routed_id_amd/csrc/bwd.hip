@@ -558,28 +558,124 @@ __global__ __launch_bounds__(256, 2) void seg_bwd_tile_kernel(BwdArgs a) {
   }
 }
 
+// Rows of ids absent from the batch get zero gradients (the column pass
+// writes every row of the present ids). Segments are in id order and an
+// id's rows are contiguous, so the absent rows are the gaps between
+// consecutive segments' row ranges (and before the first, after the last).
+// One workgroup lists them in pieces of at most 64 rows (thread t takes a
+// run of gaps; a scan of the runs' piece counts places them); then
+// zero_rows_kernel clears each piece's dK and dV rows.
+__global__ __launch_bounds__(1024) void gap_items_kernel(BwdArgs a) {
+  __shared__ int s_part[1024];
+  if (a.header[0] != 0) return;
+  const int S = a.header[1];
+  const int tid = threadIdx.x;
+  const int per = (S + 1 + 1023) / 1024;
+  const int g0 = tid * per, g1 = min(S + 1, g0 + per);
+  auto gap = [&](int g, int64_t& lo, int64_t& hi) {
+    lo = g == 0 ? 0 : a.seg_row_off[g - 1] + a.seg_n[g - 1];
+    hi = g == S ? a.rows : a.seg_row_off[g];
+  };
+  int cnt = 0;
+  for (int g = g0; g < g1; ++g) {
+    int64_t lo, hi;
+    gap(g, lo, hi);
+    if (hi > lo) cnt += static_cast<int>((hi - lo + 63) / 64);
+  }
+  s_part[tid] = cnt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? s_part[tid - o] : 0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
+  }
+  int off = s_part[tid] - cnt;
+  for (int g = g0; g < g1; ++g) {
+    int64_t lo, hi;
+    gap(g, lo, hi);
+    for (int64_t r = lo; r < hi; r += 64)
+      a.zero_map[off++] =
+          make_int2(static_cast<int>(r), static_cast<int>(min(hi - r, int64_t(64))));
+  }
+  if (tid == 1023) *a.zero_count = s_part[1023];
+}
+
+__global__ __launch_bounds__(256) void zero_rows_kernel(BwdArgs a) {
+  if (a.header[0] != 0) return;
+  const int n = *a.zero_count;
+  const float4 z = {0.f, 0.f, 0.f, 0.f};
+  for (int it = blockIdx.x; it < n; it += gridDim.x) {
+    const int2 p = a.zero_map[it];
+    float4* k = reinterpret_cast<float4*>(a.dK + static_cast<int64_t>(p.x) * a.d);
+    float4* v =
+        reinterpret_cast<float4*>(a.dV + static_cast<int64_t>(p.x) * a.d_e);
+    const int nk = p.y * a.d / 4, nv = p.y * a.d_e / 4;
+    for (int i = threadIdx.x; i < nk; i += 256) k[i] = z;
+    for (int i = threadIdx.x; i < nv; i += 256) v[i] = z;
+  }
+}
+
+hipError_t zero_absent_launch(const BwdArgs& a, int64_t items_ub,
+                              hipStream_t s) {
+  gap_items_kernel<<<1, 1024, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int grid = static_cast<int>(items_ub < 4096 ? items_ub : 4096);
+  if (grid > 0) zero_rows_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// The column pass's work list: every (segment, 64-row block) pair that
+// holds rows, in segment order. One workgroup: thread t takes a run of
+// consecutive segments, an exclusive scan of the runs' block counts gives
+// each run its place, then each thread writes its pairs.
+__global__ __launch_bounds__(1024) void rows_items_kernel(BwdArgs a) {
+  __shared__ int s_part[1024];
+  if (a.header[0] != 0) return;
+  const int S = a.header[1];
+  const int tid = threadIdx.x;
+  const int per = (S + 1023) / 1024;
+  const int s0 = tid * per, s1 = min(S, s0 + per);
+  int cnt = 0;
+  for (int s = s0; s < s1; ++s) cnt += ceil_div(a.seg_n[s], kBwdRowBlk);
+  s_part[tid] = cnt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? s_part[tid - o] : 0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
+  }
+  int off = s_part[tid] - cnt;
+  for (int s = s0; s < s1; ++s) {
+    const int nb = ceil_div(a.seg_n[s], kBwdRowBlk);
+    for (int jb = 0; jb < nb; ++jb) a.rows_map[off + jb] = make_int2(s, jb);
+    off += nb;
+  }
+  if (tid == 1023) *a.rows_count = s_part[1023];
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void seg_bwd_rows_kernel(BwdArgs a) {
   __shared__ __align__(16) float s_ds[kTokTile][kBwdRowBlk];
   __shared__ __align__(16) float s_p[kTokTile][kBwdRowBlk];
   __shared__ int s_tok[kTokTile];
   if (a.header[0] != 0) return;
-  const int S = a.header[1];
   const int tid = threadIdx.x;
   const int ncb = ceil_div(a.d + a.d_e, kBwdColBlk);
-  const int nrb = ceil_div(a.kst, kBwdRowBlk);
-  const int64_t total = static_cast<int64_t>(S) * ncb * nrb;
+  const int nitems = *a.rows_count;
+  const int64_t total = static_cast<int64_t>(nitems) * ncb;
   const T* X = static_cast<const T*>(a.x);
   for (int64_t idx = blockIdx.x; idx < total; idx += gridDim.x) {
-    // index = (row block, column block, segment): a busy id's blocks land on
-    // different workgroups
-    const int s = static_cast<int>(idx % S);
-    const int64_t rest = idx / S;
-    const int cb = static_cast<int>(rest % ncb);
-    const int jb = static_cast<int>(rest / ncb);
+    // index = (item, column block): items are in segment order, which puts
+    // the ids with most tokens (the lowest ids of a Zipf-like stream) and
+    // their longest blocks on the first workgroups dispatched
+    const int2 it = a.rows_map[idx / ncb];
+    const int cb = static_cast<int>(idx % ncb);
+    const int s = it.x, jb = it.y;
     const int n = a.seg_n[s];
     const int j0 = jb * kBwdRowBlk;
-    if (j0 >= n) continue;
     const int t_begin = a.seg_tok_start[s];
     const int t_end = a.seg_tok_start[s + 1];
     const int64_t r0 = a.seg_row_off[s];
@@ -663,6 +759,9 @@ hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int items_ub, int S_ub,
   else
     seg_bwd_tile_kernel<float><<<grid, 256, 0, s>>>(a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  rows_items_kernel<<<1, 1024, 0, s>>>(a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t blocks = static_cast<int64_t>(S_ub) *
                          ceil_div(a.d + a.d_e, kBwdColBlk) *

@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
     s.rb = first ? rB1 : rB;
     s.vb = first ? vB1 : vB;
     s.qb = first ? qB1 : qB;
-    s.kb = k0 * 2;
+    s.kb = (first || !g.b2_rel ? k0 : k0 - g.K1) * 2;
     return s;
   };
 

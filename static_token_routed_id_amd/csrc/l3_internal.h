@@ -147,6 +147,9 @@ struct GemmArgs {
   //     acc = rstd * acc - mean * rstd * c1 + c2.
   const void* B1 = nullptr;
   int64_t b1_n = 0;
+  // 256 x 256 kernel: for k >= K1 read Bm's column k - K1 instead of k
+  // (B1 then holds the k < K1 part, as for A1 / A2)
+  int b2_rel = 0;
   float* ln_stats_out = nullptr;
   const float* ln_rows = nullptr;
   const float* ln_c12 = nullptr;
@@ -296,7 +299,17 @@ struct BwdArgs {
   float* Pbuf;
   float* DSbuf;
   float* ln_part;      // [ceil(B / 256) x 2 x d] LayerNorm column partials
+  // (segment, 64-row block) pairs of the column pass, and their count
+  int2* rows_map;      // [B x ceil(kst / 64)] at most
+  int* rows_count;
+  // (first row, rows <= 64) pieces of the absent ids' rows, and their count
+  int2* zero_map;      // [rows / 64 + B + 2] at most
+  int* zero_count;
 };
+// Zeroes dK, dV rows of the ids absent from the batch (d, d_e multiples of
+// 4); items_ub bounds the number of 64-row pieces.
+hipError_t zero_absent_launch(const BwdArgs& a, int64_t items_ub,
+                              hipStream_t s);
 hipError_t fill_zero_launch(float* p, int64_t n, hipStream_t s);
 // dst [cols x rows] (row stride ldd, default rows) = transpose of src
 // [rows x cols] (row stride ld), bf16.
