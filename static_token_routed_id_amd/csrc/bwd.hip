@@ -870,6 +870,177 @@ __global__ __launch_bounds__(256) void seg_bwd_rows_kernel(BwdArgs a) {
   }
 }
 
+// Column pass on 16x16x32 bf16 MFMA (bf16 x, d a multiple of 256, d_e of
+// 64): dK_t = dS^T X_t and dV_t = P^T dA_t as small GEMMs, rows of K_t / V_t
+// the M index, columns N, the id's tokens the reduction (blocks of 32). One
+// workgroup per (id, 64-row block) pair and 256 columns of [K | V]; wave w
+// owns 64 of them (all K or all V) and all 64 rows: 4 x 4 accumulators.
+// Per token block the workgroup stages dS (K columns) or p (V columns) of
+// its 64 rows transposed in LDS as bf16 hi / lo halves ([row][token], A
+// operand: 8 consecutive tokens a lane), each wave stages its 32 token rows
+// of x (bf16) or dA (float32, as hi / lo) ([token][column]) and reads the B
+// operand with the transposing LDS read. dK = dS_hi x + dS_lo x (x is
+// exact in bf16), dV = p_hi dA_hi + p_lo dA_hi + p_hi dA_lo: products of
+// bf16 values are exact in float32, the lo halves carry the float32
+// operands to about 2^-17. Tokens past the id's last get zero weights.
+constexpr int kRAS = 32 + 8;   // A staging row stride (elements)
+constexpr int kRBS = 64 + 8;   // B staging row stride (elements)
+
+__global__ __launch_bounds__(256) void seg_bwd_rows_mfma_kernel(BwdArgs a) {
+  __shared__ __align__(16) uint16_t s_ahi[64 * kRAS];
+  __shared__ __align__(16) uint16_t s_alo[64 * kRAS];
+  __shared__ __align__(16) uint16_t s_bhi[4][32 * kRBS];
+  __shared__ __align__(16) uint16_t s_blo[4][32 * kRBS];
+  if (a.header[0] != 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int trow = 8 * g + (r >> 2), tcol = 4 * (r & 3);
+  const int ncb = ceil_div(a.d + a.d_e, kBwdColBlk);
+  const int nitems = *a.rows_count;
+  const int64_t total = static_cast<int64_t>(nitems) * ncb;
+  const uint16_t* X = static_cast<const uint16_t*>(a.x);
+  typedef __attribute__((address_space(3))) bwd_v4i16 lds_v4i16;
+  for (int64_t idx = blockIdx.x; idx < total; idx += gridDim.x) {
+    const int2 it = a.rows_map[idx / ncb];
+    const int cb = static_cast<int>(idx % ncb);
+    const int s = it.x;
+    const int n = a.seg_n[s];
+    const int j0 = it.y * kBwdRowBlk;
+    const int t_begin = a.seg_tok_start[s];
+    const int t_end = a.seg_tok_start[s + 1];
+    const int64_t r0 = a.seg_row_off[s];
+    // the workgroup's columns are all K (c < d) or all V: 256 divides d
+    const bool isK = cb * kBwdColBlk < a.d;
+    const int c0 = cb * kBwdColBlk + w * 64;   // this wave's first column
+    const bool wave_on = c0 < a.d + a.d_e;
+    const int col0 = isK ? c0 : c0 - a.d;      // within K or V
+    const float* src_a = isK ? a.DSbuf : a.Pbuf;
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
+      const int cnt = min(32, t_end - t0);
+      __syncthreads();  // the previous block is consumed
+      {
+        // A: token tt, rows jq .. jq+7 of this block (float32 -> hi / lo),
+        // written transposed
+        const int tt = tid >> 3, jq = (tid & 7) * 8;
+        float v[8];
+        if (tt < cnt) {
+          const float* p = src_a + static_cast<int64_t>(t0 + tt) * a.kst + j0 + jq;
+          const float4 u0 = *reinterpret_cast<const float4*>(p);
+          const float4 u1 = *reinterpret_cast<const float4*>(p + 4);
+          v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+          v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t h = f2bf(v[e]);
+          s_ahi[(jq + e) * kRAS + tt] = h;
+          s_alo[(jq + e) * kRAS + tt] =
+              f2bf(v[e] - __uint_as_float(static_cast<uint32_t>(h) << 16));
+        }
+      }
+      if (wave_on) {
+        // B: this wave's 32 token rows x 64 columns
+        if (isK) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int ch = q * 64 + lane, tt = ch >> 3, cq = (ch & 7) * 8;
+            const int64_t row = a.perm[t0 + min(tt, cnt - 1)];
+            const u32x4 u = *reinterpret_cast<const u32x4*>(
+                X + row * a.d + col0 + cq);
+            *reinterpret_cast<u32x4*>(&s_bhi[w][tt * kRBS + cq]) = u;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int ch = q * 64 + lane, tt = ch >> 4, cq = (ch & 15) * 4;
+            const int64_t row = a.perm[t0 + min(tt, cnt - 1)];
+            const float4 u = *reinterpret_cast<const float4*>(
+                a.dA + row * a.d_e + col0 + cq);
+            const float x[4] = {u.x, u.y, u.z, u.w};
+            uint32_t h[2], l[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              h[e] = f2bf2(x[2 * e], x[2 * e + 1]);
+              l[e] = f2bf2(x[2 * e] - __uint_as_float(h[e] << 16),
+                           x[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u));
+            }
+            *reinterpret_cast<uint2*>(&s_bhi[w][tt * kRBS + cq]) =
+                make_uint2(h[0], h[1]);
+            *reinterpret_cast<uint2*>(&s_blo[w][tt * kRBS + cq]) =
+                make_uint2(l[0], l[1]);
+          }
+        }
+      }
+      __syncthreads();
+      if (wave_on) {
+        u32x4 ahi[4], alo[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          ahi[mb] = *reinterpret_cast<const u32x4*>(&s_ahi[(mb * 16 + r) * kRAS + 8 * g]);
+          alo[mb] = *reinterpret_cast<const u32x4*>(&s_alo[(mb * 16 + r) * kRAS + 8 * g]);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const bwd_v4i16 l0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(&s_bhi[w][trow * kRBS + nb * 16 + tcol]));
+          const bwd_v4i16 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(&s_bhi[w][(trow + 4) * kRBS + nb * 16 + tcol]));
+          const uint2 la = __builtin_bit_cast(uint2, l0);
+          const uint2 ha = __builtin_bit_cast(uint2, h0);
+          const u32x4 bh = u32x4{la.x, la.y, ha.x, ha.y};
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, ahi[mb]),
+                __builtin_bit_cast(bf16x8_t, bh), acc[mb][nb], 0, 0, 0);
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, alo[mb]),
+                __builtin_bit_cast(bf16x8_t, bh), acc[mb][nb], 0, 0, 0);
+          }
+          if (!isK) {
+            const bwd_v4i16 l1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(&s_blo[w][trow * kRBS + nb * 16 + tcol]));
+            const bwd_v4i16 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(&s_blo[w][(trow + 4) * kRBS + nb * 16 + tcol]));
+            const uint2 lb = __builtin_bit_cast(uint2, l1);
+            const uint2 hb = __builtin_bit_cast(uint2, h1);
+            const u32x4 bl = u32x4{lb.x, lb.y, hb.x, hb.y};
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, ahi[mb]),
+                  __builtin_bit_cast(bf16x8_t, bl), acc[mb][nb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (wave_on) {
+      const int jn = min(kBwdRowBlk, n - j0);
+      float* dst = isK ? a.dK : a.dV;
+      const int64_t ld = isK ? a.d : a.d_e;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int jj = mb * 16 + 4 * g + i;
+          if (jj < jn) {
+            float* row = dst + (r0 + j0 + jj) * ld + col0 + r;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) row[nb * 16] = acc[mb][nb][i];
+          }
+        }
+    }
+  }
+}
+
 hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int items_ub, int S_ub,
                           hipStream_t s) {
   if (items_ub <= 0 || S_ub <= 0) return hipSuccess;
@@ -888,7 +1059,9 @@ hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int items_ub, int S_ub,
                          ceil_div(a.d + a.d_e, kBwdColBlk) *
                          ceil_div(a.kst, kBwdRowBlk);
   const int grid2 = static_cast<int>(blocks < 8192 ? blocks : 8192);
-  if (dtype == kBF16)
+  if (dtype == kBF16 && a.d % kBwdColBlk == 0 && a.d_e % 64 == 0)
+    seg_bwd_rows_mfma_kernel<<<grid2, 256, 0, s>>>(a);
+  else if (dtype == kBF16)
     seg_bwd_rows_kernel<uint16_t><<<grid2, 256, 0, s>>>(a);
   else
     seg_bwd_rows_kernel<float><<<grid2, 256, 0, s>>>(a);
