@@ -371,20 +371,27 @@ __global__ __launch_bounds__(256) void seg_items_kernel(PlanDev pd,
 }
 
 // Scan the item counts in place (a[S] = total); S is read on the device.
+// One workgroup per count array, side by side: wave items (header[2]),
+// 64-token items (header[3]), and with with_all the wave items of every id
+// (header[8]; without it header[8] repeats header[2]).
 __global__ __launch_bounds__(1024) void seg_items_scan_kernel(PlanDev pd,
                                                               int with_all) {
   __shared__ int tmp[1024 / 64 + 1];
   const int n = pd.header[1];
-  const int total = scan_excl_1024(pd.seg_item_start, n, tmp);
-  const int gtotal = scan_excl_1024(pd.seg_gitem_start, n, tmp);
-  const int atotal = with_all ? scan_excl_1024(pd.seg_aitem_start, n, tmp) : total;
+  int32_t* a = blockIdx.x == 0   ? pd.seg_item_start
+               : blockIdx.x == 1 ? pd.seg_gitem_start
+                                 : pd.seg_aitem_start;
+  const int total = scan_excl_1024(a, n, tmp);
   if (threadIdx.x == 0) {
-    pd.seg_item_start[n] = total;
-    pd.seg_gitem_start[n] = gtotal;
-    if (with_all) pd.seg_aitem_start[n] = atotal;
-    pd.header[2] = total;
-    pd.header[3] = gtotal;
-    pd.header[8] = atotal;
+    a[n] = total;
+    if (blockIdx.x == 0) {
+      pd.header[2] = total;
+      if (!with_all) pd.header[8] = total;
+    } else if (blockIdx.x == 1) {
+      pd.header[3] = total;
+    } else {
+      pd.header[8] = total;
+    }
   }
 }
 
@@ -476,7 +483,8 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
   scan_single_kernel<<<1, 1024, 0, s>>>(pd.blk, nblk, pd.blk + nblk);
   seg_write_kernel<<<nblk, 256, 0, s>>>(pd, p, nblk);
   seg_items_kernel<<<ceil_div(B, 256), 256, 0, s>>>(pd, p);
-  seg_items_scan_kernel<<<1, 1024, 0, s>>>(pd, p.group_min_rows > 0);
+  seg_items_scan_kernel<<<p.group_min_rows > 0 ? 3 : 2, 1024, 0, s>>>(
+      pd, p.group_min_rows > 0);
   item_map_kernel<<<item_map_grid(B), 256, 0, s>>>(pd, p.group_min_rows > 0);
   return hipGetLastError();
 }
