@@ -124,7 +124,7 @@ PlanDev carve_plan(Carver& c, int64_t B) {
   p.seg_gitem_start = c.take<int32_t>(nb + 1);
   p.keys_alt = c.take<int32_t>(nb);
   p.vals_alt = c.take<int32_t>(nb);
-  p.hist = c.take<int32_t>(256 * nblk);
+  p.hist = c.take<int32_t>(512 * nblk);
   p.blk = c.take<int32_t>(nblk + 1);
   p.item_map = c.take<int2>(static_cast<size_t>(wave_items_cap(B)));
   p.gitem_map = c.take<int2>(static_cast<size_t>(group_items_cap(B)));

@@ -50,7 +50,7 @@ struct PlanDev {
   int32_t* seg_gitem_start; // [B+1] group items
   int32_t* keys_alt;        // [B] radix ping-pong
   int32_t* vals_alt;        // [B]
-  int32_t* hist;            // [256 * ceil(B / kSortTile)]
+  int32_t* hist;            // [512 * ceil(B / kSortTile)] (9-bit digits)
   int32_t* blk;             // [ceil(B / kSortTile) + 1]
   int2* item_map;           // wave item -> (segment, index within segment)
   int2* gitem_map;          // group item -> (segment, tile within segment)

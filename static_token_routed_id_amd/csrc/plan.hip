@@ -181,24 +181,27 @@ __global__ void header_init_kernel(int32_t* header) {
   if (threadIdx.x < 16) header[threadIdx.x] = 0;
 }
 
-// Digit histogram of one 1024-key tile; pass 0 also checks the id range.
+// Digit histogram of one 1024-key tile (DB-bit digits, 2^DB buckets);
+// pass 0 also checks the id range.
+template <int DB>
 __global__ __launch_bounds__(256) void radix_hist_kernel(
     const int32_t* kin, int B, int shift, int32_t* hist, int nblk,
     int64_t vocab, int32_t* header, int validate) {
-  __shared__ int h[256];
+  constexpr int NB = 1 << DB;
+  __shared__ int h[NB];
   const int tid = threadIdx.x;
-  h[tid] = 0;
+  for (int q = tid; q < NB; q += 256) h[q] = 0;
   __syncthreads();
   for (int r = 0; r < kSortTile / 256; ++r) {
     int i = blockIdx.x * kSortTile + r * 256 + tid;
     if (i < B) {
       int k = kin[i];
       if (validate && (k < 0 || k >= vocab)) atomicOr(&header[0], kBadId);
-      atomicAdd(&h[(static_cast<uint32_t>(k) >> shift) & 255u], 1);
+      atomicAdd(&h[(static_cast<uint32_t>(k) >> shift) & (NB - 1u)], 1);
     }
   }
   __syncthreads();
-  hist[tid * nblk + blockIdx.x] = h[tid];
+  for (int q = tid; q < NB; q += 256) hist[q * nblk + blockIdx.x] = h[q];
 }
 
 // In-place exclusive scan of a[0..n) by one 1024-thread workgroup: rounds
@@ -257,18 +260,23 @@ __global__ __launch_bounds__(1024) void scan_single_kernel(int32_t* a, int n,
   if (threadIdx.x == 0 && total_out) *total_out = total;
 }
 
-// Stable scatter of one 1024-key tile by one digit. Keys of a tile are taken
-// in order, 256 at a time; within a wave the rank among equal digits comes
-// from a ballot match on the 8 digit bits, across waves from LDS counts.
+// Stable scatter of one 1024-key tile by one DB-bit digit. Keys of a tile
+// are taken in order, 256 at a time; within a wave the rank among equal
+// digits comes from a ballot match on the digit bits, across waves from LDS
+// counts.
+template <int DB>
 __global__ __launch_bounds__(256) void radix_scatter_kernel(
     const int32_t* kin, const int32_t* vin, int32_t* kout, int32_t* vout,
     int B, int shift, const int32_t* hist, int nblk) {
-  __shared__ int base[256];
-  __shared__ int wcnt[4][256];
+  constexpr int NB = 1 << DB;
+  __shared__ int base[NB];
+  __shared__ int wcnt[4][NB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  base[tid] = hist[tid * nblk + blockIdx.x];
+  for (int q = tid; q < NB; q += 256) {
+    base[q] = hist[q * nblk + blockIdx.x];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
+    for (int v = 0; v < 4; ++v) wcnt[v][q] = 0;
+  }
   __syncthreads();
   const unsigned long long below = (1ull << lane) - 1ull;
   for (int r = 0; r < kSortTile / 256; ++r) {
@@ -276,10 +284,10 @@ __global__ __launch_bounds__(256) void radix_scatter_kernel(
     const bool valid = i < B;
     const int key = valid ? kin[i] : 0;
     const int val = valid ? (vin ? vin[i] : i) : 0;
-    const uint32_t dig = (static_cast<uint32_t>(key) >> shift) & 255u;
+    const uint32_t dig = (static_cast<uint32_t>(key) >> shift) & (NB - 1u);
     unsigned long long match = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < DB; ++b) {
       const bool bit = (dig >> b) & 1u;
       const unsigned long long bal = __ballot(bit);
       match &= bit ? bal : ~bal;
@@ -295,9 +303,11 @@ __global__ __launch_bounds__(256) void radix_scatter_kernel(
       vout[pos] = val;
     }
     __syncthreads();
-    base[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+    for (int q = tid; q < NB; q += 256) {
+      base[q] += wcnt[0][q] + wcnt[1][q] + wcnt[2][q] + wcnt[3][q];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0;
+      for (int v = 0; v < 4; ++v) wcnt[v][q] = 0;
+    }
     __syncthreads();
   }
 }
@@ -445,10 +455,10 @@ static int item_map_grid(int B) {
   return static_cast<int>(g < 2048 ? (g > 0 ? g : 1) : 2048);
 }
 
-static int digit_passes(int64_t vocab) {
+static int id_bits(int64_t vocab) {
   int bits = 1;
   while (bits < 32 && (int64_t(1) << bits) < vocab) ++bits;
-  return (bits + 7) / 8;
+  return bits;
 }
 
 hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
@@ -461,7 +471,11 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
   }
   const int nblk = ceil_div(B, kSortTile);
   header_init_kernel<<<1, 64, 0, s>>>(pd.header);
-  const int passes = digit_passes(p.vocab);
+  // 8-bit digits, or 9-bit ones where that saves a pass (17-18 bits and
+  // 25-27 bits of id range)
+  const int bits = id_bits(p.vocab);
+  const int db = (bits + 8) / 9 < (bits + 7) / 8 ? 9 : 8;
+  const int passes = (bits + db - 1) / db;
   // ping-pong so that the last pass lands in (sorted_ids, perm)
   int32_t* ka[2] = {pd.sorted_ids, pd.keys_alt};
   int32_t* va[2] = {pd.perm, pd.vals_alt};
@@ -469,12 +483,20 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
   const int32_t* kin = p.ids;
   const int32_t* vin = nullptr;
   for (int ps = 0; ps < passes; ++ps) {
-    const int shift = 8 * ps;
-    radix_hist_kernel<<<nblk, 256, 0, s>>>(kin, B, shift, pd.hist, nblk,
-                                           p.vocab, pd.header, ps == 0);
-    scan_single_kernel<<<1, 1024, 0, s>>>(pd.hist, 256 * nblk, nullptr);
-    radix_scatter_kernel<<<nblk, 256, 0, s>>>(kin, vin, ka[out], va[out], B,
-                                              shift, pd.hist, nblk);
+    const int shift = db * ps;
+    if (db == 9) {
+      radix_hist_kernel<9><<<nblk, 256, 0, s>>>(kin, B, shift, pd.hist, nblk,
+                                                p.vocab, pd.header, ps == 0);
+      scan_single_kernel<<<1, 1024, 0, s>>>(pd.hist, 512 * nblk, nullptr);
+      radix_scatter_kernel<9><<<nblk, 256, 0, s>>>(
+          kin, vin, ka[out], va[out], B, shift, pd.hist, nblk);
+    } else {
+      radix_hist_kernel<8><<<nblk, 256, 0, s>>>(kin, B, shift, pd.hist, nblk,
+                                                p.vocab, pd.header, ps == 0);
+      scan_single_kernel<<<1, 1024, 0, s>>>(pd.hist, 256 * nblk, nullptr);
+      radix_scatter_kernel<8><<<nblk, 256, 0, s>>>(
+          kin, vin, ka[out], va[out], B, shift, pd.hist, nblk);
+    }
     kin = ka[out];
     vin = va[out];
     out ^= 1;
