@@ -92,6 +92,64 @@ def oracle_backward(w: wl.Workload):
                               dd["beta"], dd["W_mix"], dd["dy"])
 
 
+def oracle_backward_sampled(w: wl.Workload, tokens, sample_ids):
+    """Reference gradients of a whole training batch, sampled: dx rows of
+    `tokens`, dK / dV rows of the ids in `sample_ids` (dict id -> [n, .]),
+    and the weight gradients dW_mix, dW_up, dgamma, dbeta over every token.
+
+    The oracle's own per-token steps (scores, softmax, aggregate, up,
+    layernorm, layernorm_backward, softmax_backward) in the order of its
+    backward; the weight gradients' sums over tokens are taken as one matrix
+    product each (dy^T [H ; X], dU^T A) instead of per-token outer products,
+    and the softmax backward runs only for the tokens the samples need.
+    tests/test_oracle_sampled.py checks it against the oracle's backward."""
+    from oracle import l3_oracle as O
+    dd = wl.decoded(w)
+    x, dy, ids, offsets = dd["x"], dd["dy"], dd["ids"], dd["offsets"]
+    W_up, W_mix = dd["W_up"], dd["W_mix"]
+    gamma, beta = dd["gamma"], dd["beta"]
+    B, d = x.shape
+    d_e = W_up.shape[1]
+    W_a, W_b = W_mix[:, :d], W_mix[:, d:]
+    tok_set = {int(t) for t in tokens}
+    id_set = {int(t) for t in sample_ids}
+    DH = dy @ W_a  # row i: W_a^T dy_i
+    H = np.zeros((B, d))
+    A = np.zeros((B, d_e))
+    DU = np.zeros((B, d))
+    UH = np.zeros((B, d))
+    dx = {}
+    dK = {}
+    dV = {}
+    for t in id_set:
+        n = int(offsets[t + 1] - offsets[t])
+        dK[t] = np.zeros((n, d))
+        dV[t] = np.zeros((n, d_e))
+    for i in range(B):
+        t = int(ids[i])
+        r0, r1 = int(offsets[t]), int(offsets[t + 1])
+        Kt = np.asarray(dd["K"][r0:r1], dtype=np.float64)
+        Vt = np.asarray(dd["V"][r0:r1], dtype=np.float64)
+        p = O.softmax(O.scores(Kt, x[i]))
+        a = O.aggregate(Vt, p)
+        u = O.up(W_up, a)
+        h, uhat, _, var = O.layernorm(u, gamma, beta)
+        du = O.layernorm_backward(DH[i], gamma, uhat, var)
+        H[i], A[i], DU[i], UH[i] = h, a, du, uhat
+        if i in tok_set or t in id_set:
+            da = W_up.T @ du
+            ds = O.softmax_backward(p, Vt @ da)
+            if i in tok_set:
+                dx[i] = W_b.T @ dy[i] + Kt.T @ ds
+            if t in id_set:
+                dK[t] += np.outer(ds, x[i])
+                dV[t] += np.outer(p, da)
+    return dict(dx=dx, dK=dK, dV=dV,
+                dW_mix=dy.T @ np.concatenate([H, x], axis=1),
+                dW_up=DU.T @ A, dgamma=(DH * UH).sum(axis=0),
+                dbeta=DH.sum(axis=0))
+
+
 def f64(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 

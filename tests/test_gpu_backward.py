@@ -95,3 +95,38 @@ def test_prefill_shapes_bf16_backward(tokens):
         print(f"prefill shapes {k}: max abs {e:.3e} (max |ref| "
               f"{np.abs(ref[k]).max():.2f})")
         assert e <= 2e-2, k
+
+
+@pytest.mark.timeout(900)
+def test_train_prefill_full_batch_sampled():
+    """The training step as the training bench times it: the whole
+    8192-token prefill batch (bf16 projections on split-K MFMA, the float32
+    operands as hi + lo halves, the segment backward on MFMA), against the
+    oracle's steps on samples: dx of 48 tokens, dK / dV of eight ids (the
+    four busiest, 512 rows each, and four drawn among the rest), and the
+    whole-batch weight gradients dW_mix, dW_up, dgamma, dbeta."""
+    import dataclasses
+    from static_token_routed_id_amd import workloads as wl
+    w = gu.workload("prefill_bf16")
+    w = dataclasses.replace(w, dy=wl.upstream_grad(w))
+    res = gu.run(w, training=True)
+    rng = np.random.default_rng(5)
+    tokens = np.sort(rng.choice(w.batch, 48, replace=False))
+    present = np.unique(w.ids)
+    ids = [int(t) for t in present[:4]] + \
+        [int(t) for t in rng.choice(present[4:], 4, replace=False)]
+    ref = gu.oracle_backward_sampled(w, tokens, ids)
+    g = {k: gu.f64(res["grads"][k]) for k in NAMES}
+    errs = {
+        "dx": gu.max_abs(g["dx"][tokens], np.stack([ref["dx"][int(i)]
+                                                    for i in tokens])),
+        "dK": max(gu.max_abs(g["dK"][w.offsets[t]:w.offsets[t + 1]],
+                             ref["dK"][t]) for t in ids),
+        "dV": max(gu.max_abs(g["dV"][w.offsets[t]:w.offsets[t + 1]],
+                             ref["dV"][t]) for t in ids),
+    }
+    for k in ("dW_mix", "dW_up", "dgamma", "dbeta"):
+        errs[k] = gu.max_abs(g[k], ref[k])
+    for k, e in errs.items():
+        print(f"full prefill batch {k}: max abs {e:.3e}")
+        assert e <= 2e-2, k
