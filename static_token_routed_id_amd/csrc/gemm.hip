@@ -167,12 +167,55 @@ template <typename TC>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g) {
   if (g.header && g.header[0] != 0) return;
   const int64_t mn = static_cast<int64_t>(g.M) * g.N;
+  // four consecutive outputs a thread (16-byte loads) when N allows; the
+  // shares are added in order z = 0, 1, ... whatever the loads' order
+  if (g.N % 4 == 0) {
+    const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (i >= mn) return;
+    float4 v = {0.f, 0.f, 0.f, 0.f};
+    const float* p = g.part + i;
+    int z = 0;
+    for (; z + 4 <= g.nsplit; z += 4) {
+      float4 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        q[u] = *reinterpret_cast<const float4*>(p + (z + u) * mn);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v.x += q[u].x;
+        v.y += q[u].y;
+        v.z += q[u].z;
+        v.w += q[u].w;
+      }
+    }
+    for (; z < g.nsplit; ++z) {
+      const float4 q = *reinterpret_cast<const float4*>(p + z * mn);
+      v.x += q.x;
+      v.y += q.y;
+      v.z += q.z;
+      v.w += q.w;
+    }
+    const int64_t m = i / g.N, n = i - m * g.N;
+    TC* c = static_cast<TC*>(g.C);
+    st<TC>(c, m * g.c_m + n, v.x);
+    st<TC>(c, m * g.c_m + n + 1, v.y);
+    st<TC>(c, m * g.c_m + n + 2, v.z);
+    st<TC>(c, m * g.c_m + n + 3, v.w);
+    return;
+  }
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= mn) return;
   float v = 0.f;
   for (int z = 0; z < g.nsplit; ++z) v += g.part[z * mn + i];
   const int64_t m = i / g.N, n = i - m * g.N;
   st<TC>(static_cast<TC*>(g.C), m * g.c_m + n, v);
+}
+
+// grid of gemm_reduce_kernel for M x N outputs
+static int reduce_grid(const GemmArgs& g) {
+  const int64_t mn = static_cast<int64_t>(g.M) * g.N;
+  const int64_t per = g.N % 4 == 0 ? 1024 : 256;
+  return static_cast<int>((mn + per - 1) / per);
 }
 
 template <typename TA, typename TB>
@@ -220,7 +263,7 @@ hipError_t gemm_launch(const GemmArgs& g0, int a_type, int b_type, int c_type,
   if (g.nsplit > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int rgrid = static_cast<int>((mn + 255) / 256);
+    const int rgrid = reduce_grid(g);
     if (c_type == kBF16)
       gemm_reduce_kernel<uint16_t><<<rgrid, 256, 0, s>>>(g);
     else
@@ -764,7 +807,7 @@ hipError_t gemm_nt_256_splitk_launch(const GemmArgs& g0, hipStream_t s,
   const int grid = static_cast<int>(tiles) * ns;
   gemm_nt_256_kernel<float, false><<<grid, 256, 0, s>>>(g);
   if (ns > 1) {
-    const int rgrid = static_cast<int>((mn + 255) / 256);
+    const int rgrid = reduce_grid(g);
     gemm_reduce_kernel<float><<<rgrid, 256, 0, s>>>(g);
   }
   return hipGetLastError();
