@@ -429,111 +429,125 @@ __device__ __forceinline__ void dx_block_load(const BwdArgs& a, int64_t r0,
 typedef short bwd_v4i16 __attribute__((ext_vector_type(4)));
 constexpr int kDxS = 64 + 8;  // dX_att staging row stride (elements)
 
-// dX_att = dS K_t (bf16 K, d a multiple of 256) on 16x16x32 bf16 MFMA, the
+// dX_att = dS K_t (bf16 K, d a multiple of 128) on 16x16x32 bf16 MFMA, the
 // same product shape as the forward's P V_t: tokens are the rows of A (dS,
 // float32, entering as bf16 hi + lo halves, two MFMAs), K_t's rows the
-// reduction. K_t moves through a wave-private LDS buffer in blocks of 32
-// rows x 64 columns (8 lanes a 128-byte row slice), read back as the B
-// operand with the transposing LDS read; the blocks are loaded three ahead
-// in a ring of registers (the product is small, the K_t stream is what
-// takes time). Columns in passes of 256 (16 accumulators of 16 x 16); the
-// next row block's dS is loaded one block ahead. Rows past n have zero
-// weights (their K rows are clamped to row n-1).
+// reduction. Columns in passes of 128 (8 accumulators of 16 x 16); K_t in
+// blocks of 32 rows x 128 columns, double buffered in registers a block at
+// a time: each iteration first requests the next block (and its dS), then
+// moves the current one through a wave-private LDS buffer, 64 columns at a
+// time (8 lanes a 128-byte row slice), and reads it back as the B operand
+// with the transposing LDS read. (A ring of single 64-column steps carried
+// across iterations lost its depth to the waits the compiler places after
+// a loop's back edge.) Rows past n have zero weights (their K rows are
+// clamped to row n-1).
 __device__ __forceinline__ void dx_att_mfma(const BwdArgs& a, int64_t r0,
                                             int n, int tok0, int mcount,
-                                            int lane, uint16_t* stg) {
+                                            int lane, uint16_t* stg,
+                                            int c_begin, int c_end) {
   const int r = lane & 15, g = lane >> 4;
   const uint16_t* K = static_cast<const uint16_t*>(a.K);
   const int trow = 8 * g + (r >> 2), tcol = 4 * (r & 3);
   const int srow = lane >> 3, scol = (lane & 7) * 8;
   const int nrb = ceil_div(n, 32);
-  const int nsteps = nrb * 4;  // (row block, 64-column block) steps
   const bool tok_ok = r < mcount;
-  const float* dsr = a.DSbuf + static_cast<int64_t>(tok0 + min(r, mcount - 1)) * a.kst;
+  const float* dsr =
+      a.DSbuf + static_cast<int64_t>(tok0 + min(r, mcount - 1)) * a.kst;
   auto ds_load = [&](int rb, float4& v0, float4& v1) {
     const int j = min(rb, nrb - 1) * 32 + 8 * g;
     v0 = *reinterpret_cast<const float4*>(dsr + j);
     v1 = *reinterpret_cast<const float4*>(dsr + j + 4);
   };
-  for (int cc = 0; cc < a.d; cc += 256) {
-    floatx4 acc[16];
+  auto split = [&](int rb, const float4& v0, const float4& v1, u32x4& hi,
+                   u32x4& lo) {
+    const int j0 = rb * 32 + 8 * g;
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int nb = 0; nb < 16; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    constexpr int R = 4;
-    u32x4 kr[R][4];
-    auto load_k = [&](int slot, int t) {
-      const int tt = min(t, nsteps - 1);
-      const int j0 = (tt >> 2) * 32, c0 = cc + (tt & 3) * 64;
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = tok_ok && j0 + 2 * e < n ? v[2 * e] : 0.f;
+      const float x1 = tok_ok && j0 + 2 * e + 1 < n ? v[2 * e + 1] : 0.f;
+      h[e] = f2bf2(x0, x1);
+      l[e] = f2bf2(x0 - __uint_as_float(h[e] << 16),
+                   x1 - __uint_as_float(h[e] & 0xffff0000u));
+    }
+    hi = u32x4{h[0], h[1], h[2], h[3]};
+    lo = u32x4{l[0], l[1], l[2], l[3]};
+  };
+  for (int cc = c_begin; cc < c_end; cc += 128) {
+    // block rb: rows rb*32 .., columns cc .. cc+127: chunk (sb, k) of
+    // 64-column half sb, rows k*8 + srow, 8 columns at scol
+    auto load_blk = [&](u32x4 (&b)[8], int rb) {
+      const int j0 = min(rb, nrb - 1) * 32;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = min(j0 + q * 8 + srow, n - 1);
-        kr[slot][q] = *reinterpret_cast<const u32x4*>(
-            K + (r0 + j) * a.d + c0 + scol);
-      }
-    };
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-    for (int q = 0; q < R - 1; ++q) load_k(q, q);
-    float4 dn0, dn1;
-    ds_load(0, dn0, dn1);
-    u32x4 ahi = {0, 0, 0, 0}, alo = {0, 0, 0, 0};
-    for (int base = 0; base < nsteps; base += R) {
-#pragma unroll
-      for (int q = 0; q < R; ++q) {
-        const int t = base + q;
-        load_k((q + R - 1) % R, t + R - 1);
-        if (q == 0) {
-          // new row block (R = 4 steps a block): its dS as hi / lo bf16,
-          // the next block's dS requested
-          const int j0 = (t >> 2) * 32 + 8 * g;
-          const float v[8] = {dn0.x, dn0.y, dn0.z, dn0.w,
-                              dn1.x, dn1.y, dn1.z, dn1.w};
-          ds_load((t >> 2) + 1, dn0, dn1);
-          uint32_t h[4], l[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x0 = tok_ok && j0 + 2 * e < n ? v[2 * e] : 0.f;
-            const float x1 = tok_ok && j0 + 2 * e + 1 < n ? v[2 * e + 1] : 0.f;
-            h[e] = f2bf2(x0, x1);
-            const float h0 = __uint_as_float(h[e] << 16);
-            const float h1 = __uint_as_float(h[e] & 0xffff0000u);
-            l[e] = f2bf2(x0 - h0, x1 - h1);
-          }
-          ahi = u32x4{h[0], h[1], h[2], h[3]};
-          alo = u32x4{l[0], l[1], l[2], l[3]};
+        for (int k = 0; k < 4; ++k) {
+          const int j = min(j0 + k * 8 + srow, n - 1);
+          b[sb * 4 + k] = *reinterpret_cast<const u32x4*>(
+              K + (r0 + j) * a.d + cc + sb * 64 + scol);
         }
+    };
+    floatx4 acc[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // block rb's dS as the A operand, its K rows through LDS as B
+    auto consume = [&](const u32x4 (&b)[8], int rb, const float4& v0,
+                       const float4& v1) {
+      u32x4 ahi, alo;
+      split(rb, v0, v1, ahi, alo);
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           *reinterpret_cast<u32x4*>(&stg[(k * 8 + srow) * kDxS + scol]) =
-              kr[q][k];
+              b[sb * 4 + k];
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           typedef __attribute__((address_space(3))) bwd_v4i16 lds_v4i16;
-          const bwd_v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          const bwd_v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_v4i16*)(&stg[trow * kDxS + nb * 16 + tcol]));
-          const bwd_v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          const bwd_v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_v4i16*)(&stg[(trow + 4) * kDxS + nb * 16 + tcol]));
-          const uint2 l2 = __builtin_bit_cast(uint2, lo);
-          const uint2 h2 = __builtin_bit_cast(uint2, hi);
+          const uint2 l2 = __builtin_bit_cast(uint2, lo4);
+          const uint2 h2 = __builtin_bit_cast(uint2, hi4);
           const u32x4 bf = u32x4{l2.x, l2.y, h2.x, h2.y};
-          floatx4& ac = acc[q * 4 + nb];
+          floatx4& ac = acc[sb * 4 + nb];
           ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, ahi), __builtin_bit_cast(bf16x8_t, bf),
-              ac, 0, 0, 0);
+              __builtin_bit_cast(bf16x8_t, ahi),
+              __builtin_bit_cast(bf16x8_t, bf), ac, 0, 0, 0);
           ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, alo), __builtin_bit_cast(bf16x8_t, bf),
-              ac, 0, 0, 0);
+              __builtin_bit_cast(bf16x8_t, alo),
+              __builtin_bit_cast(bf16x8_t, bf), ac, 0, 0, 0);
         }
+      }
+    };
+    // two named buffers, two blocks an iteration: the block being used was
+    // requested one block earlier, and nothing is copied between buffers
+    u32x4 bA[8], bB[8];
+    float4 dA0, dA1, dB0, dB1;
+    ds_load(0, dA0, dA1);
+    load_blk(bA, 0);
+    for (int rb = 0; rb < nrb; rb += 2) {
+      ds_load(rb + 1, dB0, dB1);
+      load_blk(bB, rb + 1);
+      consume(bA, rb, dA0, dA1);
+      if (rb + 1 < nrb) {
+        ds_load(rb + 2, dA0, dA1);
+        load_blk(bA, rb + 2);
+        consume(bB, rb + 1, dB0, dB1);
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 4 * g + i;
       if (t < mcount) {
-        float* dst = a.dx + static_cast<int64_t>(a.perm[tok0 + t]) * a.d + cc + r;
+        float* dst =
+            a.dx + static_cast<int64_t>(a.perm[tok0 + t]) * a.d + cc + r;
 #pragma unroll
-        for (int nb = 0; nb < 16; ++nb) dst[nb * 16] += acc[nb][i];
+        for (int nb = 0; nb < 8; ++nb) dst[nb * 16] += acc[nb][i];
       }
     }
   }
@@ -541,8 +555,7 @@ __device__ __forceinline__ void dx_att_mfma(const BwdArgs& a, int64_t r0,
 
 template <typename T>
 __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int s, int tile,
-                                         int lane, float* lds,
-                                         uint16_t* stg) {
+                                         int lane, float* lds) {
   const int r = lane & 15, g = lane >> 4;
   const int t_begin = a.seg_tok_start[s];
   const int m = a.seg_tok_start[s + 1] - t_begin;
@@ -588,11 +601,11 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int s, int tile,
 #undef L3_NB_DISPATCH
   // dS was written by other lanes of this wave
   __threadfence_block();
+  // bf16, d a multiple of 128: dX_att is seg_bwd_dx_kernel's, one wave per
+  // (tile, 128 columns), so that a busy id's tiles do not each stream all of
+  // K_t through one wave
   if constexpr (sizeof(T) == 2) {
-    if (a.d % 256 == 0) {
-      dx_att_mfma(a, r0, n, tok0, mcount, lane, stg);
-      return;
-    }
+    if (a.d % 128 == 0) return;
   }
   // dX_att = dS K_t: lane owns 4 columns of a 256-column pass, all 16
   // tokens; per 16-row block the tokens' dS are staged transposed in this
@@ -661,10 +674,38 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int s, int tile,
   }
 }
 
+// dX_att of the tiles, after seg_bwd_tile_kernel has written their dS: one
+// wave per (tile, 128-column pass), the forward's work items in order with
+// the passes innermost (a busy id's tiles and passes spread over waves).
+__global__ __launch_bounds__(256, 2) void seg_bwd_dx_kernel(BwdArgs a) {
+  __shared__ __align__(16) uint16_t s_stg[4][32 * kDxS];
+  if (a.header[0] != 0) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n_items = a.header[a.count_slot];
+  const int npass = a.d / 128;
+  const int64_t total = static_cast<int64_t>(n_items) * npass;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 4 + w; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * 4) {
+    const int2 im = a.item_map[idx / npass];
+    const int pass = static_cast<int>(idx % npass);
+    const int s = im.x;
+    const int n = a.seg_n[s];
+    const int nch = ceil_div(n, a.chunk_rows);
+    // the forward's items are (token tile, row chunk): take each tile once
+    if (im.y % nch != 0) continue;
+    const int tile = im.y / nch;
+    const int t_begin = a.seg_tok_start[s];
+    const int m = a.seg_tok_start[s + 1] - t_begin;
+    const int tok0 = t_begin + tile * kTokTile;
+    const int mcount = min(kTokTile, m - tile * kTokTile);
+    dx_att_mfma(a, a.seg_row_off[s], n, tok0, mcount, lane, s_stg[w],
+                pass * 128, pass * 128 + 128);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256, 2) void seg_bwd_tile_kernel(BwdArgs a) {
   __shared__ __align__(16) float s_ds[4][16 * kTokTile];
-  __shared__ __align__(16) uint16_t s_stg[4][32 * kDxS];
   if (a.header[0] != 0) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n_items = a.header[a.count_slot];
@@ -675,7 +716,7 @@ __global__ __launch_bounds__(256, 2) void seg_bwd_tile_kernel(BwdArgs a) {
     const int nch = ceil_div(a.seg_n[s], a.chunk_rows);
     // the forward's items are (token tile, row chunk): take each tile once
     if (im.y % nch != 0) continue;
-    bwd_tile<T>(a, s, im.y / nch, lane, s_ds[w], s_stg[w]);
+    bwd_tile<T>(a, s, im.y / nch, lane, s_ds[w]);
   }
 }
 
@@ -1052,6 +1093,13 @@ hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int items_ub, int S_ub,
     seg_bwd_tile_kernel<float><<<grid, 256, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (dtype == kBF16 && a.d % 128 == 0) {
+    const int64_t dx_blocks = (static_cast<int64_t>(items_ub) * (a.d / 128) + 3) / 4;
+    seg_bwd_dx_kernel<<<static_cast<int>(dx_blocks < 8192 ? dx_blocks : 8192),
+                        256, 0, s>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   rows_items_kernel<<<1, 1024, 0, s>>>(a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
