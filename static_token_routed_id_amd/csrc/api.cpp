@@ -221,6 +221,7 @@ struct BwdBufs {
   int* rows_count;
   int2* zero_map;   // 64-row pieces of the absent ids' rows
   int* zero_count;
+  float4* chunk_stats;  // [B x ceil(k_max / 32)] (bf16 only)
 };
 int64_t zero_items_for(const l3_desc& d, int64_t B) {
   return d.rows / 64 + B + 2;
@@ -250,6 +251,10 @@ BwdBufs carve_bwd(Carver& c, const l3_desc& d, int64_t B) {
   b.rows_count = c.take<int>(64);
   b.zero_map = c.take<int2>(static_cast<size_t>(zero_items_for(d, B)));
   b.zero_count = c.take<int>(64);
+  // row chunks are at least 32 rows
+  b.chunk_stats = b16 ? c.take<float4>(static_cast<size_t>(B) *
+                                       ((d.k_max + 31) / 32))
+                      : nullptr;
   return b;
 }
 
@@ -1191,6 +1196,8 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
     ba.rows_count = bb.rows_count;
     ba.zero_map = bb.zero_map;
     ba.zero_count = bb.zero_count;
+    ba.chunk_stats = bb.chunk_stats;
+    ba.cs_stride = (d.k_max + 31) / 32;
     {
       StageTimer t(plan, ST_BWD_LN, s);
       e = ln_bwd_launch(ba, d.dtype, s);

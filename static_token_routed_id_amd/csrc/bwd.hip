@@ -674,6 +674,104 @@ __device__ __forceinline__ void bwd_tile(const BwdArgs& a, int s, int tile,
   }
 }
 
+// The tile pass split by row chunk (bf16, d a multiple of 128): every work
+// item (token tile, row chunk) of the saving forward is a wave of its own.
+// seg_bwd_chunk_kernel: scores and dP of the chunk (raw, into the p / dS
+// arrays) and the chunk's own softmax statistics per token (M, L, Q of its
+// rows) into a [B x chunks] array; seg_bwd_finish_kernel: the tile's chunk
+// statistics combined in chunk order (M = max M_c, L = sum L_c e^(M_c - M),
+// Q likewise), then p and dS of the chunk. A busy id's tile so spreads over
+// as many waves as it has chunks.
+template <typename T>
+__device__ __forceinline__ void chunk_item(const BwdArgs& a, int2 im,
+                                           int lane, bool finish) {
+  const int r = lane & 15, g = lane >> 4;
+  const int s = im.x;
+  const int n = a.seg_n[s];
+  const int nch = ceil_div(n, a.chunk_rows);
+  const int tile = im.y / nch, ch = im.y - tile * nch;
+  const int t_begin = a.seg_tok_start[s];
+  const int m = a.seg_tok_start[s + 1] - t_begin;
+  const int64_t r0 = a.seg_row_off[s];
+  const int tok0 = t_begin + tile * kTokTile;
+  const int mcount = min(kTokTile, m - tile * kTokTile);
+  const int c_lo = ch * a.chunk_rows, c_hi = min(n, c_lo + a.chunk_rows);
+#define L3_NB_DISPATCH(CALL)  \
+  if (nbc <= 1) {             \
+    CALL(1);                  \
+  } else if (nbc <= 2) {      \
+    CALL(2);                  \
+  } else if (nbc <= 4) {      \
+    CALL(4);                  \
+  } else {                    \
+    CALL(8);                  \
+  }
+  TileStats st;
+  if (!finish) {
+    const int64_t xi = a.perm[tok0 + min(r, mcount - 1)];
+    const T* xr = static_cast<const T*>(a.x) + xi * a.d;
+    const float* dar = a.dA + xi * a.d_e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st.M[i] = -INFINITY;
+      st.L[i] = 0.f;
+      st.Q[i] = 0.f;
+    }
+    for (int c0 = c_lo; c0 < c_hi; c0 += kWaveMaxRows) {
+      const int nc = min(kWaveMaxRows, c_hi - c0);
+      const int nbc = ceil_div(nc, 16);
+#define L3_CHUNK(NB) \
+  bwd_chunk<T, NB>(a, xr, dar, r0 + c0, nc, r, g, tok0, c0, mcount, st)
+      L3_NB_DISPATCH(L3_CHUNK)
+#undef L3_CHUNK
+    }
+    if (r == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * g + i;
+        if (t < mcount)
+          a.chunk_stats[static_cast<int64_t>(tok0 + t) * a.cs_stride + ch] =
+              make_float4(st.M[i], st.L[i], st.Q[i], 0.f);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = min(4 * g + i, mcount - 1);
+      const float4* cs = a.chunk_stats + static_cast<int64_t>(tok0 + t) * a.cs_stride;
+      float M = -INFINITY;
+      for (int c = 0; c < nch; ++c) M = fmaxf(M, cs[c].x);
+      float L = 0.f, Q = 0.f;
+      for (int c = 0; c < nch; ++c) {
+        const float4 v = cs[c];
+        const float sc = __expf(v.x - M);
+        L = fmaf(v.y, sc, L);
+        Q = fmaf(v.z, sc, Q);
+      }
+      st.M[i] = M;
+      st.L[i] = L;
+      st.Q[i] = Q;
+    }
+    for (int c0 = c_lo; c0 < c_hi; c0 += kWaveMaxRows) {
+      const int nc = min(kWaveMaxRows, c_hi - c0);
+      const int nbc = ceil_div(nc, 16);
+#define L3_FIN(NB) bwd_chunk_finish<NB>(a, nc, r, g, tok0, c0, mcount, st)
+      L3_NB_DISPATCH(L3_FIN)
+#undef L3_FIN
+    }
+  }
+#undef L3_NB_DISPATCH
+}
+
+template <typename T, bool FINISH>
+__global__ __launch_bounds__(256, 2) void seg_bwd_chunk_kernel(BwdArgs a) {
+  if (a.header[0] != 0) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n_items = a.header[a.count_slot];
+  for (int item = blockIdx.x * 4 + w; item < n_items; item += gridDim.x * 4)
+    chunk_item<T>(a, a.item_map[item], lane, FINISH);
+}
+
 // dX_att of the tiles, after seg_bwd_tile_kernel has written their dS: one
 // wave per (tile, 128-column pass), the forward's work items in order with
 // the passes innermost (a busy id's tiles and passes spread over waves).
@@ -1087,10 +1185,15 @@ hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int items_ub, int S_ub,
   if (items_ub <= 0 || S_ub <= 0) return hipSuccess;
   int grid = ceil_div(items_ub, 4);
   if (grid > 8192) grid = 8192;
-  if (dtype == kBF16)
+  const bool split = dtype == kBF16 && a.d % 128 == 0 && a.chunk_stats;
+  if (split) {
+    seg_bwd_chunk_kernel<uint16_t, false><<<grid, 256, 0, s>>>(a);
+    seg_bwd_chunk_kernel<uint16_t, true><<<grid, 256, 0, s>>>(a);
+  } else if (dtype == kBF16) {
     seg_bwd_tile_kernel<uint16_t><<<grid, 256, 0, s>>>(a);
-  else
+  } else {
     seg_bwd_tile_kernel<float><<<grid, 256, 0, s>>>(a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dtype == kBF16 && a.d % 128 == 0) {

@@ -305,6 +305,10 @@ struct BwdArgs {
   // (first row, rows <= 64) pieces of the absent ids' rows, and their count
   int2* zero_map;      // [rows / 64 + B + 2] at most
   int* zero_count;
+  // per (token, row chunk) softmax statistics (M, L, Q, -) of the chunked
+  // tile pass; NULL: one wave walks each tile's chunks
+  float4* chunk_stats; // [B x cs_stride]
+  int cs_stride;       // row chunks of the longest id
 };
 // Zeroes dK, dV rows of the ids absent from the batch (d, d_e multiples of
 // 4); items_ub bounds the number of 64-row pieces.
