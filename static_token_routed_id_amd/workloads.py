@@ -84,10 +84,18 @@ SPECS = {
     "train_skew_bf16": Spec("train_skew_bf16", "bf16", 256, 1.1, 2048, 32,
                             64, 64, 512, 1.0 / 8, 1.0 / 8, hot_frac=0.3,
                             hot_rows=512, hot_id_zipf_s=1.0, training=True),
+    # the same skew at the prefill shapes (d = 1024, d_e = 256, 8192 tokens,
+    # 30% of them on id 0, which has 512 rows)
+    "train_skew_prefill_bf16": Spec("train_skew_prefill_bf16", "bf16", 32768,
+                                    1.0, 1 << 18, 512, 1024, 256, 8192,
+                                    1.0 / 32, 1.0 / 16, hot_frac=0.3,
+                                    hot_rows=512, hot_id_zipf_s=1.0,
+                                    training=True),
 }
 # index order used by the measurement configs
 CONFIG_ORDER = ["tiny_fp32", "prefill_bf16", "decode_bf16",
-                "large_prefill_bf16", "train_skew_bf16"]
+                "large_prefill_bf16", "train_skew_bf16",
+                "train_skew_prefill_bf16"]
 
 
 def _rng(cfg: int, stream: int, block: int = 0) -> np.random.Generator:

@@ -98,16 +98,19 @@ def test_prefill_shapes_bf16_backward(tokens):
 
 
 @pytest.mark.timeout(900)
-def test_train_prefill_full_batch_sampled():
-    """The training step as the training bench times it: the whole
-    8192-token prefill batch (bf16 projections on split-K MFMA, the float32
-    operands as hi + lo halves, the segment backward on MFMA), against the
-    oracle's steps on samples: dx of 48 tokens, dK / dV of eight ids (the
-    four busiest, 512 rows each, and four drawn among the rest), and the
-    whole-batch weight gradients dW_mix, dW_up, dgamma, dbeta."""
+@pytest.mark.parametrize("name", ["prefill_bf16", "train_skew_prefill_bf16"])
+def test_train_prefill_full_batch_sampled(name):
+    """The training step as the training bench times it: a whole 8192-token
+    batch at the prefill shapes (bf16 projections on split-K MFMA, the
+    float32 operands as hi + lo halves, the segment backward on MFMA), the
+    Zipf id stream and the skewed one (30% of the tokens on id 0, 512
+    rows), against the oracle's steps on samples: dx of 48 tokens, dK / dV
+    of eight ids (the four busiest, 512 rows each, and four drawn among the
+    rest), and the whole-batch weight gradients dW_mix, dW_up, dgamma,
+    dbeta."""
     import dataclasses
     from static_token_routed_id_amd import workloads as wl
-    w = gu.workload("prefill_bf16")
+    w = gu.workload(name)
     w = dataclasses.replace(w, dy=wl.upstream_grad(w))
     res = gu.run(w, training=True)
     rng = np.random.default_rng(5)
@@ -128,5 +131,5 @@ def test_train_prefill_full_batch_sampled():
     for k in ("dW_mix", "dW_up", "dgamma", "dbeta"):
         errs[k] = gu.max_abs(g[k], ref[k])
     for k, e in errs.items():
-        print(f"full prefill batch {k}: max abs {e:.3e}")
+        print(f"{name} full batch {k}: max abs {e:.3e}")
         assert e <= 2e-2, k

@@ -8,7 +8,7 @@ from static_token_routed_id_amd import workloads as wl
 # rows R = sum of capped Zipf allocations, one per configuration
 EXPECTED_ROWS = {"tiny_fp32": 1135, "prefill_bf16": 171462,
                  "decode_bf16": 588017, "large_prefill_bf16": 1759242,
-                 "train_skew_bf16": 1615}
+                 "train_skew_bf16": 1615, "train_skew_prefill_bf16": 171462}
 
 
 @pytest.mark.parametrize("name", wl.CONFIG_ORDER)
