@@ -379,6 +379,16 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmArgs g) {
 // renumbered to give each XCD a contiguous range of the logical order, which
 // walks groups of 4 row-tiles x all column-tiles; the workgroups resident
 // on one XCD at a time share A and B panels in that XCD's L2.
+//
+// Options (GemmArgs): both operands switch source at k = K1 (A1 / A2, and
+// B1 / Bm when B1 is set; b2_rel indexes Bm's columns from K1); K split over
+// nsplit workgroups per tile into float32 partials (gemm_nt_256_splitk_
+// launch); the LayerNorm fold, producer side (ln_stats_out: per-row sum and
+// sum of squares of the tile after the stores) and consumer side (FOLD:
+// per-row and per-column terms staged in LDS, one accumulator rescale
+// between the k < K1 and k >= K1 loops, with explicit AGPR moves: a
+// conditional rescale of the accumulators inside one loop made the register
+// allocator spill, and a kernel with any spill runs several percent slower).
 constexpr int kTM = 256, kTN = 256, kTK = 64, kTL = kTK + 8;
 constexpr int kXcd = 8, kGroupM = 4;
 
