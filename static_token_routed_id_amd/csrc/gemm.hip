@@ -712,14 +712,20 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
   }
 }
 
-bool gemm_nt_256_ok(const GemmArgs& g) {
+// Shape rules of the 256 x 256 kernel; gemm_nt_256_ok adds M >= 1024 (below
+// that the launcher prefers other tilings, or the split-K form for few rows).
+static bool gemm_nt_256_shape_ok(const GemmArgs& g) {
   // buffer offsets are 32-bit: one tile's rows must span < 2 GiB
-  return g.M >= 1024 && g.N % kTN == 0 && g.K % kTK == 0 &&
+  return g.M > 0 && g.N % kTN == 0 && g.K % kTK == 0 &&
          g.K1 % kTK == 0 && g.a1_k == 1 && g.a2_k == 1 && g.b_k == 1 &&
          g.a1_m % 8 == 0 && g.a2_m % 8 == 0 && g.b_n % 8 == 0 &&
          static_cast<int64_t>(kTM) * g.a1_m * 2 < (int64_t(1) << 30) &&
          static_cast<int64_t>(kTM) * g.a2_m * 2 < (int64_t(1) << 30) &&
          static_cast<int64_t>(kTN) * g.b_n * 2 < (int64_t(1) << 30);
+}
+
+bool gemm_nt_256_ok(const GemmArgs& g) {
+  return g.M >= 1024 && gemm_nt_256_shape_ok(g);
 }
 
 // ------------------------------------------------- LayerNorm of bf16 u ---
@@ -799,8 +805,8 @@ hipError_t ln_apply_launch(const LnApplyArgs& a, hipStream_t s) {
 // (the caller then takes another path).
 hipError_t gemm_nt_256_splitk_launch(const GemmArgs& g0, hipStream_t s,
                                      float* part, int64_t part_floats,
-                                     int max_split) {
-  if (!gemm_nt_256_ok(g0)) return hipErrorInvalidValue;
+                                     int max_split, int c_type) {
+  if (!gemm_nt_256_shape_ok(g0)) return hipErrorInvalidValue;
   if (!part) part_floats = 0;
   GemmArgs g = g0;
   const int64_t tiles =
@@ -815,10 +821,17 @@ hipError_t gemm_nt_256_splitk_launch(const GemmArgs& g0, hipStream_t s,
   g.nsplit = ns;
   g.part = ns > 1 ? part : nullptr;
   const int grid = static_cast<int>(tiles) * ns;
-  gemm_nt_256_kernel<float, false><<<grid, 256, 0, s>>>(g);
+  // the shares' partials are float32 whatever C is; one share writes C
+  if (ns > 1 || c_type != kBF16)
+    gemm_nt_256_kernel<float, false><<<grid, 256, 0, s>>>(g);
+  else
+    gemm_nt_256_kernel<uint16_t, false><<<grid, 256, 0, s>>>(g);
   if (ns > 1) {
     const int rgrid = reduce_grid(g);
-    gemm_reduce_kernel<float><<<rgrid, 256, 0, s>>>(g);
+    if (c_type == kBF16)
+      gemm_reduce_kernel<uint16_t><<<rgrid, 256, 0, s>>>(g);
+    else
+      gemm_reduce_kernel<float><<<rgrid, 256, 0, s>>>(g);
   }
   return hipGetLastError();
 }
@@ -929,8 +942,14 @@ hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s,
       static_cast<int64_t>(ceil_div(g.M, kTM)) * (g.N / kTN);
   const int64_t tiles128 =
       static_cast<int64_t>(ceil_div(g.M, kBM)) * (g.N / kBN);
-  if (tiles128 < cus && part)
+  if (tiles128 < cus && part) {
+    // few rows (decode): the weights stream through every CU on the bf16
+    // 256 x 256 kernel with K split (rows past M read as zero), else the
+    // generic kernel with K split
+    if (gemm_nt_256_shape_ok(g) && !g.ln_stats_out && !g.ln_rows)
+      return gemm_nt_256_splitk_launch(g, s, part, part_floats, 32, c_type);
     return gemm_launch(g, kBF16, kBF16, c_type, s, part, part_floats);
+  }
   if (gemm_nt_256_ok(g)) {
     const int grid = static_cast<int>(tiles256);
     // the LayerNorm fold (consumer side) has its own instantiation

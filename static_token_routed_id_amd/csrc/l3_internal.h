@@ -339,7 +339,8 @@ hipError_t transpose_split_launch(const int32_t* header, const float* src,
 // if the shape rules of the 256 x 256 kernel do not hold.
 hipError_t gemm_nt_256_splitk_launch(const GemmArgs& g, hipStream_t s,
                                      float* part, int64_t part_floats,
-                                     int max_split = 16);
+                                     int max_split = 16,
+                                     int c_type = kF32);
 hipError_t ln_bwd_launch(const BwdArgs& a, int dtype, hipStream_t s);
 hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int items_ub,
                           int S_ub, hipStream_t s);
