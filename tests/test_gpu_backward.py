@@ -61,6 +61,25 @@ def test_backward_deterministic():
         assert torch.equal(g1[k], g2[k]), k
 
 
+def test_backward_deterministic_prefill_shapes():
+    """Bitwise-equal reruns where the training step takes its MFMA paths
+    (1024 tokens of the prefill batch, d = 1024): split-K shares added in
+    order, chunk statistics combined in chunk order, one writer per dK, dV
+    and dx element."""
+    import dataclasses
+    from static_token_routed_id_amd import workloads as wl
+    torch = gu.torch_cuda()
+    base = gu.workload("prefill_bf16")
+    w = wl.with_ids(base, base.ids[:1024])
+    g = np.random.default_rng(9).standard_normal((1024, base.spec.d))
+    w = dataclasses.replace(w, dy=wl.store(g, "bf16"))
+    dev = gu.Dev(w)
+    g1 = gu.run(w, dev, training=True)["grads"]
+    g2 = gu.run(w, dev, training=True)["grads"]
+    for k in NAMES:
+        assert torch.equal(g1[k], g2[k]), k
+
+
 def test_backward_without_save_is_an_error():
     L = gu.lib()
     w = gu.workload("train_skew_bf16")
