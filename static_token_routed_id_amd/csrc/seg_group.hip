@@ -48,6 +48,8 @@ namespace l3 {
 #define L3_WAVE_FIRST_EVERY 2
 #endif
 constexpr int kWaveFirstEvery = L3_WAVE_FIRST_EVERY;
+// 64-token items of ids with more rows than this take the busy-id path
+constexpr int kGroupAsHotRows = 384;
 constexpr int kGW = 8;                 // waves per workgroup
 constexpr int kGT = kGroupTok;         // tokens per item
 constexpr int kGRows = L3_MAX_ROWS_PER_ID;
@@ -700,7 +702,15 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
     const int s = im.x;
     const int t_begin = a.seg_tok_start[s];
     const int m = a.seg_tok_start[s + 1] - t_begin;
-    if (m <= kGT) {
+    if (m <= kGT && a.seg_n[s] > kGroupAsHotRows) {
+      // ids with most of the 512 rows take the busy-id path: whole-line K
+      // loads staged through LDS stream faster (≈ 22 against ≈ 19 GB/s a
+      // CU), and with > 384 rows its 64-row-per-wave split keeps the eight
+      // waves busy
+      if (threadIdx.x == 0) next = atomicAdd(&work[0], 1);
+      hot_item<2, NBV>(a, t_begin, m, a.seg_n[s], a.seg_row_off[s], smem,
+                       s_red, (s * 7) % (a.d / kHS));
+    } else if (m <= kGT) {
     const int n = a.seg_n[s];
     const int64_t rowbase = a.seg_row_off[s];
     const int tok0 = t_begin;
