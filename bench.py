@@ -119,7 +119,11 @@ def calibrate_copy(nbytes: int = 1 << 30, reps: int = 3) -> None:
 
 def gemm_flops(w) -> dict:
     B, d, d_e = w.batch, w.spec.d, w.spec.d_e
-    return dict(up_proj=2.0 * B * d * d_e, mix_proj=2.0 * B * d * 2 * d)
+    # up_quad / mix_up_proj: the forward with W_up folded into W_mix (a G
+    # over K = 2 d_e for the row variances, [a ; x] over K = d_e + d)
+    return dict(up_proj=2.0 * B * d * d_e, mix_proj=2.0 * B * d * 2 * d,
+                up_quad=2.0 * B * d_e * 2 * d_e,
+                mix_up_proj=2.0 * B * d * (d_e + d))
 
 
 def cpu_baseline_train(w, dy, budget_s: float) -> dict:
@@ -453,7 +457,7 @@ def main():
     gbs = lambda b, t: round(b / (t * 1e-3) / 1e9, 1) if t > 0 else None
     fl = gemm_flops(w)
     mfma = {}
-    for k in ("up_proj", "mix_proj"):
+    for k in ("up_proj", "mix_proj", "up_quad", "mix_up_proj"):
         if k in stage_avg and stage_avg[k] > 0:
             tf = fl[k] / (stage_avg[k] * 1e-3) / 1e12
             mfma[k] = {"tflops": round(tf, 1),

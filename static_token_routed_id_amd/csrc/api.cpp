@@ -52,12 +52,15 @@ enum Stage {
   ST_BWD_UP,
   ST_BWD_SEG,
   ST_GROUP,
+  ST_WFOLD,
+  ST_UP_QUAD,
+  ST_MIX_UP,
   ST_COUNT
 };
 const char* const kStageNames[ST_COUNT] = {
-    "plan",     "seg_fwd", "seg_combine",   "up_proj", "layernorm",
-    "mix_proj", "bwd_mix", "bwd_layernorm", "bwd_up",  "bwd_seg",
-    "seg_group"};
+    "plan",        "seg_fwd", "seg_combine",   "up_proj", "layernorm",
+    "mix_proj",    "bwd_mix", "bwd_layernorm", "bwd_up",  "bwd_seg",
+    "seg_group",   "weight_fold", "up_quad", "mix_up_proj"};
 
 bool debug_sync() {
   static const bool on = [] {
@@ -103,6 +106,13 @@ int nch_for(int64_t B, int k_max) {
 // slice); 0 disables it. Small batches keep every id on the wave kernel,
 // whose row chunks spread one id over many wavefronts.
 constexpr int kGroupMinRows = 128;
+// Whether folding W_up into W_mix pays: the flops it saves (the W_up GEMM
+// and d - d_e of W_mix's K, less the a G product) must reach 1e11, about
+// twice what the per-call weight products (~0.1 ms) cost at the GEMMs' rate.
+bool fuse_up_pays(int64_t B, int64_t d, int64_t de) {
+  const double per_row = 2.0 * d * de + 2.0 * d * (d - de) - 4.0 * de * de;
+  return static_cast<double>(B) * per_row >= 1e11;
+}
 int group_min_rows_for(const l3_desc& d, int64_t B) {
   return (d.dtype == L3_BF16 && B > 2048 && seg_group_ok(d.d, d.d_e))
              ? kGroupMinRows
@@ -875,10 +885,145 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     const int64_t fold_c = static_cast<int64_t>(d.d) * 8;
     const int64_t fold_st = B * (d.d / 256) * 8;
     const int64_t fold_rows = B * 8;
-    const bool fold = u_bf16 && !f.gpart && d.d % 256 == 0 &&
-                      gemm_nt_256_ok(up) && gemm_nt_256_ok(mx) &&
-                      fold_w1 + fold_c + fold_st + fold_rows <= B * d.d * 2;
+    const bool fold_ok = u_bf16 && !f.gpart && d.d % 256 == 0 &&
+                         gemm_nt_256_ok(up) && gemm_nt_256_ok(mx) &&
+                         fold_w1 + fold_c + fold_st + fold_rows <= B * d.d * 2;
+    // Large batches go one step further: W_up itself is folded through
+    // LayerNorm into W_mix, so u is never formed. With Wc = W_up with its
+    // columns centred over the d outputs, u - mean(u) = Wc a, hence
+    //   var(u) = a^T G a / d,  G = Wc^T Wc            (d_e x d_e)
+    //   W_mix1 h = rstd * (Mc a) + W_mix1 beta,  Mc = W_mix1 diag(gamma) Wc
+    // (d x d_e). G and Mc are products of the weights (per call, hi | lo
+    // operands on the bf16 kernel); per row, a^T G a comes from a GEMM
+    // a G whose epilogue dots each row with a itself, and y takes
+    // [a ; x] against [Mc | W_mix2] over K = d_e + d instead of 2d.
+    const int64_t DD = d.d, DE = d.d_e;
+    auto al = [](int64_t v) { return (v + 255) & ~int64_t(255); };
+    const int64_t o_t = al(4 * DD * DD), o_mt = al(o_t + 6 * DE * DD),
+                  o_g = al(o_mt + 2 * DD * DE), o_gh = al(o_g + 4 * DE * DE),
+                  o_gl = al(o_gh + 2 * DE * DE), o_mean = al(o_gl + 2 * DE * DE),
+                  o_part = al(o_mean + 4 * DE * ((DD + 63) / 64));
+    const int64_t q_c = al(DD * 8), q_st = al(B * (DE / 256) * 8);
+    const bool fuse_up = fold_ok && DE % 256 == 0 && fuse_up_pays(B, DD, DE) &&
+                         o_part + (int64_t(16) << 20) <= B * DD * 4 &&
+                         q_c + q_st + B * 8 <= B * DD * 2;
+    const bool fold = fold_ok && !fuse_up;
     LnRowsArgs lr{};
+    if (fuse_up) {
+      char* ub = reinterpret_cast<char*>(f.U);
+      char* hb = static_cast<char*>(f.h_act);
+      float* part = reinterpret_cast<float*>(ub + o_part);
+      const int64_t part_floats = (B * DD * 4 - o_part) / 4;
+      uint16_t* w1s = reinterpret_cast<uint16_t*>(ub);
+      uint16_t* tw = reinterpret_cast<uint16_t*>(ub + o_t);
+      uint16_t* mt = reinterpret_cast<uint16_t*>(ub + o_mt);
+      float* gm = reinterpret_cast<float*>(ub + o_g);
+      uint16_t* gh = reinterpret_cast<uint16_t*>(ub + o_gh);
+      uint16_t* gl = reinterpret_cast<uint16_t*>(ub + o_gl);
+      float* c12 = reinterpret_cast<float*>(hb);
+      float* stats = reinterpret_cast<float*>(hb + q_c);
+      float* rows = reinterpret_cast<float*>(hb + q_c + q_st);
+      {
+        StageTimer t(plan, ST_WFOLD, s);
+        // W1 = W_mix1 diag(gamma) as hi | lo, c12 = (0, W_mix1 beta)
+        LnFoldArgs fa;
+        fa.header = pd.header;
+        fa.W = static_cast<const uint16_t*>(W_mix);
+        fa.w_n = 2 * DD;
+        fa.gamma = static_cast<const uint16_t*>(gamma);
+        fa.beta = static_cast<const uint16_t*>(beta);
+        fa.n = d.d;
+        fa.d = d.d;
+        fa.W1 = w1s;
+        fa.c12 = c12;
+        fa.split = 1;
+        e = ln_fold_launch(fa, s);
+        // Wc^T as [hi | hi | lo] (d_e x 3d)
+        if (e == hipSuccess)
+          e = center_split_t_launch(pd.header,
+                                    static_cast<const uint16_t*>(W_up), d.d,
+                                    d.d_e, reinterpret_cast<float*>(ub + o_mean),
+                                    tw, s);
+        // Mc = [W1hi | W1lo | W1hi] . [Wc hi | hi | lo] over K = 3d (bf16)
+        GemmArgs gw{};
+        gw.A1 = w1s;
+        gw.A2 = w1s;
+        gw.a1_m = gw.a2_m = 2 * DD;
+        gw.a1_k = gw.a2_k = 1;
+        gw.K1 = 2 * d.d;
+        gw.Bm = tw;
+        gw.b_k = 1;
+        gw.b_n = 3 * DD;
+        gw.C = mt;
+        gw.c_m = DE;
+        gw.M = d.d;
+        gw.N = d.d_e;
+        gw.K = 3 * d.d;
+        gw.header = pd.header;
+        if (e == hipSuccess)
+          e = gemm_nt_256_splitk_launch(gw, s, part, part_floats, 64, kBF16);
+        // G = [hi | lo | hi] . [hi | hi | lo] of Wc^T (float32, then hi | lo)
+        GemmArgs gg = gw;
+        gg.A1 = tw + DD;
+        gg.A2 = tw;
+        gg.a1_m = gg.a2_m = 3 * DD;
+        gg.C = gm;
+        gg.M = d.d_e;
+        if (e == hipSuccess)
+          e = gemm_nt_256_splitk_launch(gg, s, part, part_floats, 64, kF32);
+        if (e == hipSuccess)
+          e = split_bf16_launch(pd.header, gm, DE * DE, gh, gl, s);
+        if (e != hipSuccess) return L3_ERR_HIP;
+      }
+      // per row a^T G a: a (G_hi + G_lo), each row dotted with a
+      GemmArgs gq{};
+      gq.A1 = f.a_act;
+      gq.A2 = f.a_act;
+      gq.a1_m = gq.a2_m = DE;
+      gq.a1_k = gq.a2_k = 1;
+      gq.K1 = d.d_e;
+      gq.B1 = gh;
+      gq.b1_n = DE;
+      gq.Bm = gl;
+      gq.b_k = 1;
+      gq.b_n = DE;
+      gq.b2_rel = 1;
+      gq.M = static_cast<int>(B);
+      gq.N = d.d_e;
+      gq.K = 2 * d.d_e;
+      gq.header = pd.header;
+      gq.ln_stats_out = stats;
+      gq.ln_quad_a = static_cast<const uint16_t*>(f.a_act);
+      gq.ln_quad_lda = DE;
+      {
+        StageTimer t(plan, ST_UP_QUAD, s);
+        e = gemm_nt_256_quad_launch(gq, s);
+      }
+      if (e != hipSuccess) return L3_ERR_HIP;
+      lr.header = pd.header;
+      lr.part = stats;
+      lr.nparts = d.d_e / 256;
+      lr.B = static_cast<int>(B);
+      lr.d = d.d;
+      lr.eps = d.ln_eps;
+      lr.rows = rows;
+      lr.quad = 1;
+      {
+        StageTimer t(plan, ST_LN, s);
+        e = ln_rows_launch(lr, s);
+      }
+      if (e != hipSuccess) return L3_ERR_HIP;
+      mx.A1 = f.a_act;
+      mx.a1_m = DE;
+      mx.K1 = d.d_e;
+      mx.B1 = mt;
+      mx.b1_n = DE;
+      mx.Bm = static_cast<const uint16_t*>(W_mix) + DD;
+      mx.b2_rel = 1;
+      mx.K = d.d_e + d.d;
+      mx.ln_rows = rows;
+      mx.ln_c12 = c12;
+    }
     if (fold) {
       char* base = static_cast<char*>(f.h_act);
       LnFoldArgs fa;
@@ -921,7 +1066,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     u2.b2_rel = 1;
     u2.K = 2 * d.d_e;
     const bool u_split = save && f.a_hi && gemm_nt_256_ok(u2);
-    {
+    if (!fuse_up) {  // (else u is not formed)
       StageTimer t(plan, ST_UP, s);
       if (u_bf16) {
         e = gemm_nt_mfma_launch(up, kBF16, s, f.gpart, f.gpart_floats);
@@ -940,7 +1085,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       e = ln_rows_launch(lr, s);
     }
     if (e != hipSuccess) return L3_ERR_HIP;
-    if (u_bf16 && !fold) {
+    if (u_bf16 && !fold && !fuse_up) {
       LnApplyArgs la;
       la.header = pd.header;
       la.U = reinterpret_cast<const uint16_t*>(f.U);
@@ -972,7 +1117,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     }
     if (e != hipSuccess) return L3_ERR_HIP;
     {
-      StageTimer t(plan, ST_MIX, s);
+      StageTimer t(plan, fuse_up ? ST_MIX_UP : ST_MIX, s);
       if (d.dtype == L3_BF16 && gemm_nt_mfma_ok(mx))
         e = gemm_nt_mfma_launch(mx, d.y_dtype, s, f.gpart, f.gpart_floats);
       else

@@ -450,7 +450,7 @@ __device__ __forceinline__ void step256(floatx16 (&acc)[4][4],
   }
 }
 
-template <typename TC, bool FOLD>
+template <typename TC, bool FOLD, bool QUAD = false>
 __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
   __shared__ __align__(16) uint16_t lds[2][2][kTM * kTL];
   // LayerNorm fold (consumer): per tile row (rstd, -mean * rstd), per tile
@@ -639,7 +639,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
                        : static_cast<TC*>(g.C);
   const int64_t c_m = g.nsplit > 1 ? g.N : g.c_m;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < (QUAD ? 0 : 4); ++i) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int gm = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + h4 + (e & 3);
@@ -660,7 +660,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
     }
   }
 
-  if (!FOLD && g.ln_stats_out) {
+  if (!FOLD && (QUAD || g.ln_stats_out)) {
     // LayerNorm fold (producer): sum and sum of squares of each tile row
     // over the tile's 256 columns, then (mean, M2 = sum of squares - sum *
     // mean) in float32 (one pass; M2 is exact to float32 rounding of the
@@ -684,11 +684,24 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
 #pragma unroll
         for (int ee = 0; ee < 4; ++ee) {
           float a = 0.f, b = 0.f;
+          if constexpr (QUAD) {
+            // quadratic form: the tile row times Q's entries at the same
+            // positions (rows past M read row M - 1; never written)
+            const int gm =
+                min(m0 + wm * 128 + i * 32 + 8 * eg + h4 + ee, g.M - 1);
+            const uint16_t* qrow = g.ln_quad_a +
+                                   static_cast<int64_t>(gm) * g.ln_quad_lda +
+                                   n0 + wn * 128 + r;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = acc[i][j][4 * eg + ee];
-            a += x;
-            b = fmaf(x, x, b);
+            for (int j = 0; j < 4; ++j)
+              b = fmaf(acc[i][j][4 * eg + ee], bf2f(qrow[j * 32]), b);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float x = acc[i][j][4 * eg + ee];
+              a += x;
+              b = fmaf(x, x, b);
+            }
           }
           vp[ee] = a;
           wp[ee] = b;
@@ -708,7 +721,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
     if (m0 + tid < g.M)
       reinterpret_cast<float2*>(g.ln_stats_out)[static_cast<int64_t>(m0 + tid) *
                                                     nt + n_tile] =
-          make_float2(mean, m2);
+          QUAD ? make_float2(sum2, 0.f) : make_float2(mean, m2);
   }
 }
 
@@ -852,26 +865,31 @@ __global__ __launch_bounds__(256) void ln_fold_kernel(LnFoldArgs a) {
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= a.n) return;
   const uint16_t* w = a.W + static_cast<int64_t>(n) * a.w_n;
-  uint16_t* w1 = a.W1 + static_cast<int64_t>(n) * a.d;
+  uint16_t* w1 = a.W1 + static_cast<int64_t>(n) * a.d * (a.split ? 2 : 1);
   float c1 = 0.f, c2 = 0.f;
   for (int e0 = lane * 8; e0 < a.d; e0 += 512) {
     const u32x4 wv = *reinterpret_cast<const u32x4*>(w + e0);
     const u32x4 gv = *reinterpret_cast<const u32x4*>(a.gamma + e0);
     const u32x4 bv = *reinterpret_cast<const u32x4*>(a.beta + e0);
-    u32x4 o;
+    u32x4 o, lo;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float w0 = __uint_as_float(wv[q] << 16);
       const float w1v = __uint_as_float(wv[q] & 0xffff0000u);
-      o[q] = f2bf2(w0 * __uint_as_float(gv[q] << 16),
-                   w1v * __uint_as_float(gv[q] & 0xffff0000u));
+      // products of two bf16 values are exact in float32
+      const float p0 = w0 * __uint_as_float(gv[q] << 16);
+      const float p1 = w1v * __uint_as_float(gv[q] & 0xffff0000u);
+      o[q] = f2bf2(p0, p1);
+      lo[q] = f2bf2(p0 - __uint_as_float(o[q] << 16),
+                    p1 - __uint_as_float(o[q] & 0xffff0000u));
       c1 += __uint_as_float(o[q] << 16) + __uint_as_float(o[q] & 0xffff0000u);
       c2 = fmaf(w0, __uint_as_float(bv[q] << 16), c2);
       c2 = fmaf(w1v, __uint_as_float(bv[q] & 0xffff0000u), c2);
     }
     *reinterpret_cast<u32x4*>(w1 + e0) = o;
+    if (a.split) *reinterpret_cast<u32x4*>(w1 + a.d + e0) = lo;
   }
-  c1 = wave_sum(c1);
+  c1 = a.split ? 0.f : wave_sum(c1);
   c2 = wave_sum(c2);
   if (lane == 0) {
     a.c12[2 * n] = c1;
@@ -895,6 +913,13 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(LnRowsArgs a) {
   if (row >= a.B) return;
   const float2* p =
       reinterpret_cast<const float2*>(a.part) + static_cast<int64_t>(row) * a.nparts;
+  if (a.quad) {
+    float q2 = 0.f;
+    for (int q = 0; q < a.nparts; ++q) q2 += p[q].x;
+    const float rstd = 1.0f / sqrtf(fmaxf(q2, 0.f) / a.d + a.eps);
+    reinterpret_cast<float2*>(a.rows)[row] = make_float2(rstd, 0.f);
+    return;
+  }
   float mean = 0.f;
   for (int q = 0; q < a.nparts; ++q) mean += p[q].x;
   mean /= a.nparts;
@@ -913,6 +938,105 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(LnRowsArgs a) {
 hipError_t ln_rows_launch(const LnRowsArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   ln_rows_kernel<<<ceil_div(a.B, 256), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// W_up folded through LayerNorm (inference): with Wc = W - 1 mean_r(W)
+// (columns centred over the d rows), u - mean(u) = Wc a, so
+//   sum_j (u_j - mean)^2 = a^T (Wc^T Wc) a  and
+//   W_mix1 h = rstd * (W_mix1 diag(gamma) Wc) a + W_mix1 beta,
+// one d_e x d_e and one d x d_e matrix built from the weights per call.
+// The centring removes the mean exactly, so neither product cancels a
+// large mean against the rest. Both take Wc^T as bf16 hi | lo (3 terms on
+// the bf16 kernel: hi hi + lo hi + hi lo, about float32 accuracy).
+// Column sums of W (rows x cols, bf16) over blocks of 64 rows:
+// part[y * cols + c] = sum of W[r, c] over rows r of block y.
+__global__ __launch_bounds__(256) void col_part_kernel(const int32_t* header,
+                                                       const uint16_t* W,
+                                                       int rows, int cols,
+                                                       float* part) {
+  if (header[0] != 0) return;
+  __shared__ float s[4][64];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + tx, r0 = blockIdx.y * 64;
+  float acc = 0.f;
+  if (c < cols) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = r0 + ty + 4 * k;
+      if (r < rows) acc += bf2f(W[static_cast<int64_t>(r) * cols + c]);
+    }
+  }
+  s[ty][tx] = acc;
+  __syncthreads();
+  if (ty == 0 && c < cols)
+    part[static_cast<int64_t>(blockIdx.y) * cols + c] =
+        (s[0][tx] + s[1][tx]) + (s[2][tx] + s[3][tx]);
+}
+
+// T from W and the block sums above (added in block order per column).
+__global__ __launch_bounds__(256) void center_split_t_kernel(
+    const int32_t* header, const uint16_t* W, int rows, int cols,
+    const float* part, uint16_t* T) {
+  if (header[0] != 0) return;
+  __shared__ float t[64][65];
+  __shared__ float s_mean[64];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  {
+    // four phases of the block sums in parallel, then in phase order
+    float m = 0.f;
+    if (c0 + tx < cols)
+#pragma unroll 8
+      for (int y = ty; y < static_cast<int>(gridDim.y); y += 4)
+        m += part[static_cast<int64_t>(y) * cols + c0 + tx];
+    t[ty][tx] = m;
+  }
+  __syncthreads();
+  if (ty == 0) s_mean[tx] = ((t[0][tx] + t[1][tx]) + (t[2][tx] + t[3][tx])) / rows;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = r0 + ty + 4 * k, c = c0 + tx;
+    if (r < rows && c < cols)
+      t[ty + 4 * k][tx] =
+          bf2f(W[static_cast<int64_t>(r) * cols + c]) - s_mean[tx];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int c = c0 + ty + 4 * k, r = r0 + tx;
+    if (r < rows && c < cols) {
+      const float v = t[tx][ty + 4 * k];
+      const uint16_t hi = f2bf(v);
+      const float hv = __uint_as_float(static_cast<uint32_t>(hi) << 16);
+      uint16_t* row = T + static_cast<int64_t>(c) * 3 * rows;
+      row[r] = hi;
+      row[rows + r] = hi;
+      row[2 * rows + r] = f2bf(v - hv);
+    }
+  }
+}
+
+hipError_t center_split_t_launch(const int32_t* header, const uint16_t* W,
+                                 int rows, int cols, float* mean, uint16_t* T,
+                                 hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  dim3 grid(ceil_div(cols, 64), ceil_div(rows, 64));
+  col_part_kernel<<<grid, 256, 0, s>>>(header, W, rows, cols, mean);
+  center_split_t_kernel<<<grid, 256, 0, s>>>(header, W, rows, cols, mean, T);
+  return hipGetLastError();
+}
+
+// The quadratic-form epilogue on 256 x 256 tiles (no K split, C unwritten).
+hipError_t gemm_nt_256_quad_launch(const GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0) return hipSuccess;
+  if (!gemm_nt_256_shape_ok(g) || !g.ln_quad_a || !g.ln_stats_out ||
+      g.ln_rows || g.nsplit != 1)
+    return hipErrorInvalidValue;
+  const int grid =
+      static_cast<int>(static_cast<int64_t>(ceil_div(g.M, kTM)) * (g.N / kTN));
+  gemm_nt_256_kernel<float, false, true><<<grid, 256, 0, s>>>(g);
   return hipGetLastError();
 }
 

@@ -153,6 +153,12 @@ struct GemmArgs {
   float* ln_stats_out = nullptr;
   const float* ln_rows = nullptr;
   const float* ln_c12 = nullptr;
+  // 256 x 256 kernel, quadratic-form epilogue (gemm_nt_256_quad_launch):
+  // ln_stats_out[m * (N / 256) + t] = (sum_n Q[m, n] * C[m, n], 0) over the
+  // 256 columns n of tile t, Q bf16 with row stride ln_quad_lda; C itself
+  // is not written.
+  const uint16_t* ln_quad_a = nullptr;
+  int64_t ln_quad_lda = 0;
 };
 
 // Row statistics of the fold from the producer's partials.
@@ -162,6 +168,9 @@ struct LnRowsArgs {
   int nparts, B, d;
   float eps;
   float* rows;         // [B] (rstd, -mean * rstd) pairs
+  // quad: the parts' first members add up to sum_j (u_j - mean)^2 itself
+  // (the quadratic-form epilogue); rows = (rstd, 0)
+  int quad = 0;
 };
 
 // Fold of LayerNorm's affine into the first K1 columns of W_mix (rows of W
@@ -176,6 +185,9 @@ struct LnFoldArgs {
   int n, d;
   uint16_t* W1;     // [n x d] bf16
   float* c12;       // [n x 2]
+  // split: W1 rows [n x 2d], the bf16 product at [0, d) and the bf16
+  // rounding residual at [d, 2d); c1 = 0
+  int split = 0;
 };
 
 // LayerNorm of float32 rows (one wave per row).
@@ -264,6 +276,14 @@ bool gemm_nt_mfma_ok(const GemmArgs& g);
 // launcher above takes it for these shapes when no split-K buffer is given.
 bool gemm_nt_256_ok(const GemmArgs& g);
 hipError_t ln_fold_launch(const LnFoldArgs& a, hipStream_t s);
+// Centred, transposed bf16 hi | lo copy of W (rows x cols, bf16):
+// T[c, r] = hi, T[c, rows + r] = hi, T[c, 2 rows + r] = lo of
+// W[r, c] - mean_r W[r, c] (T is [cols x 3 rows]); mean is scratch of
+// cols * ceil(rows / 64) floats (column sums per block of 64 rows).
+hipError_t center_split_t_launch(const int32_t* header, const uint16_t* W,
+                                 int rows, int cols, float* mean, uint16_t* T,
+                                 hipStream_t s);
+hipError_t gemm_nt_256_quad_launch(const GemmArgs& g, hipStream_t s);
 hipError_t ln_rows_launch(const LnRowsArgs& a, hipStream_t s);
 hipError_t ln_apply_launch(const LnApplyArgs& a, hipStream_t s);
 hipError_t ln_launch(const LnArgs& a, int dtype, hipStream_t s);

@@ -232,3 +232,48 @@ def test_u_far_from_zero_mean():
           f"folded {e_fold:.3e}, row {e_row:.3e}")
     assert np.median(ratio) >= 10
     assert e_fold <= 1.5 * e_row + 1e-4
+
+
+def _times8(w):
+    """The workload's ids eight times over, each copy with the rows of x
+    rolled by another offset (65536 tokens for the prefill shape)."""
+    ids = np.concatenate([w.ids] * 8)
+    x = np.ascontiguousarray(np.concatenate(
+        [np.roll(w.x, 1000 * j, axis=0) for j in range(8)]))
+    return wl.with_ids(w, ids, x=x)
+
+
+def test_prefill_bf16_w_up_folded_sampled():
+    """On large batches (here 65536 tokens of the prefill shape) inference
+    folds W_up through LayerNorm into W_mix: u is never formed; each row's variance comes from a quadratic
+    form of a, and y from [a ; x] against the composed weights. Checked on
+    sampled tokens (both ends and a random sample) at the bf16 bound."""
+    w = _times8(gu.workload("prefill_bf16"))
+    assert w.batch == 65536
+    res = gu.run(w, training=False)
+    rng = np.random.default_rng(1)
+    tokens = np.unique(np.concatenate([
+        np.arange(256), rng.choice(w.batch, 1024, replace=False),
+        np.arange(w.batch - 64, w.batch)]))
+    ref = gu.oracle_forward(w, tokens=tokens)
+    _check(w, res, ref, tokens=tokens)
+
+
+def test_u_far_from_zero_mean_w_up_folded():
+    """The offset input of the test above on 65536 tokens: with W_up's
+    columns centred before the fold, neither the variance nor the output
+    subtracts a large mean, so the error stays within 1.5x of the row
+    normalisation's on the same 64 tokens (in practice well below it)."""
+    w = wl.with_u_offset(_times8(gu.workload("prefill_bf16", True)), 50.0)
+    full = gu.f64(gu.run(w)["y"])
+    tok = np.arange(64)
+    w64 = wl.with_ids(w, w.ids[:64], x=np.ascontiguousarray(w.x[:64]))
+    small = gu.f64(gu.run(w64)["y"])
+    ref = gu.oracle_forward(w, tokens=tok)
+    ratio = np.abs(ref["mean"]) / np.sqrt(ref["var"])
+    e_fused = float(np.sqrt(np.mean((full[tok] - ref["y"]) ** 2)))
+    e_row = float(np.sqrt(np.mean((small - ref["y"]) ** 2)))
+    print(f"median |mean| / std of u {np.median(ratio):.1f}; rms error: "
+          f"W_up folded {e_fused:.3e}, row {e_row:.3e}")
+    assert np.median(ratio) >= 10
+    assert e_fused <= 1.5 * e_row + 1e-4
