@@ -944,7 +944,9 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
                                     static_cast<const uint16_t*>(W_up), d.d,
                                     d.d_e, reinterpret_cast<float*>(ub + o_mean),
                                     tw, s);
-        // Mc = [W1hi | W1lo | W1hi] . [Wc hi | hi | lo] over K = 3d (bf16)
+        // Mc = [W1hi | W1lo | W1hi] . [Wc hi | hi | lo] over K = 3d (bf16);
+        // up to 8 K shares here and 16 for G (more shares made the in-order
+        // sum of the partials cost more than the GEMM saved)
         GemmArgs gw{};
         gw.A1 = w1s;
         gw.A2 = w1s;
@@ -961,7 +963,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
         gw.K = 3 * d.d;
         gw.header = pd.header;
         if (e == hipSuccess)
-          e = gemm_nt_256_splitk_launch(gw, s, part, part_floats, 64, kBF16);
+          e = gemm_nt_256_splitk_launch(gw, s, part, part_floats, 8, kBF16);
         // G = [hi | lo | hi] . [hi | hi | lo] of Wc^T (float32, then hi | lo)
         GemmArgs gg = gw;
         gg.A1 = tw + DD;
@@ -970,7 +972,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
         gg.C = gm;
         gg.M = d.d_e;
         if (e == hipSuccess)
-          e = gemm_nt_256_splitk_launch(gg, s, part, part_floats, 64, kF32);
+          e = gemm_nt_256_splitk_launch(gg, s, part, part_floats, 16, kF32);
         if (e == hipSuccess)
           e = split_bf16_launch(pd.header, gm, DE * DE, gh, gl, s);
         if (e != hipSuccess) return L3_ERR_HIP;

@@ -670,10 +670,36 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
     // the float4 writes of 8 lanes fall in distinct banks) and one thread
     // a row adds them up.
     constexpr int kSP = kTM + 4;
+    // quadratic form: Q's tile rows staged in LDS half a tile (128 rows) at
+    // a time, [128][kQL] bf16 ahead of the sums (sq); else sums at sp, sq
+    constexpr int kQL = kTN + 8;
     float* sp = reinterpret_cast<float*>(&lds[0][0][0]);
-    float* sq = sp + 64 * kSP;
+    float* sq = QUAD ? reinterpret_cast<float*>(
+                           reinterpret_cast<uint16_t*>(sp) + 128 * kQL)
+                     : sp + 64 * kSP;
+    uint16_t* qs = reinterpret_cast<uint16_t*>(sp);
+    static_assert(128 * kQL * 2 + 64 * kSP * 4 <= sizeof(lds),
+                  "quadratic-form staging exceeds the operand LDS");
     const int wo = (wn * 32 + r) * kSP + wm * 128 + h4;
     __syncthreads();  // every wave is done with the operand buffers
+#pragma unroll
+    for (int half = 0; half < (QUAD ? 2 : 1); ++half) {
+    if constexpr (QUAD) {
+      // 128 rows x 256 columns: 8 rows a pass of 16-byte chunks
+      if (half > 0) __syncthreads();
+      const int qc = (tid & 31) * 8;
+#pragma unroll 4
+      for (int p = 0; p < 16; ++p) {
+        const int lr = p * 8 + (tid >> 5);
+        const int gm = min(m0 + half * 128 + lr, g.M - 1);
+        *reinterpret_cast<u32x4*>(&qs[lr * kQL + qc]) =
+            *reinterpret_cast<const u32x4*>(
+                g.ln_quad_a + static_cast<int64_t>(gm) * g.ln_quad_lda + n0 +
+                qc);
+      }
+      __syncthreads();
+      if (wm != half) continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -685,13 +711,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
         for (int ee = 0; ee < 4; ++ee) {
           float a = 0.f, b = 0.f;
           if constexpr (QUAD) {
-            // quadratic form: the tile row times Q's entries at the same
-            // positions (rows past M read row M - 1; never written)
-            const int gm =
-                min(m0 + wm * 128 + i * 32 + 8 * eg + h4 + ee, g.M - 1);
-            const uint16_t* qrow = g.ln_quad_a +
-                                   static_cast<int64_t>(gm) * g.ln_quad_lda +
-                                   n0 + wn * 128 + r;
+            // the tile row times Q's entries at the same positions (rows
+            // past M took row M - 1; never written)
+            const uint16_t* qrow =
+                qs + (i * 32 + 8 * eg + h4 + ee) * kQL + wn * 128 + r;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               b = fmaf(acc[i][j][4 * eg + ee], bf2f(qrow[j * 32]), b);
@@ -706,14 +729,16 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
           vp[ee] = a;
           wp[ee] = b;
         }
-        *reinterpret_cast<float4*>(sp + wo + i * 32 + 8 * eg) = v;
+        if constexpr (!QUAD)
+          *reinterpret_cast<float4*>(sp + wo + i * 32 + 8 * eg) = v;
         *reinterpret_cast<float4*>(sq + wo + i * 32 + 8 * eg) = w;
       }
+    }
     __syncthreads();
     float sum = 0.f, sum2 = 0.f;
 #pragma unroll 16
     for (int sl = 0; sl < 64; ++sl) {
-      sum += sp[sl * kSP + tid];
+      if constexpr (!QUAD) sum += sp[sl * kSP + tid];
       sum2 += sq[sl * kSP + tid];
     }
     const float mean = sum * (1.0f / kTN);
