@@ -13,7 +13,7 @@ def test_w_up_fold_identity():
     d, de, n, eps = 96, 32, 6, 1e-5
     # a common column shift puts u's mean tens of times above its spread
     W_up = (rng.standard_normal((d, de)) / np.sqrt(de)
-            + 5.0 * rng.standard_normal(de))
+            + 8.0 * rng.standard_normal(de))
     W_a = rng.standard_normal((d, d)) / np.sqrt(d)
     gamma = 1.0 + 0.1 * rng.standard_normal(d)
     beta = 0.1 * rng.standard_normal(d)
