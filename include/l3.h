@@ -140,8 +140,10 @@ l3_status l3_replan(l3_plan_t plan, const int32_t* ids, int64_t B,
  *   scratch device scratch workspace (scratch_bytes)
  * Errors: L3_ERR_NULL, L3_ERR_WORKSPACE, L3_ERR_HIP. Device-detected input
  * errors of the plan make this a no-op (see l3_plan).
- * Inference on bf16 with large batches (about 2e11 flops of W_up and W_mix
- * work or more) computes the same y without forming W_up's output: W_up,
+ * Inference on bf16 with large batches (when the fold below saves 1e11
+ * flops or more: B (2 d d_e + 2 d (d - d_e) - 4 d_e^2) >= 1e11, e.g. 65536
+ * tokens at d = 2048, d_e = 512) computes y without forming W_up's output:
+ * W_up,
  * with its columns centred, is folded through LayerNorm into W_mix (each
  * row's variance as a quadratic form of the aggregate); the results agree
  * with the unfolded path to bf16 rounding.
