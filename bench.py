@@ -205,7 +205,8 @@ def run_offload(args) -> None:
 
     def pinned(a):
         if a.dtype == np.uint16:
-            a = a.view(np.int16)
+            t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16)))
+            return t.pin_memory().view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).pin_memory()
 
     K_host, V_host = pinned(w.K), pinned(w.V)

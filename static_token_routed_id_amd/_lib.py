@@ -130,6 +130,54 @@ def _nbytes(t):
     return t.numel() * t.element_size()
 
 
+def _act_dtype(code: int):
+    import torch
+    return torch.bfloat16 if code == L3_BF16 else torch.float32
+
+
+def _arg(t, name, dtype=None, shape=None, cols=None, host=False,
+         optional=False):
+    """Checks one tensor argument before its address crosses the ABI: a
+    contiguous tensor on the GPU (host=True: in host memory) with the given
+    dtype and shape (`cols`: 2-D with that many columns, any rows). Raw
+    integer addresses pass unchecked (the caller vouches for them); None
+    passes only where the entry point takes NULL."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name}: a tensor is required")
+    if isinstance(t, int):
+        return
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t)}")
+    if host and t.is_cuda:
+        raise ValueError(f"{name}: must be in host memory")
+    if not host and not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected "
+                         f"{tuple(shape)}")
+    if cols is not None and (t.dim() != 2 or t.shape[1] != cols):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected "
+                         f"(rows, {cols})")
+
+
+def _check_params(desc, K, V, W_up, gamma, beta, W_mix):
+    act = _act_dtype(desc.dtype)
+    d, d_e = desc.d, desc.d_e
+    _arg(K, "K", act, cols=d)
+    _arg(V, "V", act, cols=d_e)
+    _arg(W_up, "W_up", act, (d, d_e))
+    _arg(gamma, "gamma", act, (d,))
+    _arg(beta, "beta", act, (d,))
+    _arg(W_mix, "W_mix", act, (d, 2 * d))
+
+
 def make_desc(vocab, rows, d, d_e, k_max=512, dtype=L3_BF16, y_dtype=L3_F32,
               ln_eps=1e-5, d_k=None) -> l3_desc:
     return l3_desc(int(vocab), int(rows), int(d), int(d if d_k is None else d_k),
@@ -163,9 +211,19 @@ class Plan:
             self.handle = None
 
 
+def _check_ids(desc, ids, offsets):
+    import torch
+    B = 0 if ids is None else ids.numel()
+    if B:
+        _arg(ids, "ids", torch.int32)
+        _arg(offsets, "offsets", torch.int64, (desc.vocab + 1,))
+
+
 def l3_plan(desc: l3_desc, ids, offsets, plan_ws, stream=None,
             check_status=True) -> Plan:
     out = c_void_p()
+    _check_ids(desc, ids, offsets)
+    _arg(plan_ws, "plan_ws", optional=True)
     B = 0 if ids is None else ids.numel()
     st = _lib.l3_plan(byref(desc), _ptr(ids), B, _ptr(offsets), _ptr(plan_ws),
                       _nbytes(plan_ws), _stream(stream), byref(out))
@@ -178,6 +236,7 @@ def l3_plan(desc: l3_desc, ids, offsets, plan_ws, stream=None,
 
 
 def l3_replan(plan: Plan, ids, offsets, stream=None) -> None:
+    _check_ids(plan.desc, ids, offsets)
     B = 0 if ids is None else ids.numel()
     _check(_lib.l3_replan(plan.handle, _ptr(ids), B, _ptr(offsets),
                           _stream(stream)), "l3_replan")
@@ -185,6 +244,14 @@ def l3_replan(plan: Plan, ids, offsets, stream=None) -> None:
 
 def l3_forward(plan: Plan, x, K, V, W_up, gamma, beta, W_mix, y, save,
                scratch, stream=None) -> None:
+    B = plan.tokens
+    if B > 0:
+        desc = plan.desc
+        _arg(x, "x", _act_dtype(desc.dtype), (B, desc.d))
+        _check_params(desc, K, V, W_up, gamma, beta, W_mix)
+        _arg(y, "y", _act_dtype(desc.y_dtype), (B, desc.d))
+        _arg(save, "save", optional=True)
+        _arg(scratch, "scratch")
     _check(_lib.l3_forward(plan.handle, _ptr(x), _ptr(K), _ptr(V), _ptr(W_up),
                            _ptr(gamma), _ptr(beta), _ptr(W_mix), _ptr(y),
                            _ptr(save), _nbytes(save), _ptr(scratch),
@@ -194,6 +261,24 @@ def l3_forward(plan: Plan, x, K, V, W_up, gamma, beta, W_mix, y, save,
 def l3_backward(plan: Plan, dy, x, K, V, W_up, gamma, beta, W_mix, save, dx,
                 dK, dV, dW_up, dgamma, dbeta, dW_mix, scratch,
                 stream=None) -> None:
+    import torch
+    desc = plan.desc
+    B, d, d_e, R = plan.tokens, desc.d, desc.d_e, desc.rows
+    f32 = torch.float32
+    if B > 0:
+        act = _act_dtype(desc.dtype)
+        _arg(dy, "dy", act, (B, d))
+        _arg(x, "x", act, (B, d))
+        _check_params(desc, K, V, W_up, gamma, beta, W_mix)
+        _arg(save, "save")
+        _arg(dx, "dx", f32, (B, d))
+        _arg(scratch, "scratch")
+    _arg(dK, "dK", f32, (R, d))
+    _arg(dV, "dV", f32, (R, d_e))
+    _arg(dW_up, "dW_up", f32, (d, d_e))
+    _arg(dgamma, "dgamma", f32, (d,))
+    _arg(dbeta, "dbeta", f32, (d,))
+    _arg(dW_mix, "dW_mix", f32, (d, 2 * d))
     _check(_lib.l3_backward(plan.handle, _ptr(dy), _ptr(x), _ptr(K), _ptr(V),
                             _ptr(W_up), _ptr(gamma), _ptr(beta), _ptr(W_mix),
                             _ptr(save), _nbytes(save), _ptr(dx), _ptr(dK),
@@ -207,6 +292,16 @@ def l3_stage_rows(plan: Plan, K_host, V_host, K_stage, V_stage,
     """Copy the batch's rows of host-resident tables into K_stage / V_stage
     (device, capacity = K_stage's rows) and point the plan at them; with
     dma=True the DMA engines copy (the call waits for `stream`)."""
+    if plan.tokens > 0:
+        act = _act_dtype(plan.desc.dtype)
+        _arg(K_host, "K_host", act, (plan.desc.rows, plan.desc.d), host=True)
+        _arg(V_host, "V_host", act, (plan.desc.rows, plan.desc.d_e),
+             host=True)
+        _arg(K_stage, "K_stage", act, cols=plan.desc.d)
+        _arg(V_stage, "V_stage", act, cols=plan.desc.d_e)
+        if (not isinstance(K_stage, int) and not isinstance(V_stage, int)
+                and V_stage.shape[0] < K_stage.shape[0]):
+            raise ValueError("V_stage holds fewer rows than K_stage")
     rows = int(K_stage.shape[0]) if K_stage is not None else 0
     fn = _lib.l3_stage_rows_dma if dma else _lib.l3_stage_rows
     _check(fn(plan.handle, _ptr(K_host), _ptr(V_host), _ptr(K_stage),

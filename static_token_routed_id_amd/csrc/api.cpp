@@ -189,6 +189,10 @@ struct FwdBufs {
   // training, bf16: the float32 aggregate as bf16 hi | lo [B x d_e] each
   uint16_t* a_hi;
   uint16_t* a_lo;
+  // bf16: W_up with its columns centred, as bf16 hi | lo [d x 2 d_e], and
+  // the column sums it is built from [ceil(d / 64) x d_e]
+  uint16_t* wc;
+  float* wc_part;
 };
 FwdBufs carve_fwd(Carver& c, const l3_desc& d, int64_t B) {
   FwdBufs f;
@@ -211,6 +215,10 @@ FwdBufs carve_fwd(Carver& c, const l3_desc& d, int64_t B) {
   const size_t ae = static_cast<size_t>(B) * d.d_e;
   f.a_hi = b16 ? c.take<uint16_t>(ae) : nullptr;
   f.a_lo = b16 ? c.take<uint16_t>(ae) : nullptr;
+  const size_t wce = static_cast<size_t>(d.d) * 2 * d.d_e;
+  f.wc = b16 ? c.take<uint16_t>(wce) : nullptr;
+  f.wc_part = b16 ? c.take<float>(static_cast<size_t>((d.d + 63) / 64) * d.d_e)
+                  : nullptr;
   return f;
 }
 
@@ -725,22 +733,22 @@ l3_status l3_plan_export(l3_plan_t plan, int32_t* perm, int32_t* S,
 l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
                      const void* V, const void* W_up, const void* gamma,
                      const void* beta, const void* W_mix, void* y, void* save,
-                     size_t save_bytes, void* scratch, size_t scratch_bytes,
+                     size_t save_bytes, void* scratch_ws, size_t scratch_bytes,
                      void* stream) {
   try {
     if (!plan) return L3_ERR_NULL;
     const int64_t B = plan->B;
     if (B == 0) return L3_OK;
     if (!x || !K || !V || !W_up || !gamma || !beta || !W_mix || !y ||
-        !scratch)
+        !scratch_ws)
       return L3_ERR_NULL;
     const l3_desc& d = plan->desc;
-    if (scratch_bytes < fwd_bytes_for(d, B) || !aligned(scratch))
+    if (scratch_bytes < fwd_bytes_for(d, B) || !aligned(scratch_ws))
       return L3_ERR_WORKSPACE;
     if (save && (save_bytes < save_bytes_for(d, B) || !aligned(save)))
       return L3_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    Carver cs(scratch);
+    Carver cs(scratch_ws);
     FwdBufs f = carve_fwd(cs, d, B);
     SaveBufs sv{nullptr, nullptr, nullptr, nullptr};
     if (save) {
@@ -908,6 +916,23 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
                          o_part + (int64_t(16) << 20) <= B * DD * 4 &&
                          q_c + q_st + B * 8 <= B * DD * 2;
     const bool fold = fold_ok && !fuse_up;
+    // Where u is stored as bf16, it is formed from W_up with its columns
+    // centred over the d outputs (as bf16 hi | lo over K = 2 d_e, the
+    // aggregate read for both halves): u - mean(u) = Wc a exactly, and
+    // LayerNorm's output does not change when its input is shifted by the
+    // row's mean, so u's rounding is relative to its spread rather than to
+    // a mean that may be many times larger.
+    if (u_bf16 && !fuse_up) {
+      {
+        StageTimer t(plan, ST_UP, s);
+        e = center_split_launch(pd.header, static_cast<const uint16_t*>(W_up),
+                                d.d, d.d_e, f.wc_part, f.wc, s);
+      }
+      if (e != hipSuccess) return L3_ERR_HIP;
+      up.Bm = f.wc;
+      up.b_n = 2 * static_cast<int64_t>(d.d_e);
+      up.K = 2 * d.d_e;
+    }
     LnRowsArgs lr{};
     if (fuse_up) {
       char* ub = reinterpret_cast<char*>(f.U);
@@ -1145,7 +1170,7 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
                       const void* gamma, const void* beta, const void* W_mix,
                       const void* save, size_t save_bytes, float* dx,
                       float* dK, float* dV, float* dW_up, float* dgamma,
-                      float* dbeta, float* dW_mix, void* scratch,
+                      float* dbeta, float* dW_mix, void* scratch_ws,
                       size_t scratch_bytes, void* stream) {
   try {
     if (!plan) return L3_ERR_NULL;
@@ -1153,7 +1178,7 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
     const int64_t B = plan->B;
     if (!dK || !dV || !dW_up || !dgamma || !dbeta || !dW_mix) return L3_ERR_NULL;
     if (B > 0 && (!dy || !x || !K || !V || !W_up || !gamma || !beta ||
-                  !W_mix || !save || !dx || !scratch))
+                  !W_mix || !save || !dx || !scratch_ws))
       return L3_ERR_NULL;
     (void)beta;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1174,11 +1199,11 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
     if (!known || plan->staged) return L3_ERR_STATE;
     if (save_bytes < save_bytes_for(d, B) || !aligned(save))
       return L3_ERR_WORKSPACE;
-    if (scratch_bytes < bwd_bytes_for(d, B) || !aligned(scratch))
+    if (scratch_bytes < bwd_bytes_for(d, B) || !aligned(scratch_ws))
       return L3_ERR_WORKSPACE;
     Carver cv(const_cast<void*>(save));
     SaveBufs sv = carve_save(cv, d, B);
-    Carver cs(scratch);
+    Carver cs(scratch_ws);
     BwdBufs bb = carve_bwd(cs, d, B);
     const PlanDev& pd = plan->dev;
     const int Bi = static_cast<int>(B);

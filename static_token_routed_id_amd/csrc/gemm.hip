@@ -1043,6 +1043,56 @@ __global__ __launch_bounds__(256) void center_split_t_kernel(
   }
 }
 
+// Row-major counterpart for the bf16-u inference paths: out row r (stride
+// 2 cols) = [hi | lo] of W[r, :] - column means, so that u = a W^T taken
+// over K = 2 cols against (a, a) is the centred u - mean(u) to about float32
+// accuracy. LayerNorm subtracts the mean anyway, so its output is unchanged,
+// and u stored as bf16 then rounds relative to its spread, not its mean.
+__global__ __launch_bounds__(256) void center_split_kernel(
+    const int32_t* header, const uint16_t* W, int rows, int cols,
+    const float* part, uint16_t* out) {
+  if (header[0] != 0) return;
+  __shared__ float t[4][64];
+  __shared__ float s_mean[64];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  {
+    float m = 0.f;
+    if (c0 + tx < cols)
+#pragma unroll 8
+      for (int y = ty; y < static_cast<int>(gridDim.y); y += 4)
+        m += part[static_cast<int64_t>(y) * cols + c0 + tx];
+    t[ty][tx] = m;
+  }
+  __syncthreads();
+  if (ty == 0) s_mean[tx] = ((t[0][tx] + t[1][tx]) + (t[2][tx] + t[3][tx])) / rows;
+  __syncthreads();
+  const int c = c0 + tx;
+  if (c >= cols) return;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = r0 + ty + 4 * k;
+    if (r < rows) {
+      const float v = bf2f(W[static_cast<int64_t>(r) * cols + c]) - s_mean[tx];
+      const uint16_t hi = f2bf(v);
+      const float hv = __uint_as_float(static_cast<uint32_t>(hi) << 16);
+      uint16_t* row = out + static_cast<int64_t>(r) * 2 * cols;
+      row[c] = hi;
+      row[cols + c] = f2bf(v - hv);
+    }
+  }
+}
+
+hipError_t center_split_launch(const int32_t* header, const uint16_t* W,
+                               int rows, int cols, float* mean, uint16_t* out,
+                               hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  dim3 grid(ceil_div(cols, 64), ceil_div(rows, 64));
+  col_part_kernel<<<grid, 256, 0, s>>>(header, W, rows, cols, mean);
+  center_split_kernel<<<grid, 256, 0, s>>>(header, W, rows, cols, mean, out);
+  return hipGetLastError();
+}
+
 hipError_t center_split_t_launch(const int32_t* header, const uint16_t* W,
                                  int rows, int cols, float* mean, uint16_t* T,
                                  hipStream_t s) {

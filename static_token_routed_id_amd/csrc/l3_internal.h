@@ -283,6 +283,12 @@ hipError_t ln_fold_launch(const LnFoldArgs& a, hipStream_t s);
 hipError_t center_split_t_launch(const int32_t* header, const uint16_t* W,
                                  int rows, int cols, float* mean, uint16_t* T,
                                  hipStream_t s);
+// Centred row-major bf16 hi | lo copy of W (rows x cols, bf16): out[r, c] =
+// hi, out[r, cols + c] = lo of W[r, c] - mean_r W[r, c] (out is
+// [rows x 2 cols]); mean as above.
+hipError_t center_split_launch(const int32_t* header, const uint16_t* W,
+                               int rows, int cols, float* mean, uint16_t* out,
+                               hipStream_t s);
 hipError_t gemm_nt_256_quad_launch(const GemmArgs& g, hipStream_t s);
 hipError_t ln_rows_launch(const LnRowsArgs& a, hipStream_t s);
 hipError_t ln_apply_launch(const LnApplyArgs& a, hipStream_t s);

@@ -40,6 +40,9 @@ class L3Layer:
         self.save = torch.empty(max(s, 256), **u8) if training else None
         self.scratch = torch.empty(max(c, 256), **u8)
         self.plan: Optional[L.Plan] = None
+        # bumped by every (re)plan: the layer holds one plan and one save
+        # workspace, so a backward belongs to the forward of the same plan
+        self.generation = 0
 
     def make_plan(self, ids: torch.Tensor, offsets: torch.Tensor,
                   check_status=True) -> L.Plan:
@@ -48,6 +51,7 @@ class L3Layer:
                                   check_status=check_status)
         else:
             L.l3_replan(self.plan, ids, offsets)
+        self.generation += 1
         return self.plan
 
     def forward(self, x, K, V, W_up, gamma, beta, W_mix, y=None, save=None):
@@ -59,15 +63,18 @@ class L3Layer:
                      self.save if save is None else save, self.scratch)
         return y
 
-    def backward(self, dy, x, K, V, W_up, gamma, beta, W_mix):
+    def backward(self, dy, x, K, V, W_up, gamma, beta, W_mix, out=None):
+        """Gradients (float32) of sum(y * dy); `out` may hold some of the
+        output tensors (dx, dK, dV, dW_up, dgamma, dbeta, dW_mix) to write
+        into, the others are allocated."""
         d, d_e, R = self.desc.d, self.desc.d_e, self.desc.rows
         f32 = dict(dtype=torch.float32, device=self.device)
         B = self.plan.tokens
-        g = dict(dx=torch.empty((B, d), **f32), dK=torch.empty((R, d), **f32),
-                 dV=torch.empty((R, d_e), **f32),
-                 dW_up=torch.empty((d, d_e), **f32),
-                 dgamma=torch.empty(d, **f32), dbeta=torch.empty(d, **f32),
-                 dW_mix=torch.empty((d, 2 * d), **f32))
+        shapes = dict(dx=(B, d), dK=(R, d), dV=(R, d_e), dW_up=(d, d_e),
+                      dgamma=(d,), dbeta=(d,), dW_mix=(d, 2 * d))
+        out = out or {}
+        g = {k: out[k] if k in out else torch.empty(v, **f32)
+             for k, v in shapes.items()}
         L.l3_backward(self.plan, dy, x, K, V, W_up, gamma, beta, W_mix,
                       self.save, g["dx"], g["dK"], g["dV"], g["dW_up"],
                       g["dgamma"], g["dbeta"], g["dW_mix"], self.scratch)
@@ -75,19 +82,34 @@ class L3Layer:
 
 
 class L3Function(torch.autograd.Function):
-    """y = L3(x; ids, K, V, W_up, gamma, beta, W_mix) with libl3 backward."""
+    """y = L3(x; ids, K, V, W_up, gamma, beta, W_mix) with libl3 backward.
+
+    The layer object holds one plan and one save workspace (it must be made
+    with training=True): a backward needs the forward of the same plan, so a
+    second forward through the same layer before the first one's backward
+    makes that backward raise. Use one L3Layer per pending forward.
+    Gradients are computed in float32 and returned in each input's dtype
+    (autograd's rule); L3Layer.backward gives the float32 ones."""
 
     @staticmethod
     def forward(ctx, layer: L3Layer, ids, offsets, x, K, V, W_up, gamma,
                 beta, W_mix):
+        if layer.save is None:
+            raise ValueError("L3Function needs an L3Layer made with "
+                             "training=True (a save workspace)")
         layer.make_plan(ids, offsets)
         y = layer.forward(x, K, V, W_up, gamma, beta, W_mix)
         ctx.layer = layer
+        ctx.generation = layer.generation
         ctx.save_for_backward(x, K, V, W_up, gamma, beta, W_mix)
         return y
 
     @staticmethod
     def backward(ctx, dy):
+        if ctx.layer.generation != ctx.generation:
+            raise RuntimeError(
+                "L3Function.backward: the layer was re-planned by another "
+                "forward after this one; its saved state is gone")
         x, K, V, W_up, gamma, beta, W_mix = ctx.saved_tensors
         dy = dy.to(x.dtype).contiguous()
         g = ctx.layer.backward(dy, x, K, V, W_up, gamma, beta, W_mix)

@@ -16,7 +16,8 @@ Technical Summary, Core Architecture, Mathematical Formulation):
   * library routines: torch.softmax, F.layer_norm, F.linear in float64 and
     torch.autograd for the backward
   * finite differences of the forward for every backward output
-  * backward identities: softmax gradients sum to zero over a token's rows
+  * backward identities: softmax gradients sum to zero over a token's rows;
+    an id's dV rows sum to its tokens' da (torch autograd of the tail)
   * plan: numpy's stable lexsort and unique give the same sort and segments
 """
 from __future__ import annotations
@@ -288,6 +289,36 @@ def pin_backward_identities(o):
         r0, r1 = c["offsets"][t], c["offsets"][t + 1]
         close(g["dK"][r0:r1], 0 * g["dK"][r0:r1], 0.0, "untouched dK rows")
         close(g["dV"][r0:r1], 0 * g["dV"][r0:r1], 0.0, "untouched dV rows")
+    # dV_t = sum_i p_i da_i^T and each p_i sums to one, so the dV rows of an
+    # id add up to the sum of its tokens' da; da from torch autograd through
+    # the layer's tail (LayerNorm of the up-projection, then W_mix) alone
+    da = torch_tail_grad(c)
+    for t in np.unique(c["ids"]):
+        r0, r1 = c["offsets"][t], c["offsets"][t + 1]
+        close(g["dV"][r0:r1].sum(axis=0), da[c["ids"] == t].sum(axis=0),
+              1e-12, "dV rows of an id sum to its tokens' da")
+
+
+def torch_tail_grad(c):
+    """d(sum(y * dy))/da for the aggregate a, with torch routines: a from
+    torch.softmax and matrix-vector products, then y = W_mix [LayerNorm(
+    W_up a) ; x] under autograd with a as the leaf."""
+    import torch
+    import torch.nn.functional as F
+    T = lambda v: torch.tensor(np.asarray(v, np.float64), dtype=torch.float64)
+    x, K, V = T(c["x"]), T(c["K"]), T(c["V"])
+    rows = []
+    for i, t in enumerate(c["ids"]):
+        r0, r1 = int(c["offsets"][t]), int(c["offsets"][t + 1])
+        p = torch.softmax(torch.mv(K[r0:r1], x[i]), dim=0)
+        rows.append(torch.mv(V[r0:r1].t(), p))
+    a = torch.stack(rows).requires_grad_(True)
+    d = x.shape[1]
+    h = F.layer_norm(F.linear(a, T(c["W_up"])), (d,), T(c["gamma"]),
+                     T(c["beta"]), eps=1e-5)
+    y = F.linear(torch.cat([h, x], dim=1), T(c["W_mix"]))
+    (y * T(c["dy"])).sum().backward()
+    return a.grad.numpy()
 
 
 # ------------------------------------------------------------------ plan ---

@@ -2,7 +2,9 @@
 
 bf16 workload: elementwise max|g - o| <= 2e-2 on dx, dK, dV, dW_up, dgamma,
 dbeta, dW_mix; float32 workload: per-tensor relative error <= 1e-4.
-Run twice, every gradient is bitwise identical (no float atomics)."""
+Gradients and workspaces start as NaN, so every element (the zero rows of
+absent ids included) must be written. Run twice, every gradient is bitwise
+identical (no float atomics)."""
 import numpy as np
 import pytest
 
@@ -20,7 +22,7 @@ def _grads_vs_oracle(name, ln_perturb=False):
         import dataclasses
         g = np.random.default_rng(77).standard_normal((w.batch, w.spec.d))
         w = dataclasses.replace(w, dy=wl.store(g, w.spec.dtype))
-    res = gu.run(w, training=True)
+    res = gu.run(w, training=True, nan_fill=True)
     ref = gu.oracle_backward(w)
     for k in NAMES:
         got = gu.f64(res["grads"][k])
@@ -38,12 +40,13 @@ def _grads_vs_oracle(name, ln_perturb=False):
 
 def test_train_skew_bf16_backward():
     w, res = _grads_vs_oracle("train_skew_bf16")
-    # untouched table rows are exactly zero
+    # untouched table rows are exactly zero (dK, dV started as NaN)
     used = np.zeros(w.rows, bool)
     for t in np.unique(w.ids):
         used[w.offsets[t]:w.offsets[t + 1]] = True
-    dK = res["grads"]["dK"].cpu().numpy()
-    assert not dK[~used].any()
+    for k in ("dK", "dV"):
+        g = res["grads"][k].cpu().numpy()
+        assert not g[~used].any(), k
 
 
 @pytest.mark.parametrize("ln_perturb", [False, True])
@@ -106,7 +109,7 @@ def test_prefill_shapes_bf16_backward(tokens):
     w = wl.with_ids(base, base.ids[:tokens])
     g = np.random.default_rng(5).standard_normal((tokens, base.spec.d))
     w = dataclasses.replace(w, dy=wl.store(g, "bf16"))
-    res = gu.run(w, training=True)
+    res = gu.run(w, training=True, nan_fill=True)
     ref = gu.oracle_backward(w)
     for k in NAMES:
         got = gu.f64(res["grads"][k])
@@ -131,7 +134,9 @@ def test_train_prefill_full_batch_sampled(name):
     from static_token_routed_id_amd import workloads as wl
     w = gu.workload(name)
     w = dataclasses.replace(w, dy=wl.upstream_grad(w))
-    res = gu.run(w, training=True)
+    res = gu.run(w, training=True, nan_fill=True)
+    for k in NAMES:
+        assert bool(res["grads"][k].isfinite().all()), k
     rng = np.random.default_rng(5)
     tokens = np.sort(rng.choice(w.batch, 48, replace=False))
     present = np.unique(w.ids)

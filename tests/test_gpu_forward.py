@@ -3,8 +3,12 @@
 Tolerances: float32 workloads -- per-tensor relative error
 max|g - o| / max|o| <= 1e-4; bf16 workloads -- elementwise max|g - o| <= 2e-2
 on y (float32 output). The aggregate a = V_t^T Softmax(K_t x) is also
-checked directly (saved float32 copy), so LayerNorm and W_mix cannot hide
-an aggregation error."""
+checked directly (the saved float32 copy when training, else the copy the
+forward leaves in its scratch workspace, bf16 on bf16 workloads), so
+LayerNorm and W_mix cannot hide an aggregation error. Both modes run on
+every workload: inference takes other kernels (fp16 softmax weights in the
+wave items, the group kernel on large batches, bf16 u) than the saving
+forward of training. Outputs and workspaces start as NaN."""
 import numpy as np
 import pytest
 
@@ -13,40 +17,16 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-F32_REL = 1e-4
-BF16_ABS = 2e-2
-A_BF16_ABS = 2e-3   # the aggregate itself (|a| < 0.3 on these inputs)
+F32_REL = gu.F32_REL
+BF16_ABS = gu.BF16_ABS
+_check = gu.check_forward
 
 
-def _check(w, res, ref, tokens=None):
-    y = gu.f64(res["y"])
-    a = gu.f64(res["a32"]) if "a32" in res else None
-    if tokens is not None:
-        y = y[tokens]
-        a = a[tokens] if a is not None else None
-    if w.spec.dtype == "f32":
-        ey = gu.linf_rel(y, ref["y"])
-        print(f"{w.spec.name}: y linf-rel {ey:.3e}")
-        assert ey <= F32_REL
-        if a is not None:
-            ea = gu.linf_rel(a, ref["a"])
-            print(f"{w.spec.name}: a linf-rel {ea:.3e}")
-            assert ea <= F32_REL
-    else:
-        ey = gu.max_abs(y, ref["y"])
-        print(f"{w.spec.name}: y max abs {ey:.3e} (max|y| "
-              f"{np.abs(ref['y']).max():.2f})")
-        assert ey <= BF16_ABS
-        if a is not None:
-            ea = gu.max_abs(a, ref["a"])
-            print(f"{w.spec.name}: a max abs {ea:.3e}")
-            assert ea <= A_BF16_ABS
-
-
+@pytest.mark.parametrize("training", [False, True])
 @pytest.mark.parametrize("ln_perturb", [False, True])
-def test_tiny_fp32(ln_perturb):
+def test_tiny_fp32(ln_perturb, training):
     w = gu.workload("tiny_fp32", ln_perturb)
-    res = gu.run(w, training=True)
+    res = gu.run(w, training=training, nan_fill=True)
     _check(w, res, gu.oracle_forward(w))
 
 
@@ -56,17 +36,18 @@ def test_prefill_bf16(training):
     statistics of the W_up epilogue) and training (float32 u, saved state)
     paths."""
     w = gu.workload("prefill_bf16", True)
-    res = gu.run(w, training=training)
+    res = gu.run(w, training=training, nan_fill=True)
     _check(w, res, gu.oracle_forward(w))
 
 
-def test_prefill_bf16_ragged_small_and_large_plan():
+@pytest.mark.parametrize("training", [False, True])
+def test_prefill_bf16_ragged_small_and_large_plan(training):
     base = gu.workload("prefill_bf16")
     for B in (1000, 8193):
         ids = wl.batch_ids(base.spec, 1, B + 7)[7:]
         w = wl.with_ids(base, ids)
-        print(f"ragged B={B}", flush=True)
-        res = gu.run(w, training=True)
+        print(f"ragged B={B} training={training}", flush=True)
+        res = gu.run(w, training=training, nan_fill=True)
         _check(w, res, gu.oracle_forward(w))
 
 
@@ -82,38 +63,52 @@ def test_prefill_bf16_output_bf16():
     assert torch.equal(y16, y32.to(torch.bfloat16))
 
 
-def test_decode_bf16():
-    w = gu.workload("decode_bf16")
-    res = gu.run(w, training=True)
+@pytest.mark.parametrize("training", [False, True])
+@pytest.mark.parametrize("ln_perturb", [False, True])
+def test_decode_bf16(training, ln_perturb):
+    """64 tokens: inference runs the wave items with fp16 softmax weights,
+    the row-chunk combine, the split-K W_up on centred weights and the
+    row LayerNorm (ln_apply); training the saving forward."""
+    w = gu.workload("decode_bf16", ln_perturb)
+    res = gu.run(w, training=training, nan_fill=True)
     _check(w, res, gu.oracle_forward(w))
 
 
 @pytest.mark.timeout(900)
-def test_large_prefill_bf16_sampled():
+def test_large_prefill_bf16_every_token():
     """Full-size batch in the benchmark's launch configuration (inference,
-    no save), checked on sampled tokens: every token of the largest and of a
-    few mid-size segments, plus a random sample."""
+    no save): y, the save-less scratch and the output start as NaN; every
+    one of the 65536 rows of y and of the bf16 aggregate must be finite (a
+    work item dropped by the group kernel's device-wide queues would leave
+    NaN rows) and match the oracle, which runs over all tokens on a thread
+    pool."""
+    import time
     w = gu.workload("large_prefill_bf16")
-    res = gu.run(w, training=False)
+    res = gu.run(w, training=False, nan_fill=True)
+    y = gu.f64(res["y"])
+    a = gu.f64(res["a_act"])
+    assert np.isfinite(y).all(), "rows of y left unwritten"
+    assert np.isfinite(a).all(), "rows of the aggregate left unwritten"
+    t0 = time.time()
+    ref = gu.oracle_forward_parallel(w)
+    print(f"oracle over {w.batch} tokens in {time.time() - t0:.1f} s",
+          flush=True)
+    _check(w, res, ref)
+    # the busiest ids' tokens (the 128-token items) and a few mid-size ones
     L = gu.lib()
     pl = L.l3_plan_export(res["layer"].plan)
     st = pl["seg_tok_start"]
-    sizes = np.diff(st)
-    order = np.argsort(-sizes, kind="stable")
-    toks = [pl["perm"][st[order[0]]:st[order[0] + 1]][:256]]
-    for q in (1, 10, 100, 1000):
+    order = np.argsort(-np.diff(st), kind="stable")
+    for q in (0, 1, 10, 100, 1000):
         g = order[min(q, len(order) - 1)]
-        toks.append(pl["perm"][st[g]:st[g + 1]][:32])
-    rng = np.random.default_rng(0)
-    toks.append(rng.choice(w.batch, 512, replace=False))
-    tokens = np.unique(np.concatenate(toks))
-    ref = gu.oracle_forward(w, tokens=tokens)
-    _check(w, res, ref, tokens=tokens)
+        tk = pl["perm"][st[g]:st[g + 1]]
+        assert gu.max_abs(y[tk], ref["y"][tk]) <= BF16_ABS
 
 
-def test_train_skew_bf16_forward():
+@pytest.mark.parametrize("training", [False, True])
+def test_train_skew_bf16_forward(training):
     w = gu.workload("train_skew_bf16")
-    res = gu.run(w, training=True)
+    res = gu.run(w, training=training, nan_fill=True)
     _check(w, res, gu.oracle_forward(w))
 
 
@@ -211,27 +206,26 @@ def test_empty_batch():
 
 
 def test_u_far_from_zero_mean():
-    """LayerNorm input whose mean is tens of times its spread. Both inference
-    paths keep u in bf16, and its rounding (relative to |mean|) then sets the
-    error, well beyond the bf16 bound of the unshifted workloads. What is
-    checked is that the folded normalisation (one-pass per-tile sums, the
-    mean term cancelled against the folded weights; the 8192-token batch)
-    adds nothing to it: on the same 64 tokens its rms error is within 1.5x
-    of the row normalisation's (two-pass statistics of each row; the same
-    tokens as a 64-token batch)."""
+    """LayerNorm input whose mean is tens of times its spread (every row of
+    W_up shifted by one common vector). Where u is stored as bf16 it is
+    formed from W_up with its columns centred, so its rounding follows the
+    spread of u, not its mean: both the folded normalisation (8192 tokens,
+    per-tile sums, the mean term folded into W_mix) and the row
+    normalisation (the same first 64 tokens as a batch of their own) meet
+    the bf16 bound against the oracle."""
     w = wl.with_u_offset(gu.workload("prefill_bf16", True), 50.0)
-    full = gu.f64(gu.run(w)["y"])
-    tok = np.arange(64)
-    w64 = wl.with_ids(w, w.ids[:64], x=np.ascontiguousarray(w.x[:64]))
-    small = gu.f64(gu.run(w64)["y"])
+    full = gu.run(w, nan_fill=True)
+    rng = np.random.default_rng(5)
+    tok = np.unique(np.concatenate([np.arange(64),
+                                    rng.choice(w.batch, 448, replace=False)]))
     ref = gu.oracle_forward(w, tokens=tok)
     ratio = np.abs(ref["mean"]) / np.sqrt(ref["var"])
-    e_fold = float(np.sqrt(np.mean((full[tok] - ref["y"]) ** 2)))
-    e_row = float(np.sqrt(np.mean((small - ref["y"]) ** 2)))
-    print(f"median |mean| / std of u {np.median(ratio):.1f}; rms error: "
-          f"folded {e_fold:.3e}, row {e_row:.3e}")
+    print(f"median |mean| / std of u {np.median(ratio):.1f}")
     assert np.median(ratio) >= 10
-    assert e_fold <= 1.5 * e_row + 1e-4
+    _check(w, full, ref, tokens=tok)
+    w64 = wl.with_ids(w, w.ids[:64], x=np.ascontiguousarray(w.x[:64]))
+    small = gu.run(w64, nan_fill=True)
+    _check(w64, small, gu.oracle_forward(w64))
 
 
 def _times8(w):
@@ -250,7 +244,7 @@ def test_prefill_bf16_w_up_folded_sampled():
     sampled tokens (both ends and a random sample) at the bf16 bound."""
     w = _times8(gu.workload("prefill_bf16"))
     assert w.batch == 65536
-    res = gu.run(w, training=False)
+    res = gu.run(w, training=False, nan_fill=True)
     rng = np.random.default_rng(1)
     tokens = np.unique(np.concatenate([
         np.arange(256), rng.choice(w.batch, 1024, replace=False),
@@ -260,20 +254,16 @@ def test_prefill_bf16_w_up_folded_sampled():
 
 
 def test_u_far_from_zero_mean_w_up_folded():
-    """The offset input of the test above on 65536 tokens: with W_up's
-    columns centred before the fold, neither the variance nor the output
-    subtracts a large mean, so the error stays within 1.5x of the row
-    normalisation's on the same 64 tokens (in practice well below it)."""
+    """The offset input of the test above on 65536 tokens: W_up folded
+    into W_mix with its columns centred first, so neither the variance nor
+    the output subtracts a large mean; the bf16 bound against the oracle."""
     w = wl.with_u_offset(_times8(gu.workload("prefill_bf16", True)), 50.0)
-    full = gu.f64(gu.run(w)["y"])
-    tok = np.arange(64)
-    w64 = wl.with_ids(w, w.ids[:64], x=np.ascontiguousarray(w.x[:64]))
-    small = gu.f64(gu.run(w64)["y"])
+    res = gu.run(w, nan_fill=True)
+    rng = np.random.default_rng(6)
+    tok = np.unique(np.concatenate([np.arange(64),
+                                    rng.choice(w.batch, 448, replace=False)]))
     ref = gu.oracle_forward(w, tokens=tok)
     ratio = np.abs(ref["mean"]) / np.sqrt(ref["var"])
-    e_fused = float(np.sqrt(np.mean((full[tok] - ref["y"]) ** 2)))
-    e_row = float(np.sqrt(np.mean((small - ref["y"]) ** 2)))
-    print(f"median |mean| / std of u {np.median(ratio):.1f}; rms error: "
-          f"W_up folded {e_fused:.3e}, row {e_row:.3e}")
+    print(f"median |mean| / std of u {np.median(ratio):.1f}")
     assert np.median(ratio) >= 10
-    assert e_fused <= 1.5 * e_row + 1e-4
+    _check(w, res, ref, tokens=tok)
