@@ -158,6 +158,30 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
                      void* stream);
 
 /*
+ * l3_forward_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the inference forward of l3_forward (save = NULL) with its
+ * scratch workspace taken from a static device array of
+ * L3_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends. It allocates nothing; the caller still passes
+ * the plan, inputs and y (same meaning, layout and ownership as
+ * l3_forward). Records no stage timings.
+ * Errors: as l3_forward; L3_ERR_WORKSPACE, before any device work, when the
+ * planned batch's forward needs more scratch than the array holds (e.g. a
+ * 64-token decode batch at d = 2048, d_e = 512 fits; an 8192-token batch at
+ * d = 1024 does not); L3_ERR_HIP if the array's device address cannot be
+ * obtained. All calls on one GPU share that GPU's array and it keeps the
+ * last call's contents: calls that overlap on one GPU (on different
+ * streams, or from different host threads without ordering) race and give
+ * wrong results; serialise them on one stream.
+ */
+#define L3_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+l3_status l3_forward_noalloc(l3_plan_t plan, const void* x, const void* K,
+                             const void* V, const void* W_up,
+                             const void* gamma, const void* beta,
+                             const void* W_mix, void* y, void* stream);
+
+/*
  * l3_backward -- gradients of sum(y * dy) for the planned batch, from the
  * state a saving l3_forward on this plan (since its last l3_plan /
  * l3_replan) left in `save` (the pages print no gradients; these are the

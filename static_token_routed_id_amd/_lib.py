@@ -61,6 +61,7 @@ def _load():
         "l3_replan": (c_int, [P, P, c_int64, P, P]),
         "l3_forward": (c_int, [P, P, P, P, P, P, P, P, P, P, c_size_t, P,
                                c_size_t, P]),
+        "l3_forward_noalloc": (c_int, [P, P, P, P, P, P, P, P, P, P]),
         "l3_backward": (c_int, [P, P, P, P, P, P, P, P, P, P, c_size_t, P, P,
                                 P, P, P, P, P, P, c_size_t, P]),
         "l3_plan_check": (c_int, [P, P]),
@@ -83,6 +84,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("l3_workspace_size", "l3_plan", "l3_replan", "l3_forward",
+            "l3_forward_noalloc",
             "l3_backward", "l3_plan_check", "l3_plan_export", "l3_plan_info",
             "l3_plan_release", "l3_plan_tokens", "l3_status_str",
             "l3_timing_enable", "l3_timing_read", "l3_stage_name",
@@ -256,6 +258,25 @@ def l3_forward(plan: Plan, x, K, V, W_up, gamma, beta, W_mix, y, save,
                            _ptr(gamma), _ptr(beta), _ptr(W_mix), _ptr(y),
                            _ptr(save), _nbytes(save), _ptr(scratch),
                            _nbytes(scratch), _stream(stream)), "l3_forward")
+
+
+L3_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def l3_forward_noalloc(plan: Plan, x, K, V, W_up, gamma, beta, W_mix, y,
+                       stream=None) -> None:
+    """Inference forward whose scratch is the library's static device array
+    (no workspace argument, nothing allocated)."""
+    B = plan.tokens
+    if B > 0:
+        desc = plan.desc
+        _arg(x, "x", _act_dtype(desc.dtype), (B, desc.d))
+        _check_params(desc, K, V, W_up, gamma, beta, W_mix)
+        _arg(y, "y", _act_dtype(desc.y_dtype), (B, desc.d))
+    _check(_lib.l3_forward_noalloc(plan.handle, _ptr(x), _ptr(K), _ptr(V),
+                                   _ptr(W_up), _ptr(gamma), _ptr(beta),
+                                   _ptr(W_mix), _ptr(y), _stream(stream)),
+           "l3_forward_noalloc")
 
 
 def l3_backward(plan: Plan, dy, x, K, V, W_up, gamma, beta, W_mix, save, dx,

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -1533,6 +1534,69 @@ l3_status l3_timing_read(l3_plan_t plan, double* ms, int64_t* count,
     if (count) count[i] = cnt[i];
   }
   return st;
+}
+
+}  // extern "C"
+
+// ---- allocation-free inference forward -----------------------------------
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops): the forward's scratch workspace is this file-scope device
+// array instead of caller memory. Each GPU the library runs on holds its
+// own copy, at its own address, until the process ends. In host code the
+// array's name is only a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current and
+// kept below; only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[L3_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (nullptr on a HIP error).
+void* static_scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+      return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+l3_status l3_forward_noalloc(l3_plan_t plan, const void* x, const void* K,
+                             const void* V, const void* W_up,
+                             const void* gamma, const void* beta,
+                             const void* W_mix, void* y, void* stream) {
+  try {
+    if (!plan) return L3_ERR_NULL;
+    if (plan->B == 0) return L3_OK;
+    // the forward's scratch must fit the static array (checked before any
+    // device work, like a caller workspace that is too small)
+    if (fwd_bytes_for(plan->desc, plan->B) > L3_NOALLOC_SCRATCH_BYTES)
+      return L3_ERR_WORKSPACE;
+    void* ptr = static_scratch_ptr();
+    if (!ptr) return L3_ERR_HIP;
+    // stage timing creates HIP events; this entry point records none
+    const bool timing = plan->timing;
+    plan->timing = false;
+    const l3_status st = l3_forward(plan, x, K, V, W_up, gamma, beta, W_mix,
+                                    y, nullptr, 0, ptr,
+                                    L3_NOALLOC_SCRATCH_BYTES, stream);
+    plan->timing = timing;
+    return st;
+  } catch (...) {
+    return L3_ERR_HIP;
+  }
 }
 
 }  // extern "C"
