@@ -233,7 +233,8 @@ def oracle_backward(w: wl.Workload):
                               dd["beta"], dd["W_mix"], dd["dy"])
 
 
-def oracle_backward_sampled(w: wl.Workload, tokens, sample_ids):
+def oracle_backward_sampled(w: wl.Workload, tokens, sample_ids, threads=16,
+                            chunk=1024):
     """Reference gradients of a whole training batch, sampled: dx rows of
     `tokens`, dK / dV rows of the ids in `sample_ids` (dict id -> [n, .]),
     and the weight gradients dW_mix, dW_up, dgamma, dbeta over every token.
@@ -243,48 +244,80 @@ def oracle_backward_sampled(w: wl.Workload, tokens, sample_ids):
     backward; the weight gradients' sums over tokens are taken as one matrix
     product each (dy^T [H ; X], dU^T A) instead of per-token outer products,
     and the softmax backward runs only for the tokens the samples need.
-    tests/test_oracle_sampled.py checks it against the oracle's backward."""
+    Tokens run in id-ordered chunks on a thread pool (BLAS single-threaded
+    inside each worker); an id's dK / dV adds its chunks' sums in chunk
+    order. tests/test_oracle_sampled.py checks it against the oracle's
+    backward."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
     from oracle import l3_oracle as O
-    dd = wl.decoded(w)
-    x, dy, ids, offsets = dd["x"], dd["dy"], dd["ids"], dd["offsets"]
-    W_up, W_mix = dd["W_up"], dd["W_mix"]
-    gamma, beta = dd["gamma"], dd["beta"]
+    x, dy = wl.decode(w.x), wl.decode(w.dy)
+    ids, offsets = w.ids.astype(np.int64), w.offsets
+    W_up, W_mix = wl.decode(w.W_up), wl.decode(w.W_mix)
+    gamma, beta = wl.decode(w.gamma), wl.decode(w.beta)
     B, d = x.shape
     d_e = W_up.shape[1]
     W_a, W_b = W_mix[:, :d], W_mix[:, d:]
     tok_set = {int(t) for t in tokens}
     id_set = {int(t) for t in sample_ids}
-    DH = dy @ W_a  # row i: W_a^T dy_i
     H = np.zeros((B, d))
     A = np.zeros((B, d_e))
     DU = np.zeros((B, d))
     UH = np.zeros((B, d))
-    dx = {}
-    dK = {}
-    dV = {}
+    order = np.argsort(ids, kind="stable")
+    chunks = [order[i:i + chunk] for i in range(0, B, chunk)]
+
+    def one(c):
+        Kr, Vr = _LastSlice(w.K), _LastSlice(w.V)
+        dx, dK, dV = {}, {}, {}
+        c = [int(i) for i in c]
+        P, Ac = [], np.zeros((len(c), d_e))
+        for j, i in enumerate(c):
+            t = int(ids[i])
+            r0, r1 = int(offsets[t]), int(offsets[t + 1])
+            p = O.softmax(O.scores(Kr[r0:r1], x[i]))
+            Ac[j] = O.aggregate(Vr[r0:r1], p)
+            P.append(p)
+        # up-projection and LayerNorm row-wise over the chunk's tokens
+        Uc = O.up(W_up, Ac)
+        Hc, UHc, _, varc = O.layernorm(Uc, gamma, beta)
+        DHc = dy[c] @ W_a
+        for j, i in enumerate(c):
+            t = int(ids[i])
+            du = O.layernorm_backward(DHc[j], gamma, UHc[j], varc[j])
+            H[i], A[i], DU[i], UH[i] = Hc[j], Ac[j], du, UHc[j]
+            if i in tok_set or t in id_set:
+                r0, r1 = int(offsets[t]), int(offsets[t + 1])
+                Kt, Vt = Kr[r0:r1], Vr[r0:r1]
+                p = P[j]
+                da = W_up.T @ du
+                ds = O.softmax_backward(p, Vt @ da)
+                if i in tok_set:
+                    dx[i] = W_b.T @ dy[i] + Kt.T @ ds
+                if t in id_set:
+                    if t not in dK:
+                        dK[t] = np.zeros((r1 - r0, d))
+                        dV[t] = np.zeros((r1 - r0, d_e))
+                    dK[t] += np.outer(ds, x[i])
+                    dV[t] += np.outer(p, da)
+        return dx, dK, dV
+
+    with threadpool_limits(limits=1):
+        with ThreadPoolExecutor(threads) as ex:
+            parts = list(ex.map(one, chunks))
+    dx, dK, dV = {}, {}, {}
     for t in id_set:
         n = int(offsets[t + 1] - offsets[t])
         dK[t] = np.zeros((n, d))
         dV[t] = np.zeros((n, d_e))
-    for i in range(B):
-        t = int(ids[i])
-        r0, r1 = int(offsets[t]), int(offsets[t + 1])
-        Kt = np.asarray(dd["K"][r0:r1], dtype=np.float64)
-        Vt = np.asarray(dd["V"][r0:r1], dtype=np.float64)
-        p = O.softmax(O.scores(Kt, x[i]))
-        a = O.aggregate(Vt, p)
-        u = O.up(W_up, a)
-        h, uhat, _, var = O.layernorm(u, gamma, beta)
-        du = O.layernorm_backward(DH[i], gamma, uhat, var)
-        H[i], A[i], DU[i], UH[i] = h, a, du, uhat
-        if i in tok_set or t in id_set:
-            da = W_up.T @ du
-            ds = O.softmax_backward(p, Vt @ da)
-            if i in tok_set:
-                dx[i] = W_b.T @ dy[i] + Kt.T @ ds
-            if t in id_set:
-                dK[t] += np.outer(ds, x[i])
-                dV[t] += np.outer(p, da)
+    for pdx, pdK, pdV in parts:
+        dx.update(pdx)
+        for t in pdK:
+            dK[t] += pdK[t]
+            dV[t] += pdV[t]
+    DH = dy @ W_a
     return dict(dx=dx, dK=dK, dV=dV,
                 dW_mix=dy.T @ np.concatenate([H, x], axis=1),
                 dW_up=DU.T @ A, dgamma=(DH * UH).sum(axis=0),

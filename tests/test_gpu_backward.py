@@ -157,3 +157,53 @@ def test_train_prefill_full_batch_sampled(name):
     for k, e in errs.items():
         print(f"{name} full batch {k}: max abs {e:.3e}")
         assert e <= 2e-2, k
+
+
+@pytest.mark.timeout(900)
+def test_train_large_prefill_sampled():
+    """The training step at the large-prefill shapes (d = 2048, d_e = 512,
+    65536 tokens, a table of 1,759,242 rows: dK alone is 14.4 GB of
+    float32), as `bench.py --train --workload large_prefill_bf16` times it.
+    Every gradient starts as NaN and must come out finite; against the
+    oracle's steps on samples: dx of 48 tokens, dK / dV of eight ids (the
+    four most frequent, 512 rows each, and four drawn among the rest), and
+    the whole-batch dW_mix, dW_up, dgamma, dbeta. Only the sampled rows of
+    dK, dV and dx leave the GPU."""
+    import dataclasses
+    import time
+    from static_token_routed_id_amd import workloads as wl
+    torch = gu.torch_cuda()
+    w = gu.workload("large_prefill_bf16")
+    w = dataclasses.replace(w, dy=wl.upstream_grad(w))
+    res = gu.run(w, training=True, nan_fill=True)
+    g = res["grads"]
+    for k in NAMES:
+        assert bool(torch.isfinite(g[k]).all()), k
+    rng = np.random.default_rng(5)
+    tokens = np.sort(rng.choice(w.batch, 48, replace=False))
+    present = np.unique(w.ids)
+    ids = [int(t) for t in present[:4]] + \
+        [int(t) for t in rng.choice(present[4:], 4, replace=False)]
+    t0 = time.time()
+    ref = gu.oracle_backward_sampled(w, tokens, ids)
+    print(f"sampled reference in {time.time() - t0:.1f} s", flush=True)
+    tix = torch.from_numpy(tokens).cuda()
+    errs = {
+        "dx": gu.max_abs(gu.f64(g["dx"][tix]),
+                         np.stack([ref["dx"][int(i)] for i in tokens])),
+        "dK": max(gu.max_abs(gu.f64(g["dK"][w.offsets[t]:w.offsets[t + 1]]),
+                             ref["dK"][t]) for t in ids),
+        "dV": max(gu.max_abs(gu.f64(g["dV"][w.offsets[t]:w.offsets[t + 1]]),
+                             ref["dV"][t]) for t in ids),
+    }
+    for k in ("dW_mix", "dW_up", "dgamma", "dbeta"):
+        errs[k] = gu.max_abs(gu.f64(g[k]), ref[k])
+    # rows of ids absent from the batch are exactly zero
+    absent = np.setdiff1d(np.arange(w.spec.vocab), present)[:64]
+    for t in absent:
+        r0, r1 = int(w.offsets[t]), int(w.offsets[t + 1])
+        assert float(g["dK"][r0:r1].abs().max()) == 0.0
+        assert float(g["dV"][r0:r1].abs().max()) == 0.0
+    for k, e in errs.items():
+        print(f"large prefill training {k}: max abs {e:.3e}")
+        assert e <= 2e-2, k

@@ -6,18 +6,23 @@ token and every id sampled, all seven gradients equal to float64 rounding.
 import dataclasses
 
 import numpy as np
+import pytest
 
 from static_token_routed_id_amd import workloads as wl
 from tests import gpu_util as gu
 
 
-def test_sampled_reference_equals_oracle_backward():
+@pytest.mark.parametrize("chunk", [1024, 64])
+def test_sampled_reference_equals_oracle_backward(chunk):
+    """chunk 64: ids spread over several chunks on four threads, so an id's
+    dK / dV adds partial sums from several workers."""
     w = wl.make("train_skew_bf16")
     w = dataclasses.replace(w, dy=wl.upstream_grad(w))
     B = w.batch
     present = np.unique(w.ids)
     ref = gu.oracle_backward(w)
-    got = gu.oracle_backward_sampled(w, range(B), present)
+    got = gu.oracle_backward_sampled(w, range(B), present, threads=4,
+                                     chunk=chunk)
     for k in ("dW_mix", "dW_up", "dgamma", "dbeta"):
         np.testing.assert_allclose(got[k], ref[k], rtol=1e-10, atol=1e-10)
     for i in range(B):
