@@ -10,7 +10,8 @@ state + backward with a seeded upstream gradient (fwd+bwd tokens/s, every
 stage's mean ms), e.g. `--train --workload train_skew_bf16`. `--offload
 --workload decode_bf16` keeps the tables in pinned host memory and stages
 the batch's rows into HBM beside a stand-in for the preceding layers,
-against the same step with the tables in HBM. `--layers L`
+against the same step with the tables in HBM. `--allocate` times the
+embedding allocation (host code) on a synthetic corpus. `--layers L`
 times plan + L layer forwards (each layer its own tables and weights over
 the same offsets, one plan for the stack): tokens/s through the stack.
 
@@ -23,8 +24,13 @@ from HIP events recorded on the launch stream around the step during the
 timed steps; `traffic` is the HBM bytes per launch from the committed
 FETCH_SIZE / WRITE_SIZE counter summary
 (profiles/traffic_gather_<workload>.md), or null when the kernels changed
-since it was taken. `cpu_baseline` is the fp64 oracle on a bounded sample of
-the same batch on the host CPU.
+since it was taken; `copy_peak_gbs` is a measured 2 GiB device copy (bytes
+read + written per second) and `frac_of_copy_peak` the gather's rate
+against it. `cpu_baseline` is the fp64 oracle on a bounded sample of the
+same batch on the host CPU (one oracle call per host thread, CPU model
+recorded). Workloads whose step moves less than 1 GiB (everything but the
+large prefill) are timed step by step with HIP events, L2 and the MALL
+flushed between steps by a 1 GiB write outside the events (`--flush`).
 """
 from __future__ import annotations
 
@@ -153,13 +159,41 @@ def cpu_baseline_train(w, dy, budget_s: float) -> dict:
         n = int(min(w.batch, max(16, budget_s / max(dt / n, 1e-6))))
         dt = run(n)
     return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"the first {n} tokens of the {w.batch}-token batch as "
                       f"a batch of their own, forward and backward in "
                       f"float64, one thread, {dt:.1f} s"}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_threads() -> int:
+    """Host threads for the oracle baseline: the CPUs this process may run
+    on, at most 16 (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(w, budget_s: float) -> dict:
-    """The oracle (as it stands) on a bounded sample of the batch."""
+    """The oracle (as it stands) on a bounded sample of the batch: the
+    sampled tokens split into one slice per host thread, each slice one
+    oracle.forward call (tokens are independent), BLAS single-threaded
+    inside each call; wall time of the whole sample."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from threadpoolctl import threadpool_limits
 
     from oracle import l3_oracle
@@ -169,19 +203,49 @@ def cpu_baseline(w, budget_s: float) -> dict:
                             "beta", "W_mix")]
     rng = np.random.default_rng(1234)
     order = rng.permutation(w.batch)
+    T = cpu_threads()
+
+    def run(n):
+        parts = np.array_split(order[:n], T)
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(T) as ex:
+            list(ex.map(lambda tk: l3_oracle.forward(*args, tokens=tk),
+                        [p for p in parts if len(p)]))
+        return time.perf_counter() - t0
+
     with threadpool_limits(limits=1):
-        n = 16
-        t0 = time.perf_counter()
-        l3_oracle.forward(*args, tokens=order[:n])
-        dt = time.perf_counter() - t0
-        n = int(min(w.batch, max(16, budget_s / max(dt / 16, 1e-6))))
-        t0 = time.perf_counter()
-        l3_oracle.forward(*args, tokens=order[:n])
-        dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        n = min(w.batch, 16 * T)
+        dt = run(n)
+        n = int(min(w.batch, max(n, budget_s / max(dt / n, 1e-6))))
+        dt = run(n)
+    return {"value": n / dt, "unit": "tokens/s", "cores": T, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{n} tokens drawn at random (seed 1234) from the "
                       f"{w.batch}-token batch, full layer forward in float64, "
-                      f"one thread, {dt:.1f} s"}
+                      f"{T} threads (one oracle.forward call per thread on "
+                      f"its share of the sample), {dt:.1f} s wall"}
+
+
+def copy_peak_gbs(nbytes: int = 1 << 31, reps: int = 5) -> float:
+    """Measured device-copy rate (bytes read + written per second) of a
+    2 GiB device-to-device copy, the practical HBM ceiling beside the 8 TB/s
+    of the data sheet."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(
+        enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
 def run_offload(args) -> None:
@@ -338,6 +402,73 @@ def run_offload(args) -> None:
     print(json.dumps(out), flush=True)
 
 
+def run_allocate(args) -> None:
+    """The embedding allocation (host code): l3_allocate's LZW-variant scan
+    of a seeded synthetic corpus at the large prefill's allocation shape
+    (vocab 131072, budget 2^22 rows, k = 512), against the oracle's scan of
+    a prefix of the same corpus; the uniform split beside it."""
+    from static_token_routed_id_amd import _lib as L
+    from static_token_routed_id_amd import workloads as wl
+    spec = wl.SPECS["large_prefill_bf16"]
+    V, budget, k = spec.vocab, spec.budget, spec.k_max
+    n = int(args.corpus_tokens)
+    t0 = time.perf_counter()
+    corpus = wl.synthetic_corpus(V, n, seed=1)
+    gen_s = time.perf_counter() - t0
+    for _ in range(max(0, args.warmup)):
+        L.l3_allocate(L.L3_ALLOC_LZW, corpus, V, budget, k)
+    reps = max(1, args.steps)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        counts, offsets = L.l3_allocate(L.L3_ALLOC_LZW, corpus, V, budget, k)
+    dt = (time.perf_counter() - t0) / reps
+    # tokens the scan read before the budget ran out: the prefix whose own
+    # scan reaches the same rows
+    t0 = time.perf_counter()
+    ucounts, _ = L.l3_allocate(L.L3_ALLOC_UNIFORM, None, V, budget, k)
+    dt_u = time.perf_counter() - t0
+    out = {
+        "metric": "embedding allocation corpus tokens/s (LZW-variant scan, "
+                  "host)",
+        "value": round(n / dt, 1), "unit": "tokens/s", "n_gpus": 0,
+        "steps": reps, "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True,
+        "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic corpus (seeded Zipf phrase book, Zipf phrase "
+                "draws)",
+        "config": {"workload": "allocation of the large prefill",
+                   "vocab": V, "budget": budget, "k_max": k,
+                   "corpus_tokens": n, "corpus_gen_s": round(gen_s, 2)},
+        "allocation": {"rows": int(counts.sum()),
+                       "max": int(counts.max()),
+                       "at_cap": int((counts == k).sum()),
+                       "at_one": int((counts == 1).sum()),
+                       "median": float(np.median(counts)),
+                       "top_1pct_share": round(float(
+                           np.sort(counts)[::-1][:V // 100].sum()
+                           / counts.sum()), 4)},
+        "uniform": {"rows": int(ucounts.sum()), "ms": round(dt_u * 1e3, 3)},
+    }
+    if args.cpu_seconds > 0:
+        from oracle import allocation as A
+        m = min(n, 200_000)
+        t0 = time.perf_counter()
+        A.lzw(corpus[:m], V, budget, k)
+        dto = time.perf_counter() - t0
+        m = int(min(n, max(m, args.cpu_seconds / max(dto / m, 1e-9))))
+        t0 = time.perf_counter()
+        ref = A.lzw(corpus[:m], V, budget, k)
+        dto = time.perf_counter() - t0
+        same, _ = L.l3_allocate(L.L3_ALLOC_LZW, corpus[:m], V, budget, k)
+        out["cpu_baseline"] = {
+            "value": m / dto, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"the first {m} corpus tokens, pure-Python scan, one "
+                      f"thread, {dto:.1f} s (library result on the same "
+                      f"prefix identical: {bool(np.array_equal(same, ref))})"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,8 +489,17 @@ def main():
     ap.add_argument("--prelayer-gb", type=float, default=5.2,
                     help="weights the preceding-layer stand-in streams a step "
                          "(5.2 GB: a 2.6B-parameter model in bf16)")
+    ap.add_argument("--allocate", action="store_true",
+                    help="time the embedding allocation (host) instead")
+    ap.add_argument("--corpus-tokens", type=float, default=16e6,
+                    help="synthetic corpus length for --allocate")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
+                    help="flush L2 and MALL between timed steps (auto: when "
+                         "a step's algorithmic bytes are under 1 GiB)")
+    ap.add_argument("--no-copy-peak", dest="copy_peak", action="store_false",
+                    help="skip the measured device-copy rate")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -371,6 +511,9 @@ def main():
         sys.exit(2)
     if args.offload:
         run_offload(args)
+        return
+    if args.allocate:
+        run_allocate(args)
         return
 
     import torch
@@ -429,17 +572,40 @@ def main():
             L.l3_backward(layer.plan, dy, *params, layer.save, *grads,
                           layer.scratch)
 
+    # Cache honesty: a step that touches less than the 256 MB MALL plus the
+    # L2s could be served from cache by the step before; unless its
+    # algorithmic bytes exceed 1 GiB, a 1 GiB write between steps (outside
+    # the timed events) evicts both, and steps are timed one by one.
+    ab_table = algorithmic_bytes(w, plan_np, info["group_min_rows"])["total"]
+    flush = args.flush == "on" or (args.flush == "auto" and
+                                   ab_table < (1 << 30))
+    flush_buf = (torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+                 if flush else None)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     L.l3_timing_read(layer.plan)          # drop warm-up events
     L.l3_timing_enable(layer.plan, True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if flush:
+        evs = [(torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a_ev, b_ev in evs:
+            flush_buf.fill_(float(len(evs)))
+            a_ev.record()
+            step()
+            b_ev.record()
+        torch.cuda.synchronize()
+        step_ms = sum(a_ev.elapsed_time(b_ev) for a_ev, b_ev in evs)
+        t0, t1 = 0.0, step_ms * 1e-3
+    else:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     L.l3_timing_enable(layer.plan, False)
     stages = L.l3_timing_read(layer.plan)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -501,7 +667,17 @@ def main():
         "plan_info": info,
         "stage_ms": {k: round(v, 4) for k, v in stage_avg.items()},
         "mfma": mfma,
+        "timing": ("HIP events around each step, L2 and MALL flushed "
+                   "between steps by a 1 GiB write outside the events"
+                   if flush else
+                   "wall clock over the timed steps, synchronised on both "
+                   "sides (no flush: a step touches far more than the "
+                   "caches hold)"),
     }
+    if args.copy_peak:
+        cp = copy_peak_gbs()
+        out["roofline"]["copy_peak_gbs"] = round(cp, 1)
+        out["roofline"]["frac_of_copy_peak"] = round(achieved / cp, 4)
     if args.cpu_seconds > 0:
         if args.train:
             cb = cpu_baseline_train(w, dy_np, args.cpu_seconds)

@@ -212,6 +212,38 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
                       size_t scratch_bytes, void* stream);
 
 /*
+ * l3_allocate -- rows per token id (the n_t of the offsets array l3_plan
+ * takes) from a budget of embeddings (gist.science explainer,
+ * Information-Theoretic Embedding Allocation: an LZW-variant scan of a
+ * corpus gives frequent context suffixes more embeddings, every token
+ * between 1 and k; Key Contributions: compared with uniform allocation).
+ * Host code, run once per model before any batch is planned (LZW's parse
+ * is a chain of dependent steps); all pointers are host memory.
+ *   method   L3_ALLOC_LZW: the dictionary starts with every single token (one
+ *            embedding each); the corpus is parsed as LZW parses it; each
+ *            added entry (phrase + next token c) is one more embedding of
+ *            c; a token owning k_max embeddings takes no new entry; the
+ *            scan stops when the embeddings reach the budget or the corpus
+ *            ends (one pass), any budget left unassigned.
+ *            L3_ALLOC_UNIFORM: budget / vocab each, the remainder one each
+ *            to the lowest ids (the corpus is not read).
+ *   corpus   int32 [n_tokens] token ids in [0, vocab) (may be NULL when
+ *            n_tokens is 0 or the method is uniform)
+ *   vocab    V >= 1; budget in [V, V * k_max]; k_max in [1, 512]
+ *   counts   int64 [vocab] out: rows of each id, in [1, k_max]
+ *   offsets  int64 [vocab + 1] out (or NULL): exclusive prefix sum of counts
+ * Errors: L3_ERR_DTYPE (unknown method), L3_ERR_NULL, L3_ERR_SHAPE,
+ * L3_ERR_TOKEN_RANGE (a corpus token outside [0, vocab); nothing written),
+ * L3_ERR_WORKSPACE (host memory for the dictionary could not be
+ * allocated).
+ */
+#define L3_ALLOC_UNIFORM 0
+#define L3_ALLOC_LZW 1
+l3_status l3_allocate(int method, const int32_t* corpus, int64_t n_tokens,
+                      int64_t vocab, int64_t budget, int32_t k_max,
+                      int64_t* counts, int64_t* offsets);
+
+/*
  * l3_stage_rows -- for tables kept in host memory (gist.science explainer,
  * Systems-Friendly Design: the tables may live in CPU memory because a
  * token's rows follow from its id alone, Core Architecture, Static

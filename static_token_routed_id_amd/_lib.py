@@ -62,6 +62,8 @@ def _load():
         "l3_forward": (c_int, [P, P, P, P, P, P, P, P, P, P, c_size_t, P,
                                c_size_t, P]),
         "l3_forward_noalloc": (c_int, [P, P, P, P, P, P, P, P, P, P]),
+        "l3_allocate": (c_int, [c_int, P, c_int64, c_int64, c_int64, c_int32,
+                                P, P]),
         "l3_backward": (c_int, [P, P, P, P, P, P, P, P, P, P, c_size_t, P, P,
                                 P, P, P, P, P, P, c_size_t, P]),
         "l3_plan_check": (c_int, [P, P]),
@@ -84,7 +86,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("l3_workspace_size", "l3_plan", "l3_replan", "l3_forward",
-            "l3_forward_noalloc",
+            "l3_forward_noalloc", "l3_allocate",
             "l3_backward", "l3_plan_check", "l3_plan_export", "l3_plan_info",
             "l3_plan_release", "l3_plan_tokens", "l3_status_str",
             "l3_timing_enable", "l3_timing_read", "l3_stage_name",
@@ -328,6 +330,28 @@ def l3_stage_rows(plan: Plan, K_host, V_host, K_stage, V_stage,
     _check(fn(plan.handle, _ptr(K_host), _ptr(V_host), _ptr(K_stage),
               _ptr(V_stage), rows, _stream(stream)),
            "l3_stage_rows_dma" if dma else "l3_stage_rows")
+
+
+L3_ALLOC_UNIFORM = 0
+L3_ALLOC_LZW = 1
+
+
+def l3_allocate(method: int, corpus, vocab: int, budget: int,
+                k_max: int = L3_MAX_ROWS_PER_ID):
+    """Rows per token id (int64 [vocab]) and the offsets (int64 [vocab+1])
+    from the embedding allocation; corpus is a host int32 array (numpy)."""
+    if corpus is None:
+        corpus = np.zeros(0, np.int32)
+    corpus = np.ascontiguousarray(corpus)
+    if corpus.dtype != np.int32 or corpus.ndim != 1:
+        raise TypeError("corpus: a 1-D int32 numpy array is required")
+    counts = np.zeros(max(int(vocab), 1), np.int64)
+    offsets = np.zeros(max(int(vocab), 1) + 1, np.int64)
+    P = lambda a: a.ctypes.data_as(c_void_p)
+    _check(_lib.l3_allocate(int(method), P(corpus), corpus.shape[0],
+                            int(vocab), int(budget), int(k_max), P(counts),
+                            P(offsets)), "l3_allocate")
+    return counts, offsets
 
 
 def l3_plan_check(plan: Plan, stream=None) -> int:

@@ -30,7 +30,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 SOURCES = ["plan.hip", "seg_fwd.hip", "seg_group.hip", "gemm.hip", "bwd.hip",
            "stage.hip",
-           "api.cpp"]
+           "api.cpp", "alloc.cpp"]
 
 
 def _run(cmd):

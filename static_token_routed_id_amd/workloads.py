@@ -367,6 +367,51 @@ def with_ids(w: Workload, ids: np.ndarray, x: Optional[np.ndarray] = None,
     return dataclasses.replace(w, ids=ids, x=x, dy=dy)
 
 
+# ------------------------------------------------------------ corpora ---
+# Seed config of the synthetic corpora (not one of the layer workloads).
+CORPUS_CFG = 100
+
+
+def synthetic_corpus(vocab: int, n_tokens: int, seed: int = 0,
+                     zipf_s: float = 1.0, phrases: int = 0,
+                     max_len: int = 6) -> np.ndarray:
+    """A seeded token stream with the repetition structure of text, for the
+    embedding allocation (the pages scan a natural-text corpus; none is
+    here): a phrase book of `phrases` (default 8 * vocab) phrases of 1 to
+    `max_len` tokens, their tokens drawn from Zipf(zipf_s) over the
+    vocabulary, and the corpus a concatenation of phrases drawn from
+    Zipf(zipf_s) over the book, cut to n_tokens (int32)."""
+    P = phrases or 8 * vocab
+    g = _rng(CORPUS_CFG, seed, 0)
+    lens = g.integers(1, max_len + 1, P)
+    starts = np.zeros(P + 1, np.int64)
+    np.cumsum(lens, out=starts[1:])
+    book = draw_ids(g, zipf_freq(vocab, zipf_s), int(starts[-1]))
+    mean_len = float(lens.mean())
+    picks = draw_ids(_rng(CORPUS_CFG, seed, 1), zipf_freq(P, zipf_s),
+                     int(n_tokens / mean_len * 1.2) + 16)
+    out = np.empty(0, np.int32)
+    while out.shape[0] < n_tokens:
+        seg = np.concatenate([book[starts[p]:starts[p + 1]] for p in picks])
+        out = np.concatenate([out, seg])
+    return np.ascontiguousarray(out[:n_tokens], dtype=np.int32)
+
+
+def with_offsets(w: Workload, offsets: np.ndarray, ids: np.ndarray,
+                 threads: Optional[int] = None) -> Workload:
+    """Same shapes and weights, another allocation: tables of offsets[-1]
+    rows drawn from this configuration's streams, the id stream `ids`, and x
+    (and dy) drawn for that many tokens. The counts behind `offsets` are
+    the caller's (e.g. an allocation scanned from a corpus)."""
+    spec, cfg, dt = w.spec, w.cfg, w.spec.dtype
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    R = int(offsets[-1])
+    K = draw_table(cfg, S_K, R, spec.d, spec.sigma_k, dt, threads)
+    V = draw_table(cfg, S_V, R, spec.d_e, spec.sigma_v, dt, threads)
+    w2 = dataclasses.replace(w, offsets=offsets, K=K, V=V)
+    return with_ids(w2, ids)
+
+
 def decoded(w: Workload) -> dict:
     """float64 copies of every (small) array, for the oracle."""
     out = dict(ids=w.ids.astype(np.int64), offsets=w.offsets.copy(),
