@@ -629,6 +629,24 @@ def main():
             tf = fl[k] / (stage_avg[k] * 1e-3) / 1e12
             mfma[k] = {"tflops": round(tf, 1),
                        "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFS, 4)}
+    # The W_up + W_mix stage as a whole, against its algorithmic flops
+    # (2 B d d_e for W_up, 4 B d^2 for W_mix: the formula's projections),
+    # whatever the kernels execute: with W_up folded into W_mix the stage is
+    # the weight products, a G with the variance epilogue, the rstd pass and
+    # W_mix over [a ; x]; otherwise W_up, LayerNorm and W_mix.
+    stage_keys = ([k for k in ("weight_fold", "up_quad", "layernorm",
+                               "mix_up_proj") if k in stage_avg]
+                  if "mix_up_proj" in stage_avg else
+                  [k for k in ("up_proj", "layernorm", "mix_proj")
+                   if k in stage_avg])
+    if stage_keys and not args.train:
+        st_ms = sum(stage_avg[k] for k in stage_keys)
+        alg = fl["up_proj"] + fl["mix_proj"]
+        tf = alg / (st_ms * 1e-3) / 1e12
+        mfma["up_mix_stage"] = {
+            "algorithmic_gflop": round(alg / 1e9, 1), "ms": round(st_ms, 4),
+            "stages": stage_keys, "tflops": round(tf, 1),
+            "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFS, 4)}
     traffic = measured_traffic(w.spec.name)
     out = {
         "metric": (METRIC_TRAIN if args.train else

@@ -1371,6 +1371,8 @@ l3_status l3_backward(l3_plan_t plan, const void* dy, const void* x,
     ba.zero_count = bb.zero_count;
     ba.chunk_stats = bb.chunk_stats;
     ba.cs_stride = (d.k_max + 31) / 32;
+    ba.gitem_map = plan->group_min_rows > 0 ? pd.gitem_map : nullptr;
+    ba.group_min_rows = plan->group_min_rows;
     {
       StageTimer t(plan, ST_BWD_LN, s);
       e = ln_bwd_launch(ba, d.dtype, s);

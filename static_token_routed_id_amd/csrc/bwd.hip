@@ -432,41 +432,55 @@ constexpr int kDxS = 64 + 8;  // dX_att staging row stride (elements)
 // dX_att = dS K_t (bf16 K, d a multiple of 128) on 16x16x32 bf16 MFMA, the
 // same product shape as the forward's P V_t: tokens are the rows of A (dS,
 // float32, entering as bf16 hi + lo halves, two MFMAs), K_t's rows the
-// reduction. Columns in passes of 128 (8 accumulators of 16 x 16); K_t in
-// blocks of 32 rows x 128 columns, double buffered in registers a block at
-// a time: each iteration first requests the next block (and its dS), then
-// moves the current one through a wave-private LDS buffer, 64 columns at a
-// time (8 lanes a 128-byte row slice), and reads it back as the B operand
-// with the transposing LDS read. (A ring of single 64-column steps carried
-// across iterations lost its depth to the waits the compiler places after
-// a loop's back edge.) Rows past n have zero weights (their K rows are
-// clamped to row n-1).
+// reduction. MB blocks of 16 tokens share every K block (MB = 4: a 64-token
+// tile of a busy id reads K_t once where four 16-token tiles read it four
+// times). Columns in passes of CW (CW / 16 accumulators of 16 x 16 per token
+// block); K_t in blocks of 32 rows x CW columns, double buffered in
+// registers a block at a time: each iteration first requests the next block
+// (and its dS), then moves the current one through a wave-private LDS
+// buffer, 64 columns at a time (8 lanes a 128-byte row slice), and reads it
+// back as the B operand with the transposing LDS read. (A ring of single
+// 64-column steps carried across iterations lost its depth to the waits the
+// compiler places after a loop's back edge.) Rows past n have zero weights
+// (their K rows are clamped to row n-1). Each output element sums the row
+// blocks in order whatever MB and CW are.
+template <int MB, int CW>
 __device__ __forceinline__ void dx_att_mfma(const BwdArgs& a, int64_t r0,
                                             int n, int tok0, int mcount,
                                             int lane, uint16_t* stg,
                                             int c_begin, int c_end) {
+  constexpr int SB = CW / 64;  // 64-column halves of a block
+  constexpr int NB = CW / 16;  // 16-column output blocks of a pass
   const int r = lane & 15, g = lane >> 4;
   const uint16_t* K = static_cast<const uint16_t*>(a.K);
   const int trow = 8 * g + (r >> 2), tcol = 4 * (r & 3);
   const int srow = lane >> 3, scol = (lane & 7) * 8;
   const int nrb = ceil_div(n, 32);
-  const bool tok_ok = r < mcount;
-  const float* dsr =
-      a.DSbuf + static_cast<int64_t>(tok0 + min(r, mcount - 1)) * a.kst;
-  auto ds_load = [&](int rb, float4& v0, float4& v1) {
+  bool tok_ok[MB];
+  const float* dsr[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int t = mb * 16 + r;
+    tok_ok[mb] = t < mcount;
+    dsr[mb] = a.DSbuf + static_cast<int64_t>(tok0 + min(t, mcount - 1)) * a.kst;
+  }
+  auto ds_load = [&](int rb, float4 (&v0)[MB], float4 (&v1)[MB]) {
     const int j = min(rb, nrb - 1) * 32 + 8 * g;
-    v0 = *reinterpret_cast<const float4*>(dsr + j);
-    v1 = *reinterpret_cast<const float4*>(dsr + j + 4);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      v0[mb] = *reinterpret_cast<const float4*>(dsr[mb] + j);
+      v1[mb] = *reinterpret_cast<const float4*>(dsr[mb] + j + 4);
+    }
   };
-  auto split = [&](int rb, const float4& v0, const float4& v1, u32x4& hi,
-                   u32x4& lo) {
+  auto split = [&](int rb, const float4& v0, const float4& v1, bool ok,
+                   u32x4& hi, u32x4& lo) {
     const int j0 = rb * 32 + 8 * g;
     const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     uint32_t h[4], l[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float x0 = tok_ok && j0 + 2 * e < n ? v[2 * e] : 0.f;
-      const float x1 = tok_ok && j0 + 2 * e + 1 < n ? v[2 * e + 1] : 0.f;
+      const float x0 = ok && j0 + 2 * e < n ? v[2 * e] : 0.f;
+      const float x1 = ok && j0 + 2 * e + 1 < n ? v[2 * e + 1] : 0.f;
       h[e] = f2bf2(x0, x1);
       l[e] = f2bf2(x0 - __uint_as_float(h[e] << 16),
                    x1 - __uint_as_float(h[e] & 0xffff0000u));
@@ -474,13 +488,13 @@ __device__ __forceinline__ void dx_att_mfma(const BwdArgs& a, int64_t r0,
     hi = u32x4{h[0], h[1], h[2], h[3]};
     lo = u32x4{l[0], l[1], l[2], l[3]};
   };
-  for (int cc = c_begin; cc < c_end; cc += 128) {
-    // block rb: rows rb*32 .., columns cc .. cc+127: chunk (sb, k) of
+  for (int cc = c_begin; cc < c_end; cc += CW) {
+    // block rb: rows rb*32 .., columns cc .. cc+CW-1: chunk (sb, k) of
     // 64-column half sb, rows k*8 + srow, 8 columns at scol
-    auto load_blk = [&](u32x4 (&b)[8], int rb) {
+    auto load_blk = [&](u32x4 (&b)[SB * 4], int rb) {
       const int j0 = min(rb, nrb - 1) * 32;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int j = min(j0 + k * 8 + srow, n - 1);
@@ -488,16 +502,20 @@ __device__ __forceinline__ void dx_att_mfma(const BwdArgs& a, int64_t r0,
               K + (r0 + j) * a.d + cc + sb * 64 + scol);
         }
     };
-    floatx4 acc[8];
+    floatx4 acc[MB][NB];
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
     // block rb's dS as the A operand, its K rows through LDS as B
-    auto consume = [&](const u32x4 (&b)[8], int rb, const float4& v0,
-                       const float4& v1) {
-      u32x4 ahi, alo;
-      split(rb, v0, v1, ahi, alo);
+    auto consume = [&](const u32x4 (&b)[SB * 4], int rb,
+                       const float4 (&v0)[MB], const float4 (&v1)[MB]) {
+      u32x4 ahi[MB], alo[MB];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
+      for (int mb = 0; mb < MB; ++mb)
+        split(rb, v0[mb], v1[mb], tok_ok[mb], ahi[mb], alo[mb]);
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int k = 0; k < 4; ++k)
@@ -514,20 +532,23 @@ __device__ __forceinline__ void dx_att_mfma(const BwdArgs& a, int64_t r0,
           const uint2 l2 = __builtin_bit_cast(uint2, lo4);
           const uint2 h2 = __builtin_bit_cast(uint2, hi4);
           const u32x4 bf = u32x4{l2.x, l2.y, h2.x, h2.y};
-          floatx4& ac = acc[sb * 4 + nb];
-          ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, ahi),
-              __builtin_bit_cast(bf16x8_t, bf), ac, 0, 0, 0);
-          ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, alo),
-              __builtin_bit_cast(bf16x8_t, bf), ac, 0, 0, 0);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            floatx4& ac = acc[mb][sb * 4 + nb];
+            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, ahi[mb]),
+                __builtin_bit_cast(bf16x8_t, bf), ac, 0, 0, 0);
+            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, alo[mb]),
+                __builtin_bit_cast(bf16x8_t, bf), ac, 0, 0, 0);
+          }
         }
       }
     };
     // two named buffers, two blocks an iteration: the block being used was
     // requested one block earlier, and nothing is copied between buffers
-    u32x4 bA[8], bB[8];
-    float4 dA0, dA1, dB0, dB1;
+    u32x4 bA[SB * 4], bB[SB * 4];
+    float4 dA0[MB], dA1[MB], dB0[MB], dB1[MB];
     ds_load(0, dA0, dA1);
     load_blk(bA, 0);
     for (int rb = 0; rb < nrb; rb += 2) {
@@ -541,15 +562,17 @@ __device__ __forceinline__ void dx_att_mfma(const BwdArgs& a, int64_t r0,
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * g + i;
-      if (t < mcount) {
-        float* dst =
-            a.dx + static_cast<int64_t>(a.perm[tok0 + t]) * a.d + cc + r;
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) dst[nb * 16] += acc[nb][i];
+      for (int i = 0; i < 4; ++i) {
+        const int t = mb * 16 + 4 * g + i;
+        if (t < mcount) {
+          float* dst =
+              a.dx + static_cast<int64_t>(a.perm[tok0 + t]) * a.d + cc + r;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) dst[nb * 16] += acc[mb][nb][i];
+        }
       }
-    }
   }
 }
 
@@ -773,21 +796,60 @@ __global__ __launch_bounds__(256, 2) void seg_bwd_chunk_kernel(BwdArgs a) {
 }
 
 // dX_att of the tiles, after seg_bwd_tile_kernel has written their dS: one
-// wave per (tile, 128-column pass), the forward's work items in order with
-// the passes innermost (a busy id's tiles and passes spread over waves).
+// wave per (tile, column pass). Ids with at least group_min_rows rows (when
+// the plan made group items for them: one item of their <= 64 tokens, or
+// items of 128 tokens) come first, one wave per (64 tokens of an item, 64
+// columns): the 16-token blocks share every K block, so K_t is read once
+// per 64 tokens. The other ids follow as the forward's work
+// items (16-token tiles) with 128-column passes, the passes innermost (a
+// busy id's tiles and passes spread over waves).
 __global__ __launch_bounds__(256, 2) void seg_bwd_dx_kernel(BwdArgs a) {
   __shared__ __align__(16) uint16_t s_stg[4][32 * kDxS];
   if (a.header[0] != 0) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n_items = a.header[a.count_slot];
+  const bool grouped = a.group_min_rows > 0 && a.gitem_map != nullptr;
+  const int n_group = grouped ? a.header[3] : 0;
+  const int gpass = a.d / 64;
+  // two 64-token halves per group item (the second is empty for items of
+  // at most 64 tokens)
+  const int64_t total_g = static_cast<int64_t>(n_group) * 2 * gpass;
   const int npass = a.d / 128;
-  const int64_t total = static_cast<int64_t>(n_items) * npass;
+  const int64_t total = total_g + static_cast<int64_t>(n_items) * npass;
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 4 + w; idx < total;
        idx += static_cast<int64_t>(gridDim.x) * 4) {
-    const int2 im = a.item_map[idx / npass];
-    const int pass = static_cast<int>(idx % npass);
+    if (idx < total_g) {
+      const int2 im = a.gitem_map[idx / (2 * gpass)];
+      const int rem = static_cast<int>(idx % (2 * gpass));
+      const int half = rem / gpass, pass = rem % gpass;
+      const int s = im.x;
+      const int t_begin = a.seg_tok_start[s];
+      const int m = a.seg_tok_start[s + 1] - t_begin;
+      const int item_tok = m > kGroupTok ? kHotTok : kGroupTok;
+      const int first = im.y * item_tok + half * kGroupTok;
+      if (half * kGroupTok >= item_tok || first >= m) continue;
+      const int tok0 = t_begin + first;
+      const int mcount = min(kGroupTok, m - first);
+      const int n = a.seg_n[s];
+      const int64_t r0 = a.seg_row_off[s];
+      if (mcount <= 16)
+        dx_att_mfma<1, 64>(a, r0, n, tok0, mcount, lane, s_stg[w],
+                           pass * 64, pass * 64 + 64);
+      else if (mcount <= 32)
+        dx_att_mfma<2, 64>(a, r0, n, tok0, mcount, lane, s_stg[w],
+                           pass * 64, pass * 64 + 64);
+      else
+        dx_att_mfma<4, 64>(a, r0, n, tok0, mcount, lane, s_stg[w],
+                           pass * 64, pass * 64 + 64);
+      continue;
+    }
+    const int64_t ix = idx - total_g;
+    const int2 im = a.item_map[ix / npass];
+    const int pass = static_cast<int>(ix % npass);
     const int s = im.x;
     const int n = a.seg_n[s];
+    // ids taken above in 64-token tiles
+    if (grouped && n >= a.group_min_rows) continue;
     const int nch = ceil_div(n, a.chunk_rows);
     // the forward's items are (token tile, row chunk): take each tile once
     if (im.y % nch != 0) continue;
@@ -796,8 +858,8 @@ __global__ __launch_bounds__(256, 2) void seg_bwd_dx_kernel(BwdArgs a) {
     const int m = a.seg_tok_start[s + 1] - t_begin;
     const int tok0 = t_begin + tile * kTokTile;
     const int mcount = min(kTokTile, m - tile * kTokTile);
-    dx_att_mfma(a, a.seg_row_off[s], n, tok0, mcount, lane, s_stg[w],
-                pass * 128, pass * 128 + 128);
+    dx_att_mfma<1, 128>(a, a.seg_row_off[s], n, tok0, mcount, lane, s_stg[w],
+                        pass * 128, pass * 128 + 128);
   }
 }
 
@@ -1197,7 +1259,10 @@ hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int items_ub, int S_ub,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dtype == kBF16 && a.d % 128 == 0) {
-    const int64_t dx_blocks = (static_cast<int64_t>(items_ub) * (a.d / 128) + 3) / 4;
+    const int64_t g_ub =
+        a.group_min_rows > 0 ? group_items_cap(a.B) * 2 * (a.d / 64) : 0;
+    const int64_t dx_blocks =
+        (static_cast<int64_t>(items_ub) * (a.d / 128) + g_ub + 3) / 4;
     seg_bwd_dx_kernel<<<static_cast<int>(dx_blocks < 8192 ? dx_blocks : 8192),
                         256, 0, s>>>(a);
     e = hipGetLastError();

@@ -335,6 +335,10 @@ struct BwdArgs {
   // tile pass; NULL: one wave walks each tile's chunks
   float4* chunk_stats; // [B x cs_stride]
   int cs_stride;       // row chunks of the longest id
+  // the plan's 64-token items (ids with at least group_min_rows rows; 0:
+  // none) for the dX_att pass
+  const int2* gitem_map = nullptr;
+  int group_min_rows = 0;
 };
 // Zeroes dK, dV rows of the ids absent from the batch (d, d_e multiples of
 // 4); items_ub bounds the number of 64-row pieces.
