@@ -287,6 +287,14 @@ def make(name_or_index, batch: Optional[int] = None, ln_perturb: bool = False,
     else:
         spec = SPECS[name_or_index]
         cfg = CONFIG_ORDER.index(spec.name)
+    return make_from_spec(spec, cfg, batch, ln_perturb, threads)
+
+
+def make_from_spec(spec: Spec, cfg: int, batch: Optional[int] = None,
+                   ln_perturb: bool = False,
+                   threads: Optional[int] = None) -> Workload:
+    """Draw a workload of any Spec (e.g. the edge-case shapes of the tests)
+    from the streams of configuration number cfg."""
     B = spec.batch if batch is None else batch
     counts = allocation(spec)
     offsets = offsets_from_counts(counts)
