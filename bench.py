@@ -26,7 +26,7 @@ FETCH_SIZE / WRITE_SIZE counter summary
 (profiles/traffic_gather_<workload>.md), or null when the kernels changed
 since it was taken; `copy_peak_gbs` is a measured 2 GiB device copy (bytes
 read + written per second) and `frac_of_copy_peak` the gather's rate
-against it. `cpu_baseline` is the fp64 oracle on a bounded sample of the
+against it (above 1: the gather mostly reads). `cpu_baseline` is the fp64 oracle on a bounded sample of the
 same batch on the host CPU (one oracle call per host thread, CPU model
 recorded). Workloads whose step moves less than 1 GiB (everything but the
 large prefill) are timed step by step with HIP events, L2 and the MALL
