@@ -26,7 +26,11 @@ FETCH_SIZE / WRITE_SIZE counter summary
 (profiles/traffic_gather_<workload>.md), or null when the kernels changed
 since it was taken; `copy_peak_gbs` is a measured 2 GiB device copy (bytes
 read + written per second) and `frac_of_copy_peak` the gather's rate
-against it (above 1: the gather mostly reads). `cpu_baseline` is the fp64 oracle on a bounded sample of the
+against it (above 1: the gather mostly reads); `read_peak_gbs` are reads
+of a 4 GiB buffer by the read probe (libl3probe.so) in the gather's own
+access pattern, contiguous, and contiguous non-temporal, with
+`frac_of_read_peak` the gather's algorithmic rate against the first and
+`traffic_rate_gbs` its counter-measured HBM bytes per second. `cpu_baseline` is the fp64 oracle on a bounded sample of the
 same batch on the host CPU (one oracle call per host thread, CPU model
 recorded). Workloads whose step moves less than 1 GiB (everything but the
 large prefill) are timed step by step with HIP events, L2 and the MALL
@@ -246,6 +250,51 @@ def copy_peak_gbs(nbytes: int = 1 << 31, reps: int = 5) -> float:
     ms = a.elapsed_time(b) / reps
     del src, dst
     return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def read_peak_gbs(nbytes: int = 1 << 32, reps: int = 5) -> dict:
+    """Measured read rates (GB/s, best over three grid sizes) of a 4 GiB
+    device buffer streamed by the read probe (csrc/read_probe.hip,
+    libl3probe.so): the gather's own access pattern (16 rows of 4 KiB a
+    64 KiB block, 64 bytes of each row per wave instruction), 1 KiB
+    contiguous per instruction, and the same with non-temporal loads."""
+    import ctypes
+
+    import torch
+    from static_token_routed_id_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        raise RuntimeError(f"{B.PROBE_LIB} is not built: run "
+                           "python -m static_token_routed_id_amd.build")
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.l3probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(7)
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    out = {}
+    for name, pattern in (("gather_pattern", 1), ("stream", 0),
+                          ("stream_nontemporal", 2)):
+        best = 0.0
+        for grid in (512, 1024, 2048):
+            def launch():
+                rc = lib.l3probe_read(buf.data_ptr(), nbytes, pattern, grid,
+                                      sink.data_ptr(), st.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"l3probe_read returned {rc}")
+            launch()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(
+                enable_timing=True)
+            a.record(st)
+            for _ in range(reps):
+                launch()
+            b.record(st)
+            torch.cuda.synchronize()
+            best = max(best, nbytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9)
+        out[name] = round(best, 1)
+    del buf
+    return out
 
 
 def run_offload(args) -> None:
@@ -499,7 +548,7 @@ def main():
                     help="flush L2 and MALL between timed steps (auto: when "
                          "a step's algorithmic bytes are under 1 GiB)")
     ap.add_argument("--no-copy-peak", dest="copy_peak", action="store_false",
-                    help="skip the measured device-copy rate")
+                    help="skip the measured device-copy and read rates")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -696,6 +745,16 @@ def main():
         cp = copy_peak_gbs()
         out["roofline"]["copy_peak_gbs"] = round(cp, 1)
         out["roofline"]["frac_of_copy_peak"] = round(achieved / cp, 4)
+        rp = read_peak_gbs()
+        out["roofline"]["read_peak_gbs"] = rp
+        out["roofline"]["frac_of_read_peak"] = round(
+            achieved / rp["gather_pattern"], 4)
+        if traffic:
+            # counter-measured HBM bytes a launch over its time
+            hbm = traffic["bytes_per_launch"] / (gather_ms * 1e-3) / 1e9
+            out["roofline"]["traffic_rate_gbs"] = round(hbm, 1)
+            out["roofline"]["traffic_frac_of_read_peak"] = round(
+                hbm / rp["gather_pattern"], 4)
     if args.cpu_seconds > 0:
         if args.train:
             cb = cpu_baseline_train(w, dy_np, args.cpu_seconds)

@@ -5,6 +5,8 @@ Usage: python -m static_token_routed_id_amd.build [--jobs N]
 Every HIP source under csrc/ and the C-ABI layer are compiled to objects
 under _build/ and linked into static_token_routed_id_amd/libl3.so. The build
 runs on any machine with ROCm (hipcc cross-compiles gfx950 code without a GPU).
+csrc/read_probe.hip, a read-bandwidth probe that bench.py times beside the
+gather, goes into libl3probe.so of its own.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libl3.so")
+# read-bandwidth probe, a library of its own (measurement only)
+PROBE_LIB = os.path.join(PKG, "libl3probe.so")
 ARCH = os.environ.get("L3_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -63,6 +67,10 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp]
          + objs)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC] + FLAGS + ["-shared", "-x", "hip",
+                            os.path.join(CSRC, "read_probe.hip"), "-o", tmp])
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -124,7 +124,7 @@ PlanDev carve_plan(Carver& c, int64_t B) {
   const size_t nb = static_cast<size_t>(B);
   const size_t nblk = (nb + kSortTile - 1) / kSortTile;
   PlanDev p;
-  p.header = c.take<int32_t>(16);
+  p.header = c.take<int32_t>(kHeaderInts);
   p.perm = c.take<int32_t>(nb);
   p.sorted_ids = c.take<int32_t>(nb);
   p.seg_id = c.take<int32_t>(nb);
@@ -139,7 +139,7 @@ PlanDev carve_plan(Carver& c, int64_t B) {
   p.blk = c.take<int32_t>(nblk + 1);
   p.item_map = c.take<int2>(static_cast<size_t>(wave_items_cap(B)));
   p.gitem_map = c.take<int2>(static_cast<size_t>(group_items_cap(B)));
-  p.hitem_map = c.take<int2>(static_cast<size_t>(group_items_cap(B)));
+  p.hitem_map = c.take<int2>(static_cast<size_t>(kXcds * hitem_cap(B)));
   p.seg_aitem_start = c.take<int32_t>(nb + 1);
   p.aitem_map = c.take<int2>(static_cast<size_t>(wave_items_cap(B)));
   p.stage_off = c.take<int64_t>(nb);
@@ -807,6 +807,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       ga.seg_gitem_start = pd.seg_gitem_start;
       ga.gitem_map = pd.gitem_map;
       ga.hitem_map = pd.hitem_map;
+      ga.hcap = static_cast<int>(hitem_cap(B));
       ga.work = pd.header + 4;
       ga.x = static_cast<const uint16_t*>(x);
       ga.K = static_cast<const uint16_t*>(K);

@@ -38,8 +38,10 @@ struct PlanDev {
   int32_t* header;          // [0] status bits, [1] S, [2] wave items,
                             // [3] group items, [4], [5], [7], [9] group-kernel
                             // work queues (zero between launches),
-                            // [6] 128-token group items, [8] wave items
-                            // of every segment
+                            // [8] wave items of every segment,
+                            // [16 + x] 128-token items of XCD x's list,
+                            // [24 + x] XCD x's queue of them (zero between
+                            // launches); kHeaderInts in all
   int32_t* perm;            // [B] token index at sorted position
   int32_t* sorted_ids;      // [B]
   int32_t* seg_id;          // [B]
@@ -54,8 +56,10 @@ struct PlanDev {
   int32_t* blk;             // [ceil(B / kSortTile) + 1]
   int2* item_map;           // wave item -> (segment, index within segment)
   int2* gitem_map;          // group item -> (segment, tile within segment)
-  int2* hitem_map;          // the 128-token group items only, any order;
-                            // their count in header[6]
+  int2* hitem_map;          // the 128-token group items only, in kXcds
+                            // lists of hitem_cap(B) entries (list x at
+                            // x * hitem_cap(B), any order within a list):
+                            // every item of one id in the same list
   // Wave items of every segment (the training forward runs all ids through
   // the wave kernel); count in header[8]. Only filled when the group kernel
   // is enabled (else the wave items are already all of them).
@@ -70,6 +74,24 @@ __host__ __device__ inline int64_t wave_items_cap(int64_t B) {
 }
 __host__ __device__ inline int64_t group_items_cap(int64_t B) {
   return B / kGroupTok + B + 1;
+}
+// Ints of a plan's header (see PlanDev::header).
+constexpr int kHeaderInts = 32;
+// XCDs of the device: the group kernel's workgroup b runs on XCD b % kXcds
+// (workgroups are dispatched to the XCDs in turn), and takes the 128-token
+// items of list b % kXcds, so all the items of one busy id run on one XCD
+// and share its L2 when they read K_t.
+constexpr int kXcds = 8;
+// Entries of one list: an id with m > kGroupTok tokens has ceil(m / kHotTok)
+// <= m / kGroupTok items, so all of them, even in one list, fit.
+__host__ __device__ inline int64_t hitem_cap(int64_t B) {
+  return B / kGroupTok + 1;
+}
+// List of segment g's 128-token items: the XCDs in turn, reversed every
+// other round (segments come in id order, and frequent ids have most items)
+__host__ __device__ inline int hot_list_of(int g) {
+  const int q = g / kXcds, r = g % kXcds;
+  return (q & 1) ? kXcds - 1 - r : r;
 }
 
 struct PlanParams {
@@ -234,10 +256,11 @@ struct SegGroupArgs {
   const int32_t* seg_n;
   const int32_t* seg_gitem_start;
   const int2* gitem_map;
-  const int2* hitem_map;
-  int* work;        // header[4..9]: queue of the 64-token pass, finished
-                    // workgroups, count of 128-token items, their queue,
-                    // (wave-item count), queue of the wave-item pass
+  const int2* hitem_map;   // kXcds lists of hcap entries
+  int hcap;
+  int* work;        // header + 4: [0] queue of the 64-token pass, [1]
+                    // finished workgroups, [5] queue of the wave-item pass,
+                    // [20 + x] queue of XCD x's 128-token items
   const uint16_t* x;
   const uint16_t* K;
   const uint16_t* V;

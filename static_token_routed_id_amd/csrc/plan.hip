@@ -80,7 +80,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
   const int B = p.B;
   int B2 = 1;
   while (B2 < B) B2 <<= 1;
-  if (tid < 16) pd.header[tid] = 0;
+  if (tid < kHeaderInts) pd.header[tid] = 0;
   __syncthreads();
 
   for (int i = tid; i < B2; i += 1024) {
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
 
 // ---------------------------------------------------------------- large ---
 __global__ void header_init_kernel(int32_t* header) {
-  if (threadIdx.x < 16) header[threadIdx.x] = 0;
+  if (threadIdx.x < kHeaderInts) header[threadIdx.x] = 0;
 }
 
 // Digit histogram of one 1024-key tile (DB-bit digits, 2^DB buckets);
@@ -422,7 +422,8 @@ __device__ __forceinline__ int seg_of(const int32_t* start, int S, int i) {
 }
 
 __global__ __launch_bounds__(256) void item_map_kernel(PlanDev pd,
-                                                       int with_all) {
+                                                       int with_all,
+                                                       int64_t hcap) {
   if (pd.header[0] != 0) return;
   const int S = pd.header[1];
   const int n_wave = pd.header[2], n_group = pd.header[3];
@@ -437,10 +438,14 @@ __global__ __launch_bounds__(256) void item_map_kernel(PlanDev pd,
       const int g = seg_of(pd.seg_gitem_start, S, i);
       const int j = i - pd.seg_gitem_start[g];
       pd.gitem_map[i] = make_int2(g, j);
-      // the 128-token items also go to a compact list of their own (its
-      // order depends on timing; the items' results do not)
-      if (pd.seg_tok_start[g + 1] - pd.seg_tok_start[g] > kGroupTok)
-        pd.hitem_map[atomicAdd(&pd.header[6], 1)] = make_int2(g, j);
+      // the 128-token items also go to compact lists of their own, all of
+      // one id's items in the same list (the order within a list depends
+      // on timing; the items' results do not)
+      if (pd.seg_tok_start[g + 1] - pd.seg_tok_start[g] > kGroupTok) {
+        const int x = hot_list_of(g);
+        pd.hitem_map[x * hcap + atomicAdd(&pd.header[16 + x], 1)] =
+            make_int2(g, j);
+      }
     }
     if (i < n_all) {
       const int g = seg_of(pd.seg_aitem_start, S, i);
@@ -466,7 +471,8 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
   const int B = p.B;
   if (B <= kSmallPlanMax) {
     plan_small_kernel<<<1, 1024, 0, s>>>(pd, p);
-    item_map_kernel<<<item_map_grid(B), 256, 0, s>>>(pd, p.group_min_rows > 0);
+    item_map_kernel<<<item_map_grid(B), 256, 0, s>>>(pd, p.group_min_rows > 0,
+                                                  hitem_cap(B));
     return hipGetLastError();
   }
   const int nblk = ceil_div(B, kSortTile);
@@ -507,7 +513,8 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
   seg_items_kernel<<<ceil_div(B, 256), 256, 0, s>>>(pd, p);
   seg_items_scan_kernel<<<p.group_min_rows > 0 ? 3 : 2, 1024, 0, s>>>(
       pd, p.group_min_rows > 0);
-  item_map_kernel<<<item_map_grid(B), 256, 0, s>>>(pd, p.group_min_rows > 0);
+  item_map_kernel<<<item_map_grid(B), 256, 0, s>>>(pd, p.group_min_rows > 0,
+                                                  hitem_cap(B));
   return hipGetLastError();
 }
 

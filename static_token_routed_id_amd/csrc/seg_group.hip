@@ -647,7 +647,7 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
   const int n_items = a.header[3];
   uint16_t* my_v = s_v + (threadIdx.x >> 6) * (kVR * kVS);
   // Passes over device-wide work queues: the 128-token items of ids with
-  // more than kGroupTok tokens (compact list), the 64-token items, the wave
+  // more than kGroupTok tokens (one list per XCD), the 64-token items, the wave
   // items (separate loops keep the paths' registers apart). A workgroup
   // requests its next 128-token item when it starts one, its next 64-token
   // or wave item once the current item's scores are done, and reads the
@@ -655,7 +655,11 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
   // the last workgroup out resets the queues for the next launch.
   __shared__ int s_next;
   int* work = a.work;
-  const int n_hot = work[2];
+  // this XCD's list of 128-token items and its queue
+  const int xl = blockIdx.x % kXcds;
+  const int n_hot = a.header[16 + xl];
+  int* hot_queue = &work[20 + xl];
+  const int2* hot_list = a.hitem_map + static_cast<int64_t>(xl) * a.hcap;
   // Half of the workgroups (alternate groups of eight: every XCD gets its
   // share) start with the wave items, the rest with the busy ids' and the
   // 64-token items; every workgroup then visits the other queues. The wave
@@ -666,13 +670,13 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
     wave_pass<NBV>(a, smem, work);
     __syncthreads();
   }
-  if (threadIdx.x == 0) s_next = atomicAdd(&work[3], 1);
+  if (threadIdx.x == 0) s_next = atomicAdd(hot_queue, 1);
   __syncthreads();
   for (int hi = s_next; hi < n_hot;) {
     __syncthreads();  // every wave has read s_next
     int next = 0;
-    if (threadIdx.x == 0) next = atomicAdd(&work[3], 1);
-    const int2 im = a.hitem_map[hi];
+    if (threadIdx.x == 0) next = atomicAdd(hot_queue, 1);
+    const int2 im = hot_list[hi];
     const int s = im.x, tile = im.y;
     const int t_begin = a.seg_tok_start[s];
     const int m = a.seg_tok_start[s + 1] - t_begin;
@@ -752,8 +756,8 @@ __global__ __launch_bounds__(512, 1) void seg_group_kernel(SegGroupArgs a) {
     if (left == static_cast<int>(gridDim.x) - 1) {
       atomicExch(&work[0], 0);
       atomicExch(&work[1], 0);
-      atomicExch(&work[3], 0);
       atomicExch(&work[5], 0);
+      for (int x = 0; x < kXcds; ++x) atomicExch(&work[20 + x], 0);
     }
   }
 }

@@ -206,7 +206,7 @@ template <int DC, typename PT>
 __device__ __forceinline__ void scores_softmax_1tok(
     const uint16_t* __restrict__ xr, const uint16_t* __restrict__ kt, int d,
     int nc, int lane, PT* P, float* ml) {
-  constexpr int RB = 2, NR = DC >= 4 ? 3 : 4;
+  constexpr int RB = 2, NR = 4;
   float xf[DC][8];
 #pragma unroll
   for (int q = 0; q < DC; ++q) {
