@@ -681,22 +681,31 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
     static_assert(128 * kQL * 2 + 64 * kSP * 4 <= sizeof(lds),
                   "quadratic-form staging exceeds the operand LDS");
     const int wo = (wn * 32 + r) * kSP + wm * 128 + h4;
+    // quadratic form: Q's tile rows, 128 at a time, as 8 rows a pass of
+    // 16-byte chunks; a thread's sixteen loads are all in flight before its
+    // first LDS write, and the second half's are issued before the first
+    // half's products
+    const int qc = (tid & 31) * 8;
+    u32x4 qv[QUAD ? 16 : 1];
+    auto load_q = [&](int half) {
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const int gm = min(m0 + half * 128 + p * 8 + (tid >> 5), g.M - 1);
+        qv[p] = *reinterpret_cast<const u32x4*>(
+            g.ln_quad_a + static_cast<int64_t>(gm) * g.ln_quad_lda + n0 + qc);
+      }
+    };
+    if constexpr (QUAD) load_q(0);
     __syncthreads();  // every wave is done with the operand buffers
 #pragma unroll
     for (int half = 0; half < (QUAD ? 2 : 1); ++half) {
     if constexpr (QUAD) {
-      // 128 rows x 256 columns: 8 rows a pass of 16-byte chunks
-      if (half > 0) __syncthreads();
-      const int qc = (tid & 31) * 8;
-#pragma unroll 4
-      for (int p = 0; p < 16; ++p) {
-        const int lr = p * 8 + (tid >> 5);
-        const int gm = min(m0 + half * 128 + lr, g.M - 1);
-        *reinterpret_cast<u32x4*>(&qs[lr * kQL + qc]) =
-            *reinterpret_cast<const u32x4*>(
-                g.ln_quad_a + static_cast<int64_t>(gm) * g.ln_quad_lda + n0 +
-                qc);
-      }
+      if (half > 0) __syncthreads();  // the first half's products are done
+#pragma unroll
+      for (int p = 0; p < 16; ++p)
+        *reinterpret_cast<u32x4*>(&qs[(p * 8 + (tid >> 5)) * kQL + qc]) =
+            qv[p];
+      if (half == 0) load_q(1);
       __syncthreads();
       if (wm != half) continue;
     }
@@ -707,27 +716,49 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
         float4 v, w;
         float* vp = reinterpret_cast<float*>(&v);
         float* wp = reinterpret_cast<float*>(&w);
+        if constexpr (QUAD) {
+          // the tile rows times Q's entries at the same positions (rows
+          // past M took row M - 1; never written): the sixteen entries
+          // this lane needs (four rows, four columns) are read first, then
+          // the accumulators by explicit AGPR reads, as in the fold above
+          // (left to the allocator, part of acc moved to VGPRs and this
+          // epilogue ran with a handful of free registers, each LDS read
+          // waited for before the next: the kernel took 104 us, now 79)
+          float q[4][4];
 #pragma unroll
-        for (int ee = 0; ee < 4; ++ee) {
-          float a = 0.f, b = 0.f;
-          if constexpr (QUAD) {
-            // the tile row times Q's entries at the same positions (rows
-            // past M took row M - 1; never written)
+          for (int ee = 0; ee < 4; ++ee) {
             const uint16_t* qrow =
                 qs + (i * 32 + 8 * eg + h4 + ee) * kQL + wn * 128 + r;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              b = fmaf(acc[i][j][4 * eg + ee], bf2f(qrow[j * 32]), b);
-          } else {
+            for (int j = 0; j < 4; ++j) q[ee][j] = bf2f(qrow[j * 32]);
+          }
+#pragma unroll
+          for (int ee = 0; ee < 4; ++ee) {
+            float b = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float x;
+              asm volatile("v_accvgpr_read_b32 %0, %1"
+                           : "=v"(x)
+                           : "a"(acc[i][j][4 * eg + ee]));
+              b = fmaf(x, q[ee][j], b);
+            }
+            vp[ee] = 0.f;
+            wp[ee] = b;
+          }
+        } else {
+#pragma unroll
+          for (int ee = 0; ee < 4; ++ee) {
+            float a = 0.f, b = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float x = acc[i][j][4 * eg + ee];
               a += x;
               b = fmaf(x, x, b);
             }
+            vp[ee] = a;
+            wp[ee] = b;
           }
-          vp[ee] = a;
-          wp[ee] = b;
         }
         if constexpr (!QUAD)
           *reinterpret_cast<float4*>(sp + wo + i * 32 + 8 * eg) = v;
