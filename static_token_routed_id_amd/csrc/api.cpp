@@ -989,19 +989,29 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
         gw.N = d.d_e;
         gw.K = 3 * d.d;
         gw.header = pd.header;
-        if (e == hipSuccess)
-          e = gemm_nt_256_splitk_launch(gw, s, part, part_floats, 8, kBF16);
-        // G = [hi | lo | hi] . [hi | hi | lo] of Wc^T (float32, then hi | lo)
+        // G = [hi | lo | hi] . [hi | hi | lo] of Wc^T (float32 sums, then
+        // hi | lo), side by side with Mc in one launch where they fit
         GemmArgs gg = gw;
         gg.A1 = tw + DD;
         gg.A2 = tw;
         gg.a1_m = gg.a2_m = 3 * DD;
         gg.C = gm;
         gg.M = d.d_e;
+        GemmArgs gp = gg;
+        gp.C = gh;
+        gp.c_m = DE;
+        hipError_t pe = hipErrorInvalidValue;
         if (e == hipSuccess)
-          e = gemm_nt_256_splitk_launch(gg, s, part, part_floats, 16, kF32);
-        if (e == hipSuccess)
-          e = split_bf16_launch(pd.header, gm, DE * DE, gh, gl, s);
+          pe = gemm_nt_256_splitk_pair_launch(gw, 8, gp, 16, gl, part,
+                                              part_floats, s);
+        if (e == hipSuccess && pe != hipSuccess) {
+          if (pe != hipErrorInvalidValue) return L3_ERR_HIP;
+          e = gemm_nt_256_splitk_launch(gw, s, part, part_floats, 8, kBF16);
+          if (e == hipSuccess)
+            e = gemm_nt_256_splitk_launch(gg, s, part, part_floats, 16, kF32);
+          if (e == hipSuccess)
+            e = split_bf16_launch(pd.header, gm, DE * DE, gh, gl, s);
+        }
         if (e != hipSuccess) return L3_ERR_HIP;
       }
       // per row a^T G a: a (G_hi + G_lo), each row dotted with a

@@ -162,15 +162,33 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GemmArgs g) {
     }
 }
 
-// C = the nsplit partial products added in order.
+// Output v of the split-K sum: to C as TC, or, with lo (C bf16), as the
+// bf16 pair hi = bf16(v) in C, lo = bf16(v - hi) in lo.
 template <typename TC>
-__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g) {
+__device__ __forceinline__ void reduce_out(TC* c, uint16_t* lo, int64_t i,
+                                           float v) {
+  if constexpr (sizeof(TC) == 2) {
+    if (lo) {
+      const uint16_t h = f2bf(v);
+      c[i] = h;
+      lo[i] = f2bf(v - __uint_as_float(static_cast<uint32_t>(h) << 16));
+      return;
+    }
+  }
+  st<TC>(c, i, v);
+}
+
+// C = the nsplit partial products added in order (block blk of the
+// reduction); with lo, as the bf16 hi | lo pair (reduce_out).
+template <typename TC>
+__device__ __forceinline__ void gemm_reduce_job(const GemmArgs& g, int blk,
+                                                uint16_t* lo) {
   if (g.header && g.header[0] != 0) return;
   const int64_t mn = static_cast<int64_t>(g.M) * g.N;
   // four consecutive outputs a thread (16-byte loads) when N allows; the
   // shares are added in order z = 0, 1, ... whatever the loads' order
   if (g.N % 4 == 0) {
-    const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    const int64_t i = (static_cast<int64_t>(blk) * 256 + threadIdx.x) * 4;
     if (i >= mn) return;
     float4 v = {0.f, 0.f, 0.f, 0.f};
     const float* p = g.part + i;
@@ -197,18 +215,35 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g) {
     }
     const int64_t m = i / g.N, n = i - m * g.N;
     TC* c = static_cast<TC*>(g.C);
-    st<TC>(c, m * g.c_m + n, v.x);
-    st<TC>(c, m * g.c_m + n + 1, v.y);
-    st<TC>(c, m * g.c_m + n + 2, v.z);
-    st<TC>(c, m * g.c_m + n + 3, v.w);
+    reduce_out<TC>(c, lo, m * g.c_m + n, v.x);
+    reduce_out<TC>(c, lo, m * g.c_m + n + 1, v.y);
+    reduce_out<TC>(c, lo, m * g.c_m + n + 2, v.z);
+    reduce_out<TC>(c, lo, m * g.c_m + n + 3, v.w);
     return;
   }
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t i = static_cast<int64_t>(blk) * 256 + threadIdx.x;
   if (i >= mn) return;
   float v = 0.f;
   for (int z = 0; z < g.nsplit; ++z) v += g.part[z * mn + i];
   const int64_t m = i / g.N, n = i - m * g.N;
-  st<TC>(static_cast<TC*>(g.C), m * g.c_m + n, v);
+  reduce_out<TC>(static_cast<TC*>(g.C), lo, m * g.c_m + n, v);
+}
+
+template <typename TC>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g) {
+  gemm_reduce_job<TC>(g, blockIdx.x, nullptr);
+}
+
+// The sums of two split-K products in one launch, both with bf16 C:
+// blocks [0, n0) g0's, the rest g1's (with lo1: g1's as hi | lo).
+__global__ __launch_bounds__(256) void gemm_reduce_pair_kernel(GemmArgs g0,
+                                                               GemmArgs g1,
+                                                               int n0,
+                                                               uint16_t* lo1) {
+  if (static_cast<int>(blockIdx.x) < n0)
+    gemm_reduce_job<uint16_t>(g0, blockIdx.x, nullptr);
+  else
+    gemm_reduce_job<uint16_t>(g1, blockIdx.x - n0, lo1);
 }
 
 // grid of gemm_reduce_kernel for M x N outputs
@@ -450,8 +485,10 @@ __device__ __forceinline__ void step256(floatx16 (&acc)[4][4],
   }
 }
 
-template <typename TC, bool FOLD, bool QUAD = false>
-__global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
+// One job (output tile and K share) of the 256 x 256 kernel; the kernel
+// runs job blockIdx.x, the paired kernel below two products' jobs.
+template <typename TC, bool FOLD, bool QUAD>
+__device__ __forceinline__ void gemm256_job(const GemmArgs& g, int job) {
   __shared__ __align__(16) uint16_t lds[2][2][kTM * kTL];
   // LayerNorm fold (consumer): per tile row (rstd, -mean * rstd), per tile
   // column (c1, c2)
@@ -462,9 +499,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
   const int wm = w >> 1, wn = w & 1;
   const int mt = ceil_div(g.M, kTM), nt = g.N / kTN;
   const int T = mt * nt;
-  // split K (nsplit > 1, float32 partials): workgroup b takes share b / T
-  // of K for tile b % T
-  const int kz = blockIdx.x / T, bt = blockIdx.x - kz * T;
+  // split K (nsplit > 1, float32 partials): job b takes share b / T of K
+  // for tile b % T
+  const int kz = job / T, bt = job - kz * T;
   int tile = bt;
   if (T % kXcd == 0 && mt % kGroupM == 0)
     tile = (bt % kXcd) * (T / kXcd) + bt / kXcd;
@@ -781,6 +818,23 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
   }
 }
 
+template <typename TC, bool FOLD, bool QUAD = false>
+__global__ __launch_bounds__(256, 1) void gemm_nt_256_kernel(GemmArgs g) {
+  gemm256_job<TC, FOLD, QUAD>(g, blockIdx.x);
+}
+
+// Two split-K products (float32 partials) in one launch: workgroups
+// [0, n0) take g0's jobs, the rest g1's (the job's LDS is the same
+// function's, so the two share it).
+__global__ __launch_bounds__(256, 1) void gemm_nt_256_pair_kernel(GemmArgs g0,
+                                                                 GemmArgs g1,
+                                                                 int n0) {
+  if (static_cast<int>(blockIdx.x) < n0)
+    gemm256_job<float, false, false>(g0, blockIdx.x);
+  else
+    gemm256_job<float, false, false>(g1, blockIdx.x - n0);
+}
+
 // Shape rules of the 256 x 256 kernel; gemm_nt_256_ok adds M >= 1024 (below
 // that the launcher prefers other tilings, or the split-K form for few rows).
 static bool gemm_nt_256_shape_ok(const GemmArgs& g) {
@@ -872,6 +926,21 @@ hipError_t ln_apply_launch(const LnApplyArgs& a, hipStream_t s) {
 // its partial product to part, then gemm_reduce_kernel adds the shares in
 // order. Returns hipErrorInvalidValue when the shape does not allow it
 // (the caller then takes another path).
+// K shares of a split-K launch: about 256 workgroups in all, at most
+// max_split, whole 64-wide slices in every share (a share may straddle K1:
+// the operands switch per slice), the partials within part_floats.
+static int splitk_shares(const GemmArgs& g, int max_split,
+                         int64_t part_floats) {
+  const int64_t tiles =
+      static_cast<int64_t>(ceil_div(g.M, kTM)) * (g.N / kTN);
+  const int64_t mn = static_cast<int64_t>(g.M) * g.N;
+  int ns = static_cast<int>(
+      std::min<int64_t>((256 + tiles - 1) / tiles, max_split));
+  while (ns > 1 && ((g.K % (ns * kTK)) != 0 || ns * mn > part_floats))
+    --ns;
+  return ns;
+}
+
 hipError_t gemm_nt_256_splitk_launch(const GemmArgs& g0, hipStream_t s,
                                      float* part, int64_t part_floats,
                                      int max_split, int c_type) {
@@ -880,13 +949,7 @@ hipError_t gemm_nt_256_splitk_launch(const GemmArgs& g0, hipStream_t s,
   GemmArgs g = g0;
   const int64_t tiles =
       static_cast<int64_t>(ceil_div(g.M, kTM)) * (g.N / kTN);
-  const int64_t mn = static_cast<int64_t>(g.M) * g.N;
-  int ns = static_cast<int>(
-      std::min<int64_t>((256 + tiles - 1) / tiles, max_split));
-  // whole 64-wide slices in every share (a share may straddle K1: the
-  // operands switch per slice)
-  while (ns > 1 && ((g.K % (ns * kTK)) != 0 || ns * mn > part_floats))
-    --ns;
+  const int ns = splitk_shares(g, max_split, part_floats);
   g.nsplit = ns;
   g.part = ns > 1 ? part : nullptr;
   const int grid = static_cast<int>(tiles) * ns;
@@ -902,6 +965,35 @@ hipError_t gemm_nt_256_splitk_launch(const GemmArgs& g0, hipStream_t s,
     else
       gemm_reduce_kernel<float><<<rgrid, 256, 0, s>>>(g);
   }
+  return hipGetLastError();
+}
+
+// Two independent products as gemm_nt_256_splitk_launch would run them (the
+// same K shares, so the same sums), in one launch of both products' jobs
+// and one of both sums: a's C as bf16, b's as the bf16 pair C (hi) and b_lo
+// (lo) of its float32 sum. a's partials come first in part, then b's.
+// Returns hipErrorInvalidValue (nothing launched) unless both shapes allow
+// the 256 x 256 kernel and both split in two or more shares.
+hipError_t gemm_nt_256_splitk_pair_launch(const GemmArgs& a0, int max_a,
+                                          const GemmArgs& b0, int max_b,
+                                          uint16_t* b_lo, float* part,
+                                          int64_t part_floats, hipStream_t s) {
+  if (!part || !b_lo || !gemm_nt_256_shape_ok(a0) ||
+      !gemm_nt_256_shape_ok(b0))
+    return hipErrorInvalidValue;
+  GemmArgs a = a0, b = b0;
+  const int64_t mn_a = static_cast<int64_t>(a.M) * a.N;
+  a.nsplit = splitk_shares(a, max_a, part_floats);
+  const int64_t left = part_floats - a.nsplit * mn_a;
+  b.nsplit = splitk_shares(b, max_b, left);
+  if (a.nsplit < 2 || b.nsplit < 2) return hipErrorInvalidValue;
+  a.part = part;
+  b.part = part + a.nsplit * mn_a;
+  const int jobs_a = ceil_div(a.M, kTM) * (a.N / kTN) * a.nsplit;
+  const int jobs_b = ceil_div(b.M, kTM) * (b.N / kTN) * b.nsplit;
+  gemm_nt_256_pair_kernel<<<jobs_a + jobs_b, 256, 0, s>>>(a, b, jobs_a);
+  const int ra = reduce_grid(a), rb = reduce_grid(b);
+  gemm_reduce_pair_kernel<<<ra + rb, 256, 0, s>>>(a, b, ra, b_lo);
   return hipGetLastError();
 }
 

@@ -394,6 +394,14 @@ hipError_t gemm_nt_256_splitk_launch(const GemmArgs& g, hipStream_t s,
                                      float* part, int64_t part_floats,
                                      int max_split = 16,
                                      int c_type = kF32);
+// Two independent products of that form in one launch (and their sums in
+// one more): a's C as bf16, b's as the bf16 hi (C) | lo (b_lo) pair of its
+// float32 sum, with the K shares the single launcher would choose.
+// hipErrorInvalidValue (nothing launched) if the shapes do not allow it.
+hipError_t gemm_nt_256_splitk_pair_launch(const GemmArgs& a, int max_a,
+                                          const GemmArgs& b, int max_b,
+                                          uint16_t* b_lo, float* part,
+                                          int64_t part_floats, hipStream_t s);
 hipError_t ln_bwd_launch(const BwdArgs& a, int dtype, hipStream_t s);
 hipError_t seg_bwd_launch(const BwdArgs& a, int dtype, int items_ub,
                           int S_ub, hipStream_t s);
