@@ -964,13 +964,11 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
         fa.W1 = w1s;
         fa.c12 = c12;
         fa.split = 1;
-        e = ln_fold_launch(fa, s);
-        // Wc^T as [hi | hi | lo] (d_e x 3d)
-        if (e == hipSuccess)
-          e = center_split_t_launch(pd.header,
-                                    static_cast<const uint16_t*>(W_up), d.d,
-                                    d.d_e, reinterpret_cast<float*>(ub + o_mean),
-                                    tw, s);
+        // with Wc^T as [hi | hi | lo] (d_e x 3d); the fold and Wc's column
+        // sums share one launch
+        e = fold_prep_launch(fa, static_cast<const uint16_t*>(W_up), d.d,
+                             d.d_e, reinterpret_cast<float*>(ub + o_mean), tw,
+                             s);
         // Mc = [W1hi | W1lo | W1hi] . [Wc hi | hi | lo] over K = 3d (bf16);
         // up to 8 K shares here and 16 for G (more shares made the in-order
         // sum of the partials cost more than the GEMM saved)

@@ -1007,10 +1007,10 @@ hipError_t gemm_nt_256_splitk_pair_launch(const GemmArgs& a0, int max_a,
 // values, so the mean term cancels against the rounded product exactly (up
 // to float32 rounding): the error follows the deviations u - mean, not u.
 // One wave per output column n, 8 elements a lane and step.
-__global__ __launch_bounds__(256) void ln_fold_kernel(LnFoldArgs a) {
+__device__ __forceinline__ void ln_fold_block(const LnFoldArgs& a, int blk) {
   if (a.header[0] != 0) return;
   const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int n = blk * 4 + (threadIdx.x >> 6);
   if (n >= a.n) return;
   const uint16_t* w = a.W + static_cast<int64_t>(n) * a.w_n;
   uint16_t* w1 = a.W1 + static_cast<int64_t>(n) * a.d * (a.split ? 2 : 1);
@@ -1043,6 +1043,10 @@ __global__ __launch_bounds__(256) void ln_fold_kernel(LnFoldArgs a) {
     a.c12[2 * n] = c1;
     a.c12[2 * n + 1] = c2;
   }
+}
+
+__global__ __launch_bounds__(256) void ln_fold_kernel(LnFoldArgs a) {
+  ln_fold_block(a, blockIdx.x);
 }
 
 hipError_t ln_fold_launch(const LnFoldArgs& a, hipStream_t s) {
@@ -1099,14 +1103,14 @@ hipError_t ln_rows_launch(const LnRowsArgs& a, hipStream_t s) {
 // the bf16 kernel: hi hi + lo hi + hi lo, about float32 accuracy).
 // Column sums of W (rows x cols, bf16) over blocks of 64 rows:
 // part[y * cols + c] = sum of W[r, c] over rows r of block y.
-__global__ __launch_bounds__(256) void col_part_kernel(const int32_t* header,
-                                                       const uint16_t* W,
-                                                       int rows, int cols,
-                                                       float* part) {
+__device__ __forceinline__ void col_part_block(const int32_t* header,
+                                               const uint16_t* W, int rows,
+                                               int cols, float* part, int bx,
+                                               int by) {
   if (header[0] != 0) return;
   __shared__ float s[4][64];
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const int c = blockIdx.x * 64 + tx, r0 = blockIdx.y * 64;
+  const int c = bx * 64 + tx, r0 = by * 64;
   float acc = 0.f;
   if (c < cols) {
 #pragma unroll
@@ -1118,8 +1122,32 @@ __global__ __launch_bounds__(256) void col_part_kernel(const int32_t* header,
   s[ty][tx] = acc;
   __syncthreads();
   if (ty == 0 && c < cols)
-    part[static_cast<int64_t>(blockIdx.y) * cols + c] =
+    part[static_cast<int64_t>(by) * cols + c] =
         (s[0][tx] + s[1][tx]) + (s[2][tx] + s[3][tx]);
+}
+
+__global__ __launch_bounds__(256) void col_part_kernel(const int32_t* header,
+                                                       const uint16_t* W,
+                                                       int rows, int cols,
+                                                       float* part) {
+  col_part_block(header, W, rows, cols, part, blockIdx.x, blockIdx.y);
+}
+
+// ln_fold's blocks (the first nfold) and col_part's (cbx column blocks a
+// row block) in one launch: the two read different weights and write
+// different buffers.
+__global__ __launch_bounds__(256) void fold_prep_kernel(LnFoldArgs a,
+                                                        const uint16_t* W,
+                                                        int rows, int cols,
+                                                        float* part, int nfold,
+                                                        int cbx) {
+  const int b = blockIdx.x;
+  if (b < nfold) {
+    ln_fold_block(a, b);
+  } else {
+    const int c = b - nfold;
+    col_part_block(a.header, W, rows, cols, part, c % cbx, c / cbx);
+  }
 }
 
 // T from W and the block sums above (added in block order per column).
@@ -1223,6 +1251,19 @@ hipError_t center_split_t_launch(const int32_t* header, const uint16_t* W,
   dim3 grid(ceil_div(cols, 64), ceil_div(rows, 64));
   col_part_kernel<<<grid, 256, 0, s>>>(header, W, rows, cols, mean);
   center_split_t_kernel<<<grid, 256, 0, s>>>(header, W, rows, cols, mean, T);
+  return hipGetLastError();
+}
+
+hipError_t fold_prep_launch(const LnFoldArgs& fa, const uint16_t* W,
+                            int rows, int cols, float* mean, uint16_t* T,
+                            hipStream_t s) {
+  if (fa.n <= 0 || rows <= 0 || cols <= 0) return hipErrorInvalidValue;
+  const int nfold = ceil_div(fa.n, 4), cbx = ceil_div(cols, 64),
+            cby = ceil_div(rows, 64);
+  fold_prep_kernel<<<nfold + cbx * cby, 256, 0, s>>>(fa, W, rows, cols, mean,
+                                                     nfold, cbx);
+  center_split_t_kernel<<<dim3(cbx, cby), 256, 0, s>>>(fa.header, W, rows,
+                                                       cols, mean, T);
   return hipGetLastError();
 }
 

@@ -303,6 +303,11 @@ hipError_t ln_fold_launch(const LnFoldArgs& a, hipStream_t s);
 // T[c, r] = hi, T[c, rows + r] = hi, T[c, 2 rows + r] = lo of
 // W[r, c] - mean_r W[r, c] (T is [cols x 3 rows]); mean is scratch of
 // cols * ceil(rows / 64) floats (column sums per block of 64 rows).
+// ln_fold_launch(fa) and center_split_t_launch(fa.header, W, ...) with the
+// fold and the column sums in one launch (they are independent).
+hipError_t fold_prep_launch(const LnFoldArgs& fa, const uint16_t* W,
+                            int rows, int cols, float* mean, uint16_t* T,
+                            hipStream_t s);
 hipError_t center_split_t_launch(const int32_t* header, const uint16_t* W,
                                  int rows, int cols, float* mean, uint16_t* T,
                                  hipStream_t s);
