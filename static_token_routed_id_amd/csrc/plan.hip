@@ -252,28 +252,58 @@ __device__ int scan_excl_1024(int32_t* a, int n, int* tmp) {
   return carry;
 }
 
-// In-place exclusive scan of n ints; the total goes to *total_out when given.
-__global__ __launch_bounds__(1024) void scan_single_kernel(int32_t* a, int n,
-                                                           int32_t* total_out) {
-  __shared__ int tmp[1024 / 64 + 1];
-  const int total = scan_excl_1024(a, n, tmp);
-  if (threadIdx.x == 0 && total_out) *total_out = total;
-}
-
-// Stable scatter of one 1024-key tile by one DB-bit digit. Keys of a tile
-// are taken in order, 256 at a time; within a wave the rank among equal
-// digits comes from a ballot match on the digit bits, across waves from LDS
-// counts.
+// Stable scatter of one 1024-key tile by one DB-bit digit. The tile's first
+// output position for each digit (every key of a smaller digit, and this
+// digit's keys in earlier tiles) comes from the raw per-tile counts
+// hist[digit * nblk + tile]: each workgroup reads them all (L2-resident)
+// instead of waiting for a separate scan. Keys of a tile are taken in
+// order, 256 at a time; within a wave the rank among equal digits comes
+// from a ballot match on the digit bits, across waves from LDS counts.
 template <int DB>
 __global__ __launch_bounds__(256) void radix_scatter_kernel(
     const int32_t* kin, const int32_t* vin, int32_t* kout, int32_t* vout,
     int B, int shift, const int32_t* hist, int nblk) {
   constexpr int NB = 1 << DB;
+  constexpr int DPT = NB / 256;  // digits a thread, consecutive
   __shared__ int base[NB];
   __shared__ int wcnt[4][NB];
+  __shared__ int tmp[256 / 64 + 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int q = tid; q < NB; q += 256) {
-    base[q] = hist[q * nblk + blockIdx.x];
+  const int me = blockIdx.x;
+  int tot[DPT], pre[DPT], mine = 0;
+#pragma unroll
+  for (int u = 0; u < DPT; ++u) {
+    const int32_t* hq = hist + static_cast<int64_t>(tid * DPT + u) * nblk;
+    int t = 0, pr = 0;
+    if (nblk % 4 == 0) {
+#pragma unroll 4
+      for (int b = 0; b < nblk; b += 4) {
+        const int4 c = *reinterpret_cast<const int4*>(hq + b);
+        const int c4 = c.x + c.y + c.z + c.w;
+        t += c4;
+        if (b + 4 <= me)
+          pr += c4;
+        else if (b < me)
+          pr += c.x + (b + 1 < me ? c.y : 0) + (b + 2 < me ? c.z : 0);
+      }
+    } else {
+      for (int b = 0; b < nblk; ++b) {
+        const int c = hq[b];
+        t += c;
+        if (b < me) pr += c;
+      }
+    }
+    tot[u] = t;
+    pre[u] = pr;
+    mine += t;
+  }
+  int all;
+  int off = block_excl_scan<256>(mine, tmp, &all);
+#pragma unroll
+  for (int u = 0; u < DPT; ++u) {
+    const int q = tid * DPT + u;
+    base[q] = off + pre[u];
+    off += tot[u];
 #pragma unroll
     for (int v = 0; v < 4; ++v) wcnt[v][q] = 0;
   }
@@ -327,14 +357,23 @@ __global__ __launch_bounds__(256) void seg_count_kernel(const int32_t* sid,
   if (tid == 0) blk[blockIdx.x] = total;
 }
 
-// Write the segment arrays; blk holds the exclusive scan of the tile counts
-// and blk[nblk] the total S.
+// Write the segment arrays; blk holds the tiles' segment counts (each
+// workgroup adds up those of the tiles before its own, and all of them: S).
 __global__ __launch_bounds__(256) void seg_write_kernel(PlanDev pd,
                                                         PlanParams p,
                                                         int nblk) {
   __shared__ int tmp[256 / 64 + 1];
   const int tid = threadIdx.x;
   const int B = p.B;
+  int before = 0, every = 0;
+  for (int i = tid; i < nblk; i += 256) {
+    const int c = pd.blk[i];
+    every += c;
+    if (i < static_cast<int>(blockIdx.x)) before += c;
+  }
+  int first, S;
+  block_excl_scan<256>(before, tmp, &first);
+  block_excl_scan<256>(every, tmp, &S);
   // each thread takes 4 consecutive positions of the tile, in order
   const int j0 = blockIdx.x * kSortTile + tid * 4;
   int c = 0;
@@ -343,7 +382,7 @@ __global__ __launch_bounds__(256) void seg_write_kernel(PlanDev pd,
     if (j < B && (j == 0 || pd.sorted_ids[j] != pd.sorted_ids[j - 1])) ++c;
   }
   int total;
-  int s = pd.blk[blockIdx.x] + block_excl_scan<256>(c, tmp, &total);
+  int s = first + block_excl_scan<256>(c, tmp, &total);
   for (int q = 0; q < 4; ++q) {
     int j = j0 + q;
     if (j < B && (j == 0 || pd.sorted_ids[j] != pd.sorted_ids[j - 1])) {
@@ -359,7 +398,6 @@ __global__ __launch_bounds__(256) void seg_write_kernel(PlanDev pd,
     }
   }
   if (blockIdx.x == 0 && tid == 0) {
-    const int S = pd.blk[nblk];
     pd.seg_tok_start[S] = B;
     pd.header[1] = S;
   }
@@ -493,13 +531,11 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
     if (db == 9) {
       radix_hist_kernel<9><<<nblk, 256, 0, s>>>(kin, B, shift, pd.hist, nblk,
                                                 p.vocab, pd.header, ps == 0);
-      scan_single_kernel<<<1, 1024, 0, s>>>(pd.hist, 512 * nblk, nullptr);
       radix_scatter_kernel<9><<<nblk, 256, 0, s>>>(
           kin, vin, ka[out], va[out], B, shift, pd.hist, nblk);
     } else {
       radix_hist_kernel<8><<<nblk, 256, 0, s>>>(kin, B, shift, pd.hist, nblk,
                                                 p.vocab, pd.header, ps == 0);
-      scan_single_kernel<<<1, 1024, 0, s>>>(pd.hist, 256 * nblk, nullptr);
       radix_scatter_kernel<8><<<nblk, 256, 0, s>>>(
           kin, vin, ka[out], va[out], B, shift, pd.hist, nblk);
     }
@@ -508,7 +544,6 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
     out ^= 1;
   }
   seg_count_kernel<<<nblk, 256, 0, s>>>(pd.sorted_ids, B, pd.blk);
-  scan_single_kernel<<<1, 1024, 0, s>>>(pd.blk, nblk, pd.blk + nblk);
   seg_write_kernel<<<nblk, 256, 0, s>>>(pd, p, nblk);
   seg_items_kernel<<<ceil_div(B, 256), 256, 0, s>>>(pd, p);
   seg_items_scan_kernel<<<p.group_min_rows > 0 ? 3 : 2, 1024, 0, s>>>(
