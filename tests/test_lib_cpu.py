@@ -114,3 +114,22 @@ def test_plan_host_checks(L):
     lib.l3_plan_release(out)
     lib.l3_plan_release(None)
     assert lib.l3_plan_tokens(None) == -1
+
+
+def test_read_probe_library():
+    """The read probe bench.py times beside the gather (libl3probe.so, built
+    with libl3.so) loads, exports its entry point and rejects a bad size or
+    pattern on the host, before any launch."""
+    path = os.path.join(ROOT, "static_token_routed_id_amd", "libl3probe.so")
+    if not os.path.exists(path):
+        pytest.fail("libl3probe.so is not built (python -m "
+                    "static_token_routed_id_amd.build)")
+    lib = ctypes.CDLL(path)
+    f = lib.l3probe_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 1000, 0, 256, None, None) == -1     # not whole 64 KiB
+    assert f(None, 0, 0, 256, None, None) == -1        # empty
+    assert f(None, 65536, 0, 0, None, None) == -1      # no workgroups
+    assert f(None, 65536, 5, 256, None, None) == -1    # no such pattern
