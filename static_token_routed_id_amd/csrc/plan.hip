@@ -14,13 +14,14 @@
 //     64-bit keys in LDS, then segment cut and work-item count in the same
 //     launch (one launch: decode-sized batches are latency bound);
 //   * larger batches: LSD radix sort of the 32-bit ids with the position as
-//     payload (stable, 8-bit digits, histogram / scan / ranked scatter per
-//     digit), then segment cut kernels.
+//     payload (stable, 8- or 9-bit digits; per digit a histogram of each
+//     1024-key tile, then a ranked scatter whose workgroups take their
+//     offsets from all the tiles' counts), then segment cut kernels.
 // After the segments, the plan counts the forward pass's work items: a
-// segment with n_g >= group_min_rows (large batches only) yields
-// ceil(m_g / 64) group items (seg_gitem_start), any other segment
-// ceil(m_g / 32) * ceil(n_g / chunk) wave items (seg_item_start); both are
-// exclusive prefix sums.
+// segment with n_g >= group_min_rows (large batches only) yields one group
+// item if m_g <= 64, else ceil(m_g / 128) (seg_gitem_start), any other
+// segment ceil(m_g / 16) * ceil(n_g / chunk) wave items (seg_item_start);
+// both are exclusive prefix sums.
 
 #include "l3_device.h"
 #include "l3_internal.h"
