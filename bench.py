@@ -20,8 +20,9 @@ bf16 batches one launch of seg_group_kernel (it also runs the wave items of
 the ids with few rows), else seg_fwd_kernel (+ seg_combine for split rows):
 algorithmic bytes per launch (each distinct id's K_t and V_t rows once, x
 read, a written, ids and segment records) over the mean launch time, taken
-from HIP events recorded on the launch stream around the step during the
-timed steps; `traffic` is the HBM bytes per launch from the committed
+from HIP events the library records on the launch stream around each
+stage in a second run of as many steps (the headline steps run without
+those events); `traffic` is the HBM bytes per launch from the committed
 FETCH_SIZE / WRITE_SIZE counter summary
 (profiles/traffic_gather_<workload>.md), or null when the kernels changed
 since it was taken; `copy_peak_gbs` is a measured 2 GiB device copy (bytes
@@ -631,30 +632,39 @@ def main():
     flush_buf = (torch.empty(1 << 28, dtype=torch.float32, device="cuda")
                  if flush else None)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    L.l3_timing_read(layer.plan)          # drop warm-up events
-    L.l3_timing_enable(layer.plan, True)
-    torch.cuda.synchronize()
-    if flush:
-        evs = [(torch.cuda.Event(enable_timing=True),
-                torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for a_ev, b_ev in evs:
-            flush_buf.fill_(float(len(evs)))
-            a_ev.record()
-            step()
-            b_ev.record()
-        torch.cuda.synchronize()
-        step_ms = sum(a_ev.elapsed_time(b_ev) for a_ev, b_ev in evs)
-        t0, t1 = 0.0, step_ms * 1e-3
-    else:
-        t0 = time.perf_counter()
+    def timed_steps():
+        """K steps, timed as a whole (or step by step with a flush between,
+        outside the events); returns the seconds they took."""
+        if flush:
+            evs = [(torch.cuda.Event(enable_timing=True),
+                    torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for a_ev, b_ev in evs:
+                flush_buf.fill_(float(len(evs)))
+                a_ev.record()
+                step()
+                b_ev.record()
+            torch.cuda.synchronize()
+            return sum(a_ev.elapsed_time(b_ev) for a_ev, b_ev in evs) * 1e-3
+        t_a = time.perf_counter()
         for _ in range(args.steps):
             step()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
+        return time.perf_counter() - t_a
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # the headline steps run without the library's stage events; the same
+    # number of steps then runs again with them, for the per-stage times
+    # (and the gather's launch time of the roofline)
+    L.l3_timing_enable(layer.plan, False)
+    L.l3_timing_read(layer.plan)          # drop warm-up events
+    torch.cuda.synchronize()
+    t0, t1 = 0.0, timed_steps()
+    L.l3_timing_enable(layer.plan, True)
+    torch.cuda.synchronize()
+    staged_s = timed_steps()
     L.l3_timing_enable(layer.plan, False)
     stages = L.l3_timing_read(layer.plan)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -739,7 +749,11 @@ def main():
                    if flush else
                    "wall clock over the timed steps, synchronised on both "
                    "sides (no flush: a step touches far more than the "
-                   "caches hold)"),
+                   "caches hold)") +
+                  "; stage_ms from the library's per-stage HIP events in a "
+                  "second run of as many steps (%.4f ms a step with the "
+                  "events), the headline steps run without them"
+                  % (staged_s * 1e3 / args.steps),
     }
     if args.copy_peak:
         cp = copy_peak_gbs()
