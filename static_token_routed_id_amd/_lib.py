@@ -210,7 +210,9 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
+        # at interpreter exit the module's globals may already be gone
+        # (the process releases everything then anyway)
+        if h and _lib is not None:
             _lib.l3_plan_release(h)
             self.handle = None
 
