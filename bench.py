@@ -258,7 +258,9 @@ def read_peak_gbs(nbytes: int = 1 << 32, reps: int = 5) -> dict:
     device buffer streamed by the read probe (csrc/read_probe.hip,
     libl3probe.so): the gather's own access pattern (16 rows of 4 KiB a
     64 KiB block, 64 bytes of each row per wave instruction), 1 KiB
-    contiguous per instruction, and the same with non-temporal loads."""
+    contiguous per instruction, the same with non-temporal loads, and the
+    gather's pattern with non-temporal loads (the two halves of each
+    128-byte line read by consecutive instructions, or four apart)."""
     import ctypes
 
     import torch
@@ -276,7 +278,9 @@ def read_peak_gbs(nbytes: int = 1 << 32, reps: int = 5) -> dict:
     st = torch.cuda.current_stream()
     out = {}
     for name, pattern in (("gather_pattern", 1), ("stream", 0),
-                          ("stream_nontemporal", 2)):
+                          ("stream_nontemporal", 2),
+                          ("gather_pattern_nontemporal", 3),
+                          ("gather_pattern_nontemporal_halves_apart", 4)):
         best = 0.0
         for grid in (512, 1024, 2048):
             def launch():

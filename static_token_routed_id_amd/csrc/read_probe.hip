@@ -14,7 +14,11 @@
 //      rows of 4 KiB, every wave instruction reading 64 bytes from each of
 //      the 16 rows (lane l: row l % 16, 16-byte piece l / 16), the rows
 //      walked in 64-byte steps, ordinary loads;
-//   2: as 0 with non-temporal (streaming) loads.
+//   2: as 0 with non-temporal (streaming) loads;
+//   3: as 1 with non-temporal loads (the two 64-byte halves of a row's
+//      128-byte line read by consecutive instructions);
+//   4: as 3 with the halves four instructions apart (of each eight loads
+//      in flight, the first halves of four lines, then their second halves).
 // Returns 0, or -1 for a bad pattern or size, or the HIP error code of the
 // launch.
 #include <hip/hip_runtime.h>
@@ -33,9 +37,10 @@ __global__ __launch_bounds__(256) void read_probe_kernel(
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int64_t waves = static_cast<int64_t>(gridDim.x) * 4;
   // lane's first byte within a block and the stride of its successive loads
-  const int first = PATTERN == 1 ? (lane & 15) * 4096 + (lane >> 4) * 16
-                                 : lane * 16;
-  const int step = PATTERN == 1 ? 64 : 1024;
+  constexpr bool rows16 = PATTERN == 1 || PATTERN >= 3;
+  constexpr bool nt = PATTERN >= 2;
+  const int first = rows16 ? (lane & 15) * 4096 + (lane >> 4) * 16 : lane * 16;
+  const int step = rows16 ? 64 : 1024;
   unsigned mix = 0;
   for (int64_t b = wave; b < nblocks; b += waves) {
     const uint8_t* p = buf + b * kBlock + first;
@@ -43,8 +48,10 @@ __global__ __launch_bounds__(256) void read_probe_kernel(
       u32x4 v[kDepth];
 #pragma unroll
       for (int u = 0; u < kDepth; ++u) {
-        const u32x4* q = reinterpret_cast<const u32x4*>(p + (i + u) * step);
-        v[u] = PATTERN == 2 ? __builtin_nontemporal_load(q) : *q;
+        // pattern 4: steps 0, 2, 4, 6, 1, 3, 5, 7 of the eight
+        const int su = PATTERN == 4 ? (u & 3) * 2 + (u >> 2) : u;
+        const u32x4* q = reinterpret_cast<const u32x4*>(p + (i + su) * step);
+        v[u] = nt ? __builtin_nontemporal_load(q) : *q;
       }
 #pragma unroll
       for (int u = 0; u < kDepth; ++u) mix += v[u].x ^ v[u].w;
@@ -65,6 +72,8 @@ extern "C" int l3probe_read(const void* buf, int64_t bytes, int pattern,
     case 0: read_probe_kernel<0><<<grid, 256, 0, stream>>>(p, nb, s); break;
     case 1: read_probe_kernel<1><<<grid, 256, 0, stream>>>(p, nb, s); break;
     case 2: read_probe_kernel<2><<<grid, 256, 0, stream>>>(p, nb, s); break;
+    case 3: read_probe_kernel<3><<<grid, 256, 0, stream>>>(p, nb, s); break;
+    case 4: read_probe_kernel<4><<<grid, 256, 0, stream>>>(p, nb, s); break;
     default: return -1;
   }
   return static_cast<int>(hipGetLastError());
