@@ -75,13 +75,15 @@ def algorithmic_bytes(w, plan, group_min_rows: int) -> dict:
 
 
 # Sources whose change invalidates the committed HBM traffic counts of the
-# gather kernels (kernel code, shared device helpers, launch configuration).
+# gather kernels (kernel code, shared device helpers, launch configuration,
+# and the plan, whose item lists set the order the items run in).
 TRAFFIC_SOURCES = ("static_token_routed_id_amd/csrc/seg_fwd.hip",
                    "static_token_routed_id_amd/csrc/seg_group.hip",
                    "static_token_routed_id_amd/csrc/seg_wave.h",
                    "static_token_routed_id_amd/csrc/l3_device.h",
                    "static_token_routed_id_amd/csrc/l3_internal.h",
-                   "static_token_routed_id_amd/csrc/api.cpp")
+                   "static_token_routed_id_amd/csrc/api.cpp",
+                   "static_token_routed_id_amd/csrc/plan.hip")
 
 
 def sources_digest() -> str:

@@ -53,7 +53,9 @@ struct PlanDev {
   int32_t* keys_alt;        // [B] radix ping-pong
   int32_t* vals_alt;        // [B]
   int32_t* hist;            // [512 * ceil(B / kSortTile)] (9-bit digits)
-  int32_t* blk;             // [ceil(B / kSortTile) + 1]
+  int32_t* blk;             // [ceil(B / kSortTile) + 1]: the first sort
+                            // pass's per-tile id checks, then the tiles'
+                            // segment counts
   int2* item_map;           // wave item -> (segment, index within segment)
   int2* gitem_map;          // group item -> (segment, tile within segment)
   int2* hitem_map;          // the 128-token group items only, in kXcds

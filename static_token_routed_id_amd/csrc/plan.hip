@@ -178,31 +178,31 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
 }
 
 // ---------------------------------------------------------------- large ---
-__global__ void header_init_kernel(int32_t* header) {
-  if (threadIdx.x < kHeaderInts) header[threadIdx.x] = 0;
-}
-
 // Digit histogram of one 1024-key tile (DB-bit digits, 2^DB buckets);
-// pass 0 also checks the id range.
+// pass 0 also checks the id range and records the tile's verdict in
+// bad[tile] (kBadId or 0), which the first scatter folds into the header.
 template <int DB>
 __global__ __launch_bounds__(256) void radix_hist_kernel(
     const int32_t* kin, int B, int shift, int32_t* hist, int nblk,
-    int64_t vocab, int32_t* header, int validate) {
+    int64_t vocab, int32_t* bad) {
   constexpr int NB = 1 << DB;
   __shared__ int h[NB];
+  __shared__ int s_bad;
   const int tid = threadIdx.x;
   for (int q = tid; q < NB; q += 256) h[q] = 0;
+  if (tid == 0) s_bad = 0;
   __syncthreads();
   for (int r = 0; r < kSortTile / 256; ++r) {
     int i = blockIdx.x * kSortTile + r * 256 + tid;
     if (i < B) {
       int k = kin[i];
-      if (validate && (k < 0 || k >= vocab)) atomicOr(&header[0], kBadId);
+      if (bad && (k < 0 || k >= vocab)) s_bad = kBadId;
       atomicAdd(&h[(static_cast<uint32_t>(k) >> shift) & (NB - 1u)], 1);
     }
   }
   __syncthreads();
   for (int q = tid; q < NB; q += 256) hist[q * nblk + blockIdx.x] = h[q];
+  if (bad && tid == 0) bad[blockIdx.x] = s_bad;
 }
 
 // In-place exclusive scan of a[0..n) by one 1024-thread workgroup: rounds
@@ -263,21 +263,45 @@ __device__ int scan_excl_1024(int32_t* a, int n, int* tmp) {
 template <int DB>
 __global__ __launch_bounds__(256) void radix_scatter_kernel(
     const int32_t* kin, const int32_t* vin, int32_t* kout, int32_t* vout,
-    int B, int shift, const int32_t* hist, int nblk) {
+    int B, int shift, const int32_t* hist, int nblk, int32_t* header,
+    const int32_t* bad) {
   constexpr int NB = 1 << DB;
   constexpr int DPT = NB / 256;  // digits a thread, consecutive
   __shared__ int base[NB];
   __shared__ int wcnt[4][NB];
   __shared__ int tmp[256 / 64 + 1];
+  __shared__ int s_bad;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int me = blockIdx.x;
+  if (header && me == 0) {
+    // first pass: the plan's header starts here (status = the tiles' id
+    // checks, every count and queue zero); nothing reads it before the
+    // segment kernels
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    int f = 0;
+    for (int i = tid; i < nblk; i += 256) f |= bad[i];
+    if (f) atomicOr(&s_bad, f);
+    __syncthreads();
+    if (tid < kHeaderInts) header[tid] = tid == 0 ? s_bad : 0;
+  }
+  // the tile's keys and payloads, loaded first: their latency hides behind
+  // the counts' reads
+  constexpr int RND = kSortTile / 256;
+  int keys[RND], vals[RND];
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
+    const int i = blockIdx.x * kSortTile + r * 256 + tid;
+    keys[r] = i < B ? kin[i] : 0;
+    vals[r] = i < B ? (vin ? vin[i] : i) : 0;
+  }
   int tot[DPT], pre[DPT], mine = 0;
 #pragma unroll
   for (int u = 0; u < DPT; ++u) {
     const int32_t* hq = hist + static_cast<int64_t>(tid * DPT + u) * nblk;
     int t = 0, pr = 0;
     if (nblk % 4 == 0) {
-#pragma unroll 4
+#pragma unroll 16
       for (int b = 0; b < nblk; b += 4) {
         const int4 c = *reinterpret_cast<const int4*>(hq + b);
         const int c4 = c.x + c.y + c.z + c.w;
@@ -310,11 +334,12 @@ __global__ __launch_bounds__(256) void radix_scatter_kernel(
   }
   __syncthreads();
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int r = 0; r < kSortTile / 256; ++r) {
+#pragma unroll
+  for (int r = 0; r < RND; ++r) {
     const int i = blockIdx.x * kSortTile + r * 256 + tid;
     const bool valid = i < B;
-    const int key = valid ? kin[i] : 0;
-    const int val = valid ? (vin ? vin[i] : i) : 0;
+    const int key = keys[r];
+    const int val = vals[r];
     const uint32_t dig = (static_cast<uint32_t>(key) >> shift) & (NB - 1u);
     unsigned long long match = __ballot(valid);
 #pragma unroll
@@ -360,41 +385,55 @@ __global__ __launch_bounds__(256) void seg_count_kernel(const int32_t* sid,
 
 // Write the segment arrays; blk holds the tiles' segment counts (each
 // workgroup adds up those of the tiles before its own, and all of them: S).
+// A thread's five ids and the rows of the ids that start a segment there
+// are read before the counts, so the three reads overlap.
 __global__ __launch_bounds__(256) void seg_write_kernel(PlanDev pd,
                                                         PlanParams p,
                                                         int nblk) {
   __shared__ int tmp[256 / 64 + 1];
   const int tid = threadIdx.x;
   const int B = p.B;
+  // each thread takes 4 consecutive positions of the tile, in order; ids
+  // of positions j0 - 1 .. j0 + 3
+  const int j0 = blockIdx.x * kSortTile + tid * 4;
+  int ids[5];
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    const int j = j0 - 1 + q;
+    ids[q] = j >= 0 && j < B ? pd.sorted_ids[j] : 0;
+  }
+  bool head[4];
+  int64_t r0[4];
+  int n[4], c = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = j0 + q;
+    head[q] = j < B && (j == 0 || ids[q + 1] != ids[q]);
+    r0[q] = 0;
+    n[q] = 0;
+    if (head[q]) {
+      id_rows(p, ids[q + 1], &r0[q], &n[q], pd.header);
+      ++c;
+    }
+  }
   int before = 0, every = 0;
   for (int i = tid; i < nblk; i += 256) {
-    const int c = pd.blk[i];
-    every += c;
-    if (i < static_cast<int>(blockIdx.x)) before += c;
+    const int cb = pd.blk[i];
+    every += cb;
+    if (i < static_cast<int>(blockIdx.x)) before += cb;
   }
   int first, S;
   block_excl_scan<256>(before, tmp, &first);
   block_excl_scan<256>(every, tmp, &S);
-  // each thread takes 4 consecutive positions of the tile, in order
-  const int j0 = blockIdx.x * kSortTile + tid * 4;
-  int c = 0;
-  for (int q = 0; q < 4; ++q) {
-    int j = j0 + q;
-    if (j < B && (j == 0 || pd.sorted_ids[j] != pd.sorted_ids[j - 1])) ++c;
-  }
   int total;
   int s = first + block_excl_scan<256>(c, tmp, &total);
+#pragma unroll
   for (int q = 0; q < 4; ++q) {
-    int j = j0 + q;
-    if (j < B && (j == 0 || pd.sorted_ids[j] != pd.sorted_ids[j - 1])) {
-      int t = pd.sorted_ids[j];
-      int64_t r0;
-      int n;
-      id_rows(p, t, &r0, &n, pd.header);
-      pd.seg_id[s] = t;
-      pd.seg_tok_start[s] = j;
-      pd.seg_row_off[s] = r0;
-      pd.seg_n[s] = n;
+    if (head[q]) {
+      pd.seg_id[s] = ids[q + 1];
+      pd.seg_tok_start[s] = j0 + q;
+      pd.seg_row_off[s] = r0[q];
+      pd.seg_n[s] = n[q];
       ++s;
     }
   }
@@ -404,39 +443,48 @@ __global__ __launch_bounds__(256) void seg_write_kernel(PlanDev pd,
   }
 }
 
-// Work items per segment (into seg_item_start / seg_gitem_start, scanned
-// afterwards).
-__global__ __launch_bounds__(256) void seg_items_kernel(PlanDev pd,
-                                                        PlanParams p) {
-  const int S = pd.header[1];
-  for (int g = blockIdx.x * 256 + threadIdx.x; g < S;
-       g += gridDim.x * 256) {
-    const int m = pd.seg_tok_start[g + 1] - pd.seg_tok_start[g];
-    pd.seg_item_start[g] = items_of(m, pd.seg_n[g], p);
-    pd.seg_gitem_start[g] = gitems_of(m, pd.seg_n[g], p);
-    if (p.group_min_rows > 0)
-      pd.seg_aitem_start[g] = aitems_of(m, pd.seg_n[g], p);
-  }
-}
-
-// Scan the item counts in place (a[S] = total); S is read on the device.
-// One workgroup per count array, side by side: wave items (header[2]),
-// 64-token items (header[3]), and with with_all the wave items of every id
-// (header[8]; without it header[8] repeats header[2]).
+// Work items per segment, exclusive-scanned (a[S] = total); S is read on
+// the device. One workgroup per count array, side by side: each first
+// writes its segments' counts (coalesced, sixteen segments a thread), then scans
+// them in place (the workgroup barrier orders its own global writes and
+// reads): wave items (seg_item_start, header[2]), 64-token items
+// (seg_gitem_start, header[3]), and with with_all the wave items of every
+// id (seg_aitem_start, header[8]; without it header[8] repeats header[2]).
 __global__ __launch_bounds__(1024) void seg_items_scan_kernel(PlanDev pd,
+                                                              PlanParams p,
                                                               int with_all) {
   __shared__ int tmp[1024 / 64 + 1];
   const int n = pd.header[1];
-  int32_t* a = blockIdx.x == 0   ? pd.seg_item_start
-               : blockIdx.x == 1 ? pd.seg_gitem_start
-                                 : pd.seg_aitem_start;
+  const int kind = blockIdx.x;
+  int32_t* a = kind == 0   ? pd.seg_item_start
+               : kind == 1 ? pd.seg_gitem_start
+                           : pd.seg_aitem_start;
+  for (int base = 0; base < n; base += 16 * 1024) {
+    // sixteen segments a thread, every load of the round issued first
+    int m[16], rows[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int g = min(base + k * 1024 + static_cast<int>(threadIdx.x), n - 1);
+      m[k] = pd.seg_tok_start[g + 1] - pd.seg_tok_start[g];
+      rows[k] = pd.seg_n[g];
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int g = base + k * 1024 + threadIdx.x;
+      if (g < n)
+        a[g] = kind == 0   ? items_of(m[k], rows[k], p)
+               : kind == 1 ? gitems_of(m[k], rows[k], p)
+                           : aitems_of(m[k], rows[k], p);
+    }
+  }
+  __syncthreads();
   const int total = scan_excl_1024(a, n, tmp);
   if (threadIdx.x == 0) {
     a[n] = total;
-    if (blockIdx.x == 0) {
+    if (kind == 0) {
       pd.header[2] = total;
       if (!with_all) pd.header[8] = total;
-    } else if (blockIdx.x == 1) {
+    } else if (kind == 1) {
       pd.header[3] = total;
     } else {
       pd.header[8] = total;
@@ -445,58 +493,47 @@ __global__ __launch_bounds__(1024) void seg_items_scan_kernel(PlanDev pd,
 }
 
 // Direct maps from a work item to its segment and its index there, so the
-// forward kernels need no search: one thread per item finds its segment by
-// binary search over the segments' first items (parallel over items, so a
-// segment with thousands of items costs no more than one with one).
-__device__ __forceinline__ int seg_of(const int32_t* start, int S, int i) {
-  int lo = 0, hi = S - 1;  // last g with start[g] <= i
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (start[mid] <= i)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
+// forward kernels need no search: one wavefront per segment writes the
+// entries of all its items (its lanes side by side), whatever the kind;
+// the 128-token items also go to a compact list of their own, all items of
+// one id as one block of their XCD's list (reserved by one atomic; the
+// order of the blocks depends on timing, the items' results do not).
 __global__ __launch_bounds__(256) void item_map_kernel(PlanDev pd,
                                                        int with_all,
                                                        int64_t hcap) {
   if (pd.header[0] != 0) return;
   const int S = pd.header[1];
-  const int n_wave = pd.header[2], n_group = pd.header[3];
-  const int n_all = with_all ? pd.header[8] : 0;
-  const int n = max(n_wave, max(n_group, n_all));
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
-    if (i < n_wave) {
-      const int g = seg_of(pd.seg_item_start, S, i);
-      pd.item_map[i] = make_int2(g, i - pd.seg_item_start[g]);
-    }
-    if (i < n_group) {
-      const int g = seg_of(pd.seg_gitem_start, S, i);
-      const int j = i - pd.seg_gitem_start[g];
-      pd.gitem_map[i] = make_int2(g, j);
-      // the 128-token items also go to compact lists of their own, all of
-      // one id's items in the same list (the order within a list depends
-      // on timing; the items' results do not)
+  const int lane = threadIdx.x & 63;
+  const int waves = gridDim.x * 4;
+  for (int g = blockIdx.x * 4 + (threadIdx.x >> 6); g < S; g += waves) {
+    const int w0 = pd.seg_item_start[g], w1 = pd.seg_item_start[g + 1];
+    const int q0 = pd.seg_gitem_start[g], q1 = pd.seg_gitem_start[g + 1];
+    for (int i = w0 + lane; i < w1; i += 64)
+      pd.item_map[i] = make_int2(g, i - w0);
+    if (q1 > q0) {
+      for (int i = q0 + lane; i < q1; i += 64)
+        pd.gitem_map[i] = make_int2(g, i - q0);
       if (pd.seg_tok_start[g + 1] - pd.seg_tok_start[g] > kGroupTok) {
         const int x = hot_list_of(g);
-        pd.hitem_map[x * hcap + atomicAdd(&pd.header[16 + x], 1)] =
-            make_int2(g, j);
+        int first = 0;
+        if (lane == 0) first = atomicAdd(&pd.header[16 + x], q1 - q0);
+        first = __shfl(first, 0);
+        int2* list = pd.hitem_map + x * hcap + first;
+        for (int j = lane; j < q1 - q0; j += 64) list[j] = make_int2(g, j);
       }
     }
-    if (i < n_all) {
-      const int g = seg_of(pd.seg_aitem_start, S, i);
-      pd.aitem_map[i] = make_int2(g, i - pd.seg_aitem_start[g]);
+    if (with_all) {
+      const int a0 = pd.seg_aitem_start[g], a1 = pd.seg_aitem_start[g + 1];
+      for (int i = a0 + lane; i < a1; i += 64)
+        pd.aitem_map[i] = make_int2(g, i - a0);
     }
   }
 }
 
+// one wavefront per segment, at most B segments
 static int item_map_grid(int B) {
-  const int64_t cap = wave_items_cap(B);
-  const int64_t g = (cap + 255) / 256;
-  return static_cast<int>(g < 2048 ? (g > 0 ? g : 1) : 2048);
+  const int g = ceil_div(B, 4);
+  return g < 4096 ? (g > 0 ? g : 1) : 4096;
 }
 
 static int id_bits(int64_t vocab) {
@@ -515,7 +552,6 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
     return hipGetLastError();
   }
   const int nblk = ceil_div(B, kSortTile);
-  header_init_kernel<<<1, 64, 0, s>>>(pd.header);
   // 8-bit digits, or 9-bit ones where that saves a pass (17-18 bits and
   // 25-27 bits of id range)
   const int bits = id_bits(p.vocab);
@@ -529,16 +565,20 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
   const int32_t* vin = nullptr;
   for (int ps = 0; ps < passes; ++ps) {
     const int shift = db * ps;
+    // pass 0: the id check's per-tile verdicts go to blk (rewritten by
+    // seg_count later), and the scatter starts the header from them
+    int32_t* bad = ps == 0 ? pd.blk : nullptr;
+    int32_t* hdr = ps == 0 ? pd.header : nullptr;
     if (db == 9) {
       radix_hist_kernel<9><<<nblk, 256, 0, s>>>(kin, B, shift, pd.hist, nblk,
-                                                p.vocab, pd.header, ps == 0);
+                                                p.vocab, bad);
       radix_scatter_kernel<9><<<nblk, 256, 0, s>>>(
-          kin, vin, ka[out], va[out], B, shift, pd.hist, nblk);
+          kin, vin, ka[out], va[out], B, shift, pd.hist, nblk, hdr, bad);
     } else {
       radix_hist_kernel<8><<<nblk, 256, 0, s>>>(kin, B, shift, pd.hist, nblk,
-                                                p.vocab, pd.header, ps == 0);
+                                                p.vocab, bad);
       radix_scatter_kernel<8><<<nblk, 256, 0, s>>>(
-          kin, vin, ka[out], va[out], B, shift, pd.hist, nblk);
+          kin, vin, ka[out], va[out], B, shift, pd.hist, nblk, hdr, bad);
     }
     kin = ka[out];
     vin = va[out];
@@ -546,9 +586,8 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
   }
   seg_count_kernel<<<nblk, 256, 0, s>>>(pd.sorted_ids, B, pd.blk);
   seg_write_kernel<<<nblk, 256, 0, s>>>(pd, p, nblk);
-  seg_items_kernel<<<ceil_div(B, 256), 256, 0, s>>>(pd, p);
   seg_items_scan_kernel<<<p.group_min_rows > 0 ? 3 : 2, 1024, 0, s>>>(
-      pd, p.group_min_rows > 0);
+      pd, p, p.group_min_rows > 0);
   item_map_kernel<<<item_map_grid(B), 256, 0, s>>>(pd, p.group_min_rows > 0,
                                                   hitem_cap(B));
   return hipGetLastError();
