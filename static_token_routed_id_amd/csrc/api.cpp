@@ -952,7 +952,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       float* rows = reinterpret_cast<float*>(hb + q_c + q_st);
       {
         StageTimer t(plan, ST_WFOLD, s);
-        // W1 = W_mix1 diag(gamma) as hi | lo, c12 = (0, W_mix1 beta)
+        // c12 = (0, W_mix1 beta); W_mix1 diag(gamma) itself is not formed
         LnFoldArgs fa;
         fa.header = pd.header;
         fa.W = static_cast<const uint16_t*>(W_mix);
@@ -961,31 +961,33 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
         fa.beta = static_cast<const uint16_t*>(beta);
         fa.n = d.d;
         fa.d = d.d;
-        fa.W1 = w1s;
+        fa.W1 = nullptr;
         fa.c12 = c12;
         fa.split = 1;
-        // with Wc^T as [hi | hi | lo] (d_e x 3d); the fold and Wc's column
+        // Wc^T as [hi | hi | lo] (d_e x 3d) and (diag(gamma) Wc)^T as
+        // [hi | lo] (d_e x 2d, in the first buffer); c12 and Wc's column
         // sums share one launch
         e = fold_prep_launch(fa, static_cast<const uint16_t*>(W_up), d.d,
                              d.d_e, reinterpret_cast<float*>(ub + o_mean), tw,
-                             s);
-        // Mc = [W1hi | W1lo | W1hi] . [Wc hi | hi | lo] over K = 3d (bf16);
-        // up to 8 K shares here and 16 for G (more shares made the in-order
-        // sum of the partials cost more than the GEMM saved)
+                             static_cast<const uint16_t*>(gamma), w1s, s);
+        // Mc = [W_mix1 | W_mix1] . [(gamma Wc) hi | lo] over K = 2d (bf16:
+        // W_mix1 is exact); up to 8 K shares here and 16 for G (more shares
+        // made the in-order sum of the partials cost more than the GEMM
+        // saved)
         GemmArgs gw{};
-        gw.A1 = w1s;
-        gw.A2 = w1s;
+        gw.A1 = W_mix;
+        gw.A2 = W_mix;
         gw.a1_m = gw.a2_m = 2 * DD;
         gw.a1_k = gw.a2_k = 1;
-        gw.K1 = 2 * d.d;
-        gw.Bm = tw;
+        gw.K1 = d.d;
+        gw.Bm = w1s;
         gw.b_k = 1;
-        gw.b_n = 3 * DD;
+        gw.b_n = 2 * DD;
         gw.C = mt;
         gw.c_m = DE;
         gw.M = d.d;
         gw.N = d.d_e;
-        gw.K = 3 * d.d;
+        gw.K = 2 * d.d;
         gw.header = pd.header;
         // G = [hi | lo | hi] . [hi | hi | lo] of Wc^T (float32 sums, then
         // hi | lo), side by side with Mc in one launch where they fit
@@ -993,6 +995,10 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
         gg.A1 = tw + DD;
         gg.A2 = tw;
         gg.a1_m = gg.a2_m = 3 * DD;
+        gg.K1 = 2 * d.d;
+        gg.Bm = tw;
+        gg.b_n = 3 * DD;
+        gg.K = 3 * d.d;
         gg.C = gm;
         gg.M = d.d_e;
         GemmArgs gp = gg;

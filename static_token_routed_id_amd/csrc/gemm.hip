@@ -1013,7 +1013,8 @@ __device__ __forceinline__ void ln_fold_block(const LnFoldArgs& a, int blk) {
   const int n = blk * 4 + (threadIdx.x >> 6);
   if (n >= a.n) return;
   const uint16_t* w = a.W + static_cast<int64_t>(n) * a.w_n;
-  uint16_t* w1 = a.W1 + static_cast<int64_t>(n) * a.d * (a.split ? 2 : 1);
+  uint16_t* w1 =
+      a.W1 ? a.W1 + static_cast<int64_t>(n) * a.d * (a.split ? 2 : 1) : nullptr;
   float c1 = 0.f, c2 = 0.f;
   for (int e0 = lane * 8; e0 < a.d; e0 += 512) {
     const u32x4 wv = *reinterpret_cast<const u32x4*>(w + e0);
@@ -1034,8 +1035,10 @@ __device__ __forceinline__ void ln_fold_block(const LnFoldArgs& a, int blk) {
       c2 = fmaf(w0, __uint_as_float(bv[q] << 16), c2);
       c2 = fmaf(w1v, __uint_as_float(bv[q] & 0xffff0000u), c2);
     }
-    *reinterpret_cast<u32x4*>(w1 + e0) = o;
-    if (a.split) *reinterpret_cast<u32x4*>(w1 + a.d + e0) = lo;
+    if (a.W1) {
+      *reinterpret_cast<u32x4*>(w1 + e0) = o;
+      if (a.split) *reinterpret_cast<u32x4*>(w1 + a.d + e0) = lo;
+    }
   }
   c1 = a.split ? 0.f : wave_sum(c1);
   c2 = wave_sum(c2);
@@ -1099,8 +1102,11 @@ hipError_t ln_rows_launch(const LnRowsArgs& a, hipStream_t s) {
 //   W_mix1 h = rstd * (W_mix1 diag(gamma) Wc) a + W_mix1 beta,
 // one d_e x d_e and one d x d_e matrix built from the weights per call.
 // The centring removes the mean exactly, so neither product cancels a
-// large mean against the rest. Both take Wc^T as bf16 hi | lo (3 terms on
-// the bf16 kernel: hi hi + lo hi + hi lo, about float32 accuracy).
+// large mean against the rest. G takes Wc^T as bf16 hi | lo (3 terms on the
+// bf16 kernel: hi hi + lo hi + hi lo, about float32 accuracy); the other
+// takes W_mix1 as it is (bf16, exact) against (diag(gamma) Wc)^T as hi | lo
+// (2 terms, the same accuracy: gamma moves to the side that is split
+// anyway, and W_mix1 diag(gamma) is never formed).
 // Column sums of W (rows x cols, bf16) over blocks of 64 rows:
 // part[y * cols + c] = sum of W[r, c] over rows r of block y.
 __device__ __forceinline__ void col_part_block(const int32_t* header,
@@ -1150,10 +1156,12 @@ __global__ __launch_bounds__(256) void fold_prep_kernel(LnFoldArgs a,
   }
 }
 
-// T from W and the block sums above (added in block order per column).
+// T from W and the block sums above (added in block order per column);
+// with T2, also T2[c, r] = hi, T2[c, rows + r] = lo of gamma[r] (W[r, c] -
+// mean_r W[r, c]) (T2 is [cols x 2 rows]).
 __global__ __launch_bounds__(256) void center_split_t_kernel(
     const int32_t* header, const uint16_t* W, int rows, int cols,
-    const float* part, uint16_t* T) {
+    const float* part, uint16_t* T, const uint16_t* gamma, uint16_t* T2) {
   if (header[0] != 0) return;
   __shared__ float t[64][65];
   __shared__ float s_mean[64];
@@ -1190,6 +1198,14 @@ __global__ __launch_bounds__(256) void center_split_t_kernel(
       row[r] = hi;
       row[rows + r] = hi;
       row[2 * rows + r] = f2bf(v - hv);
+      if (T2) {
+        const float gv = v * bf2f(gamma[r]);
+        const uint16_t ghi = f2bf(gv);
+        uint16_t* row2 = T2 + static_cast<int64_t>(c) * 2 * rows;
+        row2[r] = ghi;
+        row2[rows + r] =
+            f2bf(gv - __uint_as_float(static_cast<uint32_t>(ghi) << 16));
+      }
     }
   }
 }
@@ -1250,12 +1266,14 @@ hipError_t center_split_t_launch(const int32_t* header, const uint16_t* W,
   if (rows <= 0 || cols <= 0) return hipSuccess;
   dim3 grid(ceil_div(cols, 64), ceil_div(rows, 64));
   col_part_kernel<<<grid, 256, 0, s>>>(header, W, rows, cols, mean);
-  center_split_t_kernel<<<grid, 256, 0, s>>>(header, W, rows, cols, mean, T);
+  center_split_t_kernel<<<grid, 256, 0, s>>>(header, W, rows, cols, mean, T,
+                                             nullptr, nullptr);
   return hipGetLastError();
 }
 
 hipError_t fold_prep_launch(const LnFoldArgs& fa, const uint16_t* W,
                             int rows, int cols, float* mean, uint16_t* T,
+                            const uint16_t* gamma, uint16_t* T2,
                             hipStream_t s) {
   if (fa.n <= 0 || rows <= 0 || cols <= 0) return hipErrorInvalidValue;
   const int nfold = ceil_div(fa.n, 4), cbx = ceil_div(cols, 64),
@@ -1263,7 +1281,8 @@ hipError_t fold_prep_launch(const LnFoldArgs& fa, const uint16_t* W,
   fold_prep_kernel<<<nfold + cbx * cby, 256, 0, s>>>(fa, W, rows, cols, mean,
                                                      nfold, cbx);
   center_split_t_kernel<<<dim3(cbx, cby), 256, 0, s>>>(fa.header, W, rows,
-                                                       cols, mean, T);
+                                                       cols, mean, T, gamma,
+                                                       T2);
   return hipGetLastError();
 }
 

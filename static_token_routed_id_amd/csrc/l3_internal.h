@@ -207,7 +207,7 @@ struct LnFoldArgs {
   const uint16_t* gamma;
   const uint16_t* beta;
   int n, d;
-  uint16_t* W1;     // [n x d] bf16
+  uint16_t* W1;     // [n x d] bf16, or NULL: c12 only
   float* c12;       // [n x 2]
   // split: W1 rows [n x 2d], the bf16 product at [0, d) and the bf16
   // rounding residual at [d, 2d); c1 = 0
@@ -306,9 +306,12 @@ hipError_t ln_fold_launch(const LnFoldArgs& a, hipStream_t s);
 // W[r, c] - mean_r W[r, c] (T is [cols x 3 rows]); mean is scratch of
 // cols * ceil(rows / 64) floats (column sums per block of 64 rows).
 // ln_fold_launch(fa) and center_split_t_launch(fa.header, W, ...) with the
-// fold and the column sums in one launch (they are independent).
+// fold and the column sums in one launch (they are independent); fa.W1 may
+// be NULL (c12 only). With T2, also T2[c, r] = hi, T2[c, rows + r] = lo of
+// gamma[r] (W[r, c] - mean_r W[r, c]) (T2 is [cols x 2 rows]).
 hipError_t fold_prep_launch(const LnFoldArgs& fa, const uint16_t* W,
                             int rows, int cols, float* mean, uint16_t* T,
+                            const uint16_t* gamma, uint16_t* T2,
                             hipStream_t s);
 hipError_t center_split_t_launch(const int32_t* header, const uint16_t* W,
                                  int rows, int cols, float* mean, uint16_t* T,
