@@ -997,6 +997,138 @@ hipError_t gemm_nt_256_splitk_pair_launch(const GemmArgs& a0, int max_a,
   return hipGetLastError();
 }
 
+// ------------------------------------------------ few rows (decode) ---
+// C = A B^T for at most 64 rows of A (bf16 operands, unit k strides, the
+// A1 / A2 and B1 / Bm switches at K1 as on the 256 x 256 kernel): the
+// weights B stream from HBM once, split over (N / 64 column blocks) x
+// nsplit K shares so that every CU holds a share. A workgroup's four waves
+// own 16 columns each and all the rows (MB blocks of 16) on the 16x16x32
+// MFMA, whose operand layout lets every lane read its 16 bytes of A and B
+// straight from memory (no LDS); a ring of R steps (32 k each) keeps the
+// loads R - 1 steps ahead of the multiplies. Shares write float32 partials
+// [share][M][N] that gemm_reduce_kernel adds in order; a single share
+// writes C.
+constexpr int kSkinnyRows = 64, kSkinnyCols = 64, kSkinnyK = 32;
+
+template <typename TC, int MB>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
+  if (g.header && g.header[0] != 0) return;
+  constexpr int R = MB == 4 ? 6 : 8;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, kg = (lane >> 4) * 8;
+  const int ntiles = g.N / kSkinnyCols;
+  const int nt = blockIdx.x % ntiles, kz = blockIdx.x / ntiles;
+  const int col = nt * kSkinnyCols + w * 16 + r;  // this lane's B row
+  const int kshare = g.K / g.nsplit, kbeg = kz * kshare;
+  const int steps = kshare / kSkinnyK;
+  const uint16_t* A1 = static_cast<const uint16_t*>(g.A1);
+  const uint16_t* A2 = static_cast<const uint16_t*>(g.A2);
+  const uint16_t* a1[MB];
+  const uint16_t* a2[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = min(mb * 16 + r, g.M - 1);  // rows past M: never stored
+    a1[mb] = A1 + static_cast<int64_t>(m) * g.a1_m + kg;
+    a2[mb] = A2 + static_cast<int64_t>(m) * g.a2_m + kg;
+  }
+  const uint16_t* b1 =
+      g.B1 ? static_cast<const uint16_t*>(g.B1) + col * g.b1_n + kg : nullptr;
+  const uint16_t* bm = static_cast<const uint16_t*>(g.Bm) + col * g.b_n + kg;
+  uint4 av[R][MB], bv[R];
+  auto load = [&](int k0, uint4 (&ad)[MB], uint4& bd) {
+    const bool first = k0 < g.K1;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      ad[mb] = *reinterpret_cast<const uint4*>(first ? a1[mb] + k0
+                                                     : a2[mb] + (k0 - g.K1));
+    bd = *reinterpret_cast<const uint4*>(
+        first && b1 ? b1 + k0 : bm + (!first && g.b2_rel ? k0 - g.K1 : k0));
+  };
+  floatx4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < R - 1; ++q)
+    if (q < steps) load(kbeg + q * kSkinnyK, av[q], bv[q]);
+  for (int base = 0; base < steps; base += R) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int t = base + q;
+      if (t >= steps) break;
+      const int tn = t + R - 1;
+      if (tn < steps)
+        load(kbeg + tn * kSkinnyK, av[(q + R - 1) % R], bv[(q + R - 1) % R]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = mfma_bf16(av[q][mb], bv[q], acc[mb]);
+    }
+  }
+  // element i of block mb: row mb*16 + 4*(lane >> 4) + i, column col
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mb * 16 + (lane >> 4) * 4 + i;
+      if (m >= g.M) continue;
+      if (g.nsplit > 1)
+        g.part[(static_cast<int64_t>(kz) * g.M + m) * g.N + col] = acc[mb][i];
+      else
+        st<TC>(static_cast<TC*>(g.C), static_cast<int64_t>(m) * g.c_m + col,
+               acc[mb][i]);
+    }
+}
+
+static bool gemm_skinny_ok(const GemmArgs& g) {
+  return g.M > 0 && g.M <= kSkinnyRows && g.N % kSkinnyCols == 0 &&
+         g.K % kSkinnyK == 0 && g.K1 % kSkinnyK == 0 && g.a1_k == 1 &&
+         g.a2_k == 1 && g.b_k == 1 && g.a1_m % 8 == 0 && g.a2_m % 8 == 0 &&
+         g.b_n % 8 == 0 && (!g.B1 || g.b1_n % 8 == 0) && !g.ln_stats_out &&
+         !g.ln_rows && !g.ln_quad_a;
+}
+
+// K shares: about two workgroups a CU (the column blocks times the
+// shares) but at most 8 shares (16 made the in-order sum of the partials
+// cost more than the extra workgroups saved: 23.4 against 22.0 us for
+// W_mix at 64 tokens), whole 32-wide steps in every share, the partials
+// within part_floats.
+static hipError_t gemm_skinny_launch(const GemmArgs& g0, int c_type,
+                                     hipStream_t s, float* part,
+                                     int64_t part_floats, int cus) {
+  GemmArgs g = g0;
+  const int ntiles = g.N / kSkinnyCols;
+  const int64_t mn = static_cast<int64_t>(g.M) * g.N;
+  int ns = std::max(1, std::min(8, (2 * cus + ntiles - 1) / ntiles));
+  while (ns > 1 && (g.K % (ns * kSkinnyK) != 0 || !part ||
+                    ns * mn > part_floats))
+    --ns;
+  g.nsplit = ns;
+  g.part = ns > 1 ? part : nullptr;
+  const int grid = ntiles * ns;
+  const bool f32 = ns > 1 || c_type != kBF16;
+#define L3_SKINNY(MB)                                          \
+  {                                                            \
+    if (f32)                                                   \
+      gemm_skinny_kernel<float, MB><<<grid, 256, 0, s>>>(g);   \
+    else                                                       \
+      gemm_skinny_kernel<uint16_t, MB><<<grid, 256, 0, s>>>(g); \
+  }
+  if (g.M <= 16)
+    L3_SKINNY(1)
+  else if (g.M <= 32)
+    L3_SKINNY(2)
+  else
+    L3_SKINNY(4)
+#undef L3_SKINNY
+  if (ns > 1) {
+    const int rgrid = reduce_grid(g);
+    if (c_type == kBF16)
+      gemm_reduce_kernel<uint16_t><<<rgrid, 256, 0, s>>>(g);
+    else
+      gemm_reduce_kernel<float><<<rgrid, 256, 0, s>>>(g);
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------- LayerNorm fold into W_mix ---
 // LayerNorm followed by a product, sum_k W[n, k] h[m, k] with
 // h = gamma * (u - mean) * rstd + beta, equals
@@ -1304,9 +1436,10 @@ bool gemm_nt_mfma_ok(const GemmArgs& g) {
          g.a2_m % 8 == 0 && g.b_n % 8 == 0;
 }
 
-// bf16 operands, by size: few output tiles (few rows, e.g. decode): the
-// generic kernel with K split over workgroups, so that the weights stream
-// through every CU; else 256 x 256 tiles where their shape rules allow
+// bf16 operands, by size: at most 64 rows (decode): the few-rows kernel
+// above; other shapes with few output tiles: K split over workgroups, so
+// that the weights stream through every CU; else 256 x 256 tiles where
+// their shape rules allow
 // (faster than 128 x 128 tiles even when they do not fill the GPU: at
 // 8192 x 1024 x 2048, 0.052 ms against 0.18); else 128 x 128 tiles.
 hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s,
@@ -1324,10 +1457,12 @@ hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s,
       static_cast<int64_t>(ceil_div(g.M, kTM)) * (g.N / kTN);
   const int64_t tiles128 =
       static_cast<int64_t>(ceil_div(g.M, kBM)) * (g.N / kBN);
+  if (gemm_skinny_ok(g))
+    return gemm_skinny_launch(g, c_type, s, part, part_floats, cus);
   if (tiles128 < cus && part) {
-    // few rows (decode): the weights stream through every CU on the bf16
-    // 256 x 256 kernel with K split (rows past M read as zero), else the
-    // generic kernel with K split
+    // few rows: the weights stream through every CU on the bf16 256 x 256
+    // kernel with K split (rows past M read as zero), else the generic
+    // kernel with K split
     if (gemm_nt_256_shape_ok(g) && !g.ln_stats_out && !g.ln_rows)
       return gemm_nt_256_splitk_launch(g, s, part, part_floats, 32, c_type);
     return gemm_launch(g, kBF16, kBF16, c_type, s, part, part_floats);
