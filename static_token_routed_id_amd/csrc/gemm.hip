@@ -835,6 +835,248 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_pair_kernel(GemmArgs g0,
     gemm256_job<float, false, false>(g1, blockIdx.x - n0);
 }
 
+// ------------------------------------- bf16 MFMA, 256 x 256, eight waves ---
+// The same tile, LDS layout and slice pipeline as the four-wave kernel
+// above, with eight waves (two a SIMD): wave (wm, wn), wm < 2, wn < 4, owns
+// rows wm*128.. and columns wn*64.. as 4 x 2 blocks of 32x32x16 MFMA
+// results (128 float accumulators a lane). With two waves on each SIMD one
+// wave's MFMAs run while the other waits for its LDS fragments, its slice
+// loads or the barrier; the LDS reads per slice grow by half (each A
+// fragment is read by four waves instead of two), within gfx950's LDS rate.
+// Each 16-wide step is 8 MFMAs; the next step's six fragments are read
+// during the first six, and the next slice (512 threads: four 16-byte
+// chunks of A and four of B a thread) is staged during the first two steps,
+// one LDS write or buffer load after each MFMA. Plain float32 or bf16 C,
+// optionally the LayerNorm fold (consumer side); no split K and no
+// producer-side statistics (those stay on the four-wave kernel).
+struct FragW8 {
+  u32x4 a[4], b[2];
+};
+
+template <bool READ, int Q0, int NQ>
+__device__ __forceinline__ void step_w8(floatx16 (&acc)[4][2],
+                                        const FragW8& FC, FragW8& FN,
+                                        const uint16_t* rd_a,
+                                        const uint16_t* rd_b, int rd_k,
+                                        u32x4 (&ra)[4], u32x4 (&rb)[4],
+                                        uint16_t* wr_a, uint16_t* wr_b,
+                                        const SliceSrc& src) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    acc[m >> 1][m & 1] = mfma32_bf16(FC.a[m >> 1], FC.b[m & 1],
+                                     acc[m >> 1][m & 1]);
+    if (READ && m < 4)
+      FN.a[m] = *reinterpret_cast<const u32x4*>(rd_a + m * 32 * kTL + rd_k);
+    else if (READ && m < 6)
+      FN.b[m - 4] =
+          *reinterpret_cast<const u32x4*>(rd_b + (m - 4) * 32 * kTL + rd_k);
+    if (m < 4 * NQ) {
+      const int q = Q0 + m / 4, op = m & 3;
+      if (op == 0)
+        *reinterpret_cast<u32x4*>(wr_a + q * 64 * kTL) = ra[q];
+      else if (op == 1)
+        *reinterpret_cast<u32x4*>(wr_b + q * 64 * kTL) = rb[q];
+      else if (op == 2)
+        ra[q] = __builtin_amdgcn_raw_buffer_load_b128(src.ra, src.va,
+                                                      q * src.qa + src.ka, 0);
+      else
+        rb[q] = __builtin_amdgcn_raw_buffer_load_b128(src.rb, src.vb,
+                                                      q * src.qb + src.kb, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <typename TC, bool FOLD>
+__global__ __launch_bounds__(512, 1) void gemm_nt_256w8_kernel(GemmArgs g) {
+  __shared__ __align__(16) uint16_t lds[2][2][kTM * kTL];
+  __shared__ __align__(16) float2 s_rs[kTM];
+  __shared__ __align__(16) float2 s_c[kTN];
+  if (g.header && g.header[0] != 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  const int mt = ceil_div(g.M, kTM), nt = g.N / kTN;
+  const int T = mt * nt;
+  const int bt = blockIdx.x;
+  int tile = bt;
+  if (T % kXcd == 0 && mt % kGroupM == 0)
+    tile = (bt % kXcd) * (T / kXcd) + bt / kXcd;
+  int m_tile, n_tile;
+  if (mt % kGroupM == 0) {
+    const int grp = tile / (kGroupM * nt), in = tile % (kGroupM * nt);
+    m_tile = grp * kGroupM + in % kGroupM;
+    n_tile = in / kGroupM;
+  } else {
+    m_tile = tile / nt;
+    n_tile = tile % nt;
+  }
+  const int m0 = m_tile * kTM, n0 = n_tile * kTN;
+  const int rows = min(kTM, g.M - m0);
+
+  // global -> register mapping: 8 lanes per 128-byte row slice, 64 rows per
+  // group, 4 groups per operand
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
+  const __amdgpu_buffer_rsrc_t rA1 = make_rsrc(
+      static_cast<const uint16_t*>(g.A1) + static_cast<int64_t>(m0) * g.a1_m,
+      static_cast<int64_t>(rows) * g.a1_m * 2);
+  const __amdgpu_buffer_rsrc_t rA2 = make_rsrc(
+      static_cast<const uint16_t*>(g.A2) + static_cast<int64_t>(m0) * g.a2_m,
+      static_cast<int64_t>(rows) * g.a2_m * 2);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(
+      static_cast<const uint16_t*>(g.Bm) + static_cast<int64_t>(n0) * g.b_n,
+      static_cast<int64_t>(kTN) * g.b_n * 2);
+  const bool has_b1 = g.B1 != nullptr;
+  const int64_t b1_n = has_b1 ? g.b1_n : g.b_n;
+  const __amdgpu_buffer_rsrc_t rB1 =
+      has_b1 ? make_rsrc(static_cast<const uint16_t*>(g.B1) +
+                             static_cast<int64_t>(n0) * b1_n,
+                         static_cast<int64_t>(kTN) * b1_n * 2)
+             : rB;
+  const int vA1 = static_cast<int>((lr * g.a1_m + lc) * 2);
+  const int vA2 = static_cast<int>((lr * g.a2_m + lc) * 2);
+  const int vB = static_cast<int>((lr * g.b_n + lc) * 2);
+  const int vB1 = static_cast<int>((lr * b1_n + lc) * 2);
+  const int qA1 = static_cast<int>(64 * g.a1_m * 2);
+  const int qA2 = static_cast<int>(64 * g.a2_m * 2);
+  const int qB = static_cast<int>(64 * g.b_n * 2);
+  const int qB1 = static_cast<int>(64 * b1_n * 2);
+  auto slice_src = [&](int k0) {
+    SliceSrc s;
+    const bool first = k0 < g.K1;
+    s.ra = first ? rA1 : rA2;
+    s.va = first ? vA1 : vA2;
+    s.qa = first ? qA1 : qA2;
+    s.ka = (first ? k0 : k0 - g.K1) * 2;
+    s.rb = first ? rB1 : rB;
+    s.vb = first ? vB1 : vB;
+    s.qb = first ? qB1 : qB;
+    s.kb = (first || !g.b2_rel ? k0 : k0 - g.K1) * 2;
+    return s;
+  };
+
+  float2 lnr = make_float2(0.f, 0.f), lnc = make_float2(0.f, 0.f);
+  if constexpr (FOLD) {
+    if (tid < kTM && m0 + tid < g.M)
+      lnr = reinterpret_cast<const float2*>(g.ln_rows)[m0 + tid];
+    if (tid < kTN) lnc = reinterpret_cast<const float2*>(g.ln_c12)[n0 + tid];
+  }
+
+  u32x4 ra[4], rb[4];
+  auto load_all = [&](const SliceSrc& s) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra[q] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, s.va, q * s.qa + s.ka,
+                                                    0);
+      rb[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, s.vb, q * s.qb + s.kb,
+                                                    0);
+    }
+  };
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+
+  const int nk = g.K / kTK;
+  const int r = lane & 31, kh = (lane >> 5) * 8;
+  const int aoff = (wm * 128 + r) * kTL + kh, boff = (wn * 64 + r) * kTL + kh;
+  const int woff = lr * kTL + lc;
+  load_all(slice_src(0));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    *reinterpret_cast<u32x4*>(&lds[0][0][woff + q * 64 * kTL]) = ra[q];
+    *reinterpret_cast<u32x4*>(&lds[0][1][woff + q * 64 * kTL]) = rb[q];
+  }
+  if constexpr (FOLD) {
+    if (tid < kTM) {
+      s_rs[tid] = lnr;
+      s_c[tid] = lnc;
+    }
+  }
+  load_all(slice_src(min(1, nk - 1) * kTK));
+  __syncthreads();
+  FragW8 F0, F1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    F0.a[i] = *reinterpret_cast<const u32x4*>(&lds[0][0][aoff + i * 32 * kTL]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    F0.b[j] = *reinterpret_cast<const u32x4*>(&lds[0][1][boff + j * 32 * kTL]);
+  auto kslice = [&](int it) __attribute__((always_inline)) {
+    const int buf = it & 1;
+    // slice it+1 (in registers) goes to the other buffer, slice it+2 is
+    // fetched (clamped: the tail refetches the last slice, never read)
+    const SliceSrc src = slice_src(min(it + 2, nk - 1) * kTK);
+    const uint16_t* rda = &lds[buf][0][aoff];
+    const uint16_t* rdb = &lds[buf][1][boff];
+    uint16_t* wra = &lds[buf ^ 1][0][woff];
+    uint16_t* wrb = &lds[buf ^ 1][1][woff];
+    step_w8<true, 0, 2>(acc, F0, F1, rda, rdb, 16, ra, rb, wra, wrb, src);
+    step_w8<true, 2, 2>(acc, F1, F0, rda, rdb, 32, ra, rb, wra, wrb, src);
+    step_w8<true, 0, 0>(acc, F0, F1, rda, rdb, 48, ra, rb, wra, wrb, src);
+    __syncthreads();
+    step_w8<true, 0, 0>(acc, F1, F0, &lds[buf ^ 1][0][aoff],
+                        &lds[buf ^ 1][1][boff], 0, ra, rb, wra, wrb, src);
+  };
+  const int nk1 = FOLD ? g.K1 / kTK : nk;
+  int it = 0;
+  for (; it < nk1; ++it) kslice(it);
+  if constexpr (FOLD) {
+    // acc = rstd * acc - mean * rstd * c1 + c2 (explicit AGPR moves, as in
+    // the four-wave kernel)
+    float2 c[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) c[j] = s_c[wn * 64 + j * 32 + r];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int eg = 0; eg < 4; ++eg) {
+        const float4* rs4 = reinterpret_cast<const float4*>(
+            &s_rs[wm * 128 + i * 32 + 8 * eg + (lane >> 5) * 4]);
+        const float4 r01 = rs4[0], r23 = rs4[1];
+        const float ra4[4] = {r01.x, r01.z, r23.x, r23.z};
+        const float rb4[4] = {r01.y, r01.w, r23.y, r23.w};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int ee = 0; ee < 4; ++ee) {
+            float v;
+            asm volatile("v_accvgpr_read_b32 %0, %1"
+                         : "=v"(v)
+                         : "a"(acc[i][j][4 * eg + ee]));
+            v = fmaf(ra4[ee], v, fmaf(rb4[ee], c[j].x, c[j].y));
+            float o;
+            asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(o) : "v"(v));
+            acc[i][j][4 * eg + ee] = o;
+          }
+        }
+      }
+  }
+  for (; it < nk; ++it) kslice(it);
+
+  const int h4 = (lane >> 5) * 4;
+  TC* C = static_cast<TC*>(g.C);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int gm = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + h4 + (e & 3);
+      if (gm >= g.M) continue;
+      TC* crow = C + static_cast<int64_t>(gm) * g.c_m + n0 + wn * 64 + r;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if constexpr (sizeof(TC) == 4)
+          __builtin_nontemporal_store(acc[i][j][e],
+                                      reinterpret_cast<float*>(crow) + j * 32);
+        else
+          __builtin_nontemporal_store(
+              f2bf(acc[i][j][e]), reinterpret_cast<uint16_t*>(crow) + j * 32);
+      }
+    }
+  }
+}
+
 // Shape rules of the 256 x 256 kernel; gemm_nt_256_ok adds M >= 1024 (below
 // that the launcher prefers other tilings, or the split-K form for few rows).
 static bool gemm_nt_256_shape_ok(const GemmArgs& g) {
@@ -1474,6 +1716,8 @@ hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s,
       gemm_nt_256_kernel<uint16_t, true><<<grid, 256, 0, s>>>(g);
     else if (c_type == kBF16)
       gemm_nt_256_kernel<uint16_t, false><<<grid, 256, 0, s>>>(g);
+    else if (g.ln_rows && g.nsplit == 1 && !g.ln_stats_out)
+      gemm_nt_256w8_kernel<float, true><<<grid, 512, 0, s>>>(g);
     else if (g.ln_rows)
       gemm_nt_256_kernel<float, true><<<grid, 256, 0, s>>>(g);
     else
