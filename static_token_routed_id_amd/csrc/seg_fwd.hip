@@ -32,8 +32,14 @@ __global__ __launch_bounds__(256, 2) void seg_fwd_kernel(SegFwdArgs a) {
   if (a.header[0] != 0) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n_items = a.header[a.count_slot];
-  for (int item = blockIdx.x * 4 + w; item < n_items;
-       item += gridDim.x * 4)
+  const int G = gridDim.x;
+  // With fewer items than wavefronts (small batches) the items go to the
+  // first wave of every workgroup before the second, so that they spread
+  // over all CUs; otherwise consecutive items share a workgroup. Either
+  // order visits every item once.
+  const bool spread = n_items < G * 4;
+  for (int item = spread ? blockIdx.x + w * G : blockIdx.x * 4 + w;
+       item < n_items; item += G * 4)
     wave_item<BF16, EPL, P32>(a, item, lane, s_p[w], s_ml[w]);
 }
 
