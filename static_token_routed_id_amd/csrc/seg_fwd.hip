@@ -54,13 +54,19 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(CombineArgs a) {
   const int pos = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pos >= a.B) return;
   const int S = a.header[1];
+  // The token's segment, the last s with seg_tok_start[s] <= pos (starts
+  // ascend strictly), by a 64-ary search: each round the wave's lanes test
+  // 64 evenly spaced candidates in [lo, hi] at once and keep the span after
+  // the last one that passes (lane 0's candidate lo always does), so up to
+  // 64 segments take one round of loads and 65536 take three.
   int lo = 0, hi = S - 1;
   while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.seg_tok_start[mid] <= pos)
-      lo = mid;
-    else
-      hi = mid - 1;
+    const int step = (hi - lo + 64) / 64;
+    const int c = lo + lane * step;
+    const bool ok = c <= hi && a.seg_tok_start[c] <= pos;
+    const int k = __popcll(__ballot(ok));
+    lo += (k - 1) * step;
+    hi = min(hi, lo + step - 1);
   }
   const int n_rows = a.seg_n[lo];
   if (a.group_min_rows > 0 && n_rows >= a.group_min_rows) return;
