@@ -883,19 +883,21 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     mx.N = d.d;
     mx.K = 2 * d.d;
     mx.header = pd.header;
-    // Inference on bf16 with an MFMA GEMM: u is written as bf16. With both
-    // projections on 256 x 256 tiles, LayerNorm is folded into W_mix: the
+    // Inference on bf16 with an MFMA GEMM. With both projections on 256 x
+    // 256 tiles, LayerNorm is folded into W_mix: u is written as bf16, the
     // W_up epilogue writes per-row partial statistics, gamma and beta are
     // folded into a bf16 copy of W_mix's first d columns, and W_mix reads u
-    // itself (h is never written). Otherwise ln_apply normalises each row
-    // (statistics over the row in registers). Training and float32 keep u
-    // in float32 for the saved state.
-    const bool u_bf16 = !save && d.dtype == L3_BF16 && gemm_nt_mfma_ok(up);
+    // itself (h is never written). Otherwise (small batches) u is written
+    // in float32 and the row kernel normalises it, as for training (no
+    // centred copy of W_up is needed: float32 u keeps its spread through
+    // the mean's cancellation); training and float32 keep u in float32
+    // for the saved state.
+    const bool mfma_up = !save && d.dtype == L3_BF16 && gemm_nt_mfma_ok(up);
     const int64_t fold_w1 = static_cast<int64_t>(d.d) * d.d * 2;
     const int64_t fold_c = static_cast<int64_t>(d.d) * 8;
     const int64_t fold_st = B * (d.d / 256) * 8;
     const int64_t fold_rows = B * 8;
-    const bool fold_ok = u_bf16 && !f.gpart && d.d % 256 == 0 &&
+    const bool fold_ok = mfma_up && !f.gpart && d.d % 256 == 0 &&
                          gemm_nt_256_ok(up) && gemm_nt_256_ok(mx) &&
                          fold_w1 + fold_c + fold_st + fold_rows <= B * d.d * 2;
     // Large batches go one step further: W_up itself is folded through
@@ -918,6 +920,8 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
                          o_part + (int64_t(16) << 20) <= B * DD * 4 &&
                          q_c + q_st + B * 8 <= B * DD * 2;
     const bool fold = fold_ok && !fuse_up;
+    // bf16 u only where it feeds the LayerNorm fold
+    const bool u_bf16 = fold;
     // Where u is stored as bf16, it is formed from W_up with its columns
     // centred over the d outputs (as bf16 hi | lo over K = 2 d_e, the
     // aggregate read for both halves): u - mean(u) = Wc a exactly, and
@@ -1113,6 +1117,8 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       StageTimer t(plan, ST_UP, s);
       if (u_bf16) {
         e = gemm_nt_mfma_launch(up, kBF16, s, f.gpart, f.gpart_floats);
+      } else if (mfma_up) {
+        e = gemm_nt_mfma_launch(up, kF32, s, f.gpart, f.gpart_floats);
       } else if (u_split) {
         e = split_bf16_launch(pd.header, sv.a32, B * d.d_e, f.a_hi, f.a_lo,
                               s);
@@ -1128,20 +1134,6 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       e = ln_rows_launch(lr, s);
     }
     if (e != hipSuccess) return L3_ERR_HIP;
-    if (u_bf16 && !fold && !fuse_up) {
-      LnApplyArgs la;
-      la.header = pd.header;
-      la.U = reinterpret_cast<const uint16_t*>(f.U);
-      la.gamma = static_cast<const uint16_t*>(gamma);
-      la.beta = static_cast<const uint16_t*>(beta);
-      la.B = static_cast<int>(B);
-      la.d = d.d;
-      la.eps = d.ln_eps;
-      la.h = static_cast<uint16_t*>(f.h_act);
-      StageTimer t(plan, ST_LN, s);
-      e = ln_apply_launch(la, s);
-    }
-    if (e != hipSuccess) return L3_ERR_HIP;
     LnArgs ln;
     ln.header = pd.header;
     ln.U = f.U;
@@ -1154,7 +1146,7 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     ln.h_save = sv.h32;
     ln.uhat_save = sv.uhat;
     ln.rstd_save = sv.rstd;
-    if (!u_bf16) {
+    if (!u_bf16 && !fuse_up) {  // (with the W_up fold u is not formed)
       StageTimer t(plan, ST_LN, s);
       e = ln_launch(ln, d.dtype, s);
     }

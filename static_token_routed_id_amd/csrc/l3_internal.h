@@ -228,17 +228,6 @@ struct LnArgs {
   float* rstd_save;
 };
 
-// LayerNorm of bf16 rows (statistics from the row itself), h in bf16.
-struct LnApplyArgs {
-  const int32_t* header;
-  const uint16_t* U;       // [B x d] bf16
-  const uint16_t* gamma;
-  const uint16_t* beta;
-  int B, d;
-  float eps;
-  uint16_t* h;             // [B x d] bf16
-};
-
 enum ElemType { kF32 = L3_F32, kBF16 = L3_BF16 };
 
 // ---- launchers (return the first HIP error) -------------------------------
@@ -324,7 +313,6 @@ hipError_t center_split_launch(const int32_t* header, const uint16_t* W,
                                hipStream_t s);
 hipError_t gemm_nt_256_quad_launch(const GemmArgs& g, hipStream_t s);
 hipError_t ln_rows_launch(const LnRowsArgs& a, hipStream_t s);
-hipError_t ln_apply_launch(const LnApplyArgs& a, hipStream_t s);
 hipError_t ln_launch(const LnArgs& a, int dtype, hipStream_t s);
 
 struct BwdArgs {

@@ -67,8 +67,8 @@ def test_prefill_bf16_output_bf16():
 @pytest.mark.parametrize("ln_perturb", [False, True])
 def test_decode_bf16(training, ln_perturb):
     """64 tokens: inference runs the wave items with fp16 softmax weights,
-    the row-chunk combine, the split-K W_up on centred weights and the
-    row LayerNorm (ln_apply); training the saving forward."""
+    the row-chunk combine, the split-K W_up to float32 u and the row
+    LayerNorm with the row in registers; training the saving forward."""
     w = gu.workload("decode_bf16", ln_perturb)
     res = gu.run(w, training=training, nan_fill=True)
     _check(w, res, gu.oracle_forward(w))
@@ -207,12 +207,12 @@ def test_empty_batch():
 
 def test_u_far_from_zero_mean():
     """LayerNorm input whose mean is tens of times its spread (every row of
-    W_up shifted by one common vector). Where u is stored as bf16 it is
-    formed from W_up with its columns centred, so its rounding follows the
-    spread of u, not its mean: both the folded normalisation (8192 tokens,
-    per-tile sums, the mean term folded into W_mix) and the row
-    normalisation (the same first 64 tokens as a batch of their own) meet
-    the bf16 bound against the oracle."""
+    W_up shifted by one common vector). Where u is stored as bf16 (the
+    folded normalisation: 8192 tokens, per-tile sums, the mean term folded
+    into W_mix) it is formed from W_up with its columns centred, so its
+    rounding follows the spread of u, not its mean; the row normalisation
+    (the same first 64 tokens as a batch of their own) keeps u in float32.
+    Both meet the bf16 bound against the oracle."""
     w = wl.with_u_offset(gu.workload("prefill_bf16", True), 50.0)
     full = gu.run(w, nan_fill=True)
     rng = np.random.default_rng(5)
