@@ -835,43 +835,62 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_256_pair_kernel(GemmArgs g0,
     gemm256_job<float, false, false>(g1, blockIdx.x - n0);
 }
 
-// ------------------------------------- bf16 MFMA, 256 x 256, eight waves ---
-// The same tile, LDS layout and slice pipeline as the four-wave kernel
-// above, with eight waves (two a SIMD): wave (wm, wn), wm < 2, wn < 4, owns
-// rows wm*128.. and columns wn*64.. as 4 x 2 blocks of 32x32x16 MFMA
-// results (128 float accumulators a lane). With two waves on each SIMD one
-// wave's MFMAs run while the other waits for its LDS fragments, its slice
-// loads or the barrier; the LDS reads per slice grow by half (each A
-// fragment is read by four waves instead of two), within gfx950's LDS rate.
-// Each 16-wide step is 8 MFMAs; the next step's six fragments are read
-// during the first six, and the next slice (512 threads: four 16-byte
-// chunks of A and four of B a thread) is staged during the first two steps,
-// one LDS write or buffer load after each MFMA. Plain float32 or bf16 C,
-// optionally the LayerNorm fold (consumer side); no split K and no
-// producer-side statistics (those stay on the four-wave kernel).
+// ------------------------------- bf16 MFMA, 256 (or 128) x 256, eight waves ---
+// The same slice pipeline and LDS layout as the four-wave kernel above,
+// with eight waves (two a SIMD): wave (wm, wn), wm < 2, wn < 4, owns rows
+// wm*32*MI.. and columns wn*64.. as MI x 2 blocks of 32x32x16 MFMA results
+// (32 MI float accumulators a lane). MI = 4 is a 256 x 256 tile; MI = 2 a
+// 128 x 256 tile, for products with too few 256 x 256 tiles to fill the
+// GPU. With two waves on each SIMD one wave's MFMAs run while the other
+// waits for its LDS fragments or the barrier; the LDS reads per slice grow
+// by half (each A fragment is read by four waves instead of two), within
+// gfx950's LDS rate. Each 16-wide step is 2 MI MFMAs; the next step's
+// fragments are read during the first MI + 2 of them, and the next slice
+// (512 threads: 16-byte chunks of 64-row groups, MI of A and four of B) is
+// staged one LDS write or buffer load after each MFMA over the first steps
+// (per A group: write A, write B, reload A, reload B; then the remaining B
+// groups: write, reload). Plain float32 or bf16 C, optionally the LayerNorm
+// fold (consumer side); no split K and no producer-side statistics (those
+// stay on the four-wave kernel).
+template <int MI>
 struct FragW8 {
-  u32x4 a[4], b[2];
+  u32x4 a[MI], b[2];
 };
 
-template <bool READ, int Q0, int NQ>
-__device__ __forceinline__ void step_w8(floatx16 (&acc)[4][2],
-                                        const FragW8& FC, FragW8& FN,
+// The t-th staging operation of a slice: (row group q, kind): 0 write A,
+// 1 write B, 2 reload A, 3 reload B.
+template <int MI>
+__device__ __forceinline__ constexpr int w8_nops() {
+  return 4 * MI + 2 * (4 - MI);
+}
+
+template <int MI, bool READ, int T0>
+__device__ __forceinline__ void step_w8(floatx16 (&acc)[MI][2],
+                                        const FragW8<MI>& FC, FragW8<MI>& FN,
                                         const uint16_t* rd_a,
                                         const uint16_t* rd_b, int rd_k,
-                                        u32x4 (&ra)[4], u32x4 (&rb)[4],
+                                        u32x4 (&ra)[MI], u32x4 (&rb)[4],
                                         uint16_t* wr_a, uint16_t* wr_b,
                                         const SliceSrc& src) {
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < 2 * MI; ++m) {
     acc[m >> 1][m & 1] = mfma32_bf16(FC.a[m >> 1], FC.b[m & 1],
                                      acc[m >> 1][m & 1]);
-    if (READ && m < 4)
+    if (READ && m < MI)
       FN.a[m] = *reinterpret_cast<const u32x4*>(rd_a + m * 32 * kTL + rd_k);
-    else if (READ && m < 6)
-      FN.b[m - 4] =
-          *reinterpret_cast<const u32x4*>(rd_b + (m - 4) * 32 * kTL + rd_k);
-    if (m < 4 * NQ) {
-      const int q = Q0 + m / 4, op = m & 3;
+    else if (READ && m < MI + 2)
+      FN.b[m - MI] =
+          *reinterpret_cast<const u32x4*>(rd_b + (m - MI) * 32 * kTL + rd_k);
+    const int t = T0 + m;
+    if (t < w8_nops<MI>()) {
+      int q, op;
+      if (t < 4 * MI) {
+        q = t / 4;
+        op = t & 3;
+      } else {
+        q = MI + (t - 4 * MI) / 2;
+        op = ((t - 4 * MI) & 1) ? 3 : 1;
+      }
       if (op == 0)
         *reinterpret_cast<u32x4*>(wr_a + q * 64 * kTL) = ra[q];
       else if (op == 1)
@@ -887,15 +906,16 @@ __device__ __forceinline__ void step_w8(floatx16 (&acc)[4][2],
   }
 }
 
-template <typename TC, bool FOLD>
+template <typename TC, bool FOLD, int MI>
 __global__ __launch_bounds__(512, 1) void gemm_nt_256w8_kernel(GemmArgs g) {
+  constexpr int TM = 64 * MI;  // tile rows
   __shared__ __align__(16) uint16_t lds[2][2][kTM * kTL];
-  __shared__ __align__(16) float2 s_rs[kTM];
+  __shared__ __align__(16) float2 s_rs[TM];
   __shared__ __align__(16) float2 s_c[kTN];
   if (g.header && g.header[0] != 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w & 1, wn = w >> 1;
-  const int mt = ceil_div(g.M, kTM), nt = g.N / kTN;
+  const int mt = ceil_div(g.M, TM), nt = g.N / kTN;
   const int T = mt * nt;
   const int bt = blockIdx.x;
   int tile = bt;
@@ -910,11 +930,11 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_256w8_kernel(GemmArgs g) {
     m_tile = tile / nt;
     n_tile = tile % nt;
   }
-  const int m0 = m_tile * kTM, n0 = n_tile * kTN;
-  const int rows = min(kTM, g.M - m0);
+  const int m0 = m_tile * TM, n0 = n_tile * kTN;
+  const int rows = min(TM, g.M - m0);
 
   // global -> register mapping: 8 lanes per 128-byte row slice, 64 rows per
-  // group, 4 groups per operand
+  // group; MI groups of A, 4 of B
   const int lr = tid >> 3, lc = (tid & 7) * 8;
   const __amdgpu_buffer_rsrc_t rA1 = make_rsrc(
       static_cast<const uint16_t*>(g.A1) + static_cast<int64_t>(m0) * g.a1_m,
@@ -956,53 +976,55 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_256w8_kernel(GemmArgs g) {
 
   float2 lnr = make_float2(0.f, 0.f), lnc = make_float2(0.f, 0.f);
   if constexpr (FOLD) {
-    if (tid < kTM && m0 + tid < g.M)
+    if (tid < TM && m0 + tid < g.M)
       lnr = reinterpret_cast<const float2*>(g.ln_rows)[m0 + tid];
     if (tid < kTN) lnc = reinterpret_cast<const float2*>(g.ln_c12)[n0 + tid];
   }
 
-  u32x4 ra[4], rb[4];
+  u32x4 ra[MI], rb[4];
   auto load_all = [&](const SliceSrc& s) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < MI; ++q)
       ra[q] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, s.va, q * s.qa + s.ka,
                                                     0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
       rb[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, s.vb, q * s.qb + s.kb,
                                                     0);
-    }
   };
 
-  floatx16 acc[4][2];
+  floatx16 acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
 
   const int nk = g.K / kTK;
   const int r = lane & 31, kh = (lane >> 5) * 8;
-  const int aoff = (wm * 128 + r) * kTL + kh, boff = (wn * 64 + r) * kTL + kh;
+  const int aoff = (wm * 32 * MI + r) * kTL + kh,
+            boff = (wn * 64 + r) * kTL + kh;
   const int woff = lr * kTL + lc;
   load_all(slice_src(0));
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < MI; ++q)
     *reinterpret_cast<u32x4*>(&lds[0][0][woff + q * 64 * kTL]) = ra[q];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
     *reinterpret_cast<u32x4*>(&lds[0][1][woff + q * 64 * kTL]) = rb[q];
-  }
   if constexpr (FOLD) {
-    if (tid < kTM) {
-      s_rs[tid] = lnr;
-      s_c[tid] = lnc;
-    }
+    if (tid < TM) s_rs[tid] = lnr;
+    if (tid < kTN) s_c[tid] = lnc;
   }
   load_all(slice_src(min(1, nk - 1) * kTK));
   __syncthreads();
-  FragW8 F0, F1;
+  FragW8<MI> F0, F1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
     F0.a[i] = *reinterpret_cast<const u32x4*>(&lds[0][0][aoff + i * 32 * kTL]);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     F0.b[j] = *reinterpret_cast<const u32x4*>(&lds[0][1][boff + j * 32 * kTL]);
+  constexpr int kOps = 2 * MI;  // staging operations a step
   auto kslice = [&](int it) __attribute__((always_inline)) {
     const int buf = it & 1;
     // slice it+1 (in registers) goes to the other buffer, slice it+2 is
@@ -1012,13 +1034,17 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_256w8_kernel(GemmArgs g) {
     const uint16_t* rdb = &lds[buf][1][boff];
     uint16_t* wra = &lds[buf ^ 1][0][woff];
     uint16_t* wrb = &lds[buf ^ 1][1][woff];
-    step_w8<true, 0, 2>(acc, F0, F1, rda, rdb, 16, ra, rb, wra, wrb, src);
-    step_w8<true, 2, 2>(acc, F1, F0, rda, rdb, 32, ra, rb, wra, wrb, src);
-    step_w8<true, 0, 0>(acc, F0, F1, rda, rdb, 48, ra, rb, wra, wrb, src);
+    step_w8<MI, true, 0>(acc, F0, F1, rda, rdb, 16, ra, rb, wra, wrb, src);
+    step_w8<MI, true, kOps>(acc, F1, F0, rda, rdb, 32, ra, rb, wra, wrb,
+                            src);
+    step_w8<MI, true, 2 * kOps>(acc, F0, F1, rda, rdb, 48, ra, rb, wra, wrb,
+                                src);
     __syncthreads();
-    step_w8<true, 0, 0>(acc, F1, F0, &lds[buf ^ 1][0][aoff],
-                        &lds[buf ^ 1][1][boff], 0, ra, rb, wra, wrb, src);
+    step_w8<MI, true, 64>(acc, F1, F0, &lds[buf ^ 1][0][aoff],
+                          &lds[buf ^ 1][1][boff], 0, ra, rb, wra, wrb, src);
   };
+  static_assert(w8_nops<MI>() <= 3 * 2 * MI,
+                "a slice's staging fits in its first three steps");
   const int nk1 = FOLD ? g.K1 / kTK : nk;
   int it = 0;
   for (; it < nk1; ++it) kslice(it);
@@ -1029,11 +1055,11 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_256w8_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) c[j] = s_c[wn * 64 + j * 32 + r];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int eg = 0; eg < 4; ++eg) {
         const float4* rs4 = reinterpret_cast<const float4*>(
-            &s_rs[wm * 128 + i * 32 + 8 * eg + (lane >> 5) * 4]);
+            &s_rs[wm * 32 * MI + i * 32 + 8 * eg + (lane >> 5) * 4]);
         const float4 r01 = rs4[0], r23 = rs4[1];
         const float ra4[4] = {r01.x, r01.z, r23.x, r23.z};
         const float rb4[4] = {r01.y, r01.w, r23.y, r23.w};
@@ -1058,10 +1084,10 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_256w8_kernel(GemmArgs g) {
   const int h4 = (lane >> 5) * 4;
   TC* C = static_cast<TC*>(g.C);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int gm = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + h4 + (e & 3);
+      const int gm = m0 + wm * 32 * MI + i * 32 + 8 * (e >> 2) + h4 + (e & 3);
       if (gm >= g.M) continue;
       TC* crow = C + static_cast<int64_t>(gm) * g.c_m + n0 + wn * 64 + r;
 #pragma unroll
@@ -1647,8 +1673,14 @@ hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s,
       gemm_nt_256_kernel<uint16_t, true><<<grid, 256, 0, s>>>(g);
     else if (c_type == kBF16)
       gemm_nt_256_kernel<uint16_t, false><<<grid, 256, 0, s>>>(g);
+    else if (g.ln_rows && g.nsplit == 1 && !g.ln_stats_out && grid < cus)
+      // too few 256-row tiles to fill the GPU: 128-row tiles
+      gemm_nt_256w8_kernel<float, true, 2><<<
+          static_cast<int>(static_cast<int64_t>(ceil_div(g.M, 128)) *
+                           (g.N / kTN)),
+          512, 0, s>>>(g);
     else if (g.ln_rows && g.nsplit == 1 && !g.ln_stats_out)
-      gemm_nt_256w8_kernel<float, true><<<grid, 512, 0, s>>>(g);
+      gemm_nt_256w8_kernel<float, true, 4><<<grid, 512, 0, s>>>(g);
     else if (g.ln_rows)
       gemm_nt_256_kernel<float, true><<<grid, 256, 0, s>>>(g);
     else
