@@ -1113,12 +1113,26 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
     u2.b2_rel = 1;
     u2.K = 2 * d.d_e;
     const bool u_split = save && f.a_hi && gemm_nt_256_ok(u2);
+    LnArgs ln;
+    ln.header = pd.header;
+    ln.U = f.U;
+    ln.gamma = gamma;
+    ln.beta = beta;
+    ln.B = static_cast<int>(B);
+    ln.d = d.d;
+    ln.eps = d.ln_eps;
+    ln.h = f.h_act;
+    ln.h_save = sv.h32;
+    ln.uhat_save = sv.uhat;
+    ln.rstd_save = sv.rstd;
     if (!fuse_up) {  // (else u is not formed)
       StageTimer t(plan, ST_UP, s);
       if (u_bf16) {
         e = gemm_nt_mfma_launch(up, kBF16, s, f.gpart, f.gpart_floats);
       } else if (mfma_up) {
-        e = gemm_nt_mfma_launch(up, kF32, s, f.gpart, f.gpart_floats);
+        // float32 u and its LayerNorm (at few rows one kernel sums the K
+        // shares and normalises)
+        e = gemm_ln_launch(up, ln, d.dtype, s, f.gpart, f.gpart_floats);
       } else if (u_split) {
         e = split_bf16_launch(pd.header, sv.a32, B * d.d_e, f.a_hi, f.a_lo,
                               s);
@@ -1134,19 +1148,9 @@ l3_status l3_forward(l3_plan_t plan, const void* x, const void* K,
       e = ln_rows_launch(lr, s);
     }
     if (e != hipSuccess) return L3_ERR_HIP;
-    LnArgs ln;
-    ln.header = pd.header;
-    ln.U = f.U;
-    ln.gamma = gamma;
-    ln.beta = beta;
-    ln.B = static_cast<int>(B);
-    ln.d = d.d;
-    ln.eps = d.ln_eps;
-    ln.h = f.h_act;
-    ln.h_save = sv.h32;
-    ln.uhat_save = sv.uhat;
-    ln.rstd_save = sv.rstd;
-    if (!u_bf16 && !fuse_up) {  // (with the W_up fold u is not formed)
+    // (with the W_up fold u is not formed; float32 inference u was
+    // normalised with its product)
+    if (!u_bf16 && !fuse_up && !mfma_up) {
       StageTimer t(plan, ST_LN, s);
       e = ln_launch(ln, d.dtype, s);
     }

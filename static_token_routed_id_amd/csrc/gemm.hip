@@ -1290,16 +1290,42 @@ static bool gemm_skinny_ok(const GemmArgs& g) {
 // cost more than the extra workgroups saved: 23.4 against 22.0 us for
 // W_mix at 64 tokens), whole 32-wide steps in every share, the partials
 // within part_floats.
-static hipError_t gemm_skinny_launch(const GemmArgs& g0, int c_type,
-                                     hipStream_t s, float* part,
-                                     int64_t part_floats, int cus) {
-  GemmArgs g = g0;
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_ln_rows_kernel(LnArgs a,
+                                                           const float* part,
+                                                           int ns, int64_t mn);
+
+// K shares of the few-rows kernel for g.
+static int skinny_shares(const GemmArgs& g, const float* part,
+                         int64_t part_floats, int cus) {
   const int ntiles = g.N / kSkinnyCols;
   const int64_t mn = static_cast<int64_t>(g.M) * g.N;
   int ns = std::max(1, std::min(8, (2 * cus + ntiles - 1) / ntiles));
   while (ns > 1 && (g.K % (ns * kSkinnyK) != 0 || !part ||
                     ns * mn > part_floats))
     --ns;
+  return ns;
+}
+
+// Whether the shares' sums can go straight into the row LayerNorm: K split,
+// u = A B^T is the LayerNorm input with d = N a multiple of 1024 up to 4096,
+// no saved copies.
+static bool skinny_ln_ok(const GemmArgs& g, const LnArgs& ln, int ns) {
+  return ns > 1 && ln.d == g.N && ln.d % 1024 == 0 && ln.d <= 4096 &&
+         !ln.h_save;
+}
+
+// With ln (skinny_ln_ok must hold), the shares' sums go into the row
+// LayerNorm (reduce_ln_rows_kernel) instead of the reduce kernel: h in
+// place of u.
+static hipError_t gemm_skinny_launch(const GemmArgs& g0, int c_type,
+                                     hipStream_t s, float* part,
+                                     int64_t part_floats, int cus,
+                                     const LnArgs* ln = nullptr) {
+  GemmArgs g = g0;
+  const int ntiles = g.N / kSkinnyCols;
+  const int64_t mn = static_cast<int64_t>(g.M) * g.N;
+  const int ns = skinny_shares(g, part, part_floats, cus);
   g.nsplit = ns;
   g.part = ns > 1 ? part : nullptr;
   const int grid = ntiles * ns;
@@ -1318,7 +1344,12 @@ static hipError_t gemm_skinny_launch(const GemmArgs& g0, int c_type,
   else
     L3_SKINNY(4)
 #undef L3_SKINNY
-  if (ns > 1) {
+  if (ln) {
+    if (c_type == kBF16)
+      reduce_ln_rows_kernel<uint16_t><<<g.M, 256, 0, s>>>(*ln, part, ns, mn);
+    else
+      reduce_ln_rows_kernel<float><<<g.M, 256, 0, s>>>(*ln, part, ns, mn);
+  } else if (ns > 1) {
     const int rgrid = reduce_grid(g);
     if (c_type == kBF16)
       gemm_reduce_kernel<uint16_t><<<rgrid, 256, 0, s>>>(g);
@@ -1805,6 +1836,108 @@ hipError_t ln_launch(const LnArgs& a, int dtype, hipStream_t s) {
   else
     layernorm_rows_kernel<float><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
+}
+
+// LayerNorm of rows whose input is the in-order sum of ns split-K partials
+// (part[z * mn + row * d + col]): one workgroup a row, wave w holding
+// columns w*d/4 .. as float4s of 256-column chunks (every share's loads in
+// flight together), the row's sum and sum of squared deviations met in LDS
+// from the four waves, then h. The shares are added in share order.
+constexpr int kRedLnShares = 8;
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_ln_rows_kernel(LnArgs a,
+                                                           const float* part,
+                                                           int ns,
+                                                           int64_t mn) {
+  if (a.header[0] != 0) return;
+  __shared__ float s_red[2][4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = blockIdx.x;
+  const int ncw = a.d >> 10;  // 256-column chunks a wave, 1 .. 4
+  const int64_t base = static_cast<int64_t>(row) * a.d;
+  const int col0 = w * (a.d >> 2) + lane * 4;
+  // every load is issued unconditionally (shares past ns and chunks past
+  // the row re-read share 0 / chunk 0, inside the buffer) so that they are
+  // all in flight together; only the sums are predicated
+  float4 v[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int cc = c < ncw ? c : 0;
+    float4 q[kRedLnShares];
+#pragma unroll
+    for (int z = 0; z < kRedLnShares; ++z) {
+      const int zz = z < ns ? z : 0;
+      q[z] = *reinterpret_cast<const float4*>(part + zz * mn + base + col0 +
+                                              cc * 256);
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int z = 0; z < kRedLnShares; ++z)
+      if (z < ns) {
+        acc.x += q[z].x;
+        acc.y += q[z].y;
+        acc.z += q[z].z;
+        acc.w += q[z].w;
+      }
+    v[c] = c < ncw ? acc : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float sm = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (c < ncw) sm += (v[c].x + v[c].y) + (v[c].z + v[c].w);
+  sm = wave_sum(sm);
+  if (lane == 0) s_red[0][w] = sm;
+  __syncthreads();
+  const float mean =
+      ((s_red[0][0] + s_red[0][1]) + (s_red[0][2] + s_red[0][3])) / a.d;
+  float q = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (c < ncw) {
+      const float c0 = v[c].x - mean, c1 = v[c].y - mean, c2 = v[c].z - mean,
+                  c3 = v[c].w - mean;
+      q += (c0 * c0 + c1 * c1) + (c2 * c2 + c3 * c3);
+    }
+  q = wave_sum(q);
+  if (lane == 0) s_red[1][w] = q;
+  __syncthreads();
+  const float var =
+      ((s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3])) / a.d;
+  const float rstd = 1.0f / sqrtf(var + a.eps);
+  const T* gamma = static_cast<const T*>(a.gamma);
+  const T* beta = static_cast<const T*>(a.beta);
+  T* h = static_cast<T*>(a.h);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (c >= ncw) continue;
+    const int e = col0 + c * 256;
+    const float vv[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float uh = (vv[k] - mean) * rstd;
+      st<T>(h, base + e + k, ld<T>(gamma, e + k) * uh + ld<T>(beta, e + k));
+    }
+  }
+}
+
+// u = A B^T in float32, then LayerNorm of each row of u into ln.h (ln.U =
+// the GEMM's C). Few rows with K split: the shares' sum and the LayerNorm
+// in one kernel; otherwise the GEMM and the row pass.
+hipError_t gemm_ln_launch(const GemmArgs& g, const LnArgs& ln, int dtype,
+                          hipStream_t s, float* part, int64_t part_floats) {
+  if (g.M <= 0) return hipSuccess;
+  if (gemm_skinny_ok(g)) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                              dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    if (skinny_ln_ok(g, ln, skinny_shares(g, part, part_floats, cus)))
+      return gemm_skinny_launch(g, dtype, s, part, part_floats, cus, &ln);
+  }
+  hipError_t e = gemm_nt_mfma_launch(g, kF32, s, part, part_floats);
+  if (e == hipSuccess) e = ln_launch(ln, dtype, s);
+  return e;
 }
 
 }  // namespace l3

@@ -314,6 +314,9 @@ hipError_t center_split_launch(const int32_t* header, const uint16_t* W,
 hipError_t gemm_nt_256_quad_launch(const GemmArgs& g, hipStream_t s);
 hipError_t ln_rows_launch(const LnRowsArgs& a, hipStream_t s);
 hipError_t ln_launch(const LnArgs& a, int dtype, hipStream_t s);
+// u = A B^T (float32, into ln.U unless fused), then LayerNorm rows into ln.h
+hipError_t gemm_ln_launch(const GemmArgs& g, const LnArgs& ln, int dtype,
+                          hipStream_t s, float* part, int64_t part_floats);
 
 struct BwdArgs {
   const int32_t* header;
