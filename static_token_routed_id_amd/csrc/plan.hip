@@ -11,8 +11,9 @@
 // The sort key is (id, position), unique, so every correct sort gives the
 // same permutation. Two implementations:
 //   * batches up to 4096 tokens: one 1024-thread workgroup, bitonic sort of
-//     64-bit keys in LDS, then segment cut and work-item count in the same
-//     launch (one launch: decode-sized batches are latency bound);
+//     64-bit keys in LDS, then segment cut, work-item count and (without
+//     group items) the wave items' map in the same launch (one launch:
+//     decode-sized batches are latency bound);
 //   * larger batches: LSD radix sort of the 32-bit ids with the position as
 //     payload (stable, 8- or 9-bit digits; per digit a histogram of each
 //     1024-key tile, then a ranked scatter whose workgroups take their
@@ -174,7 +175,23 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
     pd.header[3] = gtotal;
     pd.header[8] = atotal;
   }
-  (void)s_total;
+  // Without group items (the group kernel is off at these sizes) the wave
+  // items' map is the only one, and it is written here, one wave per
+  // segment as item_map_kernel does, which saves that launch; nothing is
+  // written for a plan with a bad id or row count (as there).
+  if (p.group_min_rows == 0) {
+    __syncthreads();  // every segment's item start is written
+    if (tid == 0) s_total = atomicAdd(&pd.header[0], 0);
+    __syncthreads();
+    if (s_total == 0) {
+      const int lane = tid & 63;
+      for (int g = tid >> 6; g < S; g += 1024 / 64) {
+        const int w0 = pd.seg_item_start[g], w1 = pd.seg_item_start[g + 1];
+        for (int i = w0 + lane; i < w1; i += 64)
+          pd.item_map[i] = make_int2(g, i - w0);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- large ---
@@ -547,8 +564,9 @@ hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
   const int B = p.B;
   if (B <= kSmallPlanMax) {
     plan_small_kernel<<<1, 1024, 0, s>>>(pd, p);
-    item_map_kernel<<<item_map_grid(B), 256, 0, s>>>(pd, p.group_min_rows > 0,
-                                                  hitem_cap(B));
+    // (without group items the small plan writes the item map itself)
+    if (p.group_min_rows > 0)
+      item_map_kernel<<<item_map_grid(B), 256, 0, s>>>(pd, 1, hitem_cap(B));
     return hipGetLastError();
   }
   const int nblk = ceil_div(B, kSortTile);
