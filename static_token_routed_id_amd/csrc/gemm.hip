@@ -906,7 +906,7 @@ __device__ __forceinline__ void step_w8(floatx16 (&acc)[MI][2],
   }
 }
 
-template <typename TC, bool FOLD, int MI>
+template <typename TC, bool FOLD, int MI, bool STATS = false>
 __global__ __launch_bounds__(512, 1) void gemm_nt_256w8_kernel(GemmArgs g) {
   constexpr int TM = 64 * MI;  // tile rows
   __shared__ __align__(16) uint16_t lds[2][2][kTM * kTL];
@@ -1099,6 +1099,54 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_256w8_kernel(GemmArgs g) {
           __builtin_nontemporal_store(
               f2bf(acc[i][j][e]), reinterpret_cast<uint16_t*>(crow) + j * 32);
       }
+    }
+  }
+  if constexpr (STATS) {
+    // LayerNorm fold (producer): each tile row's sum and sum of squares over
+    // the tile's 256 columns (the float32 accumulators) as (mean, M2 = sum
+    // of squares - sum * mean; one pass, exact to float32 rounding while
+    // |mean| / std stays well below 2^12). The 128 lane sums of a row (32
+    // lanes x 4 column waves) meet in the operand LDS as [slot][row] (row
+    // stride padded by 4 floats: each float4 write of 4 rows falls in its
+    // own banks); one thread a row adds them up in slot order.
+    constexpr int kSP = TM + 4;
+    float* sp = reinterpret_cast<float*>(&lds[0][0][0]);
+    float* sq = sp + 128 * kSP;
+    static_assert(2 * 128 * kSP * 4 <= sizeof(lds),
+                  "row-sum slots exceed the operand LDS");
+    __syncthreads();  // every wave is done with the operand buffers
+    const int wo = (wn * 32 + r) * kSP + wm * 32 * MI + h4;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int eg = 0; eg < 4; ++eg) {
+        float4 v, w2;
+        float* vp = reinterpret_cast<float*>(&v);
+        float* wp = reinterpret_cast<float*>(&w2);
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) {
+          const float x0 = acc[i][0][4 * eg + ee], x1 = acc[i][1][4 * eg + ee];
+          vp[ee] = x0 + x1;
+          wp[ee] = fmaf(x0, x0, x1 * x1);
+        }
+        *reinterpret_cast<float4*>(sp + wo + i * 32 + 8 * eg) = v;
+        *reinterpret_cast<float4*>(sq + wo + i * 32 + 8 * eg) = w2;
+      }
+    __syncthreads();
+    if (tid < TM) {
+      float sum = 0.f, sum2 = 0.f;
+#pragma unroll 16
+      for (int sl = 0; sl < 128; ++sl) {
+        sum += sp[sl * kSP + tid];
+        sum2 += sq[sl * kSP + tid];
+      }
+      const float mean = sum * (1.0f / kTN);
+      const float m2 = fmaxf(sum2 - sum * mean, 0.f);
+      if (m0 + tid < g.M)
+        reinterpret_cast<float2*>(g.ln_stats_out)[static_cast<int64_t>(m0 +
+                                                                   tid) *
+                                                      nt + n_tile] =
+            make_float2(mean, m2);
     }
   }
 }
@@ -1702,6 +1750,13 @@ hipError_t gemm_nt_mfma_launch(const GemmArgs& g, int c_type, hipStream_t s,
     // the LayerNorm fold (consumer side) has its own instantiation
     if (c_type == kBF16 && g.ln_rows)
       gemm_nt_256_kernel<uint16_t, true><<<grid, 256, 0, s>>>(g);
+    else if (c_type == kBF16 && g.ln_stats_out && !g.ln_quad_a &&
+             g.nsplit == 1 && grid < cus)
+      // the fold's producer with too few 256-row tiles: 128-row tiles
+      gemm_nt_256w8_kernel<uint16_t, false, 2, true><<<
+          static_cast<int>(static_cast<int64_t>(ceil_div(g.M, 128)) *
+                           (g.N / kTN)),
+          512, 0, s>>>(g);
     else if (c_type == kBF16)
       gemm_nt_256_kernel<uint16_t, false><<<grid, 256, 0, s>>>(g);
     else if (g.ln_rows && g.nsplit == 1 && !g.ln_stats_out && grid < cus)
