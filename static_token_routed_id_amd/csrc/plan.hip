@@ -10,6 +10,8 @@
 //
 // The sort key is (id, position), unique, so every correct sort gives the
 // same permutation. Two implementations:
+//   * batches up to 64 tokens (decode): one wavefront, the sort, the
+//     segments and the item map by cross-lane operations (no barrier);
 //   * batches up to 4096 tokens: one 1024-thread workgroup, bitonic sort of
 //     64-bit keys in LDS, then segment cut, work-item count and (without
 //     group items) the wave items' map in the same launch (one launch:
@@ -70,6 +72,89 @@ __device__ __forceinline__ int aitems_of(int m, int n, const PlanParams& p) {
 __device__ __forceinline__ int gitems_of(int m, int n, const PlanParams& p) {
   if (!is_group(n, p)) return 0;
   return m > kGroupTok ? ceil_div(m, kHotTok) : 1;
+}
+
+// ----------------------------------------------------------------- tiny ---
+// Batches of at most 64 tokens without group items (decode): the whole plan
+// on one wavefront, token i on lane i, with no workgroup barrier: bitonic
+// sort of the (id, position) keys across the lanes by shuffles, segment
+// starts from a ballot of id changes, the wave items' exclusive scan by
+// shuffles, and each segment's lane writes its segment and its items' map.
+constexpr int kTinyPlanMax = 64;
+__global__ __launch_bounds__(64) void plan_tiny_kernel(PlanDev pd,
+                                                       PlanParams p) {
+  const int lane = threadIdx.x;
+  const int B = p.B;
+  if (lane < kHeaderInts) pd.header[lane] = 0;
+  __threadfence();  // the zeroed status word precedes the checks' atomics
+  unsigned long long key = ~0ull;
+  if (lane < B) {
+    const int t = p.ids[lane];
+    if (t < 0 || t >= p.vocab) atomicOr(&pd.header[0], kBadId);
+    key = (static_cast<unsigned long long>(static_cast<uint32_t>(t)) << 32) |
+          static_cast<uint32_t>(lane);
+  }
+  // bitonic sort, ascending (padding keys ~0 sort last)
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const unsigned long long other = __shfl_xor(key, stride);
+      const bool up = (lane & size) == 0;
+      const bool low = (lane & stride) == 0;
+      const unsigned long long mn = key < other ? key : other;
+      const unsigned long long mx = key < other ? other : key;
+      key = (low == up) ? mn : mx;
+    }
+  }
+  const int t = static_cast<int>(key >> 32);
+  const int tprev = __shfl_up(t, 1);
+  const bool start = lane < B && (lane == 0 || t != tprev);
+  if (lane < B) {
+    pd.perm[lane] = static_cast<int>(key & 0xffffffffu);
+    pd.sorted_ids[lane] = t;
+  }
+  const unsigned long long starts = __ballot(start);
+  const int S = __popcll(starts);
+  const unsigned long long below = (1ull << lane) - 1;
+  const int sidx = __popcll(starts & below);  // segment of a start lane
+  // tokens of the segment starting here: up to the next start, or B
+  const unsigned long long after = lane < 63 ? starts >> (lane + 1) : 0ull;
+  const int next = after ? lane + 1 + __ffsll(after) - 1 : B;
+  int n = 1, items = 0;
+  if (start) {
+    int64_t r0;
+    id_rows(p, t, &r0, &n, pd.header);
+    pd.seg_id[sidx] = t;
+    pd.seg_tok_start[sidx] = lane;
+    pd.seg_row_off[sidx] = r0;
+    pd.seg_n[sidx] = n;
+    items = aitems_of(next - lane, n, p);
+  }
+  const int incl = wave_incl_scan(items, lane);
+  const int total = __shfl(incl, 63);
+  const int w0 = incl - items;
+  if (start) {
+    pd.seg_item_start[sidx] = w0;
+    pd.seg_gitem_start[sidx] = 0;
+  }
+  if (lane == 0) {
+    pd.seg_tok_start[S] = B;
+    pd.seg_item_start[S] = total;
+    pd.seg_gitem_start[S] = 0;
+    pd.header[1] = S;
+    pd.header[2] = total;
+    pd.header[3] = 0;
+    pd.header[8] = total;
+  }
+  // the items' map, unless an id or a row count was bad (as item_map_kernel)
+  __threadfence();  // every check's atomic precedes the read
+  int bad = 0;
+  if (lane == 0) bad = atomicAdd(&pd.header[0], 0);
+  bad = __shfl(bad, 0);
+  if (bad == 0 && start)
+    for (int i = 0; i < items; ++i)
+      pd.item_map[w0 + i] = make_int2(sidx, i);
 }
 
 // ---------------------------------------------------------------- small ---
@@ -562,6 +647,10 @@ static int id_bits(int64_t vocab) {
 hipError_t plan_launch(const PlanDev& pd, const PlanParams& p,
                        hipStream_t s) {
   const int B = p.B;
+  if (B <= kTinyPlanMax && p.group_min_rows == 0) {
+    plan_tiny_kernel<<<1, 64, 0, s>>>(pd, p);
+    return hipGetLastError();
+  }
   if (B <= kSmallPlanMax) {
     plan_small_kernel<<<1, 1024, 0, s>>>(pd, p);
     // (without group items the small plan writes the item map itself)

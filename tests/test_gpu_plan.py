@@ -62,6 +62,16 @@ ADVERSARIAL = {
     "all_distinct_large": lambda: (
         np.random.default_rng(2).permutation(40000).astype(np.int32), 40000),
     "max_id_only": lambda: (np.full(17, 99, np.int32), 100),
+    # batches of at most 64 tokens (the one-wavefront plan)
+    "two_tokens_same": lambda: (np.array([9, 9], np.int32), 50),
+    "two_tokens_reversed": lambda: (np.array([30, 2], np.int32), 50),
+    "all_same_64": lambda: (np.full(64, 3, np.int32), 50),
+    "reverse_sorted_64": lambda: (np.arange(64)[::-1].astype(np.int32).copy(),
+                                  64),
+    "repeats_33": lambda: (
+        np.random.default_rng(12).integers(0, 5, 33).astype(np.int32), 5),
+    "ragged_63": lambda: (
+        np.random.default_rng(13).integers(0, 40, 63).astype(np.int32), 40),
     "presorted_large": lambda: (
         np.sort(np.random.default_rng(3).integers(0, 5000, 30000))
         .astype(np.int32), 5000),
@@ -96,7 +106,7 @@ def test_plan_hot_id_at_cap():
     _plan_and_compare(ids, offsets, vocab, k_max=512)
 
 
-@pytest.mark.parametrize("B", [100, 12000])
+@pytest.mark.parametrize("B", [50, 100, 12000])
 def test_plan_errors(B):
     torch = gu.torch_cuda()
     L = gu.lib()
