@@ -73,17 +73,29 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(CombineArgs a) {
   const int nch = ceil_div(n_rows, a.chunk_rows);
   if (nch <= 1) return;
   const int64_t slot0 = static_cast<int64_t>(pos) * a.nch_max;
-  // chunk weights w_c = e^(m_c - M) / L, all chunks' loads issued together
+  // chunk weights w_c = e^(m_c - M) / L, all chunks' loads issued together;
+  // with d_e <= 512 the chunks' partial rows (four columns a lane in each
+  // 256-column block) are loaded in the same burst, before the weights
+  // are known (chunks past nch and columns past d_e re-read chunk 0 /
+  // column 0, inside the buffer, and are never used)
   float m[kMaxChunks], l[kMaxChunks], w[kMaxChunks];
+  constexpr int kPB = 2;
+  const bool pre = a.d_e <= kPB * 256;
+  float4 pv[kMaxChunks][kPB];
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) {
-    m[c] = -INFINITY;
-    l[c] = 0.f;
-    if (c < nch) {
-      const float2 v =
-          *reinterpret_cast<const float2*>(a.part_ml + (slot0 + c) * 2);
-      m[c] = v.x;
-      l[c] = v.y;
+    const int cc = c < nch ? c : 0;
+    const float2 v =
+        *reinterpret_cast<const float2*>(a.part_ml + (slot0 + cc) * 2);
+    m[c] = c < nch ? v.x : -INFINITY;
+    l[c] = c < nch ? v.y : 0.f;
+    if (pre) {
+#pragma unroll
+      for (int b = 0; b < kPB; ++b) {
+        const int e = b * 256 + lane * 4;
+        pv[c][b] = *reinterpret_cast<const float4*>(
+            a.part + (slot0 + cc) * a.d_e + (e < a.d_e ? e : 0));
+      }
     }
   }
   float M = -INFINITY;
@@ -97,6 +109,35 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(CombineArgs a) {
   }
   const float invL = 1.0f / L;
   const int64_t orig = a.perm[pos];
+  auto emit = [&](int e, const float4& acc) __attribute__((always_inline)) {
+    const float o[4] = {acc.x * invL, acc.y * invL, acc.z * invL,
+                        acc.w * invL};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      st<T>(static_cast<T*>(a.a_out), orig * a.d_e + e + q, o[q]);
+      if (a.a_save) a.a_save[orig * a.d_e + e + q] = o[q];
+    }
+  };
+  if (pre) {
+#pragma unroll
+    for (int b = 0; b < kPB; ++b) {
+      const int e = b * 256 + lane * 4;
+      if (e < a.d_e) {
+        float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) {
+          if (c < nch) {
+            acc.x = fmaf(pv[c][b].x, w[c], acc.x);
+            acc.y = fmaf(pv[c][b].y, w[c], acc.y);
+            acc.z = fmaf(pv[c][b].z, w[c], acc.z);
+            acc.w = fmaf(pv[c][b].w, w[c], acc.w);
+          }
+        }
+        emit(e, acc);
+      }
+    }
+    return;
+  }
   // 4 columns a lane, the chunks' partial rows loaded together
   for (int e = lane * 4; e < a.d_e; e += 256) {
     float4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -111,13 +152,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(CombineArgs a) {
         acc.w = fmaf(v.w, w[c], acc.w);
       }
     }
-    const float o[4] = {acc.x * invL, acc.y * invL, acc.z * invL,
-                        acc.w * invL};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      st<T>(static_cast<T*>(a.a_out), orig * a.d_e + e + q, o[q]);
-      if (a.a_save) a.a_save[orig * a.d_e + e + q] = o[q];
-    }
+    emit(e, acc);
   }
 }
 
