@@ -42,6 +42,13 @@ CASES = [
     ("bf16_8193_two_passes", "bf16", 20000, 1.0, 1 << 17, 512, 512, 256,
      8193, 1 / 32, 1 / 16, 512),
     ("f32_one_token", "f32", 300, 1.0, 3000, 32, 64, 64, 1, 1 / 8, 1 / 8, 32),
+    # decode-sized batches at other hidden widths: the one-wavefront plan,
+    # the few-rows GEMMs, W_up's K shares summed by the LayerNorm row pass
+    # (one and four 256-column chunks a wave) and the one-burst combine
+    ("bf16_d1024_decode_40", "bf16", 4000, 1.0, 1 << 15, 256, 1024, 256, 40,
+     1 / 32, 1 / 16, 256),
+    ("bf16_d4096_decode_17", "bf16", 500, 1.0, 1 << 12, 64, 4096, 512, 17,
+     1 / 64, 1 / 16, 64),
 ]
 # small enough for the oracle's full backward
 BACKWARD = ("f32_cap7", "bf16_d192_de128", "f32_de192", "f32_one_token")
