@@ -1,8 +1,9 @@
 """GPU plan (sort by id + segments) against the oracle, bit for bit.
 
-Covers both device paths: the single-workgroup sort (up to 4096 tokens) and
-the multi-kernel radix sort (larger batches, 1 to 3 digit passes), with
-batches on both sides of the boundary."""
+Covers every device path: the one-wavefront plan (up to 64 tokens), the
+single-workgroup bitonic sort (up to 4096 tokens) and the multi-kernel radix
+sort (larger batches, 1 to 3 digit passes of 8 or 9 bits), with batches on
+both sides of each boundary."""
 import numpy as np
 import pytest
 
@@ -78,6 +79,17 @@ ADVERSARIAL = {
     "reverse_sorted_large": lambda: (
         np.sort(np.random.default_rng(4).integers(0, 5000, 30000))[::-1]
         .astype(np.int32).copy(), 5000),
+    # 4097 .. 8192 tokens: the radix sort on few tiles
+    "all_same_8192": lambda: (np.full(8192, 7, np.int32), 50),
+    "reverse_sorted_7777": lambda: (
+        np.sort(np.random.default_rng(14).integers(0, 5000, 7777))[::-1]
+        .astype(np.int32).copy(), 5000),
+    "three_digit_passes_8000": lambda: (
+        np.random.default_rng(15).integers(0, 1 << 20, 8000)
+        .astype(np.int32), 1 << 20),
+    "two_nine_bit_passes_6001": lambda: (
+        np.random.default_rng(16).integers(0, 1 << 17, 6001)
+        .astype(np.int32), 1 << 17),
     "ragged_8193": lambda: (
         np.random.default_rng(5).integers(0, 3000, 8193).astype(np.int32),
         3000),
@@ -106,7 +118,7 @@ def test_plan_hot_id_at_cap():
     _plan_and_compare(ids, offsets, vocab, k_max=512)
 
 
-@pytest.mark.parametrize("B", [50, 100, 12000])
+@pytest.mark.parametrize("B", [50, 100, 6000, 12000])
 def test_plan_errors(B):
     torch = gu.torch_cuda()
     L = gu.lib()
