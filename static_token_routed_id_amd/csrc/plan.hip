@@ -80,17 +80,20 @@ __device__ __forceinline__ int gitems_of(int m, int n, const PlanParams& p) {
 // sort of the (id, position) keys across the lanes by shuffles, segment
 // starts from a ballot of id changes, the wave items' exclusive scan by
 // shuffles, and each segment's lane writes its segment and its items' map.
+// The id and row-count checks are ballots, so the status is known in
+// registers: the header is written once at the end, and the kernel waits
+// on global memory only for the ids and for the row ranges.
 constexpr int kTinyPlanMax = 64;
+static_assert(kHeaderInts <= 64, "one lane a header word");
 __global__ __launch_bounds__(64) void plan_tiny_kernel(PlanDev pd,
                                                        PlanParams p) {
   const int lane = threadIdx.x;
   const int B = p.B;
-  if (lane < kHeaderInts) pd.header[lane] = 0;
-  __threadfence();  // the zeroed status word precedes the checks' atomics
   unsigned long long key = ~0ull;
+  bool bad_id = false;
   if (lane < B) {
     const int t = p.ids[lane];
-    if (t < 0 || t >= p.vocab) atomicOr(&pd.header[0], kBadId);
+    bad_id = t < 0 || t >= p.vocab;
     key = (static_cast<unsigned long long>(static_cast<uint32_t>(t)) << 32) |
           static_cast<uint32_t>(lane);
   }
@@ -122,15 +125,28 @@ __global__ __launch_bounds__(64) void plan_tiny_kernel(PlanDev pd,
   const unsigned long long after = lane < 63 ? starts >> (lane + 1) : 0ull;
   const int next = after ? lane + 1 + __ffsll(after) - 1 : B;
   int n = 1, items = 0;
+  bool bad_count = false;
   if (start) {
-    int64_t r0;
-    id_rows(p, t, &r0, &n, pd.header);
+    // the id's rows (a bad id keeps row 0 and one row, as the other plans)
+    int64_t r0 = 0;
+    if (t >= 0 && t < p.vocab) {
+      const int64_t a = p.offsets[t], b = p.offsets[t + 1];
+      const int64_t c = b - a;
+      if (c < 1 || c > p.k_max || a < 0 || b > p.rows) {
+        bad_count = true;
+      } else {
+        r0 = a;
+        n = static_cast<int>(c);
+      }
+    }
     pd.seg_id[sidx] = t;
     pd.seg_tok_start[sidx] = lane;
     pd.seg_row_off[sidx] = r0;
     pd.seg_n[sidx] = n;
     items = aitems_of(next - lane, n, p);
   }
+  const int status = (__ballot(bad_id) ? kBadId : 0) |
+                     (__ballot(bad_count) ? kBadCount : 0);
   const int incl = wave_incl_scan(items, lane);
   const int total = __shfl(incl, 63);
   const int w0 = incl - items;
@@ -142,17 +158,15 @@ __global__ __launch_bounds__(64) void plan_tiny_kernel(PlanDev pd,
     pd.seg_tok_start[S] = B;
     pd.seg_item_start[S] = total;
     pd.seg_gitem_start[S] = 0;
-    pd.header[1] = S;
-    pd.header[2] = total;
-    pd.header[3] = 0;
-    pd.header[8] = total;
   }
+  // status, segment and item counts; every queue and other count zero
+  if (lane < kHeaderInts)
+    pd.header[lane] = lane == 0                 ? status
+                      : lane == 1               ? S
+                      : lane == 2 || lane == 8  ? total
+                                                : 0;
   // the items' map, unless an id or a row count was bad (as item_map_kernel)
-  __threadfence();  // every check's atomic precedes the read
-  int bad = 0;
-  if (lane == 0) bad = atomicAdd(&pd.header[0], 0);
-  bad = __shfl(bad, 0);
-  if (bad == 0 && start)
+  if (status == 0 && start)
     for (int i = 0; i < items; ++i)
       pd.item_map[w0 + i] = make_int2(sidx, i);
 }
