@@ -118,7 +118,7 @@ def test_plan_hot_id_at_cap():
     _plan_and_compare(ids, offsets, vocab, k_max=512)
 
 
-@pytest.mark.parametrize("B", [50, 100, 6000, 12000])
+@pytest.mark.parametrize("B", [50, 64, 100, 6000, 12000])
 def test_plan_errors(B):
     torch = gu.torch_cuda()
     L = gu.lib()
@@ -137,6 +137,9 @@ def test_plan_errors(B):
         (np.where(np.arange(B) == 1, -1, 3), L.L3_ERR_TOKEN_RANGE),
         (np.where(np.arange(B) == 7, 10, 3), L.L3_ERR_COUNT),
         (np.where(np.arange(B) == 5, 20, 3), L.L3_ERR_COUNT),
+        # both kinds at once: the id range is reported first, on every path
+        (np.where(np.arange(B) == B - 1, vocab + 5,
+                  np.where(np.arange(B) == 7, 10, 3)), L.L3_ERR_TOKEN_RANGE),
         (rng.integers(0, 10, B), L.L3_OK),
     ]
     for ids, want in cases:
