@@ -176,19 +176,21 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
                                                           PlanParams p) {
   __shared__ unsigned long long keys[kSmallPlanMax];
   __shared__ int tmp[1024 / 64 + 1];
-  __shared__ int s_total;
+  // the checks' verdict (kBadId | kBadCount), gathered in LDS; the header
+  // is written once, after the scans
+  __shared__ int s_status;
   const int tid = threadIdx.x;
   const int B = p.B;
   int B2 = 1;
   while (B2 < B) B2 <<= 1;
-  if (tid < kHeaderInts) pd.header[tid] = 0;
+  if (tid == 0) s_status = 0;
   __syncthreads();
 
   for (int i = tid; i < B2; i += 1024) {
     unsigned long long k = ~0ull;
     if (i < B) {
       int t = p.ids[i];
-      if (t < 0 || t >= p.vocab) atomicOr(&pd.header[0], kBadId);
+      if (t < 0 || t >= p.vocab) atomicOr(&s_status, kBadId);
       k = (static_cast<unsigned long long>(static_cast<uint32_t>(t)) << 32) |
           static_cast<uint32_t>(i);
     }
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
     if (j == 0 || t != static_cast<int>(keys[j - 1] >> 32)) {
       int64_t r0;
       int n;
-      id_rows(p, t, &r0, &n, pd.header);
+      id_rows(p, t, &r0, &n, &s_status);
       pd.seg_id[s] = t;
       pd.seg_tok_start[s] = j;
       pd.seg_row_off[s] = r0;
@@ -238,10 +240,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
       ++s;
     }
   }
-  if (tid == 0) {
-    pd.seg_tok_start[S] = B;
-    pd.header[1] = S;
-  }
+  if (tid == 0) pd.seg_tok_start[S] = B;
   __syncthreads();
   // work items per segment (wave items and group items), exclusive scans
   const int sper = ceil_div(S, 1024);
@@ -270,19 +269,24 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
     pd.seg_item_start[S] = total;
     pd.seg_gitem_start[S] = gtotal;
     if (p.group_min_rows > 0) pd.seg_aitem_start[S] = atotal;
-    pd.header[2] = total;
-    pd.header[3] = gtotal;
-    pd.header[8] = atotal;
   }
+  // status (every check precedes the scans' barriers), segment and item
+  // counts; every queue and other count zero
+  const int status = s_status;
+  if (tid < kHeaderInts)
+    pd.header[tid] = tid == 0                ? status
+                     : tid == 1              ? S
+                     : tid == 2              ? total
+                     : tid == 3              ? gtotal
+                     : tid == 8              ? atotal
+                                             : 0;
   // Without group items (the group kernel is off at these sizes) the wave
   // items' map is the only one, and it is written here, one wave per
   // segment as item_map_kernel does, which saves that launch; nothing is
   // written for a plan with a bad id or row count (as there).
   if (p.group_min_rows == 0) {
     __syncthreads();  // every segment's item start is written
-    if (tid == 0) s_total = atomicAdd(&pd.header[0], 0);
-    __syncthreads();
-    if (s_total == 0) {
+    if (status == 0) {
       const int lane = tid & 63;
       for (int g = tid >> 6; g < S; g += 1024 / 64) {
         const int w0 = pd.seg_item_start[g], w1 = pd.seg_item_start[g + 1];
