@@ -9,13 +9,14 @@
 // between 1 and k rows, which the plan checks for every id that occurs.
 //
 // The sort key is (id, position), unique, so every correct sort gives the
-// same permutation. Two implementations:
+// same permutation. Three implementations:
 //   * batches up to 64 tokens (decode): one wavefront, the sort, the
 //     segments and the item map by cross-lane operations (no barrier);
 //   * batches up to 4096 tokens: one 1024-thread workgroup, bitonic sort of
-//     64-bit keys in LDS, then segment cut, work-item count and (without
-//     group items) the wave items' map in the same launch (one launch:
-//     decode-sized batches are latency bound);
+//     64-bit keys (up to 1024 tokens one key a thread in registers, the
+//     partners in a wavefront by shuffles; above, in LDS), then segment
+//     cut, work-item count and (without group items) the wave items' map
+//     in the same launch (one launch: such batches are latency bound);
 //   * larger batches: LSD radix sort of the 32-bit ids with the position as
 //     payload (stable, 8- or 9-bit digits; per digit a histogram of each
 //     1024-key tile, then a ranked scatter whose workgroups take their
@@ -186,31 +187,66 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(PlanDev pd,
   if (tid == 0) s_status = 0;
   __syncthreads();
 
-  for (int i = tid; i < B2; i += 1024) {
-    unsigned long long k = ~0ull;
-    if (i < B) {
-      int t = p.ids[i];
+  if (B2 <= 1024) {
+    // one key a thread: bitonic sort, ascending, in registers; partners
+    // within the wavefront (stride < 64) by shuffles, the others through
+    // LDS (padding keys ~0 sort last)
+    unsigned long long key = ~0ull;
+    if (tid < B) {
+      const int t = p.ids[tid];
       if (t < 0 || t >= p.vocab) atomicOr(&s_status, kBadId);
-      k = (static_cast<unsigned long long>(static_cast<uint32_t>(t)) << 32) |
-          static_cast<uint32_t>(i);
+      key = (static_cast<unsigned long long>(static_cast<uint32_t>(t))
+             << 32) |
+            static_cast<uint32_t>(tid);
     }
-    keys[i] = k;
-  }
-  __syncthreads();
-  // bitonic sort, ascending
-  for (int size = 2; size <= B2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (B2 >> 1); i += 1024) {
-        int lo = 2 * i - (i & (stride - 1));
-        int hi = lo + stride;
-        bool up = (lo & size) == 0;
-        unsigned long long a = keys[lo], b = keys[hi];
-        if ((a > b) == up) {
-          keys[lo] = b;
-          keys[hi] = a;
+    for (int size = 2; size <= B2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        unsigned long long other;
+        if (stride >= 64) {
+          if (tid < B2) keys[tid] = key;
+          __syncthreads();
+          other = tid < B2 ? keys[tid ^ stride] : key;
+          __syncthreads();
+        } else {
+          other = __shfl_xor(key, stride);
         }
+        const bool up = (tid & size) == 0;
+        const bool low = (tid & stride) == 0;
+        const unsigned long long mn = key < other ? key : other;
+        const unsigned long long mx = key < other ? other : key;
+        key = (low == up) ? mn : mx;
       }
-      __syncthreads();
+    }
+    if (tid < B2) keys[tid] = key;
+    __syncthreads();
+  } else {
+    for (int i = tid; i < B2; i += 1024) {
+      unsigned long long k = ~0ull;
+      if (i < B) {
+        int t = p.ids[i];
+        if (t < 0 || t >= p.vocab) atomicOr(&s_status, kBadId);
+        k = (static_cast<unsigned long long>(static_cast<uint32_t>(t))
+             << 32) |
+            static_cast<uint32_t>(i);
+      }
+      keys[i] = k;
+    }
+    __syncthreads();
+    // bitonic sort, ascending, in LDS
+    for (int size = 2; size <= B2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < (B2 >> 1); i += 1024) {
+          int lo = 2 * i - (i & (stride - 1));
+          int hi = lo + stride;
+          bool up = (lo & size) == 0;
+          unsigned long long a = keys[lo], b = keys[hi];
+          if ((a > b) == up) {
+            keys[lo] = b;
+            keys[hi] = a;
+          }
+        }
+        __syncthreads();
+      }
     }
   }
   // perm, sorted ids; segment flags scanned in contiguous chunks per thread

@@ -1,7 +1,8 @@
 """GPU plan (sort by id + segments) against the oracle, bit for bit.
 
 Covers every device path: the one-wavefront plan (up to 64 tokens), the
-single-workgroup bitonic sort (up to 4096 tokens) and the multi-kernel radix
+single-workgroup bitonic sort (up to 4096 tokens: in registers with one key
+a thread up to 1024, in LDS above) and the multi-kernel radix
 sort (larger batches, 1 to 3 digit passes of 8 or 9 bits), with batches on
 both sides of each boundary."""
 import numpy as np
@@ -79,6 +80,16 @@ ADVERSARIAL = {
     "reverse_sorted_large": lambda: (
         np.sort(np.random.default_rng(4).integers(0, 5000, 30000))[::-1]
         .astype(np.int32).copy(), 5000),
+    # 65 .. 1024 tokens (the single-workgroup sort with one key a thread)
+    "ragged_65": lambda: (
+        np.random.default_rng(17).integers(0, 30, 65).astype(np.int32), 30),
+    "ragged_513": lambda: (
+        np.random.default_rng(18).integers(0, 700, 513).astype(np.int32),
+        700),
+    "reverse_sorted_1000": lambda: (
+        np.sort(np.random.default_rng(19).integers(0, 400, 1000))[::-1]
+        .astype(np.int32).copy(), 400),
+    "all_same_1024": lambda: (np.full(1024, 11, np.int32), 50),
     # 4097 .. 8192 tokens: the radix sort on few tiles
     "all_same_8192": lambda: (np.full(8192, 7, np.int32), 50),
     "reverse_sorted_7777": lambda: (
